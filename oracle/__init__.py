@@ -1,0 +1,198 @@
+"""Plain CPU oracle for top-k sparse decode attention over a paged KV cache.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  It shares no code
+with the HIP library: the arithmetic lives in ``oracle.c`` (plain C, built with
+``-O2 -ffp-contract=off``), and this module only marshals numpy arrays into it.
+
+Functions and the passages they follow:
+
+* :func:`score` -- every cached token scored through the page table ("Add
+  TriAttention KV-cache compression method", Key Design Decisions: direct
+  paged-pool scoring; for the DSA indexer mode see "Overlap DSA heuristic
+  prev_topk write-back on the aux stream", Description).
+* :func:`topk` -- full sort by (score desc, index asc), the deterministic tie
+  settlement of "Add TriAttention ...", Summary / Test Plan.
+* :func:`attention` -- float64 softmax attention over the selected rows, the
+  eager golden reference of "Add DSA Vanilla sparse attention", Walkthrough.
+* :func:`local_to_global` -- the global index conversion of "Unify sparse
+  attention framework with clean backend interfaces", Dev Engineer Review.
+
+Parity pins (tests/test_oracle_pins.py) tie each function to closed forms,
+brute force, a library routine (SDPA) and invariants; see the test module.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+F32, BF16 = 0, 1
+GROUP_SUM, GROUP_MEAN, RELU_WEIGHTED = 0, 1, 2
+_MODES = {"group_sum": GROUP_SUM, "group_mean": GROUP_MEAN, "relu_weighted": RELU_WEIGHTED}
+_ERRORS = {1: "bad argument", 2: "page id out of range", 3: "NaN score", 4: "index out of range"}
+
+CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-std=c11"]
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so next to it (gcc, plain C)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", *CFLAGS, "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+class _Pool(ctypes.Structure):
+    _fields_ = [
+        ("data", ctypes.c_void_p),
+        ("dtype", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_stride", ctypes.c_int64),
+        ("head_stride", ctypes.c_int64),
+        ("token_stride", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB_PATH)
+        P, I32, I64, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+        PP = ctypes.POINTER(_Pool)
+        lib.orc_score.argtypes = [P, I32, P, I32, PP, P, I32, I32, P, I32, F, P, I32]
+        lib.orc_topk.argtypes = [P, I32, I32, I32, P, I32, P, P]
+        lib.orc_attention.argtypes = [P, I32, P, I32, P, I32, I32, PP, PP, I32, P, I32, F, P]
+        lib.orc_local_to_global.argtypes = [P, I32, I32, I32, I32, P, I32, I32, P]
+        for f in (lib.orc_score, lib.orc_topk, lib.orc_attention, lib.orc_local_to_global):
+            f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise ValueError(f"oracle {what}: {_ERRORS.get(rc, rc)}")
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError(f"oracle takes float32 or bfloat16 bits (uint16), got {a.dtype}")
+
+
+@dataclass
+class PoolView:
+    """A paged pool in host memory.  ``data`` is a numpy array (float32 or
+    uint16 bfloat16 bits); its shape is [num_pages, num_kv_heads, page_size,
+    head_dim] in any memory order, the element strides are taken from it."""
+
+    data: np.ndarray
+
+    def struct(self) -> _Pool:
+        a = self.data
+        if a.ndim != 4:
+            raise ValueError("pool must be 4-D [pages, kv_heads, page_size, head_dim]")
+        es = a.itemsize
+        st = [s // es for s in a.strides]
+        if st[3] != 1:
+            raise ValueError("pool rows must be contiguous")
+        return _Pool(a.ctypes.data, _dtype_code(a), a.shape[0], a.shape[2], a.shape[1],
+                     a.shape[3], st[0], st[1], st[2])
+
+
+def _c(a: np.ndarray, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def score(block_table, kv_lens, k_pool: np.ndarray, q: np.ndarray, weights, mode: int,
+          head_scale: float, row_len: int) -> np.ndarray:
+    """Scores [batch, num_kv_heads, row_len] float32 (-inf past kv_len)."""
+    lib = _load()
+    bt = _c(block_table, np.int32)
+    kl = _c(kv_lens, np.int32)
+    pool = PoolView(k_pool).struct()
+    qa = np.ascontiguousarray(q)
+    batch, q_heads = qa.shape[0], qa.shape[1]
+    w = None if weights is None else _c(weights, np.float32)
+    mode = _MODES[mode] if isinstance(mode, str) else int(mode)
+    out = np.empty((batch, k_pool.shape[1], row_len), dtype=np.float32)
+    rc = lib.orc_score(bt.ctypes.data, bt.shape[1], kl.ctypes.data, batch, ctypes.byref(pool),
+                       qa.ctypes.data, _dtype_code(qa), q_heads,
+                       None if w is None else w.ctypes.data, mode, float(head_scale),
+                       out.ctypes.data, row_len)
+    _check(rc, "score")
+    return out
+
+
+def topk(scores: np.ndarray, kv_lens, k: int):
+    """Returns (indices [batch, groups, k] int32, counts [batch, groups] int32)."""
+    lib = _load()
+    s = _c(scores, np.float32)
+    kl = _c(kv_lens, np.int32)
+    batch, groups, row_len = s.shape
+    idx = np.empty((batch, groups, k), dtype=np.int32)
+    cnt = np.empty((batch, groups), dtype=np.int32)
+    rc = lib.orc_topk(s.ctypes.data, batch, groups, row_len, kl.ctypes.data, k,
+                      idx.ctypes.data, cnt.ctypes.data)
+    _check(rc, "topk")
+    return idx, cnt
+
+
+def attention(block_table, kv_lens, q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
+              v_dim: int, indices: np.ndarray, scale: float) -> np.ndarray:
+    """Float64 output [batch, q_heads, v_dim]."""
+    lib = _load()
+    bt = _c(block_table, np.int32)
+    kl = _c(kv_lens, np.int32)
+    qa = np.ascontiguousarray(q)
+    kp, vp = PoolView(k_pool).struct(), PoolView(v_pool).struct()
+    ind = _c(indices, np.int32)
+    batch, q_heads = qa.shape[0], qa.shape[1]
+    out = np.empty((batch, q_heads, v_dim), dtype=np.float64)
+    rc = lib.orc_attention(bt.ctypes.data, bt.shape[1], kl.ctypes.data, batch, qa.ctypes.data,
+                           _dtype_code(qa), q_heads, ctypes.byref(kp), ctypes.byref(vp), v_dim,
+                           ind.ctypes.data, ind.shape[2], float(scale), out.ctypes.data)
+    _check(rc, "attention")
+    return out
+
+
+def local_to_global(block_table, page_size: int, num_pages: int, local: np.ndarray) -> np.ndarray:
+    lib = _load()
+    bt = _c(block_table, np.int32)
+    loc = _c(local, np.int32)
+    batch, groups, k = loc.shape
+    out = np.empty(loc.shape, dtype=np.int64)
+    rc = lib.orc_local_to_global(bt.ctypes.data, bt.shape[1], batch, page_size, num_pages,
+                                 loc.ctypes.data, groups, k, out.ctypes.data)
+    _check(rc, "local_to_global")
+    return out
+
+
+def sparse_decode(w) -> dict:
+    """The whole path on a workload object (see top_sparse_decode_amd.synth):
+    score -> top-k -> attention.  Returns scores, indices, counts and the
+    float64 output."""
+    s = score(w.block_table, w.kv_lens, w.score_k, w.score_q, w.head_weights, w.mode,
+              w.head_scale, w.max_kv_len)
+    idx, cnt = topk(s, w.kv_lens, w.topk)
+    out = attention(w.block_table, w.kv_lens, w.q, w.k, w.v, w.v_dim, idx, w.softmax_scale)
+    return {"scores": s, "indices": idx, "counts": cnt, "out": out}

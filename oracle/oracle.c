@@ -1,0 +1,297 @@
+/*
+ * oracle.c -- plain, slow, obviously correct CPU oracle for top-k sparse
+ * decode attention over a paged KV cache.
+ *
+ * TEST INFRASTRUCTURE ONLY (see oracle.h): used by the tests, the smoke check
+ * and the benchmark's CPU-baseline leg, never by the product path.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fno-fast-math -fPIC -shared.  Every float
+ * expression below is written one rounding per operation; with contraction
+ * off and SSE arithmetic on x86-64 that is exactly what executes.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ helpers */
+
+/* bfloat16 is the upper 16 bits of a binary32: widening is exact. */
+static float bf16_bits_to_float(uint16_t b) {
+  uint32_t u = ((uint32_t)b) << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+static float load_elem(const void* base, int32_t dtype, int64_t off) {
+  if (dtype == ORC_F32) return ((const float*)base)[off];
+  return bf16_bits_to_float(((const uint16_t*)base)[off]);
+}
+
+/* Logical token t of request b lives in physical page block_table[b][t/P] at
+ * slot t%P ("Unify sparse attention framework ...", Dev Engineer Review: the
+ * global index conversion goes through block_table with a page-range check).
+ * Returns the element offset of the first element of that row for KV head g,
+ * or -1 when the page id is outside [0, num_pages). */
+static int64_t row_offset(const orc_pool* p, const int32_t* block_table, int32_t max_pages,
+                          int32_t b, int32_t g, int32_t t) {
+  int32_t lp = t / p->page_size;
+  int32_t slot = t % p->page_size;
+  if (lp >= max_pages) return -1;
+  int32_t page = block_table[(int64_t)b * max_pages + lp];
+  if (page < 0 || page >= p->num_pages) return -1;
+  return (int64_t)page * p->page_stride + (int64_t)g * p->head_stride +
+         (int64_t)slot * p->token_stride;
+}
+
+/* q . k accumulated in binary32 in ascending d, each product and each sum
+ * rounded on its own:  (((+0 + q0*k0) + q1*k1) + ...) + q_{D-1}*k_{D-1}.
+ * (For bfloat16 operands every product is exact in binary32.) */
+static float dot_f32_sequential(const float* qv, const float* kv, int32_t D) {
+  float acc = 0.0f;
+  for (int32_t d = 0; d < D; ++d) {
+    float prod = qv[d] * kv[d];
+    acc = acc + prod;
+  }
+  return acc;
+}
+
+/* ------------------------------------------------------------------ scores */
+
+/* Scoring of every cached token through the page table ("Add TriAttention
+ * KV-cache compression method", Key Design Decisions: direct paged-pool
+ * scoring; Summary: per-head scores are then reduced to one score per KV
+ * head).  Modes:
+ *   GROUP_SUM      s = sum_h (dot_h * head_scale),  h ascending
+ *   GROUP_MEAN     s = (sum_h dot_h) * (1/G),       h ascending
+ *   RELU_WEIGHTED  s = sum_h (w_h * max(dot_h, +0)), h ascending
+ * The last one is the DSA indexer score: a ReLU-weighted sum over the indexer
+ * heads of q_I,h . k_I, with one indexer key row per token shared by all
+ * indexer heads ("Overlap DSA heuristic prev_topk write-back on the aux
+ * stream", Description: the indexer produces each decode step's top-k). */
+int orc_score(const int32_t* block_table, int32_t max_pages, const int32_t* kv_lens,
+              int32_t batch, const orc_pool* k, const void* q, int32_t q_dtype,
+              int32_t q_heads, const float* weights, int32_t mode, float head_scale,
+              float* scores, int32_t row_len) {
+  if (!block_table || !kv_lens || !k || !k->data || !q || !scores) return ORC_EARG;
+  if (batch < 0 || max_pages < 0 || row_len < 0 || q_heads <= 0) return ORC_EARG;
+  const int32_t Hkv = k->num_kv_heads, D = k->head_dim;
+  if (Hkv <= 0 || D <= 0 || k->page_size <= 0 || q_heads % Hkv != 0) return ORC_EARG;
+  if (mode == ORC_RELU_WEIGHTED && !weights) return ORC_EARG;
+  if (mode < ORC_GROUP_SUM || mode > ORC_RELU_WEIGHTED) return ORC_EARG;
+  const int32_t G = q_heads / Hkv;
+  const float inv_g = (float)(1.0 / (double)G);
+
+  float* qf = (float*)malloc(sizeof(float) * (size_t)q_heads * (size_t)D);
+  float* kf = (float*)malloc(sizeof(float) * (size_t)D);
+  if (!qf || !kf) { free(qf); free(kf); return ORC_EARG; }
+
+  int rc = ORC_OK;
+  for (int32_t b = 0; b < batch && rc == ORC_OK; ++b) {
+    int32_t L = kv_lens[b];
+    if (L < 0 || L > row_len || L > max_pages * k->page_size) { rc = ORC_EARG; break; }
+    for (int32_t i = 0; i < q_heads * D; ++i)
+      qf[i] = load_elem(q, q_dtype, (int64_t)b * q_heads * D + i);
+    for (int32_t g = 0; g < Hkv && rc == ORC_OK; ++g) {
+      float* row = scores + ((int64_t)b * Hkv + g) * row_len;
+      for (int32_t t = 0; t < row_len; ++t) row[t] = -INFINITY;
+      for (int32_t t = 0; t < L; ++t) {
+        int64_t off = row_offset(k, block_table, max_pages, b, g, t);
+        if (off < 0) { rc = ORC_EPAGE; break; }
+        for (int32_t d = 0; d < D; ++d) kf[d] = load_elem(k->data, k->dtype, off + d);
+        float s = 0.0f;
+        for (int32_t j = 0; j < G; ++j) {
+          int32_t h = g * G + j;
+          float dh = dot_f32_sequential(qf + (int64_t)h * D, kf, D);
+          if (mode == ORC_GROUP_SUM) {
+            float term = dh * head_scale;
+            s = s + term;
+          } else if (mode == ORC_GROUP_MEAN) {
+            s = s + dh;
+          } else {
+            float r = dh > 0.0f ? dh : 0.0f;
+            float term = weights[(int64_t)b * q_heads + h] * r;
+            s = s + term;
+          }
+        }
+        if (mode == ORC_GROUP_MEAN) s = s * inv_g;
+        row[t] = s;
+      }
+    }
+  }
+  free(qf);
+  free(kf);
+  return rc;
+}
+
+/* ------------------------------------------------------------------ top-k */
+
+typedef struct {
+  float s;
+  int32_t t;
+} scored_tok;
+
+/* (score descending, token index ascending); IEEE comparison, so -0 == +0. */
+static int cmp_rank(const void* a, const void* b) {
+  const scored_tok* x = (const scored_tok*)a;
+  const scored_tok* y = (const scored_tok*)b;
+  if (x->s > y->s) return -1;
+  if (x->s < y->s) return 1;
+  return (x->t < y->t) ? -1 : (x->t > y->t);
+}
+
+static int cmp_int(const void* a, const void* b) {
+  int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+  return (x > y) - (x < y);
+}
+
+/* Selection of the k best tokens per row with deterministic tie settlement:
+ * a full sort by (score descending, index ascending), lowest index first
+ * among equal scores ("Add TriAttention KV-cache compression method", Summary:
+ * TopK / tie settlement; Test Plan: deterministic heavy-tie settlement).  A row
+ * with kv_len <= k keeps every token (the dense-equivalent case).  The kept
+ * set is emitted in ascending token order and padded with -1; counts gets the
+ * number kept, the per-request selected length the attention op consumes
+ * ("Unify sparse attention framework ...", Description: the runtime carries
+ * indices plus per-request lengths to the attention op). */
+int orc_topk(const float* scores, int32_t batch, int32_t groups, int32_t row_len,
+             const int32_t* kv_lens, int32_t k, int32_t* indices, int32_t* counts) {
+  if (!scores || !kv_lens || !indices || batch < 0 || groups <= 0 || row_len < 0 || k <= 0)
+    return ORC_EARG;
+  scored_tok* buf = (scored_tok*)malloc(sizeof(scored_tok) * (size_t)(row_len > 0 ? row_len : 1));
+  int32_t* keep = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+  if (!buf || !keep) { free(buf); free(keep); return ORC_EARG; }
+  int rc = ORC_OK;
+  for (int32_t b = 0; b < batch && rc == ORC_OK; ++b) {
+    int32_t L = kv_lens[b];
+    if (L < 0 || L > row_len) { rc = ORC_EARG; break; }
+    for (int32_t g = 0; g < groups; ++g) {
+      const float* row = scores + ((int64_t)b * groups + g) * row_len;
+      for (int32_t t = 0; t < L; ++t) {
+        if (isnan(row[t])) { rc = ORC_ENAN; break; }
+        buf[t].s = row[t];
+        buf[t].t = t;
+      }
+      if (rc != ORC_OK) break;
+      qsort(buf, (size_t)L, sizeof(scored_tok), cmp_rank);
+      int32_t n = L < k ? L : k;
+      for (int32_t i = 0; i < n; ++i) keep[i] = buf[i].t;
+      qsort(keep, (size_t)n, sizeof(int32_t), cmp_int);
+      int32_t* out = indices + ((int64_t)b * groups + g) * k;
+      for (int32_t i = 0; i < k; ++i) out[i] = i < n ? keep[i] : -1;
+      if (counts) counts[(int64_t)b * groups + g] = n;
+    }
+  }
+  free(buf);
+  free(keep);
+  return rc;
+}
+
+/* ------------------------------------------------------------------ attention */
+
+/* Softmax attention of every query head over its KV head's selected rows, in
+ * float64 throughout: x_t = scale * sum_d q_d k_td, p_t = exp(x_t - max x),
+ * o = sum_t p_t v_t / sum_t p_t.  This is the eager golden reference's
+ * selected-token attention ("Add DSA Vanilla sparse attention", Walkthrough:
+ * it rebuilds each request's logical cache and performs selected-token
+ * attention).  For sparse MLA the value row is the leading v_dim elements of
+ * the same latent row. */
+int orc_attention(const int32_t* block_table, int32_t max_pages, const int32_t* kv_lens,
+                  int32_t batch, const void* q, int32_t q_dtype, int32_t q_heads,
+                  const orc_pool* k, const orc_pool* v, int32_t v_dim,
+                  const int32_t* indices, int32_t k_sel, float scale, double* out) {
+  if (!block_table || !kv_lens || !q || !k || !v || !k->data || !v->data || !indices || !out)
+    return ORC_EARG;
+  const int32_t Hkv = k->num_kv_heads, D = k->head_dim;
+  if (batch < 0 || q_heads <= 0 || Hkv <= 0 || q_heads % Hkv != 0 || k_sel <= 0) return ORC_EARG;
+  if (v->num_kv_heads != Hkv || v_dim <= 0 || v_dim > v->head_dim) return ORC_EARG;
+  if (v->page_size != k->page_size) return ORC_EARG;
+  const int32_t G = q_heads / Hkv;
+
+  double* x = (double*)malloc(sizeof(double) * (size_t)k_sel);
+  int64_t* koff = (int64_t*)malloc(sizeof(int64_t) * (size_t)k_sel);
+  int64_t* voff = (int64_t*)malloc(sizeof(int64_t) * (size_t)k_sel);
+  double* acc = (double*)malloc(sizeof(double) * (size_t)v_dim);
+  if (!x || !koff || !voff || !acc) { free(x); free(koff); free(voff); free(acc); return ORC_EARG; }
+
+  int rc = ORC_OK;
+  for (int32_t b = 0; b < batch && rc == ORC_OK; ++b) {
+    int32_t L = kv_lens[b];
+    for (int32_t g = 0; g < Hkv && rc == ORC_OK; ++g) {
+      const int32_t* sel = indices + ((int64_t)b * Hkv + g) * k_sel;
+      int32_t n = 0;
+      for (int32_t i = 0; i < k_sel; ++i) {
+        int32_t t = sel[i];
+        if (t < 0) continue;
+        if (t >= L) { rc = ORC_EINDEX; break; }
+        int64_t ko = row_offset(k, block_table, max_pages, b, g, t);
+        int64_t vo = row_offset(v, block_table, max_pages, b, g, t);
+        if (ko < 0 || vo < 0) { rc = ORC_EPAGE; break; }
+        koff[n] = ko;
+        voff[n] = vo;
+        ++n;
+      }
+      if (rc != ORC_OK) break;
+      for (int32_t j = 0; j < G; ++j) {
+        int32_t h = g * G + j;
+        double* o = out + ((int64_t)b * q_heads + h) * v_dim;
+        if (n == 0) {
+          for (int32_t d = 0; d < v_dim; ++d) o[d] = 0.0;
+          continue;
+        }
+        int64_t qo = ((int64_t)b * q_heads + h) * D;
+        double m = -INFINITY;
+        for (int32_t i = 0; i < n; ++i) {
+          double s = 0.0;
+          for (int32_t d = 0; d < D; ++d)
+            s += (double)load_elem(q, q_dtype, qo + d) *
+                 (double)load_elem(k->data, k->dtype, koff[i] + d);
+          x[i] = (double)scale * s;
+          if (x[i] > m) m = x[i];
+        }
+        double l = 0.0;
+        for (int32_t d = 0; d < v_dim; ++d) acc[d] = 0.0;
+        for (int32_t i = 0; i < n; ++i) {
+          double p = exp(x[i] - m);
+          l += p;
+          for (int32_t d = 0; d < v_dim; ++d)
+            acc[d] += p * (double)load_elem(v->data, v->dtype, voff[i] + d);
+        }
+        for (int32_t d = 0; d < v_dim; ++d) o[d] = acc[d] / l;
+      }
+    }
+  }
+  free(x);
+  free(koff);
+  free(voff);
+  free(acc);
+  return rc;
+}
+
+/* ------------------------------------------------------------------ indices */
+
+/* Global index conversion: request-local position -> pool slot through the
+ * block table, invalid (-1) for a negative position or a page outside the
+ * pool ("Unify sparse attention framework ...", Dev Engineer Review). */
+int orc_local_to_global(const int32_t* block_table, int32_t max_pages, int32_t batch,
+                        int32_t page_size, int32_t num_pages, const int32_t* local,
+                        int32_t groups, int32_t k, int64_t* global_out) {
+  if (!block_table || !local || !global_out || batch < 0 || groups <= 0 || k <= 0 ||
+      page_size <= 0 || max_pages < 0)
+    return ORC_EARG;
+  for (int32_t b = 0; b < batch; ++b)
+    for (int32_t g = 0; g < groups; ++g)
+      for (int32_t i = 0; i < k; ++i) {
+        int64_t idx = ((int64_t)b * groups + g) * k + i;
+        int32_t t = local[idx];
+        int64_t r = -1;
+        if (t >= 0 && t / page_size < max_pages) {
+          int32_t page = block_table[(int64_t)b * max_pages + t / page_size];
+          if (page >= 0 && page < num_pages) r = (int64_t)page * page_size + t % page_size;
+        }
+        global_out[idx] = r;
+      }
+  return ORC_OK;
+}

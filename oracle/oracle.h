@@ -1,0 +1,98 @@
+/*
+ * oracle.h -- plain CPU oracle for top-k sparse decode attention over a paged
+ * KV cache.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link or
+ * call this code; only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code, header or constant with the HIP
+ * library: every definition here is written out again from the statement of
+ * the method.
+ *
+ * What it computes (each function below cites the passage it follows):
+ *   1. scores   -- every cached token of every request is scored through the
+ *                  page table ("Add TriAttention KV-cache compression method",
+ *                  Key Design Decisions: the scorer reads paged K directly
+ *                  through a page-table snapshot);
+ *   2. top-k    -- a full sort by (score descending, token index ascending):
+ *                  deterministic tie settlement ("Add TriAttention ...", Summary
+ *                  and Test Plan);
+ *   3. attention-- exact softmax attention over the selected rows of each
+ *                  request's logical cache, in float64 ("Add DSA Vanilla sparse
+ *                  attention", Walkthrough: the eager golden reference that
+ *                  rebuilds each request's logical cache and attends over the
+ *                  selected tokens).
+ *
+ * Floating point: compiled with -O2 -ffp-contract=off and without
+ * -ffast-math, so every written float operation rounds separately (IEEE-754
+ * binary32, round to nearest even, no flush to zero).
+ */
+#ifndef TSD_ORACLE_H
+#define TSD_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+#define ORC_F32 0   /* IEEE binary32                                  */
+#define ORC_BF16 1  /* bfloat16 bits stored as uint16 (upper half of f32) */
+
+/* score modes */
+#define ORC_GROUP_SUM 0      /* s = sum_{h in group} (dot_h * head_scale)       */
+#define ORC_GROUP_MEAN 1     /* s = (sum_{h in group} dot_h) * (1/G)            */
+#define ORC_RELU_WEIGHTED 2  /* s = sum_{h in group} (w_h * max(dot_h, +0))     */
+
+/* error codes */
+#define ORC_OK 0
+#define ORC_EARG 1      /* bad argument (null pointer, bad size)            */
+#define ORC_EPAGE 2     /* a referenced page id is outside [0, num_pages)   */
+#define ORC_ENAN 3      /* a score that takes part in selection is NaN      */
+#define ORC_EINDEX 4    /* a selected index is outside [0, kv_len)          */
+
+typedef struct {
+  const void* data;  /* host memory                                          */
+  int32_t dtype;     /* ORC_F32 or ORC_BF16                                  */
+  int32_t num_pages, page_size, num_kv_heads, head_dim;
+  int64_t page_stride, head_stride, token_stride;  /* in elements            */
+} orc_pool;
+
+/* Scores for every (request b, KV head g, token t < kv_lens[b]); entries
+ * t >= kv_lens[b] of a row are set to -inf.  q is [batch][q_heads][head_dim],
+ * query head h belongs to KV head h / (q_heads / num_kv_heads).  weights is
+ * [batch][q_heads] (RELU_WEIGHTED only).  scores is [batch][num_kv_heads][row_len]. */
+int orc_score(const int32_t* block_table, int32_t max_pages, const int32_t* kv_lens,
+              int32_t batch, const orc_pool* k, const void* q, int32_t q_dtype,
+              int32_t q_heads, const float* weights, int32_t mode, float head_scale,
+              float* scores, int32_t row_len);
+
+/* Top-k of each row over t < kv_lens[b]: the min(k, kv_len) tokens that come
+ * first in (score descending, index ascending) order, written in ascending
+ * token order and padded with -1.  indices is [batch][groups][k], counts is
+ * [batch][groups] (may be NULL). */
+int orc_topk(const float* scores, int32_t batch, int32_t groups, int32_t row_len,
+             const int32_t* kv_lens, int32_t k, int32_t* indices, int32_t* counts);
+
+/* Softmax attention over the selected rows, float64.  q is
+ * [batch][q_heads][qk_dim] (qk_dim == k->head_dim), the value row is the first
+ * v_dim elements of the v pool row (v may describe the same memory as k).
+ * indices is [batch][num_kv_heads][k_sel] of request-local token positions,
+ * -1 entries are skipped.  out is [batch][q_heads][v_dim]; a head with no
+ * selected row gets zeros. */
+int orc_attention(const int32_t* block_table, int32_t max_pages, const int32_t* kv_lens,
+                  int32_t batch, const void* q, int32_t q_dtype, int32_t q_heads,
+                  const orc_pool* k, const orc_pool* v, int32_t v_dim,
+                  const int32_t* indices, int32_t k_sel, float scale, double* out);
+
+/* Request-local token position -> flat pool slot page*page_size + t%page_size,
+ * or -1 when the position is negative, past the table, or names a page outside
+ * [0, num_pages).  local is [batch][groups][k], global the same shape. */
+int orc_local_to_global(const int32_t* block_table, int32_t max_pages, int32_t batch,
+                        int32_t page_size, int32_t num_pages, const int32_t* local,
+                        int32_t groups, int32_t k, int64_t* global_out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
