@@ -1,0 +1,204 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark: top-k sparse decode attention, DSA sparse MLA at
+64K context (batch 16, 64x128 bf16 indexer, page 64, top-k 2048, 128 heads
+over a 576-wide latent row), on one MI355X.
+
+One step = one sd_sparse_decode call over the whole batch: score every
+cached token, select the top 2048 per request, attend over them.  Inputs are
+seeded synthetic tensors of that shape, resident in HBM before timing; the
+pools are replicated and the replicas rotated step by step so the scored
+indexer keys (268 MB per replica) do not sit in the 256 MB last-level cache.
+
+Prints one JSON line.  Algorithmic bytes per step = indexer K bytes scored
++ selected latent rows gathered.  The roofline entry is for the dominant
+kernel (the MFMA indexer scorer), timed with HIP events on its own stream.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse decode steps/s + achieved HBM GB/s, DSA-MLA 64K ctx top-k 2048"
+PEAK_HBM_GBPS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+SCORER_SOURCE = os.path.join(ROOT, "top_sparse_decode_amd", "csrc", "score.hip")
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--replicas", type=int, default=3, help="input replicas rotated per step")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-requests", type=int, default=3, help="requests in the oracle sample")
+    return p.parse_args()
+
+
+def scorer_traffic(kernel_hash: str):
+    """HBM bytes per scorer launch from the committed rocprofv3 counter
+    summary, or None when it is missing or was taken on another version of
+    the scorer source."""
+    path = os.path.join(PROFILES, "score_dsa_mfma_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except Exception:
+        return None
+    if d.get("source_sha256") != kernel_hash:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards by "
+              "request across GPUs with no exchange, see DESIGN.md.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from top_sparse_decode_amd import api, synth
+
+    torch.cuda.set_device(0)
+    dev = "cuda:0"
+    say("[bench] generating dsa_mla workload (B16, L65536) ...")
+    t0 = time.time()
+    w = synth.make_workload(4)
+    say(f"[bench] generated in {time.time() - t0:.1f}s; uploading {args.replicas} replicas")
+    steps = [api.prepare(w, precision=api.FAST, device=dev) for _ in range(max(1, args.replicas))]
+    torch.cuda.synchronize()
+
+    B, L, P = w.batch, int(w.kv_lens[0]), w.page_size
+    k_scored = B * L * w.score_k.shape[-1] * 2            # bytes of indexer K read
+    k_gathered = B * w.topk * w.k.shape[-1] * 2           # selected latent rows (V is inside them)
+    alg_bytes = k_scored + k_gathered
+
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        steps[i % len(steps)].run(stream)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K whole steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        steps[i % len(steps)].run(stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / args.steps
+    steps_per_s = 1000.0 / ms_step
+    say(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step")
+
+    # ---- dominant kernel: the MFMA indexer scorer, events around each launch
+    groups = 1
+    sc = torch.empty((B, groups, w.max_kv_len), dtype=torch.float32, device=dev)
+    bound = torch.empty((B, groups), dtype=torch.float32, device=dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for i in range(min(args.warmup, 5)):
+        s = steps[i % len(steps)]
+        api.sparse_score_paged(s.args.pages, s.args.score_k, s.score_q, 64, s.head_weights,
+                               api.RELU_WEIGHTED, 1.0, api.FAST, sc, bound, stream)
+    for i in range(args.steps):
+        s = steps[i % len(steps)]
+        ev[i][0].record(stream)
+        api.sparse_score_paged(s.args.pages, s.args.score_k, s.score_q, 64, s.head_weights,
+                               api.RELU_WEIGHTED, 1.0, api.FAST, sc, bound, stream)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    durs = sorted(a.elapsed_time(b) for a, b in ev)
+    score_ms = sum(durs) / len(durs)
+    score_gbps = k_scored / (score_ms * 1e-3) / 1e9
+    src_hash = hashlib.sha256(open(SCORER_SOURCE, "rb").read()).hexdigest()
+
+    result = {
+        "metric": METRIC,
+        "value": round(steps_per_s, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 pools, U(0,1) head weights)",
+        "config": {
+            "workload": "dsa_mla: batch 16, one decode query each, kv_len 65536, page 64, "
+                        "indexer 64 heads x 128 bf16 (ReLU-weighted), top-k 2048, sparse MLA "
+                        "128 heads over 576-dim latent rows (V = first 512), scale 1/sqrt(192)",
+            "batch": B, "kv_len": L, "page_size": P, "topk": w.topk,
+            "precision": "fast scores + exact band re-score (indices exact)",
+            "input_replicas": args.replicas,
+        },
+        "algorithmic_bytes_per_step": alg_bytes,
+        "step_gbps": round(alg_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "step_frac_of_hbm_peak": round(alg_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "roofline": {
+            "kernel": "score_dsa_mfma_kernel<4>",
+            "bound": "hbm",
+            "achieved": round(score_gbps, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(score_gbps / PEAK_HBM_GBPS, 4),
+            "traffic": scorer_traffic(src_hash),
+            "avg_launch_us": round(score_ms * 1e3, 2),
+            "median_launch_us": round(durs[len(durs) // 2] * 1e3, 2),
+            "bytes_per_launch": k_scored,
+        },
+    }
+
+    # ---- CPU baseline: the oracle on a bounded sample, plus a parity check
+    if not args.no_cpu_baseline:
+        import oracle
+        n = max(1, min(args.cpu_requests, B))
+        reqs = list(range(n))
+        import dataclasses
+
+        ws = dataclasses.replace(w, block_table=w.block_table[reqs], kv_lens=w.kv_lens[reqs],
+                                 score_q=w.score_q[reqs], head_weights=w.head_weights[reqs],
+                                 q=w.q[reqs])
+        say(f"[bench] oracle on {n} request(s) ...")
+        t0 = time.perf_counter()
+        ref = oracle.sparse_decode(ws)
+        cpu_s = time.perf_counter() - t0
+        per_step = cpu_s / n * B
+        result["cpu_baseline"] = {
+            "value": round(1.0 / per_step, 5),
+            "unit": "steps/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": f"{n} of {B} requests of the same workload (score all 65536 tokens, "
+                      f"full sort, float64 attention), {cpu_s:.1f}s single-threaded, scaled "
+                      f"to a whole step",
+        }
+        s0 = steps[(args.steps - 1) % len(steps)]
+        idx = s0.indices.cpu().numpy()[reqs]
+        got = s0.out.float().cpu().numpy()[reqs].astype(np.float64)
+        err = np.linalg.norm(got - ref["out"], axis=-1) / np.linalg.norm(ref["out"], axis=-1)
+        result["parity_sample"] = {"requests": reqs,
+                                   "indices_equal": bool(np.array_equal(idx, ref["indices"])),
+                                   "max_row_rel_l2": float(err.max())}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

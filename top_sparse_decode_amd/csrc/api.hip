@@ -1,0 +1,470 @@
+// api.hip -- the C ABI of libsparse_decode (declared in
+// include/sparse_decode.h): host-side validation, workspace layout and
+// kernel dispatch.  The library allocates nothing, never synchronizes, and
+// keeps no state between calls, so every entry point can be captured into a
+// HIP graph ("Unify sparse attention framework with clean backend
+// interfaces", Dev Engineer Review: buffer identity and stability under graph
+// capture; "Add TriAttention KV-cache compression method", Key Design
+// Decisions: score scratch reused, sized at the high-water mark).
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "common.h"
+#include "kernels.h"
+#include "sparse_decode.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+sd_status fail(sd_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+sd_status fail(sd_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+sd_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return SD_OK;
+  return fail(SD_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int elem_size(sd_dtype t) { return t == SD_F32 ? 4 : 2; }
+bool dtype_ok(sd_dtype t) { return t == SD_F32 || t == SD_BF16; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
+
+sd_status check_pages(const sd_pages* p, int32_t page_size) {
+  if (!p) return fail(SD_ERR_INVALID_ARGUMENT, "pages is NULL");
+  if (p->batch < 0 || p->max_pages < 0 || p->max_kv_len < 0)
+    return fail(SD_ERR_INVALID_ARGUMENT, "negative batch / max_pages / max_kv_len");
+  if (p->batch > 0 && (!p->block_table || !p->kv_lens))
+    return fail(SD_ERR_INVALID_ARGUMENT, "block_table or kv_lens is NULL");
+  if (p->batch > 0 && p->max_pages == 0 && p->max_kv_len > 0)
+    return fail(SD_ERR_INVALID_ARGUMENT, "max_pages is 0 but max_kv_len > 0");
+  if ((int64_t)p->max_pages * page_size < p->max_kv_len)
+    return fail(SD_ERR_INVALID_ARGUMENT, "max_kv_len %d exceeds max_pages*page_size", p->max_kv_len);
+  return SD_OK;
+}
+
+sd_status check_pool(const sd_pool* k, const char* name) {
+  if (!k) return fail(SD_ERR_INVALID_ARGUMENT, "%s pool is NULL", name);
+  if (!dtype_ok(k->dtype)) return fail(SD_ERR_INVALID_ARGUMENT, "%s: bad dtype", name);
+  if (!k->data) return fail(SD_ERR_INVALID_ARGUMENT, "%s: data is NULL", name);
+  if (k->num_pages <= 0 || k->page_size <= 0 || k->num_kv_heads <= 0 || k->head_dim <= 0)
+    return fail(SD_ERR_INVALID_ARGUMENT, "%s: non-positive size", name);
+  if (k->page_stride < 0 || k->head_stride < 0 || k->token_stride < 0)
+    return fail(SD_ERR_INVALID_ARGUMENT, "%s: negative stride", name);
+  const int es = elem_size(k->dtype);
+  if (!aligned16(k->data) || ((int64_t)k->head_dim * es) % 16 || (k->page_stride * es) % 16 ||
+      (k->head_stride * es) % 16 || (k->token_stride * es) % 16)
+    return fail(SD_ERR_INVALID_ARGUMENT, "%s: rows must be 16-byte aligned", name);
+  return SD_OK;
+}
+
+sd::ScoreArgs make_score_args(const sd_pages* pg, const sd_pool* k, const void* q, int32_t q_heads,
+                              const float* w, sd_score_mode mode, float head_scale, float* scores,
+                              float* row_bound) {
+  sd::ScoreArgs a{};
+  a.block_table = pg->block_table;
+  a.kv_lens = pg->kv_lens;
+  a.batch = pg->batch;
+  a.max_pages = pg->max_pages;
+  a.max_kv_len = pg->max_kv_len;
+  a.k = k->data;
+  a.dtype = k->dtype == SD_F32 ? 0 : 1;
+  a.num_pages = k->num_pages;
+  a.page_size = k->page_size;
+  a.num_kv_heads = k->num_kv_heads;
+  a.head_dim = k->head_dim;
+  a.page_stride = k->page_stride;
+  a.head_stride = k->head_stride;
+  a.token_stride = k->token_stride;
+  a.q = q;
+  a.q_heads = q_heads;
+  a.head_weights = w;
+  a.mode = (int32_t)mode;
+  a.head_scale = head_scale;
+  const int G = q_heads / k->num_kv_heads;
+  a.inv_g = (float)(1.0 / (double)G);
+  a.scores = scores;
+  a.row_bound = row_bound;
+  return a;
+}
+
+// need_ptrs = false for size queries, which check shapes only.
+sd_status check_score(const sd_pages* pg, const sd_pool* k, const void* q, sd_dtype q_dtype,
+                      int32_t q_heads, const float* w, sd_score_mode mode, const float* scores,
+                      bool need_ptrs) {
+  sd_status st = check_pool(k, "score k");
+  if (st != SD_OK) return st;
+  if ((st = check_pages(pg, k->page_size)) != SD_OK) return st;
+  if (q_dtype != k->dtype) return fail(SD_ERR_UNSUPPORTED, "score q dtype must equal the K pool dtype");
+  if (need_ptrs) {
+    if (!q) return fail(SD_ERR_INVALID_ARGUMENT, "score q is NULL");
+    if (!aligned16(q)) return fail(SD_ERR_INVALID_ARGUMENT, "score q must be 16-byte aligned");
+  }
+  if (q_heads <= 0 || q_heads % k->num_kv_heads)
+    return fail(SD_ERR_INVALID_ARGUMENT, "q_heads %d is not a multiple of num_kv_heads %d", q_heads,
+                k->num_kv_heads);
+  if (mode != SD_SCORE_GROUP_SUM && mode != SD_SCORE_GROUP_MEAN && mode != SD_SCORE_RELU_WEIGHTED)
+    return fail(SD_ERR_INVALID_ARGUMENT, "bad score mode %d", (int)mode);
+  if (need_ptrs && mode == SD_SCORE_RELU_WEIGHTED && !w)
+    return fail(SD_ERR_INVALID_ARGUMENT, "RELU_WEIGHTED needs head_weights");
+  if (!sd::score_exact_supported(q_heads / k->num_kv_heads))
+    return fail(SD_ERR_UNSUPPORTED, "query heads per KV head must be 1, 2, 4, 8, 16, 32 or 64");
+  if (need_ptrs && !scores && pg->batch > 0 && pg->max_kv_len > 0)
+    return fail(SD_ERR_INVALID_ARGUMENT, "scores is NULL");
+  return SD_OK;
+}
+
+sd_status run_score(const sd::ScoreArgs& a, sd_score_precision precision, hipStream_t st) {
+  if (precision == SD_SCORE_FAST && sd::score_fast_supported(a)) {
+    if (a.row_bound) {
+      sd_status s = hip_status(sd::launch_fill_f32(a.row_bound, (int64_t)a.batch * a.num_kv_heads, 0.0f, st),
+                               "fill");
+      if (s != SD_OK) return s;
+    }
+    return hip_status(sd::launch_score_fast(a, st), "score_fast");
+  }
+  return hip_status(sd::launch_score_exact(a, st), "score_exact");
+}
+
+// ---------------------------------------------------------------- attention
+
+struct AttnPlan {
+  sd::AttnArgs a;
+  bool mla;
+  size_t ws_bytes;
+};
+
+sd_status plan_attn(const sd_pages* pg, const void* q, sd_dtype q_dtype, int32_t q_heads,
+                    const sd_pool* k, const sd_pool* v, int32_t v_dim, const int32_t* indices,
+                    int32_t k_sel, float scale, void* out, sd_dtype out_dtype, bool need_ptrs,
+                    AttnPlan* plan) {
+  sd_status st;
+  if ((st = check_pool(k, "attention k")) != SD_OK) return st;
+  if ((st = check_pool(v, "attention v")) != SD_OK) return st;
+  if ((st = check_pages(pg, k->page_size)) != SD_OK) return st;
+  if (v->page_size != k->page_size || v->num_kv_heads != k->num_kv_heads)
+    return fail(SD_ERR_INVALID_ARGUMENT, "k and v pools must share page_size and num_kv_heads");
+  if (k->dtype != v->dtype || q_dtype != k->dtype)
+    return fail(SD_ERR_UNSUPPORTED, "q, k and v must have one dtype");
+  if (q_heads <= 0 || q_heads % k->num_kv_heads)
+    return fail(SD_ERR_INVALID_ARGUMENT, "q_heads %d is not a multiple of num_kv_heads", q_heads);
+  if (v_dim <= 0 || v_dim > v->head_dim) return fail(SD_ERR_INVALID_ARGUMENT, "bad v_dim %d", v_dim);
+  if (k_sel <= 0) return fail(SD_ERR_INVALID_ARGUMENT, "k_sel must be >= 1");
+  if (!dtype_ok(out_dtype)) return fail(SD_ERR_INVALID_ARGUMENT, "bad out dtype");
+  if (need_ptrs) {
+    if (!q || !indices || !out) return fail(SD_ERR_INVALID_ARGUMENT, "q, indices or out is NULL");
+    if (!aligned16(q)) return fail(SD_ERR_INVALID_ARGUMENT, "q must be 16-byte aligned");
+  }
+  sd::AttnArgs a{};
+  a.block_table = pg->block_table;
+  a.kv_lens = pg->kv_lens;
+  a.batch = pg->batch;
+  a.max_pages = pg->max_pages;
+  a.max_kv_len = pg->max_kv_len;
+  a.q = q;
+  a.q_heads = q_heads;
+  a.dtype = k->dtype == SD_F32 ? 0 : 1;
+  a.k = k->data;
+  a.k_num_pages = k->num_pages;
+  a.page_size = k->page_size;
+  a.num_kv_heads = k->num_kv_heads;
+  a.head_dim = k->head_dim;
+  a.k_page_stride = k->page_stride;
+  a.k_head_stride = k->head_stride;
+  a.k_token_stride = k->token_stride;
+  a.v = v->data;
+  a.v_num_pages = v->num_pages;
+  a.v_page_stride = v->page_stride;
+  a.v_head_stride = v->head_stride;
+  a.v_token_stride = v->token_stride;
+  a.v_dim = v_dim;
+  a.indices = indices;
+  a.k_sel = k_sel;
+  a.scale = scale;
+  a.out = out;
+  a.out_dtype = out_dtype == SD_F32 ? 0 : 1;
+  const bool mla = sd::attn_mla_supported(a);
+  if (!mla && !sd::attn_vec_supported(a))
+    return fail(SD_ERR_UNSUPPORTED,
+                "attention shape not supported: head_dim %d, v_dim %d, %d query heads per KV head "
+                "(vector path: head_dim 64/128 = v_dim, 1/2/4/8 heads; MLA path: bf16 576/512, "
+                "one shared latent pool, 32/64/128 heads)",
+                k->head_dim, v_dim, q_heads / k->num_kv_heads);
+  a.chunk = sd::attn_rows_per_split(a, mla);
+  a.splits = (k_sel + a.chunk - 1) / a.chunk;
+  const size_t parts = (size_t)pg->batch * q_heads * a.splits;
+  plan->ws_bytes = align_up(parts * (size_t)v_dim * 4) + align_up(parts * 2 * 4);
+  plan->a = a;
+  plan->mla = mla;
+  return SD_OK;
+}
+
+void bind_attn_ws(AttnPlan* p, void* ws) {
+  const size_t parts = (size_t)p->a.batch * p->a.q_heads * p->a.splits;
+  char* base = static_cast<char*>(ws);
+  p->a.part_o = reinterpret_cast<float*>(base);
+  p->a.part_ml = reinterpret_cast<float*>(base + align_up(parts * (size_t)p->a.v_dim * 4));
+}
+
+// ---------------------------------------------------------------- fused plan
+
+struct FusedPlan {
+  sd::ScoreArgs score;
+  bool fast;
+  AttnPlan attn;
+  int32_t groups;
+  size_t off_scores, off_bound, off_thr, off_refined, off_idx, off_attn, total;
+};
+
+sd_status plan_fused(const sd_sparse_decode_args* x, bool need_ptrs, FusedPlan* f) {
+  if (!x) return fail(SD_ERR_INVALID_ARGUMENT, "args is NULL");
+  // the fused call scores into its own workspace: no scores pointer to check
+  static const float kNonNull = 0.0f;
+  sd_status st = check_score(&x->pages, &x->score_k, x->score_q, x->score_q_dtype, x->score_heads,
+                             x->head_weights, x->mode, &kNonNull, need_ptrs);
+  if (st != SD_OK) return st;
+  if (x->topk <= 0) return fail(SD_ERR_INVALID_ARGUMENT, "topk must be >= 1");
+  if (x->precision != SD_SCORE_EXACT && x->precision != SD_SCORE_FAST)
+    return fail(SD_ERR_INVALID_ARGUMENT, "bad precision");
+  if (x->k.page_size != x->score_k.page_size)
+    return fail(SD_ERR_INVALID_ARGUMENT, "score and attention pools must share the page size");
+  if (x->k.num_kv_heads != x->score_k.num_kv_heads)
+    return fail(SD_ERR_INVALID_ARGUMENT, "score and attention pools must have the same KV heads");
+  const int32_t groups = x->score_k.num_kv_heads;
+  // indices come from the selection step (caller buffer or workspace)
+  static const int32_t kIdx = 0;
+  st = plan_attn(&x->pages, x->q, x->q_dtype, x->q_heads, &x->k, &x->v, x->v_dim,
+                 x->indices_out ? x->indices_out : &kIdx, x->topk, x->softmax_scale, x->out,
+                 x->out_dtype, need_ptrs, &f->attn);
+  if (st != SD_OK) return st;
+  f->score = make_score_args(&x->pages, &x->score_k, x->score_q, x->score_heads, x->head_weights,
+                             x->mode, x->head_scale, nullptr, nullptr);
+  f->fast = x->precision == SD_SCORE_FAST && sd::score_fast_supported(f->score);
+  f->groups = groups;
+  const size_t rows = (size_t)x->pages.batch * groups;
+  const size_t sc = align_up(rows * (size_t)x->pages.max_kv_len * 4);
+  size_t off = 0;
+  f->off_scores = off; off += sc;
+  f->off_bound = off; off += align_up(rows * 4);
+  f->off_thr = off; off += align_up(rows * 4);
+  f->off_refined = off; off += f->fast ? sc : 0;
+  f->off_idx = off; off += x->indices_out ? 0 : align_up(rows * (size_t)x->topk * 4);
+  f->off_attn = off; off += f->attn.ws_bytes;
+  f->total = off;
+  return SD_OK;
+}
+
+}  // namespace
+
+// ====================================================================== ABI
+
+extern "C" {
+
+const char* sd_status_string(sd_status s) {
+  switch (s) {
+    case SD_OK: return "ok";
+    case SD_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case SD_ERR_UNSUPPORTED: return "unsupported";
+    case SD_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case SD_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* sd_last_error(void) { return g_err.c_str(); }
+
+int32_t sd_version(void) { return SD_VERSION; }
+
+sd_status sd_sparse_score_paged(const sd_pages* pages, const sd_pool* k_pool, const void* q,
+                                sd_dtype q_dtype, int32_t q_heads, const float* head_weights,
+                                sd_score_mode mode, float head_scale,
+                                sd_score_precision precision, float* scores, float* row_bound,
+                                hipStream_t stream) {
+  g_err.clear();
+  sd_status st = check_score(pages, k_pool, q, q_dtype, q_heads, head_weights, mode, scores, true);
+  if (st != SD_OK) return st;
+  if (precision != SD_SCORE_EXACT && precision != SD_SCORE_FAST)
+    return fail(SD_ERR_INVALID_ARGUMENT, "bad precision");
+  const sd::ScoreArgs a = make_score_args(pages, k_pool, q, q_heads, head_weights, mode, head_scale,
+                                          scores, row_bound);
+  return run_score(a, precision, stream);
+}
+
+sd_status sd_topk_workspace_size(int32_t batch, int32_t groups, int32_t row_stride, int32_t k,
+                                 size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(SD_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  if (batch < 0 || groups <= 0 || row_stride < 0 || k <= 0)
+    return fail(SD_ERR_INVALID_ARGUMENT, "bad sizes");
+  *bytes = 0;
+  return SD_OK;
+}
+
+sd_status sd_topk_select(const float* scores, int32_t batch, int32_t groups, int32_t row_stride,
+                         const int32_t* kv_lens, int32_t k, int32_t* indices, int32_t* counts,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_err.clear();
+  (void)workspace;
+  (void)workspace_bytes;
+  if (batch < 0 || groups <= 0 || row_stride < 0 || k <= 0)
+    return fail(SD_ERR_INVALID_ARGUMENT, "bad sizes (batch %d, groups %d, row_stride %d, k %d)", batch,
+                groups, row_stride, k);
+  if (batch > 0 && (!scores || !kv_lens || !indices))
+    return fail(SD_ERR_INVALID_ARGUMENT, "scores, kv_lens or indices is NULL");
+  sd::TopkArgs a{scores, batch, groups, row_stride, kv_lens, k, indices, counts};
+  return hip_status(sd::launch_topk(a, stream), "topk");
+}
+
+sd_status sd_sparse_decode_attn_workspace_size(const sd_pages* pages, int32_t q_heads,
+                                               const sd_pool* k_pool, int32_t v_dim,
+                                               int32_t k_sel, size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(SD_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  AttnPlan p;
+  sd_status st = plan_attn(pages, nullptr, k_pool ? k_pool->dtype : SD_F32, q_heads, k_pool, k_pool,
+                           v_dim, nullptr, k_sel, 1.0f, nullptr, SD_F32, false, &p);
+  if (st != SD_OK) return st;
+  *bytes = p.ws_bytes;
+  return SD_OK;
+}
+
+sd_status sd_sparse_decode_attn(const sd_pages* pages, const void* q, sd_dtype q_dtype,
+                                int32_t q_heads, const sd_pool* k_pool, const sd_pool* v_pool,
+                                int32_t v_dim, const int32_t* indices, int32_t k_sel,
+                                float softmax_scale, void* out, sd_dtype out_dtype,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_err.clear();
+  AttnPlan p;
+  sd_status st = plan_attn(pages, q, q_dtype, q_heads, k_pool, v_pool, v_dim, indices, k_sel,
+                           softmax_scale, out, out_dtype, true, &p);
+  if (st != SD_OK) return st;
+  if (workspace_bytes < p.ws_bytes || (p.ws_bytes && !workspace))
+    return fail(SD_ERR_WORKSPACE_TOO_SMALL, "attention needs %zu workspace bytes", p.ws_bytes);
+  if (!aligned16(workspace)) return fail(SD_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  bind_attn_ws(&p, workspace);
+  return hip_status(sd::launch_attn(p.a, stream), "attention");
+}
+
+sd_status sd_sparse_decode_workspace_size(const sd_sparse_decode_args* args, size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(SD_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  FusedPlan f;
+  sd_status st = plan_fused(args, false, &f);
+  if (st != SD_OK) return st;
+  *bytes = f.total;
+  return SD_OK;
+}
+
+sd_status sd_sparse_decode(const sd_sparse_decode_args* x, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  g_err.clear();
+  FusedPlan f;
+  sd_status st = plan_fused(x, true, &f);
+  if (st != SD_OK) return st;
+  if (workspace_bytes < f.total || (f.total && !workspace))
+    return fail(SD_ERR_WORKSPACE_TOO_SMALL, "sparse_decode needs %zu workspace bytes", f.total);
+  if (!aligned16(workspace)) return fail(SD_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  if (x->pages.batch == 0) return SD_OK;
+  char* ws = static_cast<char*>(workspace);
+  float* scores = reinterpret_cast<float*>(ws + f.off_scores);
+  float* bound = reinterpret_cast<float*>(ws + f.off_bound);
+  float* thr = reinterpret_cast<float*>(ws + f.off_thr);
+  int32_t* idx = x->indices_out ? x->indices_out : reinterpret_cast<int32_t*>(ws + f.off_idx);
+
+  // 1. score
+  f.score.scores = scores;
+  f.score.row_bound = f.fast ? bound : nullptr;
+  st = run_score(f.score, f.fast ? SD_SCORE_FAST : SD_SCORE_EXACT, stream);
+  if (st != SD_OK) return st;
+  // 2. select
+  sd::TopkArgs t{scores, x->pages.batch, f.groups, x->pages.max_kv_len, x->pages.kv_lens, x->topk,
+                 idx, x->counts_out};
+  if (f.fast) {
+    if ((st = hip_status(sd::launch_topk_threshold(t, thr, stream), "topk_threshold")) != SD_OK) return st;
+    sd::RefineArgs r{};
+    r.score = f.score;
+    r.row_bound = bound;
+    r.thr = thr;
+    r.refined = reinterpret_cast<float*>(ws + f.off_refined);
+    r.k = x->topk;
+    if ((st = hip_status(sd::launch_refine_band(r, stream), "refine")) != SD_OK) return st;
+    t.scores = r.refined;
+  }
+  if ((st = hip_status(sd::launch_topk(t, stream), "topk")) != SD_OK) return st;
+  // 3. attend
+  f.attn.a.indices = idx;
+  bind_attn_ws(&f.attn, ws + f.off_attn);
+  return hip_status(sd::launch_attn(f.attn.a, stream), "attention");
+}
+
+sd_status sd_local_to_global(const sd_pages* pages, int32_t page_size, int32_t num_pages,
+                             const int32_t* local, int32_t groups, int32_t k, int64_t* global_out,
+                             hipStream_t stream) {
+  g_err.clear();
+  if (!pages) return fail(SD_ERR_INVALID_ARGUMENT, "pages is NULL");
+  if (page_size <= 0 || num_pages < 0 || groups <= 0 || k <= 0 || pages->batch < 0 || pages->max_pages < 0)
+    return fail(SD_ERR_INVALID_ARGUMENT, "bad sizes");
+  if (pages->batch > 0 && (!pages->block_table || !local || !global_out))
+    return fail(SD_ERR_INVALID_ARGUMENT, "block_table, local or global_out is NULL");
+  return hip_status(sd::launch_local_to_global(pages->block_table, pages->max_pages, pages->batch, page_size,
+                                               num_pages, local, groups, k, global_out, stream),
+                    "local_to_global");
+}
+
+}  // extern "C"
+
+// ====================================================================== small kernels
+
+namespace sd {
+
+__global__ void fill_f32_kernel(float* p, int64_t n, float v) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  fill_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(p, n, v);
+  return hipGetLastError();
+}
+
+__global__ void local_to_global_kernel(const int32_t* bt, int32_t max_pages, int32_t page_size,
+                                       int32_t num_pages, const int32_t* local, int32_t per_req,
+                                       int64_t total, int64_t* out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int b = (int)(i / per_req);
+  const int t = local[i];
+  int64_t r = -1;
+  if (t >= 0 && t / page_size < max_pages) {
+    const int page = bt[(int64_t)b * max_pages + t / page_size];
+    if (page >= 0 && page < num_pages) r = (int64_t)page * page_size + t % page_size;
+  }
+  out[i] = r;
+}
+
+hipError_t launch_local_to_global(const int32_t* bt, int32_t max_pages, int32_t batch,
+                                  int32_t page_size, int32_t num_pages, const int32_t* local,
+                                  int32_t groups, int32_t k, int64_t* out, hipStream_t st) {
+  const int64_t per_req = (int64_t)groups * k;
+  const int64_t total = (int64_t)batch * per_req;
+  if (total == 0) return hipSuccess;
+  local_to_global_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(
+      bt, max_pages, page_size, num_pages, local, (int32_t)per_req, total, out);
+  return hipGetLastError();
+}
+
+}  // namespace sd

@@ -1,0 +1,88 @@
+// kernels.h -- internal kernel argument blocks and launchers (not part of
+// the public ABI; see include/sparse_decode.h for that).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sd {
+
+struct ScoreArgs {
+  const int32_t* block_table;
+  const int32_t* kv_lens;
+  int32_t batch, max_pages, max_kv_len;
+  const void* k;
+  int32_t dtype;  // 0 f32, 1 bf16 (q has the same type)
+  int32_t num_pages, page_size, num_kv_heads, head_dim;
+  int64_t page_stride, head_stride, token_stride;
+  const void* q;
+  int32_t q_heads;
+  const float* head_weights;
+  int32_t mode;  // 0 group sum, 1 group mean, 2 relu weighted
+  float head_scale;
+  float inv_g;
+  float* scores;     // [batch][num_kv_heads][max_kv_len]
+  float* row_bound;  // [batch][num_kv_heads] or null
+};
+
+struct TopkArgs {
+  const float* scores;
+  int32_t batch, groups, row_stride;
+  const int32_t* kv_lens;
+  int32_t k;
+  int32_t* indices;
+  int32_t* counts;
+};
+
+struct RefineArgs {
+  ScoreArgs score;  // the fast scores in score.scores
+  const float* row_bound;
+  const float* thr;
+  float* refined;   // same shape as the scores
+  int32_t k;
+};
+
+struct AttnArgs {
+  const int32_t* block_table;
+  const int32_t* kv_lens;
+  int32_t batch, max_pages, max_kv_len;
+  const void* q;
+  int32_t q_heads;
+  int32_t dtype;  // q, k, v share it
+  const void* k;
+  int32_t k_num_pages, page_size, num_kv_heads, head_dim;
+  int64_t k_page_stride, k_head_stride, k_token_stride;
+  const void* v;
+  int32_t v_num_pages;
+  int64_t v_page_stride, v_head_stride, v_token_stride;
+  int32_t v_dim;
+  const int32_t* indices;  // [batch][num_kv_heads][k_sel]
+  int32_t k_sel;
+  float scale;
+  int32_t splits, chunk;  // split s covers index slots [s*chunk, (s+1)*chunk)
+  float* part_o;          // [batch][q_heads][splits][v_dim]
+  float* part_ml;         // [batch][q_heads][splits][2]
+  void* out;
+  int32_t out_dtype;
+};
+
+bool score_exact_supported(int G);
+bool score_fast_supported(const ScoreArgs& a);
+hipError_t launch_score_exact(const ScoreArgs& a, hipStream_t st);
+hipError_t launch_score_fast(const ScoreArgs& a, hipStream_t st);
+
+hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+hipError_t launch_topk_threshold(const TopkArgs& a, float* thr, hipStream_t st);
+hipError_t launch_refine_band(const RefineArgs& a, hipStream_t st);
+
+bool attn_mla_supported(const AttnArgs& a);
+bool attn_vec_supported(const AttnArgs& a);
+int attn_rows_per_split(const AttnArgs& a, bool mla);
+hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
+
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t st);
+hipError_t launch_local_to_global(const int32_t* bt, int32_t max_pages, int32_t batch,
+                                  int32_t page_size, int32_t num_pages, const int32_t* local,
+                                  int32_t groups, int32_t k, int64_t* out, hipStream_t st);
+
+}  // namespace sd
