@@ -80,7 +80,10 @@ def test_topk_argument_validation():
     assert f(16, 2, 0, 100, 8, 4, 16, None, None, 0, 0) == api.ERR_INVALID_ARGUMENT
     assert f(None, 0, 1, 100, None, 4, None, None, None, 0, 0) == api.OK
     n = ctypes.c_size_t(7)
-    assert lib.sd_topk_workspace_size(4, 2, 100, 8, ctypes.byref(n)) == api.OK and n.value == 0
+    assert lib.sd_topk_workspace_size(4, 2, 100, 8, ctypes.byref(n)) == api.OK
+    assert n.value >= 4 * 2 * 100 * 4           # one key per score
+    assert f(16, 4, 2, 100, 32, 8, 48, None, 4096, n.value - 1, 0) == api.ERR_WORKSPACE_TOO_SMALL
+    assert f(16, 4, 2, 300000, 32, 8, 48, None, 4096, 1 << 30, 0) == api.ERR_UNSUPPORTED
 
 
 def _attn(k=None, v=None, heads=128, v_dim=512, k_sel=2048, ws_bytes=0, q=16384, idx=20480, out=24576):

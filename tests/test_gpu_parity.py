@@ -116,7 +116,9 @@ def test_topk_select_heavy_ties():
         say(f"[topk ties] k={k}")
         idx = torch.empty((B, G, k), dtype=torch.int32, device="cuda")
         cnt = torch.empty((B, G), dtype=torch.int32, device="cuda")
-        api.topk_select(torch.from_numpy(s).cuda(), B, G, S, torch.from_numpy(kv).cuda(), k, idx, cnt)
+        ws = torch.empty(api.topk_workspace_size(B, G, S, k), dtype=torch.uint8, device="cuda")
+        api.topk_select(torch.from_numpy(s).cuda(), B, G, S, torch.from_numpy(kv).cuda(), k, idx, cnt,
+                        ws, ws.numel())
         torch.cuda.synchronize()
         ref_i, ref_c = oracle.topk(s, kv, k)
         assert np.array_equal(idx.cpu().numpy(), ref_i)
@@ -129,10 +131,37 @@ def test_topk_select_long_rows_random_scores():
     s = rs.standard_normal((B, 1, S)).astype(np.float32) * 30 + 100
     kv = np.array([131072, 99999], np.int32)
     idx = torch.empty((B, 1, 2048), dtype=torch.int32, device="cuda")
-    api.topk_select(torch.from_numpy(s).cuda(), B, 1, S, torch.from_numpy(kv).cuda(), 2048, idx)
+    ws = torch.empty(api.topk_workspace_size(B, 1, S, 2048), dtype=torch.uint8, device="cuda")
+    api.topk_select(torch.from_numpy(s).cuda(), B, 1, S, torch.from_numpy(kv).cuda(), 2048, idx, None,
+                    ws, ws.numel())
     torch.cuda.synchronize()
     ref_i, _ = oracle.topk(s, kv, 2048)
     assert np.array_equal(idx.cpu().numpy(), ref_i)
+
+
+def test_topk_select_edge_rows():
+    # constant rows, rows with -inf (absent) tokens that must fill the quota,
+    # a row of distinct scores with one huge outlier, and a long row past
+    # the register-resident size
+    S = 70000
+    rows = np.zeros((5, 1, S), np.float32)
+    rows[0, 0, :] = 3.5
+    rows[1, 0, :] = -np.inf
+    rows[1, 0, 100:130] = np.arange(30, dtype=np.float32)
+    rows[2, 0, :] = np.random.default_rng(4).standard_normal(S).astype(np.float32)
+    rows[2, 0, 777] = 1e30
+    rows[3, 0, :] = np.random.default_rng(5).integers(0, 3, S).astype(np.float32)
+    rows[4, 0, :] = np.random.default_rng(6).standard_normal(S).astype(np.float32)
+    kv = np.array([S, 5000, S, S, 66000], np.int32)
+    for k in (64, 2048):
+        say(f"[topk edges] k={k}")
+        idx = torch.empty((5, 1, k), dtype=torch.int32, device="cuda")
+        ws = torch.empty(api.topk_workspace_size(5, 1, S, k), dtype=torch.uint8, device="cuda")
+        api.topk_select(torch.from_numpy(rows).cuda(), 5, 1, S, torch.from_numpy(kv).cuda(), k, idx, None,
+                        ws, ws.numel())
+        torch.cuda.synchronize()
+        ref_i, _ = oracle.topk(rows, kv, k)
+        assert np.array_equal(idx.cpu().numpy(), ref_i)
 
 
 @pytest.mark.parametrize("name", ["tiny_f32", "mha_bf16", "gqa_bf16", "dsa"])
@@ -169,6 +198,19 @@ def test_fast_and_exact_agree_and_repeat_bitwise():
     a.run()
     torch.cuda.synchronize()
     assert torch.equal(first.view(torch.int16), a.out.view(torch.int16))
+
+
+def test_fast_path_band_overflow_falls_back_exactly():
+    # Identical indexer keys on one request: every fast score is equal, so the
+    # whole row is one band (far more than the band list holds); selection
+    # must still be the exact one (all-equal exact scores -> lowest positions).
+    w = synth.make_workload(4, batch=2, kv_len=[6000, 5000], topk=2048)
+    P = w.page_size
+    row0 = w.score_k[w.block_table[0, 0], 0, 0].copy()
+    for t in range(6000):
+        w.score_k[w.block_table[0, t // P], 0, t % P] = row0
+    say("[band overflow]")
+    check_fused(w, api.FAST, what="band overflow")
 
 
 def test_empty_request_and_k_one():

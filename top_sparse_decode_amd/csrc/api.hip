@@ -226,7 +226,7 @@ struct FusedPlan {
   bool fast;
   AttnPlan attn;
   int32_t groups;
-  size_t off_scores, off_bound, off_thr, off_refined, off_idx, off_attn, total;
+  size_t off_scores, off_bound, off_keys, off_idx, off_attn, total;
 };
 
 sd_status plan_fused(const sd_sparse_decode_args* x, bool need_ptrs, FusedPlan* f) {
@@ -237,6 +237,8 @@ sd_status plan_fused(const sd_sparse_decode_args* x, bool need_ptrs, FusedPlan* 
                              x->head_weights, x->mode, &kNonNull, need_ptrs);
   if (st != SD_OK) return st;
   if (x->topk <= 0) return fail(SD_ERR_INVALID_ARGUMENT, "topk must be >= 1");
+  if (x->pages.max_kv_len > sd::select_max_row())
+    return fail(SD_ERR_UNSUPPORTED, "max_kv_len above %d tokens", sd::select_max_row());
   if (x->precision != SD_SCORE_EXACT && x->precision != SD_SCORE_FAST)
     return fail(SD_ERR_INVALID_ARGUMENT, "bad precision");
   if (x->k.page_size != x->score_k.page_size)
@@ -259,8 +261,7 @@ sd_status plan_fused(const sd_sparse_decode_args* x, bool need_ptrs, FusedPlan* 
   size_t off = 0;
   f->off_scores = off; off += sc;
   f->off_bound = off; off += align_up(rows * 4);
-  f->off_thr = off; off += align_up(rows * 4);
-  f->off_refined = off; off += f->fast ? sc : 0;
+  f->off_keys = off; off += align_up(sd::select_workspace_bytes((int)rows, x->pages.max_kv_len));
   f->off_idx = off; off += x->indices_out ? 0 : align_up(rows * (size_t)x->topk * 4);
   f->off_attn = off; off += f->attn.ws_bytes;
   f->total = off;
@@ -309,7 +310,7 @@ sd_status sd_topk_workspace_size(int32_t batch, int32_t groups, int32_t row_stri
   if (!bytes) return fail(SD_ERR_INVALID_ARGUMENT, "bytes is NULL");
   if (batch < 0 || groups <= 0 || row_stride < 0 || k <= 0)
     return fail(SD_ERR_INVALID_ARGUMENT, "bad sizes");
-  *bytes = 0;
+  *bytes = align_up(sd::select_workspace_bytes(batch * groups, row_stride));
   return SD_OK;
 }
 
@@ -317,15 +318,33 @@ sd_status sd_topk_select(const float* scores, int32_t batch, int32_t groups, int
                          const int32_t* kv_lens, int32_t k, int32_t* indices, int32_t* counts,
                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
   g_err.clear();
-  (void)workspace;
-  (void)workspace_bytes;
   if (batch < 0 || groups <= 0 || row_stride < 0 || k <= 0)
     return fail(SD_ERR_INVALID_ARGUMENT, "bad sizes (batch %d, groups %d, row_stride %d, k %d)", batch,
                 groups, row_stride, k);
+  if (row_stride > sd::select_max_row())
+    return fail(SD_ERR_UNSUPPORTED, "rows longer than %d tokens", sd::select_max_row());
   if (batch > 0 && (!scores || !kv_lens || !indices))
     return fail(SD_ERR_INVALID_ARGUMENT, "scores, kv_lens or indices is NULL");
-  sd::TopkArgs a{scores, batch, groups, row_stride, kv_lens, k, indices, counts};
-  return hip_status(sd::launch_topk(a, stream), "topk");
+  const size_t need = align_up(sd::select_workspace_bytes(batch * groups, row_stride));
+  if (batch > 0 && (workspace_bytes < need || !workspace))
+    return fail(SD_ERR_WORKSPACE_TOO_SMALL, "topk needs %zu workspace bytes", need);
+  if (batch > 0 && !aligned16(workspace)) return fail(SD_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  if (batch == 0) return SD_OK;
+  sd::SelectArgs a{};
+  a.scores = scores;
+  a.batch = batch;
+  a.groups = groups;
+  a.row_stride = row_stride;
+  a.kv_lens = kv_lens;
+  a.k = k;
+  a.indices = indices;
+  a.counts = counts;
+  a.row_bound = nullptr;
+  sd::select_bind_workspace(&a, workspace);
+  sd_status s;
+  if ((s = hip_status(sd::launch_select_init(a, stream), "select_init")) != SD_OK) return s;
+  if ((s = hip_status(sd::launch_select_stats(a, stream), "select_stats")) != SD_OK) return s;
+  return hip_status(sd::launch_select(a, stream), "select");
 }
 
 sd_status sd_sparse_decode_attn_workspace_size(const sd_pages* pages, int32_t q_heads,
@@ -381,29 +400,29 @@ sd_status sd_sparse_decode(const sd_sparse_decode_args* x, void* workspace, size
   char* ws = static_cast<char*>(workspace);
   float* scores = reinterpret_cast<float*>(ws + f.off_scores);
   float* bound = reinterpret_cast<float*>(ws + f.off_bound);
-  float* thr = reinterpret_cast<float*>(ws + f.off_thr);
   int32_t* idx = x->indices_out ? x->indices_out : reinterpret_cast<int32_t*>(ws + f.off_idx);
 
-  // 1. score
+  // 0. selection statistics zeroed; 1. score (also the row min / max keys)
+  sd::SelectArgs t{};
+  t.scores = scores;
+  t.batch = x->pages.batch;
+  t.groups = f.groups;
+  t.row_stride = x->pages.max_kv_len;
+  t.kv_lens = x->pages.kv_lens;
+  t.k = x->topk;
+  t.indices = idx;
+  t.counts = x->counts_out;
+  t.row_bound = f.fast ? bound : nullptr;
+  sd::select_bind_workspace(&t, ws + f.off_keys);
+  if ((st = hip_status(sd::launch_select_init(t, stream), "select_init")) != SD_OK) return st;
   f.score.scores = scores;
   f.score.row_bound = f.fast ? bound : nullptr;
+  f.score.row_stats = t.stats;
   st = run_score(f.score, f.fast ? SD_SCORE_FAST : SD_SCORE_EXACT, stream);
   if (st != SD_OK) return st;
-  // 2. select
-  sd::TopkArgs t{scores, x->pages.batch, f.groups, x->pages.max_kv_len, x->pages.kv_lens, x->topk,
-                 idx, x->counts_out};
-  if (f.fast) {
-    if ((st = hip_status(sd::launch_topk_threshold(t, thr, stream), "topk_threshold")) != SD_OK) return st;
-    sd::RefineArgs r{};
-    r.score = f.score;
-    r.row_bound = bound;
-    r.thr = thr;
-    r.refined = reinterpret_cast<float*>(ws + f.off_refined);
-    r.k = x->topk;
-    if ((st = hip_status(sd::launch_refine_band(r, stream), "refine")) != SD_OK) return st;
-    t.scores = r.refined;
-  }
-  if ((st = hip_status(sd::launch_topk(t, stream), "topk")) != SD_OK) return st;
+  // 2. select (exactly, also from fast scores)
+  t.score = f.score;
+  if ((st = hip_status(sd::launch_select(t, stream), "select")) != SD_OK) return st;
   // 3. attend
   f.attn.a.indices = idx;
   bind_attn_ws(&f.attn, ws + f.off_attn);

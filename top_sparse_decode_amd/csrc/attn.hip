@@ -183,34 +183,49 @@ __global__ __launch_bounds__(256) void attn_vec_kernel(AttnArgs a) {
 
 // ------------------------------------------------------------------ MLA path
 
-// Sparse MLA decode on bf16 MFMA 32x32x16.  One block per (split, request)
-// with NW waves; wave w owns query heads 32w..32w+31.  The selected latent
-// rows of a split are staged 32 at a time into LDS (double buffered) and
-// shared by every wave:
-//   S^T[token][head] = K_tile (A, 32 tokens x 16 dims per step) * Q^T (B,
-//                      held in registers for all 36 steps of the 576 dims),
-//   O[head][dv]     += P (A, the bf16 probabilities already in registers)
-//                      * V (B, read from the same LDS rows, first 512 dims).
+// Sparse MLA decode on bf16 MFMA 32x32x16.  One block per (split of 128
+// selected rows, request) with NW waves (one per SIMD); wave w owns query
+// heads 32w..32w+31.  All 128 latent rows of the split are fetched at once
+// by direct global->LDS loads and stay resident (147 KB of LDS):
+//   S^T[token][head] = K_chunk (A operand, 32 tokens x 16 dims per step) *
+//     Q^T (B operand, the wave's 32 heads over all 36 steps of the 576 dims,
+//     held in registers), for all four 32-row chunks; the block max is then
+//     exact, P = 2^(x - max) is formed once (bf16, in registers) and never
+//     rescaled;
+//   O[:, 0:256] += P * V[:, 0:256], then O[:, 256:512] += P * V[:, 256:512].
+// Splitting the value columns across the two passes halves the live
+// accumulators (128 instead of 256 per lane) without computing S twice.
 // 32x32x16 operand layout: lane l holds A[row l%32][8 k-values of half
-// l/32], B[8 k-values of half l/32][col l%32], and
-// C[rows 8*(r/4)+4*(l/32)+(r%4), r<16][col l%32].
+// l/32], B[8 k-values of half l/32][col l%32], and C[rows
+// 8*(r/4)+4*(l/32)+(r%4), r<16][col l%32].
+//
+// LDS rows are 72 sixteen-byte units plus one pad unit (1168-byte stride):
+// the 32 rows read by one A fragment fall on different banks, and every LDS
+// address is affine in the loop indices (immediate offsets).
 constexpr int kMlaD = 576;
 constexpr int kMlaDv = 512;
-constexpr int kMlaRows = 32;
-constexpr int kMlaStride = kMlaD + 8;  // LDS row stride (elements)
+constexpr int kMlaChunkRows = 32;
+constexpr int kMlaChunks = 4;
+constexpr int kMlaSplitRows = kMlaChunkRows * kMlaChunks;  // 128 rows per block
+constexpr int kMlaUnits = kMlaD / 8;                       // 72 units per row
+constexpr int kMlaStride = kMlaUnits + 1;                  // LDS row stride in units
+
+__device__ __forceinline__ int mla_unit(int row, int unit) { return row * kMlaStride + unit; }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 template <int NW>
-__global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
+__global__ __launch_bounds__(NW * 64, 1) void attn_mla_kernel(AttnArgs a) {
   constexpr int NT = NW * 64;
   constexpr int KSTEPS = kMlaD / 16;  // 36
-  __shared__ __attribute__((aligned(16))) uint16_t s_kv[2][kMlaRows][kMlaStride];
-  __shared__ int s_ok[2][kMlaRows];
+  __shared__ __attribute__((aligned(16))) uint4 s_kv[kMlaSplitRows * kMlaStride];
+  __shared__ int64_t s_off[kMlaSplitRows];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int col = lane & 31, hf = lane >> 5;
   const int b = blockIdx.y;
   const int split = blockIdx.x;
-  const int r0 = split * a.chunk, r1 = min(a.k_sel, r0 + a.chunk);
+  const int r0 = split * kMlaSplitRows, r1 = min(a.k_sel, r0 + kMlaSplitRows);
   const int cap = min(a.max_kv_len, a.max_pages * a.page_size);
   const int L = clamp_len(a.kv_lens[b], cap);
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
@@ -219,6 +234,25 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
   const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.k);
   const int head0 = wid * 32;
 
+  // ---- row offsets of the split (element offset, -1 = not usable)
+  for (int r = tid; r < kMlaSplitRows; r += NT) {
+    const int i = r0 + r;
+    const int t = i < r1 ? sel[i] : -1;
+    s_off[r] = sel_row(a, bt, L, t, 0, a.k_page_stride, a.k_head_stride, a.k_token_stride, a.k_num_pages);
+  }
+  __syncthreads();
+  // unusable rows are zero (their probabilities are zero; values must be finite)
+  for (int u = tid; u < kMlaSplitRows * kMlaStride; u += NT)
+    if (s_off[u / kMlaStride] < 0) s_kv[u] = make_uint4(0, 0, 0, 0);
+  // ---- every usable row: one direct global->LDS load per 16-byte unit; a
+  // wave's instruction covers 64 consecutive LDS units (pad units: no load)
+  for (int ub = wid * 64; ub < kMlaSplitRows * kMlaStride; ub += NT) {
+    const int u = ub + lane;
+    const int row = u / kMlaStride, slot = u % kMlaStride;
+    const int64_t off = s_off[row];
+    if (off >= 0 && slot < kMlaUnits)
+      __builtin_amdgcn_global_load_lds(kb + off + slot * 8, (lds_ptr_t)&s_kv[ub], 16, 0, 0);
+  }
   // Q^T fragments: lane holds head (head0+col), dims 16s + 8hf .. +8
   bf16x8 qf[KSTEPS];
   {
@@ -226,171 +260,162 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
   }
-
-  floatx16 acc[16];
-#pragma unroll
-  for (int n = 0; n < 16; ++n) acc[n] = floatx16{};
-  float m_run = -__builtin_inff();  // per head `col` (both halves agree)
-  float l_run = 0.0f;               // partial over this half's tokens
-
-  // staging: thread -> (row tr, 16-byte chunks tc + 8i, i < 9).  K and V are
-  // the same latent rows (the launcher checks that the pools alias).
-  const int tr = tid / 8 % kMlaRows, tc = tid % 8;
-  const int nchunks = (r1 - r0 + kMlaRows - 1) / kMlaRows;
-  uint4 pre[9];
-  int pre_ok = 0;
-  auto fetch = [&](int chunk) {
-    const int i = r0 + chunk * kMlaRows + tr;
-    const int t = i < r1 ? sel[i] : -1;
-    const int64_t ko = sel_row(a, bt, L, t, 0, a.k_page_stride, a.k_head_stride, a.k_token_stride, a.k_num_pages);
-    pre_ok = ko >= 0;
-#pragma unroll
-    for (int q = 0; q < 9; ++q) {
-      const int ch = tc + 8 * q;  // 16-byte chunk 0..71 of the 1152-byte row
-      pre[q] = pre_ok ? *reinterpret_cast<const uint4*>(kb + ko + ch * 8) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int q = 0; q < 9; ++q) *reinterpret_cast<uint4*>(&s_kv[buf][tr][(tc + 8 * q) * 8]) = pre[q];
-    if (tc == 0) s_ok[buf][tr] = pre_ok;
-  };
-
-  // NT threads cover 32 rows x 8 chunk lanes when NT == 256; smaller blocks
-  // loop over row groups.
-  constexpr int RPASS = NT / 8;  // rows staged per pass
-  auto fetch_stash_all = [&](int chunk, int buf) {
-    for (int rp = 0; rp < kMlaRows; rp += RPASS) {
-      const int row = rp + tid / 8;
-      const int i = r0 + chunk * kMlaRows + row;
-      const int t = i < r1 ? sel[i] : -1;
-      const int64_t ko = sel_row(a, bt, L, t, 0, a.k_page_stride, a.k_head_stride, a.k_token_stride, a.k_num_pages);
-      const int ok = ko >= 0;
-#pragma unroll
-      for (int q = 0; q < 9; ++q) {
-        const int ch = tc + 8 * q;
-        const uint4 v = ok ? *reinterpret_cast<const uint4*>(kb + ko + ch * 8) : make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4*>(&s_kv[buf][row][ch * 8]) = v;
-      }
-      if (tc == 0) s_ok[buf][row] = ok;
-    }
-  };
-
-  if (nchunks > 0) {
-    if constexpr (NT == 256) {
-      fetch(0);
-      stash(0);
-    } else {
-      fetch_stash_all(0, 0);
-    }
-  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  for (int ck = 0; ck < nchunks; ++ck) {
-    const int buf = ck & 1;
-    const bool more = ck + 1 < nchunks;
-    if constexpr (NT == 256) {
-      if (more) fetch(ck + 1);
-    }
-    // ---- S^T = K Q^T for 32 tokens x 32 heads
+  floatx16 acc[8];
+  uint32_t pw[kMlaChunks][8];  // bf16 P of each chunk, A-operand layout
+
+  // ---- S^T for all 128 rows first, so the block max is exact and P needs
+  // no later rescaling.  This lane: head `col`, tokens
+  // 32j + 8*(r/4) + 4*hf + (r%4).
+  float sc[kMlaChunks][16];
+  float cmax = -__builtin_inff();
+#pragma unroll
+  for (int j = 0; j < kMlaChunks; ++j) {
     floatx16 st = floatx16{};
-    const uint16_t* arow = &s_kv[buf][col][8 * hf];
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
-      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(arow + 16 * s);
+      const bf16x8 kf = __builtin_bit_cast(bf16x8, s_kv[mla_unit(kMlaChunkRows * j + col, 2 * s + hf)]);
       st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], st, 0, 0, 0);
+      // bound the scheduler's look-ahead of LDS reads (register pressure)
+      if (s % 6 == 5) __builtin_amdgcn_sched_barrier(0);
     }
-    // ---- online softmax for head `col`; this lane's 16 tokens:
-    //      token(r) = 8*(r/4) + 4*hf + (r%4)
-    float x[16];
-    float cmax = -__builtin_inff();
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int tk = 8 * (r / 4) + 4 * hf + (r % 4);
-      x[r] = s_ok[buf][tk] ? st[r] * c : -__builtin_inff();
-      cmax = fmaxf(cmax, x[r]);
+      const int tk = kMlaChunkRows * j + 8 * (r / 4) + 4 * hf + (r % 4);
+      sc[j][r] = s_off[tk] >= 0 ? st[r] * c : -__builtin_inff();
+      cmax = fmaxf(cmax, sc[j][r]);
     }
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-    const float m_new = fmaxf(m_run, cmax);
-    const float alpha = (m_new == -__builtin_inff()) ? 1.0f : exp2f(m_run - m_new);
-    m_run = m_new;
-    float psum = 0.0f;
-    uint32_t pw[8];
+  }
+  const float m_blk = fmaxf(cmax, __shfl_xor(cmax, 32));
+  // masked tokens: exp2(-inf - mref) = 0 (mref finite even with no token)
+  const float mref = m_blk == -__builtin_inff() ? 0.0f : m_blk;
+  float psum = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kMlaChunks; ++j)
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      const float p0 = (x[r] == -__builtin_inff()) ? 0.0f : exp2f(x[r] - m_new);
-      const float p1 = (x[r + 1] == -__builtin_inff()) ? 0.0f : exp2f(x[r + 1] - m_new);
+      const float p0 = __builtin_amdgcn_exp2f(sc[j][r] - mref);
+      const float p1 = __builtin_amdgcn_exp2f(sc[j][r + 1] - mref);
       psum += p0 + p1;
-      pw[r / 2] = uint32_t(f32_to_bf16(p0)) | (uint32_t(f32_to_bf16(p1)) << 16);
+      pw[j][r / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector((float2v){p0, p1}, bf16x2));
     }
-    l_run = l_run * alpha + psum;
-    // rescale O rows (heads) whose max moved; O rows are heads
-    // 8*(r/4)+4*hf+(r%4), the lane that owns head h's alpha is lane h.
-    if (__ballot(alpha != 1.0f)) {
-      float ar[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) ar[r] = __shfl(alpha, 8 * (r / 4) + 4 * hf + (r % 4));
-#pragma unroll
-      for (int n = 0; n < 16; ++n)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[n][r] *= ar[r];
-    }
-    // ---- O += P V over the 32 tokens: two k-steps of 16 tokens.  In k-step
-    // ks the lane's 8 P values are tokens 16ks + 8(p/4) + 4hf + p%4 (p<8),
-    // so its V fragment must hold those tokens too.
+
+  // O[:, 256*half ...] += P_j V_j for chunk j (V: first 512 dims of the rows)
+  auto pv = [&](int j, int half) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 pa = __builtin_bit_cast(bf16x8, u32x4{pw[4 * ks], pw[4 * ks + 1], pw[4 * ks + 2], pw[4 * ks + 3]});
+        __builtin_amdgcn_sched_barrier(0);
+      const bf16x8 pa = __builtin_bit_cast(bf16x8, u32x4{pw[j][4 * ks], pw[j][4 * ks + 1], pw[j][4 * ks + 2], pw[j][4 * ks + 3]});
+      // In k-step ks the lane's 8 P values are tokens 16ks + 8(p/4) + 4hf +
+      // p%4; its V fragments hold those tokens.  Four N tiles at a time: 4
+      // dv values (8 bytes) of each of the 8 tokens, dv = 256*half + 8*col + cc.
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        // rows of the 8 tokens, 8 dv values each: dv = 256*half + 8*col + cc
-        u32x4 vr[8];
+      for (int c0 = 0; c0 < 8; c0 += 4) {
+        uint2 vr[8];
 #pragma unroll
         for (int p = 0; p < 8; ++p) {
-          const int tk = 16 * ks + 8 * (p / 4) + 4 * hf + (p % 4);
-          vr[p] = *reinterpret_cast<const u32x4*>(&s_kv[buf][tk][256 * half + 8 * col]);
+          const int tk = kMlaChunkRows * j + 16 * ks + 8 * (p / 4) + 4 * hf + (p % 4);
+          vr[p] = reinterpret_cast<const uint2*>(&s_kv[mla_unit(tk, 32 * half + col)])[c0 / 4];
         }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int cc = 0; cc < 8; ++cc) {
-          // B fragment of N tile (half, cc): element p = V[token p][dv cc]
+        for (int cc = c0; cc < c0 + 4; ++cc) {
+          // B fragment of N tile cc: element p = V[token p][256*half + 8*col + cc]
           u32x4 bw;
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
-            const uint32_t lo = vr[2 * w][cc / 2], hi = vr[2 * w + 1][cc / 2];
-            // pick the 16-bit half cc%2 of each
+            const int q = (cc - c0) / 2;
+            const uint32_t lo = q ? vr[2 * w].y : vr[2 * w].x, hi = q ? vr[2 * w + 1].y : vr[2 * w + 1].x;
             bw[w] = (cc & 1) ? __builtin_amdgcn_perm(hi, lo, 0x07060302u)
                              : __builtin_amdgcn_perm(hi, lo, 0x05040100u);
           }
-          acc[8 * half + cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              pa, __builtin_bit_cast(bf16x8, bw), acc[8 * half + cc], 0, 0, 0);
+          acc[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, __builtin_bit_cast(bf16x8, bw), acc[cc], 0, 0, 0);
         }
       }
     }
-    if constexpr (NT == 256) {
-      if (more) stash(buf ^ 1);
-    } else {
-      if (more) fetch_stash_all(ck + 1, buf ^ 1);
-    }
-    __syncthreads();
-  }
-
-  // ---- partials: m, l per head; O[head][dv]
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const int64_t pb = ((int64_t)b * a.q_heads + head0) * a.splits + split;
-  if (hf == 0) {
-    const int64_t p = pb + (int64_t)col * a.splits;
-    a.part_ml[p * 2 + 0] = m_run;
-    a.part_ml[p * 2 + 1] = l_tot;
-  }
+  };
+  // ---- partials in register order: part_o[((b*splits+split)*NW + w)][n][lane][16]
+  // (n < 8: dv 0..255, n >= 8: dv 256..511); m / l per head:
+  // part_ml[(b*splits+split)*q_heads + h][2]
+  const int64_t blk = (int64_t)b * a.splits + split;
+  float* po = a.part_o + ((blk * NW + wid) * 16) * (64 * 16);
+  auto store = [&](int n0) {
 #pragma unroll
-  for (int n = 0; n < 16; ++n) {
-    const int half = n / 8, cc = n % 8;
-    const int dv = 256 * half + 8 * col + cc;
+    for (int n = 0; n < 8; ++n) {
+      float4* dst = reinterpret_cast<float4*>(po + ((int64_t)(n0 + n) * 64 + lane) * 16);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        dst[jj] = make_float4(acc[n][4 * jj], acc[n][4 * jj + 1], acc[n][4 * jj + 2], acc[n][4 * jj + 3]);
+    }
+  };
+  // value columns 0..255, then 256..511, from the same probabilities
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int n = 0; n < 8; ++n) acc[n] = floatx16{};
+#pragma unroll
+    for (int j = 0; j < kMlaChunks; ++j) pv(j, half);
+    store(8 * half);
+  }
+  const float l_tot = psum + __shfl_xor(psum, 32);
+  if (hf == 0) {
+    float* ml = a.part_ml + (blk * a.q_heads + head0 + col) * 2;
+    ml[0] = m_blk;
+    ml[1] = l_tot;
+  }
+}
+
+// Combine of the MLA partials: one 64-thread block per (request, wave w,
+// N tile n); lane l owns heads 32w + 8(r/4) + 4(l/32) + r%4 (r < 16) at
+// dv = 256*(n/8) + 8*(l%32) + n%8.
+__global__ __launch_bounds__(64) void attn_mla_combine_kernel(AttnArgs a, int nw) {
+  const int lane = threadIdx.x;
+  const int n = blockIdx.x % 16, w = (blockIdx.x / 16) % nw, b = blockIdx.x / (16 * nw);
+  const int col = lane & 31, hf = lane >> 5;
+  const int dv = 256 * (n / 8) + 8 * col + (n % 8);
+  float M[16], inv[16], o[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int h = 32 * w + 8 * (r / 4) + 4 * hf + (r % 4);
+    float mx = -__builtin_inff();
+    for (int s = 0; s < a.splits; ++s) mx = fmaxf(mx, a.part_ml[(((int64_t)b * a.splits + s) * a.q_heads + h) * 2]);
+    float Ls = 0.0f;
+    if (mx != -__builtin_inff())
+      for (int s = 0; s < a.splits; ++s) {
+        const float* ml = a.part_ml + (((int64_t)b * a.splits + s) * a.q_heads + h) * 2;
+        if (ml[0] != -__builtin_inff()) Ls += ml[1] * exp2f(ml[0] - mx);
+      }
+    M[r] = mx;
+    inv[r] = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+    o[r] = 0.0f;
+  }
+  for (int s = 0; s < a.splits; ++s) {
+    const int64_t blk = (int64_t)b * a.splits + s;
+    const float4* src = reinterpret_cast<const float4*>(a.part_o + (((blk * nw + w) * 16 + n) * 64 + lane) * 16);
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 q = src[j];
+      v[4 * j] = q.x; v[4 * j + 1] = q.y; v[4 * j + 2] = q.z; v[4 * j + 3] = q.w;
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int h = 8 * (r / 4) + 4 * hf + (r % 4);
-      a.part_o[(pb + (int64_t)h * a.splits) * kMlaDv + dv] = acc[n][r];
+      const int h = 32 * w + 8 * (r / 4) + 4 * hf + (r % 4);
+      const float m = a.part_ml[(blk * a.q_heads + h) * 2];
+      if (m != -__builtin_inff()) o[r] += v[r] * exp2f(m - M[r]);
     }
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int h = 32 * w + 8 * (r / 4) + 4 * hf + (r % 4);
+    const float val = o[r] * inv[r];
+    const int64_t oi = ((int64_t)b * a.q_heads + h) * kMlaDv + dv;
+    if (a.out_dtype == 0)
+      reinterpret_cast<float*>(a.out)[oi] = val;
+    else
+      reinterpret_cast<uint16_t*>(a.out)[oi] = f32_to_bf16(val);
   }
 }
 
@@ -440,13 +465,15 @@ bool attn_vec_supported(const AttnArgs& a) {
 }
 
 int attn_rows_per_split(const AttnArgs& a, bool mla) {
+  if (mla) return kMlaSplitRows;
   // aim for a few hundred blocks; rows per split a multiple of 32
   const int rows_tot = a.k_sel;
   const int units = a.batch * (mla ? 1 : a.num_kv_heads);
-  int want_splits = units >= 512 ? 1 : (512 + units - 1) / units;
+  const int target = mla ? 256 : 512;  // MLA: one 4-wave block per CU
+  int want_splits = units >= target ? 1 : (target + units - 1) / units;
   int chunk = (rows_tot + want_splits - 1) / want_splits;
   chunk = ((chunk + 31) / 32) * 32;
-  const int min_chunk = mla ? 128 : 64;
+  const int min_chunk = 64;
   if (chunk < min_chunk) chunk = min_chunk;
   return chunk;
 }
@@ -467,14 +494,18 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
   if (a.batch == 0) return hipSuccess;
   hipError_t e;
   if (attn_mla_supported(a)) {
+    if (a.chunk != kMlaSplitRows) return hipErrorInvalidValue;
     dim3 grid(a.splits, a.batch);
-    switch (a.q_heads / 32) {
+    const int nw = a.q_heads / 32;
+    switch (nw) {
       case 1: attn_mla_kernel<1><<<grid, 64, 0, st>>>(a); break;
       case 2: attn_mla_kernel<2><<<grid, 128, 0, st>>>(a); break;
       case 4: attn_mla_kernel<4><<<grid, 256, 0, st>>>(a); break;
       default: return hipErrorInvalidValue;
     }
-    e = hipGetLastError();
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    attn_mla_combine_kernel<<<a.batch * nw * 16, 64, 0, st>>>(a, nw);
+    return hipGetLastError();
   } else {
     dim3 grid(a.splits, a.batch * a.num_kv_heads);
     if (a.dtype == 0)

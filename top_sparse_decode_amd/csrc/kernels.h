@@ -23,23 +23,29 @@ struct ScoreArgs {
   float inv_g;
   float* scores;     // [batch][num_kv_heads][max_kv_len]
   float* row_bound;  // [batch][num_kv_heads] or null
+  int32_t* row_stats;  // selection statistics (min/max keys of finite scores) or null
 };
 
-struct TopkArgs {
-  const float* scores;
+// Per-row selection statistics: [kmin key, kmax key, band count, 5 spare,
+// 2048-bin histogram].
+constexpr int kStatStride = 8 + 2048;
+constexpr int kSelChunk = 4096;   // tokens per block in the multi-block selection
+constexpr int kBandCap = 4096;    // band entries kept per row before falling back
+
+struct SelectArgs {
+  const float* scores;  // [batch][groups][row_stride]
   int32_t batch, groups, row_stride;
   const int32_t* kv_lens;
   int32_t k;
-  int32_t* indices;
-  int32_t* counts;
-};
-
-struct RefineArgs {
-  ScoreArgs score;  // the fast scores in score.scores
-  const float* row_bound;
-  const float* thr;
-  float* refined;   // same shape as the scores
-  int32_t k;
+  int32_t* indices;     // [batch][groups][k]
+  int32_t* counts;      // [batch][groups] or null
+  float* keys;          // scratch, same shape as scores
+  const float* row_bound;  // fast scores: per-row bound on |fast - exact|; null = exact scores
+  ScoreArgs score;      // fast scores: the inputs needed to re-score band tokens exactly
+  int32_t* stats;       // [rows][kStatStride]
+  int32_t* chunk_counts;  // [rows][nchunks][2]: kept-for-sure count, -inf count
+  uint64_t* band;       // [rows][kBandCap]: (key << 32) | ~position
+  int32_t nchunks;      // ceil(row_stride / kSelChunk)
 };
 
 struct AttnArgs {
@@ -71,9 +77,13 @@ bool score_fast_supported(const ScoreArgs& a);
 hipError_t launch_score_exact(const ScoreArgs& a, hipStream_t st);
 hipError_t launch_score_fast(const ScoreArgs& a, hipStream_t st);
 
-hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
-hipError_t launch_topk_threshold(const TopkArgs& a, float* thr, hipStream_t st);
-hipError_t launch_refine_band(const RefineArgs& a, hipStream_t st);
+int select_max_row();
+size_t select_workspace_bytes(int rows, int row_stride);
+void select_bind_workspace(SelectArgs* a, void* ws);
+// init must run before the scorer (or launch_select_stats) writes row_stats
+hipError_t launch_select_init(const SelectArgs& a, hipStream_t st);
+hipError_t launch_select_stats(const SelectArgs& a, hipStream_t st);
+hipError_t launch_select(const SelectArgs& a, hipStream_t st);
 
 bool attn_mla_supported(const AttnArgs& a);
 bool attn_vec_supported(const AttnArgs& a);

@@ -62,6 +62,22 @@ __device__ __forceinline__ float dot_step<uint16_t>(float acc, float q, float k)
   return __builtin_fmaf(q, k, acc);
 }
 
+// Fold a wave's finite scores into the row's min / max keys (selection
+// statistics): one atomic pair per wave.
+__device__ __forceinline__ void note_minmax(int32_t* stat, float s, bool finite) {
+  uint32_t kmin = finite ? score_key(s) : 0xFFFFFFFFu;
+  uint32_t kmax = finite ? score_key(s) : 0u;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+  }
+  if ((threadIdx.x & 63) == 0 && kmin <= kmax) {
+    atomicMin(reinterpret_cast<unsigned int*>(stat), kmin);
+    atomicMax(reinterpret_cast<unsigned int*>(stat + 1), kmax);
+  }
+}
+
 template <typename KT, int G>
 __global__ __launch_bounds__(256) void score_exact_kernel(ScoreArgs a) {
   constexpr int EPU = Elems<KT>::kPerUnit;
@@ -72,8 +88,8 @@ __global__ __launch_bounds__(256) void score_exact_kernel(ScoreArgs a) {
   const int t = (blockIdx.x * 4 + wid) * kWave + lane;
   float* row = a.scores + (int64_t)blockIdx.y * a.max_kv_len;
   if (a.row_bound && blockIdx.x == 0 && threadIdx.x == 0) a.row_bound[blockIdx.y] = 0.0f;
-  if (t >= a.max_kv_len) return;
-  bool ok = t < L;
+  const bool in_row = t < a.max_kv_len;
+  bool ok = in_row && t < L;
   int64_t off = 0;
   if (ok) {
     const int page = a.block_table[(int64_t)b * a.max_pages + t / a.page_size];
@@ -81,44 +97,44 @@ __global__ __launch_bounds__(256) void score_exact_kernel(ScoreArgs a) {
     off = (int64_t)page * a.page_stride + (int64_t)g * a.head_stride +
           (int64_t)(t % a.page_size) * a.token_stride;
   }
-  if (!ok) {
-    row[t] = -__builtin_inff();
-    return;
-  }
-  const KT* krow = reinterpret_cast<const KT*>(a.k) + off;
-  const KT* qbase = reinterpret_cast<const KT*>(a.q) + ((int64_t)b * a.q_heads + g * G) * a.head_dim;
-  float acc[G];
+  float s = -__builtin_inff();
+  if (ok) {
+    const KT* krow = reinterpret_cast<const KT*>(a.k) + off;
+    const KT* qbase = reinterpret_cast<const KT*>(a.q) + ((int64_t)b * a.q_heads + g * G) * a.head_dim;
+    float acc[G];
 #pragma unroll
-  for (int j = 0; j < G; ++j) acc[j] = 0.0f;
-  const int units = a.head_dim / EPU;
-  for (int u = 0; u < units; ++u) {
-    float kv[EPU];
-    unpack_unit(*reinterpret_cast<const uint4*>(krow + u * EPU), kv);
+    for (int j = 0; j < G; ++j) acc[j] = 0.0f;
+    const int units = a.head_dim / EPU;
+    for (int u = 0; u < units; ++u) {
+      float kv[EPU];
+      unpack_unit(*reinterpret_cast<const uint4*>(krow + u * EPU), kv);
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-      float qv[EPU];
-      unpack_unit(*reinterpret_cast<const uint4*>(qbase + (int64_t)j * a.head_dim + u * EPU), qv);
+      for (int j = 0; j < G; ++j) {
+        float qv[EPU];
+        unpack_unit(*reinterpret_cast<const uint4*>(qbase + (int64_t)j * a.head_dim + u * EPU), qv);
 #pragma unroll
-      for (int e = 0; e < EPU; ++e) acc[j] = dot_step<KT>(acc[j], qv[e], kv[e]);
+        for (int e = 0; e < EPU; ++e) acc[j] = dot_step<KT>(acc[j], qv[e], kv[e]);
+      }
+    }
+    s = 0.0f;
+    if (a.mode == 0) {
+#pragma unroll
+      for (int j = 0; j < G; ++j) s = __fadd_rn(s, __fmul_rn(acc[j], a.head_scale));
+    } else if (a.mode == 1) {
+#pragma unroll
+      for (int j = 0; j < G; ++j) s = __fadd_rn(s, acc[j]);
+      s = __fmul_rn(s, a.inv_g);
+    } else {
+      const float* w = a.head_weights + (int64_t)b * a.q_heads + g * G;
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const float r = acc[j] > 0.0f ? acc[j] : 0.0f;
+        s = __fadd_rn(s, __fmul_rn(w[j], r));
+      }
     }
   }
-  float s = 0.0f;
-  if (a.mode == 0) {
-#pragma unroll
-    for (int j = 0; j < G; ++j) s = __fadd_rn(s, __fmul_rn(acc[j], a.head_scale));
-  } else if (a.mode == 1) {
-#pragma unroll
-    for (int j = 0; j < G; ++j) s = __fadd_rn(s, acc[j]);
-    s = __fmul_rn(s, a.inv_g);
-  } else {
-    const float* w = a.head_weights + (int64_t)b * a.q_heads + g * G;
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const float r = acc[j] > 0.0f ? acc[j] : 0.0f;
-      s = __fadd_rn(s, __fmul_rn(w[j], r));
-    }
-  }
-  row[t] = s;
+  if (in_row) row[t] = s;
+  if (a.row_stats) note_minmax(a.row_stats + (int64_t)blockIdx.y * kStatStride, s, ok && __builtin_isfinite(s));
 }
 
 // ------------------------------------------------------------------ fast DSA
@@ -194,12 +210,16 @@ __global__ __launch_bounds__(256) void score_dsa_mfma_kernel(ScoreArgs a, int it
   const float u24 = 5.9604644775390625e-8f, u23 = 1.1920928955078125e-7f;
   const float gD = gamma_n((float)D, u23), gH = gamma_n((float)(G + 1), u24);
   float dmax = 0.0f;
+  float smin = __builtin_inff(), smax = -__builtin_inff();  // finite scores of this lane
 
-  for (int it = 0; it < iters; ++it) {
-    const int t0 = tb0 + (it * 4 + wid) * 32;
-    if (t0 >= a.max_kv_len) break;
+  // One 32-token tile (two 16-token N tiles) per step; the next tile's key
+  // fragments are loaded before the current one is computed, so two tiles'
+  // worth of loads (16 KB per wave) are in flight.
+  struct Tile {
     bf16x8 kf[2][KS];
-    bool okn[2];
+    bool ok[2];
+  };
+  auto load_tile = [&](int t0, Tile& T) {
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
       const int t = t0 + 16 * n + col;
@@ -210,16 +230,13 @@ __global__ __launch_bounds__(256) void score_dsa_mfma_kernel(ScoreArgs a, int it
         ok = page >= 0 && page < a.num_pages;
         off = (int64_t)page * a.page_stride + (int64_t)(t % a.page_size) * a.token_stride;
       }
-      okn[n] = ok;
+      T.ok[n] = ok;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (ok) {
-          kf[n][ks] = *reinterpret_cast<const bf16x8*>(kbase + off + 32 * ks + 8 * grp);
-        } else {
-          kf[n][ks] = bf16x8{};
-        }
-      }
+      for (int ks = 0; ks < KS; ++ks)
+        T.kf[n][ks] = ok ? *reinterpret_cast<const bf16x8*>(kbase + off + 32 * ks + 8 * grp) : bf16x8{};
     }
+  };
+  auto compute_tile = [&](int t0, const Tile& T) {
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
       floatx4 acc[MT];
@@ -228,7 +245,7 @@ __global__ __launch_bounds__(256) void score_dsa_mfma_kernel(ScoreArgs a, int it
         acc[mt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[mt][ks], kf[n][ks], acc[mt], 0, 0, 0);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[mt][ks], T.kf[n][ks], acc[mt], 0, 0, 0);
       }
       float s = 0.0f, m = 0.0f;
 #pragma unroll
@@ -242,7 +259,7 @@ __global__ __launch_bounds__(256) void score_dsa_mfma_kernel(ScoreArgs a, int it
       float bsum = 0.0f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 kw = __builtin_bit_cast(u32x4, kf[n][ks]);
+        const u32x4 kw = __builtin_bit_cast(u32x4, T.kf[n][ks]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           bsum += av[ks][2 * e] * fabsf(bf16_lo(kw[e]));
@@ -256,14 +273,37 @@ __global__ __launch_bounds__(256) void score_dsa_mfma_kernel(ScoreArgs a, int it
       bsum += __shfl_xor(bsum, 16);
       bsum += __shfl_xor(bsum, 32);
       const int t = t0 + 16 * n + col;
-      if (okn[n]) {
+      if (T.ok[n]) {
         // |fast - exact| <= gH*(2M + 2gD*B) + 2gD*B   (see topk.hip / header)
         const float bterm = 2.0f * gD * bsum;
         const float d = gH * (2.0f * m + bterm) + bterm;
         dmax = fmaxf(dmax, d);
       }
-      if (grp == 0 && t < a.max_kv_len) row[t] = okn[n] ? s : -__builtin_inff();
+      if (grp == 0 && t < a.max_kv_len) row[t] = T.ok[n] ? s : -__builtin_inff();
+      if (T.ok[n]) {
+        smin = fminf(smin, s);
+        smax = fmaxf(smax, s);
+      }
     }
+  };
+  auto tile_t0 = [&](int it) { return tb0 + (it * 4 + wid) * 32; };
+  auto live = [&](int it) { return it < iters && tile_t0(it) < a.max_kv_len; };
+  Tile A, B;
+  if (live(0)) load_tile(tile_t0(0), A);
+  for (int it = 0; live(it); it += 2) {
+    const bool hasB = live(it + 1);
+    if (hasB) load_tile(tile_t0(it + 1), B);
+    compute_tile(tile_t0(it), A);
+    if (!hasB) break;
+    const bool hasA = live(it + 2);
+    if (hasA) load_tile(tile_t0(it + 2), A);
+    compute_tile(tile_t0(it + 1), B);
+    if (!hasA) break;
+  }
+  if (a.row_stats) {
+    int32_t* stat = a.row_stats + (int64_t)blockIdx.y * kStatStride;
+    note_minmax(stat, smin, smin <= smax);
+    note_minmax(stat, smax, smin <= smax);
   }
   if (a.row_bound) {
     dmax = wave_max(dmax);
@@ -312,7 +352,7 @@ bool score_fast_supported(const ScoreArgs& a) {
 hipError_t launch_score_fast(const ScoreArgs& a, hipStream_t st) {
   if (a.batch == 0 || a.max_kv_len == 0) return hipSuccess;
   const int G = a.q_heads / a.num_kv_heads;
-  const int iters = 8;
+  const int iters = 16;
   dim3 grid((a.max_kv_len + 4 * 32 * iters - 1) / (4 * 32 * iters), a.batch * a.num_kv_heads);
   switch (G / 16) {
     case 1: score_dsa_mfma_kernel<1><<<grid, 256, 0, st>>>(a, iters); break;

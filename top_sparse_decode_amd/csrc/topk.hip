@@ -4,245 +4,938 @@
 // that come first in (score descending, position ascending) order, and
 // writes them in ascending position order padded with -1 ("Add TriAttention
 // KV-cache compression method", Summary: TopK / tie settlement; Test Plan:
-// deterministic heavy-tie settlement; the indices feed core sparse attention
-// as in "Overlap DSA heuristic prev_topk write-back on the aux stream",
-// Description).
+// deterministic heavy-tie settlement; the indices then feed core sparse
+// attention as in "Overlap DSA heuristic prev_topk write-back on the aux
+// stream", Description).
 //
-// Method: radix select on order-preserving 32-bit keys (11 + 11 + 10 bits)
-// finds the k-th largest key K* and how many of the keys equal to K* are
-// kept (the lowest positions first); an ordered compaction then emits every
-// position with key > K* plus the first `need` positions with key == K*.
+// One 512-thread block per row.  Thread `tid` owns the float4 groups
+// t = sc*2048*NI + i*2048 + 4*tid + e (super-chunk sc, tile i, element e), so
+// every load is a coalesced float4.  Rows up to 16 tiles (32768 tokens) stay
+// in registers; longer rows are re-read from L2 in each pass that needs the
+// values (up to 4 super-chunks of 65536).  Steps:
+//   1. min / max / count of the finite scores;
+//   2. a 2048-bin histogram that is linear in the score value over [min,max]
+//      (value-linear bins keep LDS-atomic contention low where exponent bins
+//      would put a whole row into a handful of bins), and the bin B* that
+//      holds the k-th largest score;
+//   3. every token is classed IN (certainly kept), OUT (certainly dropped) or
+//      BAND (decided exactly below), and IN is counted;
+//   4. a radix select (11+11+10 bits) over the order-preserving keys of the
+//      BAND tokens only finds the key K* of the last kept token and how many
+//      BAND tokens equal to K* are kept (the lowest positions);
+//   5. ordered emission, one block scan per 2048-token tile.
 //
-// Exact selection from fast scores: given fast scores s~ with |s~ - s| <= d
-// for every token of a row (s the exact score) and T~ the k-th largest s~,
-// the exact k-th score T lies in [T~ - d, T~ + d].  Tokens with s~ > T~ + 2d
-// are certainly kept, tokens with s~ < T~ - 2d certainly dropped; the rest
-// (the band) are re-scored in the exact order.  Replacing kept scores by
-// +inf and dropped ones by -inf and running the exact selection above on the
-// result gives exactly the top-k of the exact scores.
+// Exact scores: BAND = bin B*, IN = bins above, OUT = bins below.
+// Fast scores s~ with |s~ - s| <= d on every token of the row (d from the
+// scorer): with [lo*, hi*] the range of s~ inside bin B*, the k-th largest s~
+// lies in [lo*, hi*], so the exact k-th score T lies in [lo* - d, hi* + d].
+// A token with s~ > hi* + 2d has s > T (kept); one with s~ < lo* - 2d has
+// s < T (dropped); the tokens in between are re-scored in the exact order
+// (one wave per token: lane h evaluates head h's dot product left to right,
+// then the head terms are added in head order) and selected on exact keys.
+// The result is exactly the top-k of the exact scores.
 #include "common.h"
 #include "kernels.h"
 
 namespace sd {
 
-constexpr int kTopkThreads = 1024;
+constexpr int kSelThreads = 512;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kBins = 2048;
+constexpr int kTile = 4 * kSelThreads;  // tokens per tile (one float4 per thread)
+constexpr int kMaxNI = 32;              // tiles held in registers: rows up to 65536
+constexpr int kMaxChunks = 4;           // longer rows: up to 4 super-chunks, re-read per pass
+enum : uint32_t { kOut = 0, kIn = 1, kBand = 2, kPad = 3 };
 
-struct RadixResult {
-  uint32_t key;  // k-th largest key
-  int need;      // how many keys equal to `key` are kept
+struct SelShared {
+  int hist[kBins];
+  int tmp[kSelWaves];
+  int win[2];
+  float redf[2][kSelWaves];
+  int redi[kSelWaves];
+  uint8_t cls[kMaxChunks * kMaxNI * kSelThreads];  // 4 x 2-bit classes per byte
 };
 
-// Block-wide radix select of the k-th largest key among s[0..L).  Requires
-// k <= L.  hist needs 2048 ints; tmp 16 ints; win 2 ints.
-__device__ RadixResult radix_select_kth(const float* __restrict__ s, int L, int k, int* hist,
-                                        int* tmp, int* win) {
-  const int tid = threadIdx.x;
-  uint32_t prefix = 0, pmask = 0;
-  int remaining = k;
-  const int shifts[3] = {21, 10, 0};
-  const int nbits[3] = {11, 11, 10};
-#pragma unroll 1
-  for (int p = 0; p < 3; ++p) {
-    const int shift = shifts[p];
-    const int nb = 1 << nbits[p];
-    for (int i = tid; i < 2048; i += kTopkThreads) hist[i] = 0;
-    __syncthreads();
-    for (int t = tid; t < L; t += kTopkThreads) {
-      const uint32_t key = score_key(s[t]);
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & (nb - 1)], 1);
-    }
-    __syncthreads();
-    // bins in descending order: thread i owns bins nb-1-2i and nb-2-2i
-    int c0 = 0, c1 = 0;
-    const int b0 = nb - 1 - 2 * tid, b1 = nb - 2 - 2 * tid;
-    if (b0 >= 0) c0 = hist[b0];
-    if (b1 >= 0) c1 = hist[b1];
-    int total;
-    const int excl = block_excl_scan<kTopkThreads>(c0 + c1, tmp, &total);
-    if (b0 >= 0 && excl < remaining && remaining <= excl + c0) {
-      win[0] = b0;
-      win[1] = excl;
-    }
-    if (b1 >= 0 && excl + c0 < remaining && remaining <= excl + c0 + c1) {
-      win[0] = b1;
-      win[1] = excl + c0;
-    }
-    __syncthreads();
-    const int bin = win[0];
-    remaining -= win[1];
-    prefix |= (uint32_t)bin << shift;
-    pmask |= (uint32_t)(nb - 1) << shift;
-    __syncthreads();
-  }
-  return RadixResult{prefix, remaining};
+__device__ __forceinline__ float block_min_f(float v, SelShared& sh) {
+  v = fminf(v, __shfl_xor(v, 32)); v = fminf(v, __shfl_xor(v, 16)); v = fminf(v, __shfl_xor(v, 8));
+  v = fminf(v, __shfl_xor(v, 4)); v = fminf(v, __shfl_xor(v, 2)); v = fminf(v, __shfl_xor(v, 1));
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  if (lane == 0) sh.redf[0][wid] = v;
+  __syncthreads();
+  float r = sh.redf[0][0];
+  for (int w = 1; w < kSelWaves; ++w) r = fminf(r, sh.redf[0][w]);
+  __syncthreads();
+  return r;
+}
+__device__ __forceinline__ float block_max_f(float v, SelShared& sh) {
+  v = fmaxf(v, __shfl_xor(v, 32)); v = fmaxf(v, __shfl_xor(v, 16)); v = fmaxf(v, __shfl_xor(v, 8));
+  v = fmaxf(v, __shfl_xor(v, 4)); v = fmaxf(v, __shfl_xor(v, 2)); v = fmaxf(v, __shfl_xor(v, 1));
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  if (lane == 0) sh.redf[1][wid] = v;
+  __syncthreads();
+  float r = sh.redf[1][0];
+  for (int w = 1; w < kSelWaves; ++w) r = fmaxf(r, sh.redf[1][w]);
+  __syncthreads();
+  return r;
+}
+__device__ __forceinline__ int block_sum_i(int v, SelShared& sh) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  if (lane == 0) sh.redi[wid] = v;
+  __syncthreads();
+  int r = 0;
+  for (int w = 0; w < kSelWaves; ++w) r += sh.redi[w];
+  __syncthreads();
+  return r;
 }
 
-// Ordered compaction of the kept positions of one row into out[0..k).
-__device__ void emit_selected(const float* __restrict__ s, int L, uint32_t kth, int need,
-                              int32_t* __restrict__ out, int* tmp) {
+// Neighbouring binary32 values (finite inputs).
+__device__ __forceinline__ float next_up(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if (x == 0.0f) return __uint_as_float(1u);
+  return __uint_as_float((u & 0x80000000u) ? u - 1u : u + 1u);
+}
+__device__ __forceinline__ float next_down(float x) { return -next_up(-x); }
+
+// LDS histogram increment; when every active lane of the wave hits the same
+// bin (ties, constant rows) one lane adds the whole count.
+__device__ __forceinline__ void hist_add(int* hist, int bin, bool active) {
+  const uint64_t act = __ballot(active);
+  if (!act) return;
+  const int first = __shfl(bin, __builtin_ctzll(act));
+  const uint64_t same = __ballot(active && bin == first);
+  if (same == act) {
+    if ((threadIdx.x & 63) == __builtin_ctzll(act)) atomicAdd(&hist[first], __popcll(act));
+  } else if (active) {
+    atomicAdd(&hist[bin], 1);
+  }
+}
+
+// Find, over bins in descending order, the bin holding the `want`-th
+// element (1-based); returns (bin, count strictly above it) via sh.win.
+__device__ __forceinline__ void find_bin(SelShared& sh, int nb, int want) {
+  constexpr int BPT = kBins / kSelThreads;  // bins per thread
   const int tid = threadIdx.x;
-  const int seg = (L + kTopkThreads - 1) / kTopkThreads;
-  const int t0 = min(L, tid * seg), t1 = min(L, t0 + seg);
-  int gt = 0, eq = 0;
-  for (int t = t0; t < t1; ++t) {
-    const uint32_t key = score_key(s[t]);
-    gt += key > kth;
-    eq += key == kth;
+  int c[BPT];
+  int sum = 0;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    const int bin = nb - 1 - (tid * BPT + j);
+    c[j] = bin >= 0 ? sh.hist[bin] : 0;
+    sum += c[j];
   }
   int total;
-  const int eq_before = block_excl_scan<kTopkThreads>(eq, tmp, &total);
-  const int take_eq = max(0, min(eq, need - eq_before));
-  int pos = block_excl_scan<kTopkThreads>(gt + take_eq, tmp, &total);
-  int taken = 0;
-  for (int t = t0; t < t1; ++t) {
-    const uint32_t key = score_key(s[t]);
-    if (key > kth) {
-      out[pos++] = t;
-    } else if (key == kth && taken < take_eq) {
-      out[pos++] = t;
-      ++taken;
+  int excl = block_excl_scan<kSelThreads>(sum, sh.tmp, &total);
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    const int bin = nb - 1 - (tid * BPT + j);
+    if (bin >= 0 && excl < want && want <= excl + c[j]) {
+      sh.win[0] = bin;
+      sh.win[1] = excl;
     }
+    excl += c[j];
   }
+  __syncthreads();
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(TopkArgs a) {
-  __shared__ int hist[2048];
-  __shared__ int tmp[16];
-  __shared__ int win[2];
-  const int row = blockIdx.x;
+// find_bin for any block size NT, on a plain histogram array
+template <int NT>
+__device__ __forceinline__ void find_bin_n(const int* hist, int* tmp, int* win, int nb, int want) {
+  constexpr int BPT = kBins / NT;
+  const int tid = threadIdx.x;
+  int c[BPT];
+  int sum = 0;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    const int bin = nb - 1 - (tid * BPT + j);
+    c[j] = bin >= 0 ? hist[bin] : 0;
+    sum += c[j];
+  }
+  int total;
+  int excl = block_excl_scan<NT>(sum, tmp, &total);
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    const int bin = nb - 1 - (tid * BPT + j);
+    if (bin >= 0 && excl < want && want <= excl + c[j]) {
+      win[0] = bin;
+      win[1] = excl;
+    }
+    excl += c[j];
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
+}
+
+// Exact score of one token, evaluated by a whole wave in the library's exact
+// order (DSA mode, bf16, head_dim 128): lane h forms dot_h left to right,
+// then the terms w_h * relu(dot_h) are added in head order.
+__device__ float exact_dsa_score(const ScoreArgs& sa, int b, int g, int t, float* lds_terms) {
+  const int lane = threadIdx.x & 63;
+  const int G = sa.q_heads / sa.num_kv_heads;
+  const uint16_t* qb = reinterpret_cast<const uint16_t*>(sa.q) + ((int64_t)b * sa.q_heads + g * G) * 128;
+  const float* wb = sa.head_weights + (int64_t)b * sa.q_heads + g * G;
+  const int page = sa.block_table[(int64_t)b * sa.max_pages + t / sa.page_size];
+  const uint16_t* krow = reinterpret_cast<const uint16_t*>(sa.k) + (int64_t)page * sa.page_stride +
+                         (int64_t)g * sa.head_stride + (int64_t)(t % sa.page_size) * sa.token_stride;
+  float total = 0.0f;
+  for (int h0 = 0; h0 < G; h0 += kWave) {
+    const int h = h0 + lane;
+    float term = 0.0f;
+    if (h < G) {
+      const uint16_t* qh = qb + (int64_t)h * 128;
+      float acc = 0.0f;
+#pragma unroll 2
+      for (int d = 0; d < 128; d += 8) {
+        const uint4 kv = *reinterpret_cast<const uint4*>(krow + d);
+        const uint4 qv = *reinterpret_cast<const uint4*>(qh + d);
+        acc = __builtin_fmaf(bf16_lo(qv.x), bf16_lo(kv.x), acc);
+        acc = __builtin_fmaf(bf16_hi(qv.x), bf16_hi(kv.x), acc);
+        acc = __builtin_fmaf(bf16_lo(qv.y), bf16_lo(kv.y), acc);
+        acc = __builtin_fmaf(bf16_hi(qv.y), bf16_hi(kv.y), acc);
+        acc = __builtin_fmaf(bf16_lo(qv.z), bf16_lo(kv.z), acc);
+        acc = __builtin_fmaf(bf16_hi(qv.z), bf16_hi(kv.z), acc);
+        acc = __builtin_fmaf(bf16_lo(qv.w), bf16_lo(kv.w), acc);
+        acc = __builtin_fmaf(bf16_hi(qv.w), bf16_hi(kv.w), acc);
+      }
+      const float r = acc > 0.0f ? acc : 0.0f;
+      term = __fmul_rn(wb[h], r);
+    }
+    lds_terms[lane] = term;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int n = min(kWave, G - h0);
+    // 16 terms at a time into registers, then the ordered sum
+    for (int j0 = 0; j0 < n; j0 += 16) {
+      float tv[16];
+#pragma unroll
+      for (int j = 0; j < 16; j += 4) {
+        const float4 q4 = *reinterpret_cast<const float4*>(lds_terms + j0 + j);
+        tv[j] = q4.x; tv[j + 1] = q4.y; tv[j + 2] = q4.z; tv[j + 3] = q4.w;
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (j0 + j < n) total = __fadd_rn(total, tv[j]);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  return total;
+}
+
+// The whole selection of one row by one 512-thread block.  Used as the
+// fallback of the multi-block path when a row's band does not fit the band
+// list (e.g. long runs of equal scores).
+template <int NI, bool RESIDENT, bool FAST>
+__device__ __noinline__ void select_row_block(const SelectArgs& a, int row, SelShared& sh,
+                                 float (*s_terms)[kWave]) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int b = row / a.groups;
   const int L = clamp_len(a.kv_lens[b], a.row_stride);
   const int k = a.k;
   int32_t* out = a.indices + (int64_t)row * k;
-  if (L <= k) {
-    for (int i = threadIdx.x; i < k; i += kTopkThreads) out[i] = i < L ? i : -1;
-    if (a.counts && threadIdx.x == 0) a.counts[row] = L;
+  if (L <= k) {  // every token is kept
+    for (int i = tid; i < k; i += kSelThreads) out[i] = i < L ? i : -1;
+    if (a.counts && tid == 0) a.counts[row] = L;
     return;
   }
   const float* s = a.scores + (int64_t)row * a.row_stride;
-  const RadixResult r = radix_select_kth(s, L, k, hist, tmp, win);
-  emit_selected(s, L, r.key, r.need, out, tmp);
-  if (a.counts && threadIdx.x == 0) a.counts[row] = k;
-}
+  uint32_t* keys = reinterpret_cast<uint32_t*>(a.keys) + (int64_t)row * a.row_stride;
+  constexpr int PER = kTile * NI;
+  const int nsc = RESIDENT ? 1 : (L + PER - 1) / PER;
+  const bool vec = ((reinterpret_cast<uintptr_t>(s) & 15) == 0);
+  const float kNan = __builtin_nanf("");
 
-// k-th largest fast score per row (rows with kv_len <= k need none).
-__global__ __launch_bounds__(kTopkThreads) void topk_threshold_kernel(TopkArgs a, float* thr) {
-  __shared__ int hist[2048];
-  __shared__ int tmp[16];
-  __shared__ int win[2];
-  const int row = blockIdx.x;
-  const int b = row / a.groups;
-  const int L = clamp_len(a.kv_lens[b], a.row_stride);
-  if (L <= a.k) {
-    if (threadIdx.x == 0) thr[row] = -__builtin_inff();
-    return;
-  }
-  const float* s = a.scores + (int64_t)row * a.row_stride;
-  const RadixResult r = radix_select_kth(s, L, a.k, hist, tmp, win);
-  if (threadIdx.x == 0) thr[row] = key_to_score(r.key);
-}
+  auto load4 = [&](int t0) -> float4 {
+    if (vec && t0 + 3 < L) return *reinterpret_cast<const float4*>(s + t0);
+    float4 r;
+    r.x = t0 < L ? s[t0] : kNan;
+    r.y = t0 + 1 < L ? s[t0 + 1] : kNan;
+    r.z = t0 + 2 < L ? s[t0 + 2] : kNan;
+    r.w = t0 + 3 < L ? s[t0 + 3] : kNan;
+    return r;
+  };
+  auto tok = [&](int sc, int i) {
+    int t4 = 4 * tid;
+    asm volatile("" : "+v"(t4));  // recomputed at each use: no per-tile offsets held live
+    return sc * PER + i * kTile + t4;
+  };
 
-// Replace each fast score by +inf (certainly kept), -inf (certainly
-// dropped) or its exact score (band).  One wave per 64 tokens; the band
-// tokens of a wave are re-scored one at a time by the whole wave: lane h
-// evaluates head h's dot product left to right, then one lane adds the
-// group's weighted ReLU terms in head order.
-__global__ __launch_bounds__(256) void refine_band_kernel(RefineArgs a) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const ScoreArgs& sa = a.score;
-  const int row = blockIdx.y;
-  const int b = row / sa.num_kv_heads, g = row % sa.num_kv_heads;
-  const int cap = min(sa.max_kv_len, sa.max_pages * sa.page_size);
-  const int L = clamp_len(sa.kv_lens[b], cap);
-  const int t = (blockIdx.x * 4 + wid) * kWave + lane;
-  if ((blockIdx.x * 4 + wid) * kWave >= L) return;
-  const float* srow = sa.scores + (int64_t)row * sa.max_kv_len;
-  float* rrow = a.refined + (int64_t)row * sa.max_kv_len;
-  const bool live = t < L;
-  float fast = live ? srow[t] : -__builtin_inff();
-  if (L <= a.k) {  // every token is kept: the values do not matter
-    if (live) rrow[t] = fast;
-    return;
+  float4 v[NI];
+  auto get = [&](int sc, int i) -> float4 {
+    if constexpr (RESIDENT) return v[i];
+    return load4(tok(sc, i));
+  };
+  if constexpr (RESIDENT) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) v[i] = load4(tok(0, i));
   }
-  const double d2 = 2.0 * (double)a.row_bound[row];
-  const double diff = (double)fast - (double)a.thr[row];
-  float out;
-  bool band = false;
-  if (!live || fast == -__builtin_inff()) {
-    out = -__builtin_inff();
-  } else if (diff > d2) {
-    out = __builtin_inff();
-  } else if (diff < -d2) {
-    out = -__builtin_inff();
-  } else {
-    band = true;
-    out = 0.0f;
-  }
-  // exact re-score of the band tokens of this wave
-  const int G = sa.q_heads / sa.num_kv_heads;
-  uint64_t mask = __ballot(band);
-  const uint16_t* qb = reinterpret_cast<const uint16_t*>(sa.q) + ((int64_t)b * sa.q_heads + g * G) * 128;
-  const float* wb = sa.head_weights + (int64_t)b * sa.q_heads + g * G;
-  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(sa.k) + (int64_t)g * sa.head_stride;
-  const int32_t* bt = sa.block_table + (int64_t)b * sa.max_pages;
-  while (mask) {
-    const int src = __builtin_ctzll(mask);
-    mask &= mask - 1;
-    const int tt = (blockIdx.x * 4 + wid) * kWave + src;
-    const int page = bt[tt / sa.page_size];
-    const uint16_t* krow =
-        kbase + (int64_t)page * sa.page_stride + (int64_t)(tt % sa.page_size) * sa.token_stride;
-    float total = 0.0f;
-    for (int h0 = 0; h0 < G; h0 += kWave) {
-      const int h = h0 + lane;
-      float term = 0.0f;
-      if (h < G) {
-        const uint16_t* qh = qb + (int64_t)h * 128;
-        float acc = 0.0f;
-        for (int d = 0; d < 128; d += 8) {
-          const uint4 kv = *reinterpret_cast<const uint4*>(krow + d);
-          const uint4 qv = *reinterpret_cast<const uint4*>(qh + d);
-          acc = __builtin_fmaf(bf16_lo(qv.x), bf16_lo(kv.x), acc);
-          acc = __builtin_fmaf(bf16_hi(qv.x), bf16_hi(kv.x), acc);
-          acc = __builtin_fmaf(bf16_lo(qv.y), bf16_lo(kv.y), acc);
-          acc = __builtin_fmaf(bf16_hi(qv.y), bf16_hi(kv.y), acc);
-          acc = __builtin_fmaf(bf16_lo(qv.z), bf16_lo(kv.z), acc);
-          acc = __builtin_fmaf(bf16_hi(qv.z), bf16_hi(kv.z), acc);
-          acc = __builtin_fmaf(bf16_lo(qv.w), bf16_lo(kv.w), acc);
-          acc = __builtin_fmaf(bf16_hi(qv.w), bf16_hi(kv.w), acc);
+
+  // ---- 1. min / max / count of finite scores
+  float lo = __builtin_inff(), hi = -__builtin_inff();
+  int nfin = 0;
+  for (int sc = 0; sc < nsc; ++sc) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const float4 x = get(sc, i);
+      const float e4[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (__builtin_isfinite(e4[e])) {
+          lo = fminf(lo, e4[e]);
+          hi = fmaxf(hi, e4[e]);
+          ++nfin;
         }
-        const float r = acc > 0.0f ? acc : 0.0f;
-        term = __fmul_rn(wb[h], r);
-      }
-      const int n = min(kWave, G - h0);
-      for (int j = 0; j < n; ++j) total = __fadd_rn(total, __shfl(term, j));
     }
-    if (lane == src) out = total;
   }
-  if (live) rrow[t] = out;
+  lo = block_min_f(lo, sh);
+  hi = block_max_f(hi, sh);
+  nfin = block_sum_i(nfin, sh);
+
+  // ---- 2. histogram and the bin of the k-th largest
+  // value-linear bins; float arithmetic is monotone in x, which is all the
+  // classification needs (NaN only if the range overflows: top bin)
+  const float fscale = hi > lo ? (float)((double)kBins / ((double)hi - (double)lo)) : 0.0f;
+  auto bin_of = [&](float x) -> int {
+    const float f = (x - lo) * fscale;
+    return (f >= (float)(kBins - 1) || f != f) ? kBins - 1 : (int)f;
+  };
+  int bstar = -1;
+  if (nfin >= k) {
+    for (int i = tid; i < kBins; i += kSelThreads) sh.hist[i] = 0;
+    __syncthreads();
+    for (int sc = 0; sc < nsc; ++sc) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const float4 x = get(sc, i);
+        const float e4[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool fin = __builtin_isfinite(e4[e]);
+          hist_add(sh.hist, fin ? bin_of(e4[e]) : 0, fin);
+        }
+      }
+    }
+    __syncthreads();
+    find_bin(sh, kBins, k);
+    bstar = sh.win[0];
+    __syncthreads();
+  }
+
+  // ---- 3. classes
+  // bstar < 0: fewer than k finite scores -> every finite one is kept and the
+  // -inf (absent) tokens compete, lowest position first.
+  float band_lo = 0.0f, band_hi = 0.0f;  // outward-rounded band edges
+  if constexpr (FAST) {
+    if (bstar >= 0) {
+      float mlo = __builtin_inff(), mhi = -__builtin_inff();
+      for (int sc = 0; sc < nsc; ++sc) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const float4 x = get(sc, i);
+          const float e4[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (__builtin_isfinite(e4[e]) && bin_of(e4[e]) == bstar) {
+              mlo = fminf(mlo, e4[e]);
+              mhi = fmaxf(mhi, e4[e]);
+            }
+        }
+      }
+      mlo = block_min_f(mlo, sh);
+      mhi = block_max_f(mhi, sh);
+      const double d2 = 2.0 * (double)a.row_bound[row];
+      const double blo = (double)mlo - d2, bhi = (double)mhi + d2;
+      band_lo = (float)blo;
+      band_hi = (float)bhi;
+      if ((double)band_lo > blo) band_lo = next_down(band_lo);
+      if ((double)band_hi < bhi) band_hi = next_up(band_hi);
+    }
+  }
+  int n_in = 0;
+  for (int sc = 0; sc < nsc; ++sc) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const float4 x = get(sc, i);
+      const float e4[4] = {x.x, x.y, x.z, x.w};
+      uint32_t byte = 0;
+      const int t0 = tok(sc, i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float val = e4[e];
+        uint32_t c;
+        if (t0 + e >= L) {
+          c = kPad;
+        } else if (bstar < 0) {
+          c = __builtin_isfinite(val) ? kIn : kBand;
+        } else if (!__builtin_isfinite(val)) {
+          c = kOut;
+        } else if constexpr (FAST) {
+          c = val > band_hi ? kIn : (val < band_lo ? kOut : kBand);
+        } else {
+          const int bn = bin_of(val);
+          c = bn > bstar ? kIn : (bn < bstar ? kOut : kBand);
+        }
+        n_in += c == kIn;
+        if (c == kBand && (!FAST || bstar < 0)) keys[t0 + e] = score_key(val);
+        byte |= c << (2 * e);
+      }
+      sh.cls[(sc * NI + i) * kSelThreads + tid] = (uint8_t)byte;
+    }
+  }
+  n_in = block_sum_i(n_in, sh);  // (has __syncthreads: classes visible)
+
+  // ---- FAST: exact scores of the band tokens (each wave re-scores the band
+  // tokens among its own 64 threads' positions)
+  if constexpr (FAST) {
+    if (bstar >= 0) {
+      const int g = row % a.groups;
+      for (int sc = 0; sc < nsc; ++sc)
+        for (int i = 0; i < NI; ++i) {
+          const uint32_t byte = sh.cls[(sc * NI + i) * kSelThreads + tid];
+          for (int e = 0; e < 4; ++e) {
+            uint64_t m = __ballot(((byte >> (2 * e)) & 3u) == kBand);
+            while (m) {
+              const int src = __builtin_ctzll(m);
+              m &= m - 1;
+              const int t = sc * PER + i * kTile + 4 * (wid * 64 + src) + e;
+              const float ex = exact_dsa_score(a.score, b, g, t, s_terms[wid]);
+              if (lane == 0) keys[t] = score_key(ex);
+            }
+          }
+        }
+      __threadfence_block();
+      __syncthreads();
+    }
+  }
+
+  // ---- 4. radix select over the band keys
+  int remaining = k - n_in;  // band tokens to keep (>= 1)
+  uint32_t prefix = 0, pmask = 0;
+  {
+    const int shifts[3] = {21, 10, 0};
+    const int nbits[3] = {11, 11, 10};
+#pragma unroll 1
+    for (int p = 0; p < 3; ++p) {
+      const int nb = 1 << nbits[p];
+      for (int i = tid; i < kBins; i += kSelThreads) sh.hist[i] = 0;
+      __syncthreads();
+      for (int sc = 0; sc < nsc; ++sc)
+        for (int i = 0; i < NI; ++i) {
+          const uint32_t byte = sh.cls[(sc * NI + i) * kSelThreads + tid];
+          const int t0 = tok(sc, i);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            bool act = ((byte >> (2 * e)) & 3u) == kBand;
+            uint32_t key = 0;
+            if (act) {
+              key = keys[t0 + e];
+              act = (key & pmask) == prefix;
+            }
+            hist_add(sh.hist, (int)((key >> shifts[p]) & (uint32_t)(nb - 1)), act);
+          }
+        }
+      __syncthreads();
+      find_bin(sh, nb, remaining);
+      remaining -= sh.win[1];
+      prefix |= (uint32_t)sh.win[0] << shifts[p];
+      pmask |= (uint32_t)(nb - 1) << shifts[p];
+      __syncthreads();
+    }
+  }
+  const uint32_t kth = prefix;
+  int need = remaining;  // band tokens equal to kth that are kept, lowest positions first
+
+  // ---- 5. ordered emission, tile by tile
+  int base = 0;
+  for (int sc = 0; sc < nsc; ++sc)
+    for (int i = 0; i < NI; ++i) {
+      const uint32_t byte = sh.cls[(sc * NI + i) * kSelThreads + tid];
+      const int t0 = tok(sc, i);
+      int gt = 0, eq = 0;
+      uint32_t flags = 0;  // bit e: strictly kept, bit 4+e: tie
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t c = (byte >> (2 * e)) & 3u;
+        if (c == kIn) {
+          flags |= 1u << e;
+          ++gt;
+        } else if (c == kBand) {
+          const uint32_t key = keys[t0 + e];
+          if (key > kth) {
+            flags |= 1u << e;
+            ++gt;
+          } else if (key == kth) {
+            flags |= 16u << e;
+            ++eq;
+          }
+        }
+      }
+      int total;
+      const int packed = block_excl_scan<kSelThreads>((eq << 16) | gt, sh.tmp, &total);
+      const int gt_before = packed & 0xFFFF, eq_before = packed >> 16;
+      const int tot_gt = total & 0xFFFF, tot_eq = total >> 16;
+      const int take_before = min(max(need, 0), eq_before);
+      int take = max(0, min(eq, need - eq_before));
+      int pos = base + gt_before + take_before;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool keep = (flags & (1u << e)) || ((flags & (16u << e)) && take > 0);
+        if (!(flags & (1u << e)) && keep) --take;
+        if (keep && pos < k) out[pos] = t0 + e;
+        pos += keep;
+      }
+      const int took = min(max(need, 0), tot_eq);
+      base += tot_gt + took;
+      need -= took;
+    }
+  if (a.counts && tid == 0) a.counts[row] = k;
+}
+
+// ------------------------------------------------------------------ multi-block path
+//
+// The rows are long and few (16 rows of 65536 tokens for the DSA decode), so
+// every pass over the scores is spread over all CUs, 4096 tokens per block:
+//   init     per-row statistics zeroed (before the scorer, which adds the
+//            min / max keys of the finite scores with one atomic per wave);
+//   hist     value-linear 2048-bin histogram of every row;
+//   classify the bin of the k-th largest score, every token classed IN /
+//            OUT / BAND (as in the one-block path), IN counted per chunk,
+//            BAND tokens (re-scored exactly for fast scores) appended to the
+//            row's band list;
+//   emit     the band list sorted by (key desc, position asc); its first
+//            k - |IN| entries are kept; every block writes its chunk's kept
+//            positions at the offset given by the per-chunk counts.
+// A row whose band overflows the list is finished by one block with
+// select_row_block (exact, slower).
+
+constexpr int kChunkThreads = 512;
+constexpr int kPerThread = kSelChunk / kChunkThreads;  // 8 contiguous tokens
+
+struct RowView {
+  int L;
+  bool any_finite;
+  float lo, hi, fscale;
+};
+
+__device__ __forceinline__ RowView row_view(const SelectArgs& a, int row) {
+  const int b = row / a.groups;
+  RowView v;
+  v.L = clamp_len(a.kv_lens[b], a.row_stride);
+  const int32_t* st = a.stats + (int64_t)row * kStatStride;
+  const uint32_t kmin = (uint32_t)st[0], kmax = (uint32_t)st[1];
+  v.any_finite = kmin <= kmax;
+  v.lo = v.any_finite ? key_to_score(kmin) : 0.0f;
+  v.hi = v.any_finite ? key_to_score(kmax) : 0.0f;
+  // identical to the one-block path: same bins, same classes
+  v.fscale = v.hi > v.lo ? (float)((double)kBins / ((double)v.hi - (double)v.lo)) : 0.0f;
+  return v;
+}
+
+__device__ __forceinline__ int bin_of_v(const RowView& v, float x) {
+  const float f = (x - v.lo) * v.fscale;
+  return (f >= (float)(kBins - 1) || f != f) ? kBins - 1 : (int)f;
+}
+
+// this thread's 8 contiguous tokens of chunk c (NaN past kv_len)
+__device__ __forceinline__ void load8(const float* s, int t0, int L, float (&x)[kPerThread]) {
+  if (t0 + kPerThread <= L && ((reinterpret_cast<uintptr_t>(s + t0) & 15) == 0)) {
+    const float4 p = *reinterpret_cast<const float4*>(s + t0);
+    const float4 q = *reinterpret_cast<const float4*>(s + t0 + 4);
+    x[0] = p.x; x[1] = p.y; x[2] = p.z; x[3] = p.w;
+    x[4] = q.x; x[5] = q.y; x[6] = q.z; x[7] = q.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) x[e] = t0 + e < L ? s[t0 + e] : __builtin_nanf("");
+  }
+}
+
+struct ChunkShared {
+  int hist[kBins];
+  int tmp[kSelWaves];
+  int win[2];
+  int redi[kSelWaves];
+  float redf[2][kSelWaves];
+};
+
+__device__ __forceinline__ int chunk_sum_i(int v, int* red) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  if (lane == 0) red[wid] = v;
+  __syncthreads();
+  int r = 0;
+  for (int w = 0; w < kSelWaves; ++w) r += red[w];
+  __syncthreads();
+  return r;
+}
+
+// Decision data of a row, identical in every block: the bin of the k-th
+// largest finite score (or -1 when fewer than k scores are finite) and, for
+// fast scores, the band edges.
+struct RowCut {
+  int bstar;
+  int nfin;
+  float band_lo, band_hi;
+};
+
+__device__ RowCut row_cut(const SelectArgs& a, int row, const RowView& v, ChunkShared& sh, bool fast) {
+  const int32_t* gh = a.stats + (int64_t)row * kStatStride + 8;
+  int part = 0;
+  for (int i = threadIdx.x; i < kBins; i += kChunkThreads) {
+    const int h = v.any_finite ? gh[i] : 0;
+    sh.hist[i] = h;
+    part += h;
+  }
+  RowCut c;
+  c.nfin = chunk_sum_i(part, sh.redi);  // (barriers: hist visible)
+  c.bstar = -1;
+  c.band_lo = c.band_hi = 0.0f;
+  if (c.nfin >= a.k) {
+    find_bin_n<kChunkThreads>(sh.hist, sh.tmp, sh.win, kBins, a.k);
+    c.bstar = sh.win[0];
+    __syncthreads();
+    if (fast) {
+      // values in bin B* lie in [e_lo, e_hi]: the bin edges widened by the
+      // rounding of the bin arithmetic (three binary32 roundings)
+      const double dlo = v.lo, dhi = v.hi;
+      const double w = v.fscale > 0.0f ? 1.0 / (double)v.fscale : 0.0;
+      const double eps = 8.0 * 5.9604644775390625e-8 * (dhi - dlo) + 1e-30;
+      double e_lo = dlo + c.bstar * w - eps, e_hi = dlo + (c.bstar + 1) * w + eps;
+      if (c.bstar == 0 || e_lo < dlo) e_lo = dlo;
+      if (c.bstar == kBins - 1 || e_hi > dhi) e_hi = dhi;
+      const double d2 = 2.0 * (double)a.row_bound[row];
+      const double blo = e_lo - d2, bhi = e_hi + d2;
+      c.band_lo = (float)blo;
+      c.band_hi = (float)bhi;
+      if ((double)c.band_lo > blo) c.band_lo = next_down(c.band_lo);
+      if ((double)c.band_hi < bhi) c.band_hi = next_up(c.band_hi);
+    }
+  }
+  return c;
+}
+
+// IN / OUT / BAND of one token (NaN = past kv_len -> kPad)
+__device__ __forceinline__ uint32_t classify(const RowView& v, const RowCut& c, float x, bool fast) {
+  if (x != x) return kPad;
+  if (c.bstar < 0) return __builtin_isfinite(x) ? kIn : kBand;  // -inf tokens fill the quota
+  if (!__builtin_isfinite(x)) return kOut;
+  if (fast) return x > c.band_hi ? kIn : (x < c.band_lo ? kOut : kBand);
+  const int bn = bin_of_v(v, x);
+  return bn > c.bstar ? kIn : (bn < c.bstar ? kOut : kBand);
+}
+
+__global__ __launch_bounds__(256) void select_init_kernel(SelectArgs a) {
+  const int row = blockIdx.x;
+  int32_t* st = a.stats + (int64_t)row * kStatStride;
+  for (int i = threadIdx.x; i < kStatStride; i += 256) st[i] = 0;
+  if (threadIdx.x == 0) st[0] = (int32_t)0xFFFFFFFFu;  // kmin starts at the largest key
+}
+
+// min / max keys of the finite scores (standalone selection; the scorers do
+// this themselves in the fused path)
+__global__ __launch_bounds__(kChunkThreads) void select_stats_kernel(SelectArgs a) {
+  const int row = blockIdx.y, c = blockIdx.x;
+  const int L = clamp_len(a.kv_lens[row / a.groups], a.row_stride);
+  const int t0 = c * kSelChunk + kPerThread * threadIdx.x;
+  if (L <= a.k || c * kSelChunk >= L) return;
+  float x[kPerThread];
+  load8(a.scores + (int64_t)row * a.row_stride, t0, L, x);
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e)
+    if (__builtin_isfinite(x[e])) {
+      const uint32_t key = score_key(x[e]);
+      kmin = min(kmin, key);
+      kmax = max(kmax, key);
+    }
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
+  if ((threadIdx.x & 63) == 0 && kmin <= kmax) {
+    int32_t* st = a.stats + (int64_t)row * kStatStride;
+    atomicMin(reinterpret_cast<unsigned int*>(st), kmin);
+    atomicMax(reinterpret_cast<unsigned int*>(st + 1), kmax);
+  }
+}
+
+__global__ __launch_bounds__(kChunkThreads) void select_hist_kernel(SelectArgs a) {
+  __shared__ int hist[kBins];
+  const int row = blockIdx.y, c = blockIdx.x;
+  const RowView v = row_view(a, row);
+  if (v.L <= a.k || c * kSelChunk >= v.L || !v.any_finite) return;
+  for (int i = threadIdx.x; i < kBins; i += kChunkThreads) hist[i] = 0;
+  __syncthreads();
+  float x[kPerThread];
+  const int t0 = c * kSelChunk + kPerThread * threadIdx.x;
+  load8(a.scores + (int64_t)row * a.row_stride, t0, v.L, x);
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    const bool fin = __builtin_isfinite(x[e]);
+    hist_add(hist, fin ? bin_of_v(v, x[e]) : 0, fin);
+  }
+  __syncthreads();
+  int32_t* gh = a.stats + (int64_t)row * kStatStride + 8;
+  for (int i = threadIdx.x; i < kBins; i += kChunkThreads)
+    if (hist[i]) atomicAdd(&gh[i], hist[i]);
+}
+
+template <bool FAST>
+__global__ __launch_bounds__(kChunkThreads) void select_classify_kernel(SelectArgs a) {
+  __shared__ ChunkShared sh;
+  __shared__ int s_band[kSelChunk];
+  __shared__ int s_nband;
+  __shared__ __attribute__((aligned(16))) float s_terms[kSelWaves][kWave];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int row = blockIdx.y, c = blockIdx.x;
+  const RowView v = row_view(a, row);
+  if (v.L <= a.k || c * kSelChunk >= v.L) return;
+  const RowCut cut = row_cut(a, row, v, sh, FAST);
+  if (tid == 0) s_nband = 0;
+  __syncthreads();
+  float x[kPerThread];
+  const int t0 = c * kSelChunk + kPerThread * tid;
+  load8(a.scores + (int64_t)row * a.row_stride, t0, v.L, x);
+  int n_in = 0, n_neg = 0;
+  uint32_t* keys = reinterpret_cast<uint32_t*>(a.keys) + (int64_t)row * a.row_stride;
+  int32_t* st = a.stats + (int64_t)row * kStatStride;
+  uint64_t* band = a.band + (int64_t)row * kBandCap;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    const uint32_t cl = classify(v, cut, x[e], FAST);
+    n_in += cl == kIn;
+    n_neg += (x[e] == -__builtin_inff());
+    if (cl == kBand) {
+      if (FAST && cut.bstar >= 0) {
+        s_band[atomicAdd(&s_nband, 1)] = t0 + e;  // re-scored below
+      } else {
+        const uint32_t key = score_key(x[e]);
+        keys[t0 + e] = key;
+        const int slot = atomicAdd(&st[2], 1);
+        if (slot < kBandCap) band[slot] = ((uint64_t)key << 32) | (uint32_t)~(uint32_t)(t0 + e);
+      }
+    }
+  }
+  n_in = chunk_sum_i(n_in, sh.redi);
+  n_neg = chunk_sum_i(n_neg, sh.redi);  // (barrier: s_band complete)
+  if (tid == 0) {
+    int32_t* cc = a.chunk_counts + ((int64_t)row * a.nchunks + c) * 2;
+    cc[0] = n_in;
+    cc[1] = n_neg;
+  }
+  if constexpr (FAST) {
+    const int nb = s_nband;
+    const int g = row % a.groups, b = row / a.groups;
+    for (int i = wid; i < nb; i += kSelWaves) {
+      const int t = s_band[i];
+      const uint32_t key = score_key(exact_dsa_score(a.score, b, g, t, s_terms[wid]));
+      if (lane == 0) {
+        keys[t] = key;
+        const int slot = atomicAdd(&st[2], 1);
+        if (slot < kBandCap) band[slot] = ((uint64_t)key << 32) | (uint32_t)~(uint32_t)t;
+      }
+    }
+  }
+}
+
+struct EmitShared {
+  ChunkShared cs;
+  uint64_t band[kBandCap];
+  uint32_t chosen[kSelChunk / 32];  // chunk-local bitmap of kept band tokens
+  int red2[kSelWaves];
+};
+
+template <bool FAST>
+__global__ __launch_bounds__(kChunkThreads) void select_emit_kernel(SelectArgs a) {
+  __shared__ union {
+    EmitShared e;
+    SelShared one;  // fallback: one block finishes the row
+  } u;
+  __shared__ __attribute__((aligned(16))) float s_terms[kSelWaves][kWave];
+  const int tid = threadIdx.x;
+  const int row = blockIdx.y, c = blockIdx.x;
+  const RowView v = row_view(a, row);
+  const int k = a.k;
+  int32_t* out = a.indices + (int64_t)row * k;
+  const int cstart = c * kSelChunk;
+  if (v.L <= k) {  // every token kept (dense-equivalent)
+    for (int t = cstart + tid; t < min(v.L, cstart + kSelChunk); t += kChunkThreads) out[t] = t;
+    if (c == 0) {
+      for (int i = v.L + tid; i < k; i += kChunkThreads) out[i] = -1;
+      if (a.counts && tid == 0) a.counts[row] = v.L;
+    }
+    return;
+  }
+  if (cstart >= v.L) return;
+  const int32_t* st = a.stats + (int64_t)row * kStatStride;
+  const int nband = st[2];
+  if (nband > kBandCap) {
+    if (c == 0) select_row_block<kMaxNI, false, FAST>(a, row, u.one, s_terms);
+    return;
+  }
+  const RowCut cut = row_cut(a, row, v, u.e.cs, FAST);
+  // per-chunk counts: kept-for-sure before this chunk and in total
+  const int nch = (v.L + kSelChunk - 1) / kSelChunk;
+  const int32_t* cc = a.chunk_counts + (int64_t)row * a.nchunks * 2;
+  int in_before = 0, in_total = 0, neg_before = 0;
+  for (int i = tid; i < nch; i += kChunkThreads) {
+    in_total += cc[2 * i];
+    if (i < c) {
+      in_before += cc[2 * i];
+      neg_before += cc[2 * i + 1];
+    }
+  }
+  in_total = chunk_sum_i(in_total, u.e.cs.redi);
+  in_before = chunk_sum_i(in_before, u.e.cs.redi);
+  neg_before = chunk_sum_i(neg_before, u.e.cs.redi);
+  const int need = k - in_total;  // BAND tokens to keep (>= 1)
+
+  // band: sort (key desc, position asc) = descending 64-bit composite
+  int nb_pow = 1;
+  while (nb_pow < nband) nb_pow <<= 1;
+  for (int i = tid; i < nb_pow; i += kChunkThreads)
+    u.e.band[i] = i < nband ? a.band[(int64_t)row * kBandCap + i] : 0ull;
+  for (int i = tid; i < kSelChunk / 32; i += kChunkThreads) u.e.chosen[i] = 0u;
+  __syncthreads();
+  for (int size = 2; size <= nb_pow; size <<= 1)
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < nb_pow / 2; i += kChunkThreads) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool desc = (lo & size) == 0;
+        const uint64_t x0 = u.e.band[lo], x1 = u.e.band[hi];
+        if ((x0 < x1) == desc) {
+          u.e.band[lo] = x1;
+          u.e.band[hi] = x0;
+        }
+      }
+      __syncthreads();
+    }
+  // kept band entries: the first `need`; those of this chunk go to the
+  // bitmap, those before it shift the offset
+  int chosen_before = 0;
+  if (cut.bstar >= 0) {
+    for (int i = tid; i < need && i < nband; i += kChunkThreads) {
+      const int t = (int)~(uint32_t)(u.e.band[i] & 0xFFFFFFFFull);
+      if (t < cstart) ++chosen_before;
+      else if (t < cstart + kSelChunk) atomicOr(&u.e.chosen[(t - cstart) >> 5], 1u << ((t - cstart) & 31));
+    }
+  }
+  chosen_before = chunk_sum_i(chosen_before, u.e.red2);  // (barrier: bitmap complete)
+
+  float x[kPerThread];
+  const int t0 = cstart + kPerThread * tid;
+  load8(a.scores + (int64_t)row * a.row_stride, t0, v.L, x);
+  uint32_t keep = 0;
+  int nkeep = 0, nneg = 0;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    const uint32_t cl = classify(v, cut, x[e], FAST);
+    bool kp = cl == kIn;
+    if (cl == kBand) {
+      if (cut.bstar >= 0) {
+        const int r = t0 + e - cstart;
+        kp = (u.e.chosen[r >> 5] >> (r & 31)) & 1u;
+      } else {
+        ++nneg;  // -inf filler: decided by rank below
+      }
+    }
+    keep |= (uint32_t)kp << e;
+    nkeep += kp;
+  }
+  int total;
+  int offset;
+  if (cut.bstar >= 0) {
+    offset = in_before + chosen_before + block_excl_scan<kChunkThreads>(nkeep, u.e.cs.tmp, &total);
+  } else {
+    // fewer finite scores than k: all finite kept, then -inf ones by position
+    const int need_neg = k - in_total;
+    const int neg_rank = neg_before + block_excl_scan<kChunkThreads>(nneg, u.e.cs.tmp, &total);
+    int taken_before = min(max(need_neg, 0), neg_before);
+    // kept so far in earlier chunks: their finite ones plus their taken -inf
+    offset = in_before + taken_before;
+    // this thread: finite kept before it in the chunk + -inf taken before it
+    int fin_prefix = block_excl_scan<kChunkThreads>(nkeep, u.e.cs.tmp, &total);
+    const int take_before_me = min(max(need_neg, 0), neg_rank) - taken_before;
+    offset += fin_prefix + take_before_me;
+    int r = neg_rank;
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      if (x[e] == -__builtin_inff()) {
+        if (r < need_neg) keep |= 1u << e;
+        ++r;
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e)
+    if ((keep >> e) & 1u) {
+      if (offset < k) out[offset] = t0 + e;
+      ++offset;
+    }
+  if (a.counts && c == 0 && tid == 0) a.counts[row] = k;
 }
 
 // ------------------------------------------------------------------ launch
 
-hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
+int select_max_row() { return kMaxChunks * kMaxNI * kTile; }
+
+static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+size_t select_workspace_bytes(int rows, int row_stride) {
+  const int nch = (row_stride + kSelChunk - 1) / kSelChunk;
+  return align256((size_t)rows * row_stride * 4) + align256((size_t)rows * kStatStride * 4) +
+         align256((size_t)rows * nch * 2 * 4) + align256((size_t)rows * kBandCap * 8);
+}
+
+void select_bind_workspace(SelectArgs* a, void* ws) {
+  const int rows = a->batch * a->groups;
+  a->nchunks = (a->row_stride + kSelChunk - 1) / kSelChunk;
+  char* p = static_cast<char*>(ws);
+  a->keys = reinterpret_cast<float*>(p);
+  p += align256((size_t)rows * a->row_stride * 4);
+  a->stats = reinterpret_cast<int32_t*>(p);
+  p += align256((size_t)rows * kStatStride * 4);
+  a->chunk_counts = reinterpret_cast<int32_t*>(p);
+  p += align256((size_t)rows * a->nchunks * 2 * 4);
+  a->band = reinterpret_cast<uint64_t*>(p);
+}
+
+hipError_t launch_select_init(const SelectArgs& a, hipStream_t st) {
   const int rows = a.batch * a.groups;
   if (rows == 0) return hipSuccess;
-  topk_row_kernel<<<rows, kTopkThreads, 0, st>>>(a);
+  select_init_kernel<<<rows, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 
-hipError_t launch_topk_threshold(const TopkArgs& a, float* thr, hipStream_t st) {
+hipError_t launch_select_stats(const SelectArgs& a, hipStream_t st) {
   const int rows = a.batch * a.groups;
-  if (rows == 0) return hipSuccess;
-  topk_threshold_kernel<<<rows, kTopkThreads, 0, st>>>(a, thr);
+  if (rows == 0 || a.nchunks == 0) return hipSuccess;
+  select_stats_kernel<<<dim3(a.nchunks, rows), kChunkThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 
-hipError_t launch_refine_band(const RefineArgs& a, hipStream_t st) {
-  const ScoreArgs& s = a.score;
-  if (s.batch == 0 || s.max_kv_len == 0) return hipSuccess;
-  dim3 grid((s.max_kv_len + 255) / 256, s.batch * s.num_kv_heads);
-  refine_band_kernel<<<grid, 256, 0, st>>>(a);
+hipError_t launch_select(const SelectArgs& a, hipStream_t st) {
+  const int rows = a.batch * a.groups;
+  if (rows == 0) return hipSuccess;
+  if (a.row_stride > select_max_row()) return hipErrorInvalidValue;
+  const dim3 grid(max(a.nchunks, 1), rows);
+  if (a.nchunks > 0) {
+    select_hist_kernel<<<grid, kChunkThreads, 0, st>>>(a);
+    if (a.row_bound) select_classify_kernel<true><<<grid, kChunkThreads, 0, st>>>(a);
+    else select_classify_kernel<false><<<grid, kChunkThreads, 0, st>>>(a);
+  }
+  // emit also covers the output of rows whose tokens are all kept
+  const dim3 egrid(max(a.nchunks, (a.k + kSelChunk - 1) / kSelChunk), rows);
+  if (a.row_bound) select_emit_kernel<true><<<egrid, kChunkThreads, 0, st>>>(a);
+  else select_emit_kernel<false><<<egrid, kChunkThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 
