@@ -367,33 +367,45 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_mla_kernel(AttnArgs a) {
   }
 }
 
-// Combine of the MLA partials: one 64-thread block per (request, wave w,
-// N tile n); lane l owns heads 32w + 8(r/4) + 4(l/32) + r%4 (r < 16) at
-// dv = 256*(n/8) + 8*(l%32) + n%8.
-__global__ __launch_bounds__(64) void attn_mla_combine_kernel(AttnArgs a, int nw) {
-  const int lane = threadIdx.x;
-  const int n = blockIdx.x % 16, w = (blockIdx.x / 16) % nw, b = blockIdx.x / (16 * nw);
+// Combine of the MLA partials: one 512-thread block per (request, wave w,
+// value half): thread (tile n, lane l) owns heads 32w + 8(r/4) + 4(l/32) + r%4
+// (r < 16) at dv = 256*half + 8*(l%32) + n%8.  Split weights
+// 2^(m_s - M) / sum_s l_s 2^(m_s - M) are computed once per head into LDS; the
+// result is transposed through LDS so output rows are written contiguously.
+constexpr int kMlaMaxSplits = 64;
+
+__global__ __launch_bounds__(512) void attn_mla_combine_kernel(AttnArgs a, int nw) {
+  __shared__ float s_w[kMlaMaxSplits][32];   // weight of split s for head 32w + h
+  __shared__ float s_out[32][256 + 4];       // [head][dv in half], padded
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, n = tid >> 6;  // tile within the half: 0..7
+  const int half = blockIdx.x % 2, w = (blockIdx.x / 2) % nw, b = blockIdx.x / (2 * nw);
   const int col = lane & 31, hf = lane >> 5;
-  const int dv = 256 * (n / 8) + 8 * col + (n % 8);
-  float M[16], inv[16], o[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int h = 32 * w + 8 * (r / 4) + 4 * hf + (r % 4);
+  const int S = a.splits;
+  // ---- weights: thread h < 32 handles head 32w + h
+  if (tid < 32) {
+    const int h = 32 * w + tid;
     float mx = -__builtin_inff();
-    for (int s = 0; s < a.splits; ++s) mx = fmaxf(mx, a.part_ml[(((int64_t)b * a.splits + s) * a.q_heads + h) * 2]);
+    for (int s = 0; s < S; ++s) mx = fmaxf(mx, a.part_ml[(((int64_t)b * S + s) * a.q_heads + h) * 2]);
     float Ls = 0.0f;
-    if (mx != -__builtin_inff())
-      for (int s = 0; s < a.splits; ++s) {
-        const float* ml = a.part_ml + (((int64_t)b * a.splits + s) * a.q_heads + h) * 2;
-        if (ml[0] != -__builtin_inff()) Ls += ml[1] * exp2f(ml[0] - mx);
-      }
-    M[r] = mx;
-    inv[r] = Ls > 0.0f ? 1.0f / Ls : 0.0f;
-    o[r] = 0.0f;
+    for (int s = 0; s < S; ++s) {
+      const float* ml = a.part_ml + (((int64_t)b * S + s) * a.q_heads + h) * 2;
+      const float e = ml[0] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(ml[0] - mx);
+      s_w[s][tid] = e;
+      Ls += ml[1] * e;
+    }
+    const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+    for (int s = 0; s < S; ++s) s_w[s][tid] *= inv;
   }
-  for (int s = 0; s < a.splits; ++s) {
-    const int64_t blk = (int64_t)b * a.splits + s;
-    const float4* src = reinterpret_cast<const float4*>(a.part_o + (((blk * nw + w) * 16 + n) * 64 + lane) * 16);
+  __syncthreads();
+  // ---- weighted sum over splits of this thread's 16 partial values
+  float o[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) o[r] = 0.0f;
+  const int tile = 8 * half + n;
+  for (int s = 0; s < S; ++s) {
+    const int64_t blk = (int64_t)b * S + s;
+    const float4* src = reinterpret_cast<const float4*>(a.part_o + (((blk * nw + w) * 16 + tile) * 64 + lane) * 16);
     float v[16];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -401,21 +413,19 @@ __global__ __launch_bounds__(64) void attn_mla_combine_kernel(AttnArgs a, int nw
       v[4 * j] = q.x; v[4 * j + 1] = q.y; v[4 * j + 2] = q.z; v[4 * j + 3] = q.w;
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int h = 32 * w + 8 * (r / 4) + 4 * hf + (r % 4);
-      const float m = a.part_ml[(blk * a.q_heads + h) * 2];
-      if (m != -__builtin_inff()) o[r] += v[r] * exp2f(m - M[r]);
-    }
+    for (int r = 0; r < 16; ++r) o[r] += v[r] * s_w[s][8 * (r / 4) + 4 * hf + (r % 4)];
   }
+  // ---- transpose to [head][dv] and write rows
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int h = 32 * w + 8 * (r / 4) + 4 * hf + (r % 4);
-    const float val = o[r] * inv[r];
-    const int64_t oi = ((int64_t)b * a.q_heads + h) * kMlaDv + dv;
+  for (int r = 0; r < 16; ++r) s_out[8 * (r / 4) + 4 * hf + (r % 4)][8 * col + n] = o[r];
+  __syncthreads();
+  for (int i = tid; i < 32 * 256; i += 512) {
+    const int h = i / 256, d = i % 256;
+    const int64_t oi = ((int64_t)b * a.q_heads + 32 * w + h) * kMlaDv + 256 * half + d;
     if (a.out_dtype == 0)
-      reinterpret_cast<float*>(a.out)[oi] = val;
+      reinterpret_cast<float*>(a.out)[oi] = s_out[h][d];
     else
-      reinterpret_cast<uint16_t*>(a.out)[oi] = f32_to_bf16(val);
+      reinterpret_cast<uint16_t*>(a.out)[oi] = f32_to_bf16(s_out[h][d]);
   }
 }
 
@@ -455,7 +465,8 @@ bool attn_mla_supported(const AttnArgs& a) {
   return a.dtype == 1 && a.head_dim == kMlaD && a.v_dim == kMlaDv && a.num_kv_heads == 1 &&
          (a.q_heads == 32 || a.q_heads == 64 || a.q_heads == 128) && a.k == a.v &&
          a.k_page_stride == a.v_page_stride && a.k_token_stride == a.v_token_stride &&
-         a.k_num_pages == a.v_num_pages && (a.k_token_stride % 8) == 0 && (a.k_page_stride % 8) == 0;
+         a.k_num_pages == a.v_num_pages && (a.k_token_stride % 8) == 0 && (a.k_page_stride % 8) == 0 &&
+         a.k_sel <= kMlaMaxSplits * kMlaSplitRows;
 }
 
 bool attn_vec_supported(const AttnArgs& a) {
@@ -494,7 +505,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
   if (a.batch == 0) return hipSuccess;
   hipError_t e;
   if (attn_mla_supported(a)) {
-    if (a.chunk != kMlaSplitRows) return hipErrorInvalidValue;
+    if (a.chunk != kMlaSplitRows || a.splits > kMlaMaxSplits) return hipErrorInvalidValue;
     dim3 grid(a.splits, a.batch);
     const int nw = a.q_heads / 32;
     switch (nw) {
@@ -504,7 +515,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
       default: return hipErrorInvalidValue;
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    attn_mla_combine_kernel<<<a.batch * nw * 16, 64, 0, st>>>(a, nw);
+    attn_mla_combine_kernel<<<a.batch * nw * 2, 512, 0, st>>>(a, nw);
     return hipGetLastError();
   } else {
     dim3 grid(a.splits, a.batch * a.num_kv_heads);

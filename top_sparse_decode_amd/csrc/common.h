@@ -29,6 +29,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return uint16_t(u >> 16);
 }
 
+// Smallest bfloat16 >= x for finite x >= 0 (bits in the low half).
+__device__ __forceinline__ uint32_t bf16_round_up(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u & 0xFFFFu) u += 0x10000u;
+  return u >> 16;
+}
+
 // Order-preserving key: larger float -> larger key; -0 maps like +0.
 __device__ __forceinline__ uint32_t score_key(float f) {
   uint32_t u = __float_as_uint(f);

@@ -143,6 +143,9 @@ __global__ __launch_bounds__(256) void score_exact_kernel(ScoreArgs a) {
 // are charged 2^-23 per addition, which also covers truncating adders.
 __device__ __forceinline__ float gamma_n(float n, float u) { return n * u / (1.0f - n * u); }
 
+constexpr int kScoreIters = 16;                    // 32-token tiles per wave
+constexpr int kScoreSpan = 4 * 32 * kScoreIters;   // tokens per block
+
 // MT = query heads / 16.  Each wave handles 32 consecutive tokens per
 // iteration as two 16-token N tiles: C[16 heads x 16 tokens] per (M tile, N
 // tile), K = 128 split into four 32-wide steps.  MFMA operand layout for
@@ -152,18 +155,23 @@ __device__ __forceinline__ float gamma_n(float n, float u) { return n * u / (1.0
 // group l/16 carries dims 32*ks + 8*(l/16) .. +8, so four lanes read 64
 // contiguous bytes of a key row.
 template <int MT>
-__global__ __launch_bounds__(256) void score_dsa_mfma_kernel(ScoreArgs a, int iters) {
+__global__ __launch_bounds__(256) void score_dsa_mfma_kernel(ScoreArgs a) {
   constexpr int D = 128;
   constexpr int KS = D / 32;
   constexpr int G = 16 * MT;
   __shared__ float s_a[D];   // a_d = sum_h |w_h| |q_hd|
   __shared__ float s_part[2][D];
+  __shared__ int s_page[kScoreSpan / 16 + 2];  // page ids of the block's tokens (-1: absent)
+  // the group's query heads, rows padded by 16 bytes so a fragment's 16 rows
+  // fall on different banks
+  __shared__ __attribute__((aligned(16))) uint16_t s_q[G][D + 8];
 
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int b = blockIdx.y / a.num_kv_heads, g = blockIdx.y % a.num_kv_heads;
   const int cap = min(a.max_kv_len, a.max_pages * a.page_size);
   const int L = clamp_len(a.kv_lens[b], cap);
-  const int span = 4 * 32 * iters;
+  constexpr int iters = kScoreIters;
+  constexpr int span = kScoreSpan;
   const int tb0 = blockIdx.x * span;
   float* row = a.scores + (int64_t)blockIdx.y * a.max_kv_len;
   if (tb0 >= a.max_kv_len) return;
@@ -176,6 +184,55 @@ __global__ __launch_bounds__(256) void score_dsa_mfma_kernel(ScoreArgs a, int it
   const uint16_t* qb = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)b * a.q_heads + g * G) * D;
   const float* wb = a.head_weights + (int64_t)b * a.q_heads + g * G;
 
+  // page ids of the span: logical page p of the block -> physical page
+  {
+    const int p0 = tb0 / a.page_size;
+    const int np = (tb0 + span - 1) / a.page_size - p0 + 1;
+    for (int i = threadIdx.x; i < np; i += 256) {
+      const int lp = p0 + i;
+      int page = -1;
+      if (lp < a.max_pages && lp * a.page_size < L) {
+        page = a.block_table[(int64_t)b * a.max_pages + lp];
+        if (page < 0 || page >= a.num_pages) page = -1;
+      }
+      s_page[i] = page;
+    }
+  }
+  __syncthreads();  // s_page visible
+  const int col = lane & 15, grp = lane >> 4;
+  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k) + (int64_t)g * a.head_stride;
+  // One 32-token tile (two 16-token N tiles) per step.
+  struct Tile {
+    bf16x8 kf[2][KS];
+    bool ok[2];
+  };
+  // Page ids of the block's span come from LDS (staged below), so a tile's
+  // loads never wait on a global load issued after the previous tile's; an
+  // absent token loads row 0 of the pool (always mapped) and is masked.
+  auto load_tile = [&](int t0, Tile& T) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int t = t0 + 16 * n + col;
+      const int page = t < L ? s_page[t / a.page_size - tb0 / a.page_size] : -1;
+      const bool ok = page >= 0;
+      const int64_t off = ok ? (int64_t)page * a.page_stride + (int64_t)(t % a.page_size) * a.token_stride : 0;
+      T.ok[n] = ok;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        T.kf[n][ks] = *reinterpret_cast<const bf16x8*>(kbase + off + 32 * ks + 8 * grp);
+    }
+  };
+  auto tile_t0 = [&](int it) { return tb0 + (it * 4 + wid) * 32; };
+  // The first two tiles' loads go out before the per-block set-up below.
+  Tile T[3];
+  load_tile(tile_t0(0), T[0]);
+  load_tile(tile_t0(1), T[1]);
+
+  // the group's query rows into LDS (visible after the barriers below)
+  for (int i = threadIdx.x; i < G * D / 8; i += 256) {
+    const int h = i / (D / 8), c = i % (D / 8);
+    *reinterpret_cast<uint4*>(&s_q[h][8 * c]) = *reinterpret_cast<const uint4*>(qb + h * D + 8 * c);
+  }
   // a_d for the bound: 256 threads, two halves of the heads per dim.
   {
     const int d = threadIdx.x & (D - 1), half = threadIdx.x >> 7;
@@ -187,97 +244,68 @@ __global__ __launch_bounds__(256) void score_dsa_mfma_kernel(ScoreArgs a, int it
     __syncthreads();
   }
 
-  const int col = lane & 15, grp = lane >> 4;
-  bf16x8 qf[MT][KS];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qf[mt][ks] = *reinterpret_cast<const bf16x8*>(qb + (16 * mt + col) * D + 32 * ks + 8 * grp);
   float wv[MT][4];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) wv[mt][r] = wb[16 * mt + 4 * grp + r];
-  float av[KS][8];
+  // The bound's sum_d a_d |k_d| runs on the matrix cores as one more M tile
+  // whose row 0 holds a_d rounded up to bf16 (an upper bound of a_d) and
+  // whose B operand is |K|.
+  bf16x8 af[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
+  for (int ks = 0; ks < KS; ++ks) {
+    u32x4 w4;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) av[ks][e] = s_a[32 * ks + 8 * grp + e];
-
-  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k) + (int64_t)g * a.head_stride;
-  const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = col == 0 ? bf16_round_up(s_a[32 * ks + 8 * grp + 2 * e]) : 0u;
+      const uint32_t hi = col == 0 ? bf16_round_up(s_a[32 * ks + 8 * grp + 2 * e + 1]) : 0u;
+      w4[e] = lo | (hi << 16);
+    }
+    af[ks] = __builtin_bit_cast(bf16x8, w4);
+  }
   const float u24 = 5.9604644775390625e-8f, u23 = 1.1920928955078125e-7f;
   const float gD = gamma_n((float)D, u23), gH = gamma_n((float)(G + 1), u24);
+  const float bcoef = 2.0f * gH * (1.0f + gD) + 2.0f * gD;
   float dmax = 0.0f;
   float smin = __builtin_inff(), smax = -__builtin_inff();  // finite scores of this lane
 
-  // One 32-token tile (two 16-token N tiles) per step; the next tile's key
-  // fragments are loaded before the current one is computed, so two tiles'
-  // worth of loads (16 KB per wave) are in flight.
-  struct Tile {
-    bf16x8 kf[2][KS];
-    bool ok[2];
-  };
-  auto load_tile = [&](int t0, Tile& T) {
+  auto compute_tile = [&](int t0, Tile& T) {
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
-      const int t = t0 + 16 * n + col;
-      bool ok = t < L;
-      int64_t off = 0;
-      if (ok) {
-        const int page = bt[t / a.page_size];
-        ok = page >= 0 && page < a.num_pages;
-        off = (int64_t)page * a.page_stride + (int64_t)(t % a.page_size) * a.token_stride;
+      if (!T.ok[n]) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) T.kf[n][ks] = bf16x8{};
       }
-      T.ok[n] = ok;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        T.kf[n][ks] = ok ? *reinterpret_cast<const bf16x8*>(kbase + off + 32 * ks + 8 * grp) : bf16x8{};
-    }
-  };
-  auto compute_tile = [&](int t0, const Tile& T) {
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
       floatx4 acc[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         acc[mt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[mt][ks], T.kf[n][ks], acc[mt], 0, 0, 0);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              *reinterpret_cast<const bf16x8*>(&s_q[16 * mt + col][32 * ks + 8 * grp]), T.kf[n][ks], acc[mt], 0, 0, 0);
       }
-      float s = 0.0f, m = 0.0f;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float x = acc[mt][r] > 0.0f ? acc[mt][r] : 0.0f;
-          s += wv[mt][r] * x;
-          m += fabsf(wv[mt][r]) * x;
-        }
-      float bsum = 0.0f;
+      floatx4 accb = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const u32x4 kw = __builtin_bit_cast(u32x4, T.kf[n][ks]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          bsum += av[ks][2 * e] * fabsf(bf16_lo(kw[e]));
-          bsum += av[ks][2 * e + 1] * fabsf(bf16_hi(kw[e]));
-        }
+        const u32x4 ka = kw & 0x7FFF7FFFu;  // |K|
+        accb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks], __builtin_bit_cast(bf16x8, ka), accb, 0, 0, 0);
       }
+      // s~ = sum_h w_h relu(dot_h): this lane's 4*MT heads, then the 4 lane groups
+      float s = 0.0f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s = __builtin_fmaf(wv[mt][r], fmaxf(acc[mt][r], 0.0f), s);
       s += __shfl_xor(s, 16);
       s += __shfl_xor(s, 32);
-      m += __shfl_xor(m, 16);
-      m += __shfl_xor(m, 32);
-      bsum += __shfl_xor(bsum, 16);
-      bsum += __shfl_xor(bsum, 32);
       const int t = t0 + 16 * n + col;
-      if (T.ok[n]) {
-        // |fast - exact| <= gH*(2M + 2gD*B) + 2gD*B   (see topk.hip / header)
-        const float bterm = 2.0f * gD * bsum;
-        const float d = gH * (2.0f * m + bterm) + bterm;
-        dmax = fmaxf(dmax, d);
+      if (grp == 0 && T.ok[n]) {
+        // B_t = sum_d a_d |k_td| (row 0 of the extra tile, lanes 0..15) bounds both
+        // sum_h |w_h| relu(.) terms, so |s~ - s| <= B_t * (2 gH (1 + gD) + 2 gD)
+        dmax = fmaxf(dmax, accb[0] * bcoef);
       }
       if (grp == 0 && t < a.max_kv_len) row[t] = T.ok[n] ? s : -__builtin_inff();
       if (T.ok[n]) {
@@ -286,19 +314,13 @@ __global__ __launch_bounds__(256) void score_dsa_mfma_kernel(ScoreArgs a, int it
       }
     }
   };
-  auto tile_t0 = [&](int it) { return tb0 + (it * 4 + wid) * 32; };
-  auto live = [&](int it) { return it < iters && tile_t0(it) < a.max_kv_len; };
-  Tile A, B;
-  if (live(0)) load_tile(tile_t0(0), A);
-  for (int it = 0; live(it); it += 2) {
-    const bool hasB = live(it + 1);
-    if (hasB) load_tile(tile_t0(it + 1), B);
-    compute_tile(tile_t0(it), A);
-    if (!hasB) break;
-    const bool hasA = live(it + 2);
-    if (hasA) load_tile(tile_t0(it + 2), A);
-    compute_tile(tile_t0(it + 1), B);
-    if (!hasA) break;
+  // Fully unrolled, with every look-ahead load unconditional (a tile past
+  // the row reads pool row 0 and is masked), so the compiler's wait counts
+  // are exact: tiles it+1 and it+2 are in flight while tile it is computed.
+#pragma unroll
+  for (int it = 0; it < iters; ++it) {
+    if (it + 2 < iters) load_tile(tile_t0(it + 2), T[(it + 2) % 3]);
+    if (tile_t0(it) < a.max_kv_len) compute_tile(tile_t0(it), T[it % 3]);
   }
   if (a.row_stats) {
     int32_t* stat = a.row_stats + (int64_t)blockIdx.y * kStatStride;
@@ -352,13 +374,12 @@ bool score_fast_supported(const ScoreArgs& a) {
 hipError_t launch_score_fast(const ScoreArgs& a, hipStream_t st) {
   if (a.batch == 0 || a.max_kv_len == 0) return hipSuccess;
   const int G = a.q_heads / a.num_kv_heads;
-  const int iters = 16;
-  dim3 grid((a.max_kv_len + 4 * 32 * iters - 1) / (4 * 32 * iters), a.batch * a.num_kv_heads);
+  dim3 grid((a.max_kv_len + kScoreSpan - 1) / kScoreSpan, a.batch * a.num_kv_heads);
   switch (G / 16) {
-    case 1: score_dsa_mfma_kernel<1><<<grid, 256, 0, st>>>(a, iters); break;
-    case 2: score_dsa_mfma_kernel<2><<<grid, 256, 0, st>>>(a, iters); break;
-    case 3: score_dsa_mfma_kernel<3><<<grid, 256, 0, st>>>(a, iters); break;
-    case 4: score_dsa_mfma_kernel<4><<<grid, 256, 0, st>>>(a, iters); break;
+    case 1: score_dsa_mfma_kernel<1><<<grid, 256, 0, st>>>(a); break;
+    case 2: score_dsa_mfma_kernel<2><<<grid, 256, 0, st>>>(a); break;
+    case 3: score_dsa_mfma_kernel<3><<<grid, 256, 0, st>>>(a); break;
+    case 4: score_dsa_mfma_kernel<4><<<grid, 256, 0, st>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
