@@ -43,6 +43,9 @@ def parse():
     p.add_argument("--replicas", type=int, default=3, help="input replicas rotated per step")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-requests", type=int, default=3, help="requests in the oracle sample")
+    p.add_argument("--copy-bytes", type=int, default=0,
+                   help="also run a plain device copy of this many bytes (3 launches) before the "
+                        "steps: the reference kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE")
     return p.parse_args()
 
 
@@ -50,7 +53,7 @@ def scorer_traffic(kernel_hash: str):
     """HBM bytes per scorer launch from the committed rocprofv3 counter
     summary, or None when it is missing or was taken on another version of
     the scorer source."""
-    path = os.path.join(PROFILES, "score_dsa_mfma_traffic.json")
+    path = os.path.join(PROFILES, "score_dsa_traffic.json")
     if not os.path.exists(path):
         return None
     try:
@@ -89,6 +92,15 @@ def main():
     alg_bytes = k_scored + k_gathered
 
     stream = torch.cuda.current_stream()
+    if args.copy_bytes > 0:
+        n = args.copy_bytes // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        say(f"[bench] copy reference: 3 x {n * 4} bytes")
+        del src, dst
     for i in range(args.warmup):
         steps[i % len(steps)].run(stream)
     torch.cuda.synchronize()
@@ -107,19 +119,19 @@ def main():
     say(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step")
 
     # ---- dominant kernel: the MFMA indexer scorer, events around each launch
-    groups = 1
+    groups, hi = 1, w.score_q.shape[1]
     sc = torch.empty((B, groups, w.max_kv_len), dtype=torch.float32, device=dev)
     bound = torch.empty((B, groups), dtype=torch.float32, device=dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     for i in range(min(args.warmup, 5)):
         s = steps[i % len(steps)]
-        api.sparse_score_paged(s.args.pages, s.args.score_k, s.score_q, 64, s.head_weights,
+        api.sparse_score_paged(s.args.pages, s.args.score_k, s.score_q, hi, s.head_weights,
                                api.RELU_WEIGHTED, 1.0, api.FAST, sc, bound, stream)
     for i in range(args.steps):
         s = steps[i % len(steps)]
         ev[i][0].record(stream)
-        api.sparse_score_paged(s.args.pages, s.args.score_k, s.score_q, 64, s.head_weights,
+        api.sparse_score_paged(s.args.pages, s.args.score_k, s.score_q, hi, s.head_weights,
                                api.RELU_WEIGHTED, 1.0, api.FAST, sc, bound, stream)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
@@ -153,7 +165,7 @@ def main():
         "step_gbps": round(alg_bytes / (ms_step * 1e-3) / 1e9, 1),
         "step_frac_of_hbm_peak": round(alg_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         "roofline": {
-            "kernel": "score_dsa_mfma_kernel<4>",
+            "kernel": "score_dsa_kernel<4, 4, 4, 32>",
             "bound": "hbm",
             "achieved": round(score_gbps, 1),
             "peak": PEAK_HBM_GBPS,

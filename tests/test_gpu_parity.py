@@ -49,6 +49,10 @@ SMALL = {
     "dsa": (4, dict(batch=2, kv_len=[9000, 4100], topk=2048)),
     "dsa_short": (4, dict(batch=3, kv_len=[1, 100, 2047], topk=2048)),
     "dsa_mixed": (5, dict(batch=3, min_len=2000, max_len=9000, topk=2048)),
+    # the matrix-core scorer at 16 and 32 indexer heads and small pages
+    "dsa_h16_p16": (4, dict(batch=2, kv_len=[3000, 1500], topk=512, idx_heads=16, page_size=16)),
+    "dsa_h32": (4, dict(batch=3, kv_len=[7000, 64, 4097], topk=256, idx_heads=32)),
+    "dsa_h32_p32": (4, dict(batch=2, kv_len=[5000, 33], topk=1024, idx_heads=32, page_size=32)),
 }
 
 
@@ -80,7 +84,9 @@ def test_exact_scores_bitwise(name):
 
 
 @pytest.mark.parametrize("kw", [dict(batch=2, kv_len=[9000, 4100]),
-                                dict(batch=2, kv_lens=[6000, 3000], bias_frac=0.01)])
+                                dict(batch=2, kv_lens=[6000, 3000], bias_frac=0.01),
+                                dict(batch=2, kv_len=[3000, 1500], idx_heads=16, page_size=16),
+                                dict(batch=3, kv_len=[5000, 700, 1], idx_heads=32, page_size=32)])
 def test_fast_scores_within_bound(kw):
     cfg = 5 if "kv_lens" in kw else 4
     w = synth.make_workload(cfg, **kw)
@@ -88,7 +94,7 @@ def test_fast_scores_within_bound(kw):
     step = api.prepare(w, precision=api.FAST)
     scores = torch.empty((w.batch, 1, w.max_kv_len), dtype=torch.float32, device="cuda")
     bound = torch.empty((w.batch, 1), dtype=torch.float32, device="cuda")
-    api.sparse_score_paged(step.args.pages, step.args.score_k, step.score_q, 64, step.head_weights,
+    api.sparse_score_paged(step.args.pages, step.args.score_k, step.score_q, w.score_q.shape[1], step.head_weights,
                            api.RELU_WEIGHTED, 1.0, api.FAST, scores, bound)
     torch.cuda.synchronize()
     ref = oracle.score(w.block_table, w.kv_lens, w.score_k, w.score_q, w.head_weights, w.mode, 1.0,

@@ -20,6 +20,11 @@ ARCH = os.environ.get("SD_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["api.hip", "score.hip", "topk.hip", "attn.hip"]
 
+# Per-source options.  The scorer keeps its matrix-core accumulators in
+# ordinary VGPRs (its epilogue reads every one of them on the VALU; AGPR
+# accumulators would cost a v_accvgpr_read per value).
+EXTRA = {"score.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 FLAGS = [
     f"--offload-arch={ARCH}",
     "-O3",
@@ -39,7 +44,7 @@ def build(verbose: bool = False) -> str:
     objs = []
     for src in SOURCES:
         obj = os.path.join(CSRC, src.replace(".hip", ".o"))
-        cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.check_call(cmd)

@@ -11,7 +11,7 @@
 //    product and per sum; for bf16 operands the product is exact, so a fused
 //    multiply-add per step gives the same bits), then reduces over the group's
 //    heads in head order.  Bit-identical to any other evaluation in that order.
-//  * score_dsa_mfma_kernel: the DSA indexer score s_t = sum_h w_h relu(q_h.k_t)
+//  * score_dsa_kernel: the DSA indexer score s_t = sum_h w_h relu(q_h.k_t)
 //    ("Overlap DSA heuristic prev_topk write-back on the aux stream",
 //    Description: the indexer scores every token before the top-k kernel) on
 //    bf16 MFMA 16x16x32 tiles -- heads x tokens x head_dim is a real dense
@@ -20,6 +20,9 @@
 //    be made exact (see topk.hip).
 #include "common.h"
 #include "kernels.h"
+
+#include <algorithm>
+#include <type_traits>
 
 namespace sd {
 
@@ -143,126 +146,197 @@ __global__ __launch_bounds__(256) void score_exact_kernel(ScoreArgs a) {
 // are charged 2^-23 per addition, which also covers truncating adders.
 __device__ __forceinline__ float gamma_n(float n, float u) { return n * u / (1.0f - n * u); }
 
-constexpr int kScoreIters = 16;                    // 32-token tiles per wave
-constexpr int kScoreSpan = 4 * 32 * kScoreIters;   // tokens per block
+typedef __attribute__((address_space(3))) void* lds_ptr;
 
-// MT = query heads / 16.  Each wave handles 32 consecutive tokens per
-// iteration as two 16-token N tiles: C[16 heads x 16 tokens] per (M tile, N
-// tile), K = 128 split into four 32-wide steps.  MFMA operand layout for
-// 16x16x32 bf16: lane l holds A[row l%16][8 k-values], B[8 k-values][col
-// l%16], and C[rows 4*(l/16)+r][col l%16].  Which head dims a lane's 8
-// k-values stand for is free as long as A and B agree; here k-step ks, lane
-// group l/16 carries dims 32*ks + 8*(l/16) .. +8, so four lanes read 64
-// contiguous bytes of a key row.
-template <int MT>
-__global__ __launch_bounds__(256) void score_dsa_mfma_kernel(ScoreArgs a) {
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+constexpr int kTileTok = 32;                // tokens per wave per step
+constexpr int kTileBytes = kTileTok * 256;  // their bf16 K rows (D = 128)
+
+// relu on the bit pattern: negative floats (and -0) are negative integers.
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// Sum over the 16 lanes of a DPP row (the 16 rows of one MFMA column group).
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, false));  // row_ror 4
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false));  // row_ror 8
+  return v;
+}
+
+// The K ring is filled by DMA (global_load_lds), which the compiler tracks
+// as one LDS write per instruction in flight: an ordinary LDS load would make
+// it drain every DMA before the read.  Fragment reads are therefore one asm
+// block that waits for its own results (so no output register is live while
+// its load is in flight).  Eight 16-byte reads: four k-steps of the two
+// 16-token halves of a tile, the halves 4096 bytes apart.
+template <int OFF>
+__device__ __forceinline__ void ring_read8(u32x4 (&f)[8], const uint32_t (&addr)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %8 offset:%12\n\t"
+      "ds_read_b128 %1, %9 offset:%12\n\t"
+      "ds_read_b128 %2, %10 offset:%12\n\t"
+      "ds_read_b128 %3, %11 offset:%12\n\t"
+      "ds_read_b128 %4, %8 offset:%13\n\t"
+      "ds_read_b128 %5, %9 offset:%13\n\t"
+      "ds_read_b128 %6, %10 offset:%13\n\t"
+      "ds_read_b128 %7, %11 offset:%13\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3]), "=&v"(f[4]), "=&v"(f[5]), "=&v"(f[6]),
+        "=&v"(f[7])
+      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "i"(OFF), "i"(OFF + 4096)
+      : "memory");
+}
+// A score into the LDS staging row (same reason: no compiler-visible LDS access).
+__device__ __forceinline__ void lds_store_f32(uint32_t addr, float v) {
+  asm volatile("ds_write_b32 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "i"(N) : "memory");
+}
+
+// MT = query heads / 16, NW waves per block, S ring stages per wave.
+//
+// Each wave scores 32-token tiles; tile it of wave w starts at token
+// tb0 + (it * NW + w) * 32.  A tile's K rows (32 x 256 bytes) reach the
+// wave's LDS ring by DMA, eight 1 KB instructions of four whole rows each
+// (64 lanes x 16 bytes, fully coalesced), S - 1 tiles ahead of the one being
+// computed.  Within a row the 16-byte units are stored XOR-swizzled
+// (position = unit ^ (row & 15)) so that the fragment reads below hit 16
+// different bank groups.
+//
+// MFMA 16x16x32 bf16, C[16 heads x 16 tokens] per (M tile, token half),
+// K = 128 in four 32-wide steps.  Operand layout: lane l holds A[row l%16]
+// [8 k-values], B[8 k-values][col l%16], C[rows 4*(l/16)+r][col l%16].  The
+// head dims a lane's 8 k-values stand for are free as long as A and B agree:
+// k-step ks, lane group l/16 carries dims 32*ks + 8*(l/16) .. +8.
+template <int MT, int NW, int S, int MAXIT>
+__global__ __launch_bounds__(NW * 64) void score_dsa_kernel(ScoreArgs a, int iters) {
   constexpr int D = 128;
   constexpr int KS = D / 32;
   constexpr int G = 16 * MT;
-  __shared__ float s_a[D];   // a_d = sum_h |w_h| |q_hd|
-  __shared__ float s_part[2][D];
-  __shared__ int s_page[kScoreSpan / 16 + 2];  // page ids of the block's tokens (-1: absent)
-  // the group's query heads, rows padded by 16 bytes so a fragment's 16 rows
-  // fall on different banks
-  __shared__ __attribute__((aligned(16))) uint16_t s_q[G][D + 8];
+  __shared__ __attribute__((aligned(1024))) uint4 s_ring[NW * S * kTileBytes / 16];
+  __shared__ float s_out[NW * kTileTok * MAXIT];
 
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, grp = lane >> 4;
   const int b = blockIdx.y / a.num_kv_heads, g = blockIdx.y % a.num_kv_heads;
   const int cap = min(a.max_kv_len, a.max_pages * a.page_size);
   const int L = clamp_len(a.kv_lens[b], cap);
-  constexpr int iters = kScoreIters;
-  constexpr int span = kScoreSpan;
+  const int span = NW * kTileTok * iters;
   const int tb0 = blockIdx.x * span;
   float* row = a.scores + (int64_t)blockIdx.y * a.max_kv_len;
   if (tb0 >= a.max_kv_len) return;
+  const int tend = min(tb0 + span, a.max_kv_len);
   if (tb0 >= L) {  // nothing to score: fill -inf
-    const int end = min(tb0 + span, a.max_kv_len);
-    for (int t = tb0 + threadIdx.x; t < end; t += 256) row[t] = -__builtin_inff();
+    for (int t = tb0 + threadIdx.x; t < tend; t += NW * 64) row[t] = -__builtin_inff();
     return;
   }
+  const int ps = a.page_size;
+  const int p0 = tb0 / ps;
+  // tiles of this wave that hold a token below L
+  const int n_it = min(iters, max(0, (L - tb0 - wid * kTileTok + NW * kTileTok - 1) / (NW * kTileTok)));
 
+  // page ids of the span's logical pages, lane i <- page p0 + i (-1: absent)
+  // (loaded from a clamped slot, checked once the loads below are out)
+  const int lp = p0 + lane;
+  const int pg_raw = a.block_table[(int64_t)b * a.max_pages + min(lp, a.max_pages - 1)];
+  // this wave's query fragments and weights
   const uint16_t* qb = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)b * a.q_heads + g * G) * D;
   const float* wb = a.head_weights + (int64_t)b * a.q_heads + g * G;
-
-  // page ids of the span: logical page p of the block -> physical page
-  {
-    const int p0 = tb0 / a.page_size;
-    const int np = (tb0 + span - 1) / a.page_size - p0 + 1;
-    for (int i = threadIdx.x; i < np; i += 256) {
-      const int lp = p0 + i;
-      int page = -1;
-      if (lp < a.max_pages && lp * a.page_size < L) {
-        page = a.block_table[(int64_t)b * a.max_pages + lp];
-        if (page < 0 || page >= a.num_pages) page = -1;
-      }
-      s_page[i] = page;
-    }
-  }
-  __syncthreads();  // s_page visible
-  const int col = lane & 15, grp = lane >> 4;
-  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k) + (int64_t)g * a.head_stride;
-  // One 32-token tile (two 16-token N tiles) per step.
-  struct Tile {
-    bf16x8 kf[2][KS];
-    bool ok[2];
-  };
-  // Page ids of the block's span come from LDS (staged below), so a tile's
-  // loads never wait on a global load issued after the previous tile's; an
-  // absent token loads row 0 of the pool (always mapped) and is masked.
-  auto load_tile = [&](int t0, Tile& T) {
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      const int t = t0 + 16 * n + col;
-      const int page = t < L ? s_page[t / a.page_size - tb0 / a.page_size] : -1;
-      const bool ok = page >= 0;
-      const int64_t off = ok ? (int64_t)page * a.page_stride + (int64_t)(t % a.page_size) * a.token_stride : 0;
-      T.ok[n] = ok;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        T.kf[n][ks] = *reinterpret_cast<const bf16x8*>(kbase + off + 32 * ks + 8 * grp);
-    }
-  };
-  auto tile_t0 = [&](int it) { return tb0 + (it * 4 + wid) * 32; };
-  // The first two tiles' loads go out before the per-block set-up below.
-  Tile T[3];
-  load_tile(tile_t0(0), T[0]);
-  load_tile(tile_t0(1), T[1]);
-
-  // the group's query rows into LDS (visible after the barriers below)
-  for (int i = threadIdx.x; i < G * D / 8; i += 256) {
-    const int h = i / (D / 8), c = i % (D / 8);
-    *reinterpret_cast<uint4*>(&s_q[h][8 * c]) = *reinterpret_cast<const uint4*>(qb + h * D + 8 * c);
-  }
-  // a_d for the bound: 256 threads, two halves of the heads per dim.
-  {
-    const int d = threadIdx.x & (D - 1), half = threadIdx.x >> 7;
-    float acc = 0.0f;
-    for (int h = half; h < G; h += 2) acc += fabsf(wb[h]) * fabsf(bf16_to_f32(qb[h * D + d]));
-    s_part[half][d] = acc;
-    __syncthreads();
-    if (threadIdx.x < D) s_a[threadIdx.x] = s_part[0][threadIdx.x] + s_part[1][threadIdx.x];
-    __syncthreads();
-  }
-
-  float wv[MT][4];
+  bf16x8 qf[MT][KS];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[mt][ks] = *reinterpret_cast<const bf16x8*>(qb + (16 * mt + col) * D + 32 * ks + 8 * grp);
+  float wv[MT][4], wa[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
     for (int r = 0; r < 4; ++r) wv[mt][r] = wb[16 * mt + 4 * grp + r];
-  // The bound's sum_d a_d |k_d| runs on the matrix cores as one more M tile
-  // whose row 0 holds a_d rounded up to bf16 (an upper bound of a_d) and
-  // whose B operand is |K|.
+    wa[mt] = fabsf(wb[16 * mt + col]);
+  }
+
+  // Every ordinary load completes before the first DMA: the compiler counts
+  // DMA and ordinary loads as different kinds of memory event and, with both
+  // outstanding, can only wait for zero.  These empty asm uses make it wait
+  // here, once, for all of them.
+  asm volatile("" : : "v"(pg_raw));
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" : : "v"(qf[mt][ks]));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) asm volatile("" : : "v"(wv[mt][r]));
+    asm volatile("" : : "v"(wa[mt]));
+  }
+  const int mypage = (lp < a.max_pages && lp * ps < L && pg_raw >= 0 && pg_raw < a.num_pages) ? pg_raw : -1;
+
+  // DMA lane layout: lane (r = l/16, p = l%16) of chunk c' moves row 4c'+r,
+  // 16-byte unit p ^ (4c'+r) of a 16-row half tile.
+  const int64_t ts2 = a.token_stride * 2;
+  uint32_t vofs[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) vofs[c] = (uint32_t)((4 * c + grp) * ts2 + 16 * (col ^ (4 * c + grp)));
+  const char* kbase = reinterpret_cast<const char*>(a.k) + (int64_t)g * a.head_stride * 2;
+  const uint32_t ring0 = (uint32_t)(uintptr_t)(lds_ptr)s_ring + (uint32_t)(wid * S * kTileBytes);
+  auto tile_t0 = [&](int it) { return tb0 + (it * NW + wid) * kTileTok; };
+  auto half_page = [&](int t) { return __builtin_amdgcn_readlane(mypage, min(t / ps - p0, 63)); };
+  auto issue = [&](int it, int stage) {
+    const int t0 = tile_t0(it);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int t = t0 + 16 * h;
+      const int pg = max(half_page(t), 0);  // an absent page reads page 0 (masked)
+      const char* hb = kbase + ((int64_t)pg * a.page_stride + (int64_t)(t % ps) * a.token_stride) * 2;
+      const uint32_t dst = ring0 + (uint32_t)(stage * kTileBytes + h * 4096);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        __builtin_amdgcn_global_load_lds(hb + vofs[c], (lds_ptr)(uintptr_t)(dst + c * 1024), 16, 0, 0);
+    }
+  };
+  // The first S - 1 tiles go out before the per-wave set-up below, whether
+  // or not the wave has that many (a tile past L reads pages it holds, or
+  // page 0, and is never used), so that the compiler sees straight-line
+  // code and keeps its waits for the loads above exact.
+  static_for<0, S - 1>([&](auto j) { issue(decltype(j)::value, decltype(j)::value); });
+
+  // a_d = sum_h |w_h| |q_hd| for the bound: this lane's 4*MT heads per dim,
+  // then the 16 lanes of each column group.  The bound's sum_d a_d |k_d|
+  // runs on the matrix cores as one more M tile whose row 0 holds a_d
+  // rounded up to bf16 (an upper bound of a_d) and whose B operand is |K|.
   bf16x8 af[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    u32x4 w4;
+    float part[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) part[j] = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const u32x4 w4 = __builtin_bit_cast(u32x4, qf[mt][ks]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        part[2 * e] += wa[mt] * fabsf(bf16_lo(w4[e]));
+        part[2 * e + 1] += wa[mt] * fabsf(bf16_hi(w4[e]));
+      }
+    }
+    u32x4 p4;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const uint32_t lo = col == 0 ? bf16_round_up(s_a[32 * ks + 8 * grp + 2 * e]) : 0u;
-      const uint32_t hi = col == 0 ? bf16_round_up(s_a[32 * ks + 8 * grp + 2 * e + 1]) : 0u;
-      w4[e] = lo | (hi << 16);
+      const float lo = row16_sum(part[2 * e]), hi = row16_sum(part[2 * e + 1]);
+      p4[e] = col == 0 ? (bf16_round_up(lo) | (bf16_round_up(hi) << 16)) : 0u;
     }
-    af[ks] = __builtin_bit_cast(bf16x8, w4);
+    af[ks] = __builtin_bit_cast(bf16x8, p4);
   }
   const float u24 = 5.9604644775390625e-8f, u23 = 1.1920928955078125e-7f;
   const float gD = gamma_n((float)D, u23), gH = gamma_n((float)(G + 1), u24);
@@ -270,58 +344,80 @@ __global__ __launch_bounds__(256) void score_dsa_mfma_kernel(ScoreArgs a) {
   float dmax = 0.0f;
   float smin = __builtin_inff(), smax = -__builtin_inff();  // finite scores of this lane
 
-  auto compute_tile = [&](int t0, Tile& T) {
+  // fragment read addresses: token row col, unit 4*ks + grp (swizzled)
+  uint32_t raddr[4];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) raddr[ks] = ring0 + col * 256 + 16 * ((4 * ks + grp) ^ col);
+  const uint32_t out0 = (uint32_t)(uintptr_t)(lds_ptr)s_out;
+
+  auto compute = [&](int it, auto sc) {
+    constexpr int s = decltype(sc)::value;
+    u32x4 kb[8];
+    ring_read8<s * kTileBytes>(kb, raddr);
+    const int t0 = tile_t0(it);
+    float sv[2];
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
-      if (!T.ok[n]) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) T.kf[n][ks] = bf16x8{};
-      }
       floatx4 acc[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         acc[mt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              *reinterpret_cast<const bf16x8*>(&s_q[16 * mt + col][32 * ks + 8 * grp]), T.kf[n][ks], acc[mt], 0, 0, 0);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[mt][ks], __builtin_bit_cast(bf16x8, kb[4 * n + ks]),
+                                                            acc[mt], 0, 0, 0);
       }
       floatx4 accb = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 kw = __builtin_bit_cast(u32x4, T.kf[n][ks]);
-        const u32x4 ka = kw & 0x7FFF7FFFu;  // |K|
-        accb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks], __builtin_bit_cast(bf16x8, ka), accb, 0, 0, 0);
-      }
+      for (int ks = 0; ks < KS; ++ks)
+        accb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks], __builtin_bit_cast(bf16x8, kb[4 * n + ks] & 0x7FFF7FFFu),
+                                                       accb, 0, 0, 0);
       // s~ = sum_h w_h relu(dot_h): this lane's 4*MT heads, then the 4 lane groups
-      float s = 0.0f;
+      float sum = 0.0f;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s = __builtin_fmaf(wv[mt][r], fmaxf(acc[mt][r], 0.0f), s);
-      s += __shfl_xor(s, 16);
-      s += __shfl_xor(s, 32);
+        for (int r = 0; r < 4; ++r) sum = __builtin_fmaf(wv[mt][r], relu_bits(acc[mt][r]), sum);
+      sum += __shfl_xor(sum, 16);
+      sum += __shfl_xor(sum, 32);
       const int t = t0 + 16 * n + col;
-      if (grp == 0 && T.ok[n]) {
+      const bool ok = t < L && half_page(t0 + 16 * n) >= 0;
+      if (ok) {
         // B_t = sum_d a_d |k_td| (row 0 of the extra tile, lanes 0..15) bounds both
         // sum_h |w_h| relu(.) terms, so |s~ - s| <= B_t * (2 gH (1 + gD) + 2 gD)
-        dmax = fmaxf(dmax, accb[0] * bcoef);
+        if (grp == 0) dmax = fmaxf(dmax, accb[0] * bcoef);
+        smin = fminf(smin, sum);
+        smax = fmaxf(smax, sum);
       }
-      if (grp == 0 && t < a.max_kv_len) row[t] = T.ok[n] ? s : -__builtin_inff();
-      if (T.ok[n]) {
-        smin = fminf(smin, s);
-        smax = fmaxf(smax, s);
-      }
+      sv[n] = ok ? sum : -__builtin_inff();
     }
+    // lanes 0..15 hold tokens t0 + col, lanes 16..31 the second half's
+    if (lane < 32) lds_store_f32(out0 + 4 * (t0 - tb0 + lane), lane < 16 ? sv[0] : sv[1]);
   };
-  // Fully unrolled, with every look-ahead load unconditional (a tile past
-  // the row reads pool row 0 and is masked), so the compiler's wait counts
-  // are exact: tiles it+1 and it+2 are in flight while tile it is computed.
-#pragma unroll
-  for (int it = 0; it < iters; ++it) {
-    if (it + 2 < iters) load_tile(tile_t0(it + 2), T[(it + 2) % 3]);
-    if (tile_t0(it) < a.max_kv_len) compute_tile(tile_t0(it), T[it % 3]);
+
+  for (int it0 = 0; it0 < n_it; it0 += S) {
+    static_for<0, S>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      const int it = it0 + s;
+      if (it < n_it) {
+        const int ahead = min(n_it - 1 - it, S - 1);  // tiles in flight after tile it
+        if (ahead == S - 1) {
+          issue(it + S - 1, (s + S - 1) % S);
+          wait_vmcnt<8 * (S - 1)>();
+        } else {
+          static_for<0, S - 1>([&](auto j) {
+            if (ahead == decltype(j)::value) wait_vmcnt<8 * decltype(j)::value>();
+          });
+        }
+        compute(it, sc);
+      }
+    });
   }
+  // no DMA may still be writing the ring when the wave leaves (a wave with
+  // fewer than S - 1 tiles has prologue tiles in flight), and the staged
+  // scores are written
+  wait_vmcnt<0>();
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   if (a.row_stats) {
     int32_t* stat = a.row_stats + (int64_t)blockIdx.y * kStatStride;
     note_minmax(stat, smin, smin <= smax);
@@ -334,6 +430,9 @@ __global__ __launch_bounds__(256) void score_dsa_mfma_kernel(ScoreArgs a) {
     dmax = dmax * 1.001f + 1e-30f;
     if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(a.row_bound + blockIdx.y), __float_as_uint(dmax));
   }
+  __syncthreads();
+  // every token below L lies in a scored tile; the rest of the span is -inf
+  for (int t = tb0 + threadIdx.x; t < tend; t += NW * 64) row[t] = t < L ? s_out[t - tb0] : -__builtin_inff();
 }
 
 // ------------------------------------------------------------------ launch
@@ -366,23 +465,48 @@ hipError_t launch_score_exact(const ScoreArgs& a, hipStream_t st) {
 
 bool score_fast_supported(const ScoreArgs& a) {
   const int G = a.q_heads / a.num_kv_heads;
-  return a.dtype == 1 && a.mode == 2 && a.head_dim == 128 && (G % 16) == 0 && G <= 64 &&
+  return a.dtype == 1 && a.mode == 2 && a.head_dim == 128 && (G == 16 || G == 32 || G == 64) &&
          (a.page_size % 16) == 0 && (a.token_stride % 8) == 0 && (a.page_stride % 8) == 0 &&
          (a.head_stride % 8) == 0;
 }
 
+namespace {
+constexpr int kScoreNW = 4, kScoreStages = 4, kScoreMaxIt = 32, kScoreBlocksPerCU = 1;
+
+template <int MT>
+hipError_t launch_dsa(const ScoreArgs& a, hipStream_t st) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  // tiles per wave: enough blocks to fill the chip once, and a span that
+  // overlaps at most 64 logical pages (their ids ride in one register per
+  // lane): span / page_size pages when the span is a whole number of pages,
+  // else up to two more.
+  const int64_t rows = (int64_t)a.batch * a.num_kv_heads;
+  const int64_t tiles = rows * ((a.max_kv_len + kTileTok - 1) / kTileTok);
+  const int64_t per_block = (tiles + (int64_t)cus * kScoreBlocksPerCU - 1) / ((int64_t)cus * kScoreBlocksPerCU);
+  int iters = (int)std::min<int64_t>((per_block + kScoreNW - 1) / kScoreNW, kScoreMaxIt);
+  auto pages_spanned = [&](int it) {
+    const int span = kScoreNW * kTileTok * it;
+    return span % a.page_size == 0 ? span / a.page_size : (span - 1) / a.page_size + 2;
+  };
+  while (iters > 1 && pages_spanned(iters) > 64) --iters;
+  iters = std::max(iters, 1);
+  const int span = kScoreNW * kTileTok * iters;
+  dim3 grid((a.max_kv_len + span - 1) / span, (unsigned)rows);
+  score_dsa_kernel<MT, kScoreNW, kScoreStages, kScoreMaxIt><<<grid, kScoreNW * 64, 0, st>>>(a, iters);
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_score_fast(const ScoreArgs& a, hipStream_t st) {
   if (a.batch == 0 || a.max_kv_len == 0) return hipSuccess;
-  const int G = a.q_heads / a.num_kv_heads;
-  dim3 grid((a.max_kv_len + kScoreSpan - 1) / kScoreSpan, a.batch * a.num_kv_heads);
-  switch (G / 16) {
-    case 1: score_dsa_mfma_kernel<1><<<grid, 256, 0, st>>>(a); break;
-    case 2: score_dsa_mfma_kernel<2><<<grid, 256, 0, st>>>(a); break;
-    case 3: score_dsa_mfma_kernel<3><<<grid, 256, 0, st>>>(a); break;
-    case 4: score_dsa_mfma_kernel<4><<<grid, 256, 0, st>>>(a); break;
+  switch (a.q_heads / a.num_kv_heads / 16) {
+    case 1: return launch_dsa<1>(a, st);
+    case 2: return launch_dsa<2>(a, st);
+    case 4: return launch_dsa<4>(a, st);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace sd
