@@ -128,9 +128,12 @@ typedef struct sd_pages {
  *   head_scale   GROUP_SUM factor (ignored by the other modes)
  *   scores       device [batch][num_kv_heads][max_kv_len] float; entries at
  *                t >= kv_len (and absent tokens) are set to -inf
- *   row_bound    device [batch][num_kv_heads] float or NULL.  When given, it
- *                receives d >= 0 with |scores[t] - exact score(t)| <= d for
- *                every t < kv_len of the row (0 for SD_SCORE_EXACT).
+ *   row_bound    device [batch][num_kv_heads] float or NULL, caller-initialised
+ *                (normally to 0).  SD_SCORE_FAST raises each entry to at
+ *                least d >= 0 with |scores[t] - exact score(t)| <= d for
+ *                every t < kv_len of the row (a max into the existing value,
+ *                so one zero fill serves any number of calls on the same
+ *                inputs); SD_SCORE_EXACT leaves it unchanged.
  * Follows "Add TriAttention ...", Key Design Decisions (direct paged-pool
  * scoring) and, for RELU_WEIGHTED, the DSA indexer of "Overlap DSA heuristic
  * prev_topk write-back ...", Description. */

@@ -72,7 +72,7 @@ def test_exact_scores_bitwise(name):
     step = api.prepare(w, precision=api.EXACT)
     groups = w.score_k.shape[1]
     scores = torch.empty((w.batch, groups, w.max_kv_len), dtype=torch.float32, device="cuda")
-    bound = torch.full((w.batch, groups), -1.0, device="cuda")
+    bound = torch.full((w.batch, groups), -1.0, device="cuda")  # exact scores leave it alone
     api.sparse_score_paged(step.args.pages, step.args.score_k, step.score_q, w.score_q.shape[1],
                            step.head_weights, api.MODES[w.mode], w.head_scale, api.EXACT, scores, bound)
     torch.cuda.synchronize()
@@ -80,7 +80,7 @@ def test_exact_scores_bitwise(name):
                        w.head_scale, w.max_kv_len)
     got = scores.cpu().numpy()
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
-    assert torch.all(bound == 0)
+    assert torch.all(bound == -1.0)
 
 
 @pytest.mark.parametrize("kw", [dict(batch=2, kv_len=[9000, 4100]),
@@ -93,7 +93,7 @@ def test_fast_scores_within_bound(kw):
     say(f"[fast bound] {kw}")
     step = api.prepare(w, precision=api.FAST)
     scores = torch.empty((w.batch, 1, w.max_kv_len), dtype=torch.float32, device="cuda")
-    bound = torch.empty((w.batch, 1), dtype=torch.float32, device="cuda")
+    bound = torch.zeros((w.batch, 1), dtype=torch.float32, device="cuda")  # max-accumulated
     api.sparse_score_paged(step.args.pages, step.args.score_k, step.score_q, w.score_q.shape[1], step.head_weights,
                            api.RELU_WEIGHTED, 1.0, api.FAST, scores, bound)
     torch.cuda.synchronize()

@@ -128,15 +128,14 @@ sd_status check_score(const sd_pages* pg, const sd_pool* k, const void* q, sd_dt
 }
 
 sd_status run_score(const sd::ScoreArgs& a, sd_score_precision precision, hipStream_t st) {
-  if (precision == SD_SCORE_FAST && sd::score_fast_supported(a)) {
-    if (a.row_bound) {
-      sd_status s = hip_status(sd::launch_fill_f32(a.row_bound, (int64_t)a.batch * a.num_kv_heads, 0.0f, st),
-                               "fill");
-      if (s != SD_OK) return s;
-    }
+  // the fast scorer max-accumulates its bound into row_bound (zeroed by the
+  // caller, or by the selection's init kernel in the fused path); exact
+  // scores carry no error and leave it alone
+  if (precision == SD_SCORE_FAST && sd::score_fast_supported(a))
     return hip_status(sd::launch_score_fast(a, st), "score_fast");
-  }
-  return hip_status(sd::launch_score_exact(a, st), "score_exact");
+  sd::ScoreArgs e = a;
+  e.row_bound = nullptr;
+  return hip_status(sd::launch_score_exact(e, st), "score_exact");
 }
 
 // ---------------------------------------------------------------- attention

@@ -40,7 +40,7 @@ struct SelectArgs {
   int32_t* indices;     // [batch][groups][k]
   int32_t* counts;      // [batch][groups] or null
   float* keys;          // scratch, same shape as scores
-  const float* row_bound;  // fast scores: per-row bound on |fast - exact|; null = exact scores
+  float* row_bound;     // fast scores: per-row bound on |fast - exact| (zeroed by init); null = exact
   ScoreArgs score;      // fast scores: the inputs needed to re-score band tokens exactly
   int32_t* stats;       // [rows][kStatStride]
   int32_t* chunk_counts;  // [rows][nchunks][2]: kept-for-sure count, -inf count

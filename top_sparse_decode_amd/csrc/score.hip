@@ -90,7 +90,6 @@ __global__ __launch_bounds__(256) void score_exact_kernel(ScoreArgs a) {
   const int L = clamp_len(a.kv_lens[b], cap);
   const int t = (blockIdx.x * 4 + wid) * kWave + lane;
   float* row = a.scores + (int64_t)blockIdx.y * a.max_kv_len;
-  if (a.row_bound && blockIdx.x == 0 && threadIdx.x == 0) a.row_bound[blockIdx.y] = 0.0f;
   const bool in_row = t < a.max_kv_len;
   bool ok = in_row && t < L;
   int64_t off = 0;
@@ -225,6 +224,7 @@ __global__ __launch_bounds__(NW * 64) void score_dsa_kernel(ScoreArgs a, int ite
   constexpr int G = 16 * MT;
   __shared__ __attribute__((aligned(1024))) uint4 s_ring[NW * S * kTileBytes / 16];
   __shared__ float s_out[NW * kTileTok * MAXIT];
+  __shared__ uint32_t s_red[NW][3];
 
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -418,19 +418,37 @@ __global__ __launch_bounds__(NW * 64) void score_dsa_kernel(ScoreArgs a, int ite
   // scores are written
   wait_vmcnt<0>();
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  if (a.row_stats) {
-    int32_t* stat = a.row_stats + (int64_t)blockIdx.y * kStatStride;
-    note_minmax(stat, smin, smin <= smax);
-    note_minmax(stat, smax, smin <= smax);
-  }
-  if (a.row_bound) {
-    dmax = wave_max(dmax);
-    // 1e-3 relative slack covers the rounding of the bound's own evaluation,
-    // the absolute term any flushed subnormal.
-    dmax = dmax * 1.001f + 1e-30f;
-    if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(a.row_bound + blockIdx.y), __float_as_uint(dmax));
+  // the block's min / max finite score keys and its bound: one atomic each
+  uint32_t kmin = smin <= smax ? score_key(smin) : 0xFFFFFFFFu;
+  uint32_t kmax = smin <= smax ? score_key(smax) : 0u;
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
+  dmax = wave_max(dmax);
+  if (lane == 0) {
+    s_red[wid][0] = kmin;
+    s_red[wid][1] = kmax;
+    s_red[wid][2] = __float_as_uint(dmax);
   }
   __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t bmin = s_red[0][0], bmax = s_red[0][1];
+    float bd = __uint_as_float(s_red[0][2]);
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      bmin = min(bmin, s_red[w][0]);
+      bmax = max(bmax, s_red[w][1]);
+      bd = fmaxf(bd, __uint_as_float(s_red[w][2]));
+    }
+    if (a.row_stats && bmin <= bmax) {
+      int32_t* stat = a.row_stats + (int64_t)blockIdx.y * kStatStride;
+      atomicMin(reinterpret_cast<unsigned int*>(stat), bmin);
+      atomicMax(reinterpret_cast<unsigned int*>(stat + 1), bmax);
+    }
+    // 1e-3 relative slack covers the rounding of the bound's own evaluation,
+    // the absolute term any flushed subnormal.
+    if (a.row_bound)
+      atomicMax(reinterpret_cast<unsigned int*>(a.row_bound + blockIdx.y), __float_as_uint(bd * 1.001f + 1e-30f));
+  }
   // every token below L lies in a scored tile; the rest of the span is -inf
   for (int t = tb0 + threadIdx.x; t < tend; t += NW * 64) row[t] = t < L ? s_out[t - tb0] : -__builtin_inff();
 }

@@ -165,17 +165,6 @@ __device__ __forceinline__ void find_bin_n(const int* hist, int* tmp, int* win, 
   __syncthreads();
 }
 
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o));
-  return v;
-}
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
-  return v;
-}
-
 // Exact score of one token, evaluated by a whole wave in the library's exact
 // order (DSA mode, bf16, head_dim 128): lane h forms dot_h left to right,
 // then the terms w_h * relu(dot_h) are added in head order.
@@ -638,6 +627,8 @@ __global__ __launch_bounds__(256) void select_init_kernel(SelectArgs a) {
   int32_t* st = a.stats + (int64_t)row * kStatStride;
   for (int i = threadIdx.x; i < kStatStride; i += 256) st[i] = 0;
   if (threadIdx.x == 0) st[0] = (int32_t)0xFFFFFFFFu;  // kmin starts at the largest key
+  // the fast scorer max-accumulates its error bound into row_bound
+  if (threadIdx.x == 0 && a.row_bound) a.row_bound[row] = 0.0f;
 }
 
 // min / max keys of the finite scores (standalone selection; the scorers do
