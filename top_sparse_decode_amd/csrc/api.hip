@@ -205,7 +205,8 @@ sd_status plan_attn(const sd_pages* pg, const void* q, sd_dtype q_dtype, int32_t
   a.chunk = sd::attn_rows_per_split(a, mla);
   a.splits = (k_sel + a.chunk - 1) / a.chunk;
   const size_t parts = (size_t)pg->batch * q_heads * a.splits;
-  plan->ws_bytes = align_up(parts * (size_t)v_dim * 4) + align_up(parts * 2 * 4);
+  // partial outputs: fp32, bf16 on the MLA path
+  plan->ws_bytes = align_up(parts * (size_t)v_dim * (mla ? 2 : 4)) + align_up(parts * 2 * 4);
   plan->a = a;
   plan->mla = mla;
   return SD_OK;
@@ -215,7 +216,7 @@ void bind_attn_ws(AttnPlan* p, void* ws) {
   const size_t parts = (size_t)p->a.batch * p->a.q_heads * p->a.splits;
   char* base = static_cast<char*>(ws);
   p->a.part_o = reinterpret_cast<float*>(base);
-  p->a.part_ml = reinterpret_cast<float*>(base + align_up(parts * (size_t)p->a.v_dim * 4));
+  p->a.part_ml = reinterpret_cast<float*>(base + align_up(parts * (size_t)p->a.v_dim * (p->mla ? 2 : 4)));
 }
 
 // ---------------------------------------------------------------- fused plan

@@ -14,6 +14,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace sd {
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -185,14 +187,16 @@ __global__ __launch_bounds__(256) void attn_vec_kernel(AttnArgs a) {
 
 // Sparse MLA decode on bf16 MFMA 32x32x16.  One block per (split of 128
 // selected rows, request) with NW waves (one per SIMD); wave w owns query
-// heads 32w..32w+31.  All 128 latent rows of the split are fetched at once
-// by direct global->LDS loads and stay resident (147 KB of LDS):
+// heads 32w..32w+31.  The split's 128 latent rows reach LDS by DMA
+// (global_load_lds) in four 32-row chunks and stay resident (147 KB):
 //   S^T[token][head] = K_chunk (A operand, 32 tokens x 16 dims per step) *
 //     Q^T (B operand, the wave's 32 heads over all 36 steps of the 576 dims,
-//     held in registers), for all four 32-row chunks; the block max is then
-//     exact, P = 2^(x - max) is formed once (bf16, in registers) and never
-//     rescaled;
-//   O[:, 0:256] += P * V[:, 0:256], then O[:, 256:512] += P * V[:, 256:512].
+//     held in registers), chunk by chunk as each chunk lands; the block max
+//     is then exact, P = 2^(x - max) is formed once (bf16, in registers) and
+//     never rescaled;
+//   O[:, 0:256] += P * V[:, 0:256], then O[:, 256:512] += P * V[:, 256:512],
+//     the V operand fetched with the transposing LDS read (ds_read_b64_tr_b16)
+//     that hands each lane one value column of four rows.
 // Splitting the value columns across the two passes halves the live
 // accumulators (128 instead of 256 per lane) without computing S twice.
 // 32x32x16 operand layout: lane l holds A[row l%32][8 k-values of half
@@ -200,8 +204,18 @@ __global__ __launch_bounds__(256) void attn_vec_kernel(AttnArgs a) {
 // 8*(r/4)+4*(l/32)+(r%4), r<16][col l%32].
 //
 // LDS rows are 72 sixteen-byte units plus one pad unit (1168-byte stride):
-// the 32 rows read by one A fragment fall on different banks, and every LDS
-// address is affine in the loop indices (immediate offsets).
+// the 32 rows read by one A fragment fall on different banks.
+//
+// DMA bookkeeping.  Every DMA instruction moves 64 consecutive LDS units and
+// always has an active lane, so each wave knows exactly how many it has in
+// flight and waits for a chunk with an exact count.  The compiler cannot
+// order its own waits against DMA (it would drain all of it before any
+// ordinary load or LDS read), so nothing in between does either: the row
+// offsets sit in registers (lane l: rows l and l + 64) and are fetched with
+// v_readlane, and the K fragments are read by asm blocks that wait for
+// their own results.  A row that is not usable (index -1, past kv_len, bad
+// page) is filled from the request's first query row instead: any finite
+// data will do, its probability is exactly zero.
 constexpr int kMlaD = 576;
 constexpr int kMlaDv = 512;
 constexpr int kMlaChunkRows = 32;
@@ -209,19 +223,59 @@ constexpr int kMlaChunks = 4;
 constexpr int kMlaSplitRows = kMlaChunkRows * kMlaChunks;  // 128 rows per block
 constexpr int kMlaUnits = kMlaD / 8;                       // 72 units per row
 constexpr int kMlaStride = kMlaUnits + 1;                  // LDS row stride in units
-
-__device__ __forceinline__ int mla_unit(int row, int unit) { return row * kMlaStride + unit; }
+constexpr int kMlaRowBytes = kMlaStride * 16;              // 1168
+constexpr int kMlaChunkUnits = kMlaChunkRows * kMlaStride;  // 2336
+constexpr int kMlaChunkInsts = (kMlaChunkUnits + 63) / 64;  // 37 DMA instructions per chunk
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+
+// Wait until at most N vector memory operations of this wave are in flight
+// (the counter holds 63 at most; a smaller count only waits longer), then
+// meet the block at a barrier.  One asm block: __syncthreads() would add a
+// workgroup fence, for which the compiler drains every DMA in flight.  LDS
+// needs no fence: data a DMA has delivered is visible to the whole block.
+template <int N>
+__device__ __forceinline__ void mla_wait_vmcnt_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "i"(N < 63 ? N : 63) : "memory");
+}
+
+// Six K fragments (k-steps s0 .. s0+5) of this lane's row; one asm block
+// that waits for its own results.
+template <int S0>
+__device__ __forceinline__ void mla_kfrag6(u32x4 (&f)[6], uint32_t addr) {
+  asm volatile(
+      "ds_read_b128 %0, %6 offset:%7\n\t"
+      "ds_read_b128 %1, %6 offset:%8\n\t"
+      "ds_read_b128 %2, %6 offset:%9\n\t"
+      "ds_read_b128 %3, %6 offset:%10\n\t"
+      "ds_read_b128 %4, %6 offset:%11\n\t"
+      "ds_read_b128 %5, %6 offset:%12\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3]), "=&v"(f[4]), "=&v"(f[5])
+      : "v"(addr), "i"(32 * S0), "i"(32 * (S0 + 1)), "i"(32 * (S0 + 2)), "i"(32 * (S0 + 3)),
+        "i"(32 * (S0 + 4)), "i"(32 * (S0 + 5))
+      : "memory");
+}
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void mla_static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    mla_static_for<I + 1, N>(f);
+  }
+}
 
 template <int NW>
 __global__ __launch_bounds__(NW * 64, 1) void attn_mla_kernel(AttnArgs a) {
-  constexpr int NT = NW * 64;
   constexpr int KSTEPS = kMlaD / 16;  // 36
+  // DMA instructions of one chunk issued by wave w (instructions i = w, w + NW, ...)
+  constexpr int kInst0 = (kMlaChunkInsts + NW - 1) / NW;  // wave 0
+  constexpr int kInstN = kMlaChunkInsts / NW;             // waves 1.. (equal when NW divides 37: never)
   __shared__ __attribute__((aligned(16))) uint4 s_kv[kMlaSplitRows * kMlaStride];
-  __shared__ int64_t s_off[kMlaSplitRows];
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 31, hf = lane >> 5;
   const int b = blockIdx.y;
   const int split = blockIdx.x;
@@ -231,67 +285,93 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_mla_kernel(AttnArgs a) {
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
   const int32_t* sel = a.indices + (int64_t)b * a.k_sel;
   const float c = a.scale * kLog2e;
-  const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.k);
+  const char* kb = reinterpret_cast<const char*>(a.k);
+  const char* qrow0 = reinterpret_cast<const char*>(a.q) + (int64_t)b * a.q_heads * kMlaD * 2;
   const int head0 = wid * 32;
 
-  // ---- row offsets of the split (element offset, -1 = not usable)
-  for (int r = tid; r < kMlaSplitRows; r += NT) {
-    const int i = r0 + r;
-    const int t = i < r1 ? sel[i] : -1;
-    s_off[r] = sel_row(a, bt, L, t, 0, a.k_page_stride, a.k_head_stride, a.k_token_stride, a.k_num_pages);
-  }
-  __syncthreads();
-  // unusable rows are zero (their probabilities are zero; values must be finite)
-  for (int u = tid; u < kMlaSplitRows * kMlaStride; u += NT)
-    if (s_off[u / kMlaStride] < 0) s_kv[u] = make_uint4(0, 0, 0, 0);
-  // ---- every usable row: one direct global->LDS load per 16-byte unit; a
-  // wave's instruction covers 64 consecutive LDS units (pad units: no load)
-  for (int ub = wid * 64; ub < kMlaSplitRows * kMlaStride; ub += NT) {
-    const int u = ub + lane;
-    const int row = u / kMlaStride, slot = u % kMlaStride;
-    const int64_t off = s_off[row];
-    if (off >= 0 && slot < kMlaUnits)
-      __builtin_amdgcn_global_load_lds(kb + off + slot * 8, (lds_ptr_t)&s_kv[ub], 16, 0, 0);
-  }
-  // Q^T fragments: lane holds head (head0+col), dims 16s + 8hf .. +8
+  // ---- Q^T fragments: lane holds head (head0+col), dims 16s + 8hf .. +8
   bf16x8 qf[KSTEPS];
   {
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)b * a.q_heads + head0 + col) * kMlaD + 8 * hf;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  // ---- byte offsets of rows lane and lane + 64 of the split (-1: not usable)
+  int64_t off_lo, off_hi;
+  {
+    const int i0 = r0 + lane, i1 = r0 + 64 + lane;
+    const int t0 = i0 < r1 ? sel[i0] : -1;
+    const int t1 = i1 < r1 ? sel[i1] : -1;
+    const int64_t e0 = sel_row(a, bt, L, t0, 0, a.k_page_stride, a.k_head_stride, a.k_token_stride, a.k_num_pages);
+    const int64_t e1 = sel_row(a, bt, L, t1, 0, a.k_page_stride, a.k_head_stride, a.k_token_stride, a.k_num_pages);
+    off_lo = e0 < 0 ? -1 : e0 * 2;
+    off_hi = e1 < 0 ? -1 : e1 * 2;
+  }
+  // every ordinary load is complete before the first DMA (see above)
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) asm volatile("" : : "v"(qf[s]));
+  asm volatile("" : : "v"(off_lo), "v"(off_hi));
+  // usable-row masks, rows 0..63 and 64..127
+  const uint64_t ok_lo = __ballot(off_lo >= 0), ok_hi = __ballot(off_hi >= 0);
 
-  floatx16 acc[8];
-  uint32_t pw[kMlaChunks][8];  // bf16 P of each chunk, A-operand layout
-
-  // ---- S^T for all 128 rows first, so the block max is exact and P needs
-  // no later rescaling.  This lane: head `col`, tokens
-  // 32j + 8*(r/4) + 4*hf + (r%4).
-  float sc[kMlaChunks][16];
-  float cmax = -__builtin_inff();
+  // ---- DMA of the four chunks: LDS unit u = row * 73 + slot
+  const uint32_t kv0 = (uint32_t)(uintptr_t)(lds_ptr_t)s_kv;
+  auto row_off = [&](int row) -> int64_t {  // wave-uniform row
+    const int64_t v = row < 64 ? off_lo : off_hi;
+    const int ln = row & 63;
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)(uint64_t)v, ln);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)v >> 32), ln);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+  };
 #pragma unroll
   for (int j = 0; j < kMlaChunks; ++j) {
-    floatx16 st = floatx16{};
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      const bf16x8 kf = __builtin_bit_cast(bf16x8, s_kv[mla_unit(kMlaChunkRows * j + col, 2 * s + hf)]);
-      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], st, 0, 0, 0);
-      // bound the scheduler's look-ahead of LDS reads (register pressure)
-      if (s % 6 == 5) __builtin_amdgcn_sched_barrier(0);
+    for (int i = wid; i < kMlaChunkInsts; i += NW) {
+      const int ub = j * kMlaChunkUnits + 64 * i;   // first unit of the instruction (uniform)
+      const int rowA = ub / kMlaStride;             // the at most two rows it touches
+      const int64_t oA = row_off(rowA);
+      const int64_t oB = rowA + 1 < kMlaSplitRows ? row_off(rowA + 1) : -1;
+      const int u = ub + lane;
+      const int row = u / kMlaStride, slot = u - row * kMlaStride;
+      const int64_t ro = row == rowA ? oA : oB;
+      // pad units and unusable rows read the first query row (finite, in bounds)
+      const char* src = (ro >= 0 && slot < kMlaUnits) ? kb + ro + slot * 16 : qrow0 + (slot < kMlaUnits ? slot : 0) * 16;
+      if (u < kMlaSplitRows * kMlaStride)
+        __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(uintptr_t)(kv0 + 16u * ub), 16, 0, 0);
     }
+  }
+
+  // ---- S^T chunk by chunk as the chunks land.  This lane: head `col`,
+  // tokens 32j + 8*(r/4) + 4*hf + (r%4).
+  float sc[kMlaChunks][16];
+  float cmax = -__builtin_inff();
+  const uint32_t kaddr = kv0 + (uint32_t)(col * kMlaRowBytes + hf * 16);
+  mla_static_for<0, kMlaChunks>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    // wait for this wave's DMA of chunk j, then for everyone's
+    if (wid == 0) mla_wait_vmcnt_barrier<(kMlaChunks - 1 - j) * kInst0>();
+    else mla_wait_vmcnt_barrier<(kMlaChunks - 1 - j) * kInstN>();
+    floatx16 st = floatx16{};
+    mla_static_for<0, KSTEPS / 6>([&](auto gc) {
+      constexpr int g = decltype(gc)::value;
+      u32x4 kf[6];
+      mla_kfrag6<6 * g>(kf, kaddr + (uint32_t)(j * kMlaChunkRows * kMlaRowBytes));
+#pragma unroll
+      for (int e = 0; e < 6; ++e)
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[e]), qf[6 * g + e], st, 0, 0, 0);
+    });
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int tk = kMlaChunkRows * j + 8 * (r / 4) + 4 * hf + (r % 4);
-      sc[j][r] = s_off[tk] >= 0 ? st[r] * c : -__builtin_inff();
+      const bool ok = ((tk < 64 ? ok_lo : ok_hi) >> (tk & 63)) & 1;
+      sc[j][r] = ok ? st[r] * c : -__builtin_inff();
       cmax = fmaxf(cmax, sc[j][r]);
     }
-  }
+  });
   const float m_blk = fmaxf(cmax, __shfl_xor(cmax, 32));
   // masked tokens: exp2(-inf - mref) = 0 (mref finite even with no token)
   const float mref = m_blk == -__builtin_inff() ? 0.0f : m_blk;
   float psum = 0.0f;
+  uint32_t pw[kMlaChunks][8];  // bf16 P of each chunk, A-operand layout
 #pragma unroll
   for (int j = 0; j < kMlaChunks; ++j)
 #pragma unroll
@@ -302,63 +382,53 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_mla_kernel(AttnArgs a) {
       pw[j][r / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector((float2v){p0, p1}, bf16x2));
     }
 
-  // O[:, 256*half ...] += P_j V_j for chunk j (V: first 512 dims of the rows)
-  auto pv = [&](int j, int half) {
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        __builtin_amdgcn_sched_barrier(0);
-      const bf16x8 pa = __builtin_bit_cast(bf16x8, u32x4{pw[j][4 * ks], pw[j][4 * ks + 1], pw[j][4 * ks + 2], pw[j][4 * ks + 3]});
-      // In k-step ks the lane's 8 P values are tokens 16ks + 8(p/4) + 4hf +
-      // p%4; its V fragments hold those tokens.  Four N tiles at a time: 4
-      // dv values (8 bytes) of each of the 8 tokens, dv = 256*half + 8*col + cc.
-#pragma unroll
-      for (int c0 = 0; c0 < 8; c0 += 4) {
-        uint2 vr[8];
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-          const int tk = kMlaChunkRows * j + 16 * ks + 8 * (p / 4) + 4 * hf + (p % 4);
-          vr[p] = reinterpret_cast<const uint2*>(&s_kv[mla_unit(tk, 32 * half + col)])[c0 / 4];
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int cc = c0; cc < c0 + 4; ++cc) {
-          // B fragment of N tile cc: element p = V[token p][256*half + 8*col + cc]
-          u32x4 bw;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const int q = (cc - c0) / 2;
-            const uint32_t lo = q ? vr[2 * w].y : vr[2 * w].x, hi = q ? vr[2 * w + 1].y : vr[2 * w + 1].x;
-            bw[w] = (cc & 1) ? __builtin_amdgcn_perm(hi, lo, 0x07060302u)
-                             : __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-          }
-          acc[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, __builtin_bit_cast(bf16x8, bw), acc[cc], 0, 0, 0);
-        }
-      }
-    }
-  };
-  // ---- partials in register order: part_o[((b*splits+split)*NW + w)][n][lane][16]
-  // (n < 8: dv 0..255, n >= 8: dv 256..511); m / l per head:
-  // part_ml[(b*splits+split)*q_heads + h][2]
+  // ---- O[:, 256*half ...] += P_j V_j.  In k-step ks of chunk j the lane's
+  // 8 P values are tokens 32j + 16ks + 4hf + e (e < 4) and 32j + 16ks + 8 +
+  // 4hf + (e - 4); the transposing read gives lane i of each 16-lane group
+  // the value column i of four rows, lane 4m + c of the group naming row m,
+  // columns 4c .. 4c+3.  Group G of the wave covers value columns 16*(G%2) ..
+  // +16 of the N tile for k half G/2 = hf.
+  const int g16 = lane & 15, G = lane >> 4;
+  const uint32_t vaddr = kv0 + (uint32_t)((4 * hf + (g16 >> 2)) * kMlaRowBytes + (16 * (G & 1) + 4 * (g16 & 3)) * 2);
+  floatx16 acc[8];
   const int64_t blk = (int64_t)b * a.splits + split;
-  float* po = a.part_o + ((blk * NW + wid) * 16) * (64 * 16);
-  auto store = [&](int n0) {
-#pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      float4* dst = reinterpret_cast<float4*>(po + ((int64_t)(n0 + n) * 64 + lane) * 16);
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        dst[jj] = make_float4(acc[n][4 * jj], acc[n][4 * jj + 1], acc[n][4 * jj + 2], acc[n][4 * jj + 3]);
-    }
-  };
-  // value columns 0..255, then 256..511, from the same probabilities
+  uint16_t* po = reinterpret_cast<uint16_t*>(a.part_o) + ((blk * NW + wid) * 16) * (64 * 16);
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
 #pragma unroll
     for (int n = 0; n < 8; ++n) acc[n] = floatx16{};
 #pragma unroll
-    for (int j = 0; j < kMlaChunks; ++j) pv(j, half);
-    store(8 * half);
+    for (int j = 0; j < kMlaChunks; ++j)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 pa = __builtin_bit_cast(bf16x8, u32x4{pw[j][4 * ks], pw[j][4 * ks + 1], pw[j][4 * ks + 2], pw[j][4 * ks + 3]});
+        const uint32_t rbase = vaddr + (uint32_t)((32 * j + 16 * ks) * kMlaRowBytes + 2 * 256 * half);
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) {
+          const uint32_t ad = rbase + (uint32_t)(2 * 32 * cc);
+          const shortx4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) shortx4*)(uintptr_t)ad);
+          const shortx4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) shortx4*)(uintptr_t)(ad + 8 * kMlaRowBytes));
+          const bf16x8 vb = __builtin_bit_cast(bf16x8, (shortx8){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+          acc[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, vb, acc[cc], 0, 0, 0);
+        }
+      }
+    // partials in register order, bf16: part_o[((b*splits+split)*NW + w)][n][lane][16]
+    // (n < 8: dv 0..255, n >= 8: dv 256..511)
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      u32x4 w0, w1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        w0[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector((float2v){acc[n][2 * e], acc[n][2 * e + 1]}, bf16x2));
+        w1[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector((float2v){acc[n][8 + 2 * e], acc[n][8 + 2 * e + 1]}, bf16x2));
+      }
+      uint4* dst = reinterpret_cast<uint4*>(po + ((int64_t)(8 * half + n) * 64 + lane) * 16);
+      dst[0] = make_uint4(w0[0], w0[1], w0[2], w0[3]);
+      dst[1] = make_uint4(w1[0], w1[1], w1[2], w1[3]);
+    }
   }
+  // m / l per head: part_ml[(b*splits+split)*q_heads + h][2]
   const float l_tot = psum + __shfl_xor(psum, 32);
   if (hf == 0) {
     float* ml = a.part_ml + (blk * a.q_heads + head0 + col) * 2;
@@ -369,7 +439,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_mla_kernel(AttnArgs a) {
 
 // Combine of the MLA partials: one 512-thread block per (request, wave w,
 // value half): thread (tile n, lane l) owns heads 32w + 8(r/4) + 4(l/32) + r%4
-// (r < 16) at dv = 256*half + 8*(l%32) + n%8.  Split weights
+// (r < 16) at dv = 256*half + 32*(n%8) + l%32.  Split weights
 // 2^(m_s - M) / sum_s l_s 2^(m_s - M) are computed once per head into LDS; the
 // result is transposed through LDS so output rows are written contiguously.
 constexpr int kMlaMaxSplits = 64;
@@ -405,19 +475,23 @@ __global__ __launch_bounds__(512) void attn_mla_combine_kernel(AttnArgs a, int n
   const int tile = 8 * half + n;
   for (int s = 0; s < S; ++s) {
     const int64_t blk = (int64_t)b * S + s;
-    const float4* src = reinterpret_cast<const float4*>(a.part_o + (((blk * nw + w) * 16 + tile) * 64 + lane) * 16);
+    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.part_o) +
+                                                      (((blk * nw + w) * 16 + tile) * 64 + lane) * 16);
     float v[16];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float4 q = src[j];
-      v[4 * j] = q.x; v[4 * j + 1] = q.y; v[4 * j + 2] = q.z; v[4 * j + 3] = q.w;
+    for (int j = 0; j < 2; ++j) {
+      const uint4 q = src[j];
+      v[8 * j + 0] = bf16_lo(q.x); v[8 * j + 1] = bf16_hi(q.x);
+      v[8 * j + 2] = bf16_lo(q.y); v[8 * j + 3] = bf16_hi(q.y);
+      v[8 * j + 4] = bf16_lo(q.z); v[8 * j + 5] = bf16_hi(q.z);
+      v[8 * j + 6] = bf16_lo(q.w); v[8 * j + 7] = bf16_hi(q.w);
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[r] += v[r] * s_w[s][8 * (r / 4) + 4 * hf + (r % 4)];
   }
   // ---- transpose to [head][dv] and write rows
 #pragma unroll
-  for (int r = 0; r < 16; ++r) s_out[8 * (r / 4) + 4 * hf + (r % 4)][8 * col + n] = o[r];
+  for (int r = 0; r < 16; ++r) s_out[8 * (r / 4) + 4 * hf + (r % 4)][32 * n + col] = o[r];
   __syncthreads();
   for (int i = tid; i < 32 * 256; i += 512) {
     const int h = i / 256, d = i % 256;
