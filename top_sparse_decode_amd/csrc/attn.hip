@@ -203,8 +203,12 @@ __global__ __launch_bounds__(256) void attn_vec_kernel(AttnArgs a) {
 // l/32], B[8 k-values of half l/32][col l%32], and C[rows
 // 8*(r/4)+4*(l/32)+(r%4), r<16][col l%32].
 //
-// LDS rows are 72 sixteen-byte units plus one pad unit (1168-byte stride):
-// the 32 rows read by one A fragment fall on different banks.
+// LDS rows are 72 sixteen-byte units plus four pad units (1216-byte
+// stride), and within a row the units are stored XOR-swizzled: data unit u
+// of row r sits at position u ^ ((r >> 2) & 7) (which stays inside the
+// unit's aligned group of eight).  With that, the 16 rows of an A-fragment
+// read and the 4 rows x 64 bytes of a transposed V read each hit 64
+// different banks; a 32-row chunk is exactly 38 DMA instructions.
 //
 // DMA bookkeeping.  Every DMA instruction moves 64 consecutive LDS units and
 // always has an active lane, so each wave knows exactly how many it has in
@@ -222,10 +226,13 @@ constexpr int kMlaChunkRows = 32;
 constexpr int kMlaChunks = 4;
 constexpr int kMlaSplitRows = kMlaChunkRows * kMlaChunks;  // 128 rows per block
 constexpr int kMlaUnits = kMlaD / 8;                       // 72 units per row
-constexpr int kMlaStride = kMlaUnits + 1;                  // LDS row stride in units
-constexpr int kMlaRowBytes = kMlaStride * 16;              // 1168
-constexpr int kMlaChunkUnits = kMlaChunkRows * kMlaStride;  // 2336
-constexpr int kMlaChunkInsts = (kMlaChunkUnits + 63) / 64;  // 37 DMA instructions per chunk
+constexpr int kMlaStride = kMlaUnits + 4;                  // LDS row stride in units
+constexpr int kMlaRowBytes = kMlaStride * 16;              // 1216
+constexpr int kMlaChunkUnits = kMlaChunkRows * kMlaStride;  // 2432
+constexpr int kMlaChunkInsts = (kMlaChunkUnits + 63) / 64;  // 38 DMA instructions per chunk
+
+// swizzle of row r's units (see above)
+__host__ __device__ constexpr int mla_swz(int r) { return (r >> 2) & 7; }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef short shortx4 __attribute__((ext_vector_type(4)));
@@ -241,22 +248,26 @@ __device__ __forceinline__ void mla_wait_vmcnt_barrier() {
 }
 
 // Six K fragments (k-steps s0 .. s0+5) of this lane's row; one asm block
-// that waits for its own results.
+// that waits for its own results.  Step s reads base[s & 3] + 128 * (s >> 2)
+// (the swizzle permutes units within aligned groups of eight, i.e. within
+// four consecutive k-steps).
+#define MLA_KF_OFF(S) "v"(addr[(S) & 3]), "i"(128 * ((S) >> 2))
 template <int S0>
-__device__ __forceinline__ void mla_kfrag6(u32x4 (&f)[6], uint32_t addr) {
+__device__ __forceinline__ void mla_kfrag6(u32x4 (&f)[6], const uint32_t (&addr)[4]) {
   asm volatile(
       "ds_read_b128 %0, %6 offset:%7\n\t"
-      "ds_read_b128 %1, %6 offset:%8\n\t"
-      "ds_read_b128 %2, %6 offset:%9\n\t"
-      "ds_read_b128 %3, %6 offset:%10\n\t"
-      "ds_read_b128 %4, %6 offset:%11\n\t"
-      "ds_read_b128 %5, %6 offset:%12\n\t"
+      "ds_read_b128 %1, %8 offset:%9\n\t"
+      "ds_read_b128 %2, %10 offset:%11\n\t"
+      "ds_read_b128 %3, %12 offset:%13\n\t"
+      "ds_read_b128 %4, %14 offset:%15\n\t"
+      "ds_read_b128 %5, %16 offset:%17\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3]), "=&v"(f[4]), "=&v"(f[5])
-      : "v"(addr), "i"(32 * S0), "i"(32 * (S0 + 1)), "i"(32 * (S0 + 2)), "i"(32 * (S0 + 3)),
-        "i"(32 * (S0 + 4)), "i"(32 * (S0 + 5))
+      : MLA_KF_OFF(S0), MLA_KF_OFF(S0 + 1), MLA_KF_OFF(S0 + 2), MLA_KF_OFF(S0 + 3), MLA_KF_OFF(S0 + 4),
+        MLA_KF_OFF(S0 + 5)
       : "memory");
 }
+#undef MLA_KF_OFF
 
 template <int I, int N, typename F>
 __device__ __forceinline__ void mla_static_for(F&& f) {
@@ -269,16 +280,20 @@ __device__ __forceinline__ void mla_static_for(F&& f) {
 template <int NW>
 __global__ __launch_bounds__(NW * 64, 1) void attn_mla_kernel(AttnArgs a) {
   constexpr int KSTEPS = kMlaD / 16;  // 36
-  // DMA instructions of one chunk issued by wave w (instructions i = w, w + NW, ...)
-  constexpr int kInst0 = (kMlaChunkInsts + NW - 1) / NW;  // wave 0
-  constexpr int kInstN = kMlaChunkInsts / NW;             // waves 1.. (equal when NW divides 37: never)
   __shared__ __attribute__((aligned(16))) uint4 s_kv[kMlaSplitRows * kMlaStride];
 
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 31, hf = lane >> 5;
-  const int b = blockIdx.y;
-  const int split = blockIdx.x;
+  // Blocks are handed to the 8 XCDs round robin by index.  Block L runs
+  // work item (xcd * per + L / 8), xcd = L % 8, so each XCD takes a
+  // contiguous run of (request, split) items: a request's splits share one
+  // L2 and read its query rows from there.
+  int item = blockIdx.x;
+  const int nitems = gridDim.x;
+  if ((nitems & 7) == 0) item = (item & 7) * (nitems >> 3) + (item >> 3);
+  const int b = item / a.splits;
+  const int split = item - b * a.splits;
   const int r0 = split * kMlaSplitRows, r1 = min(a.k_sel, r0 + kMlaSplitRows);
   const int cap = min(a.max_kv_len, a.max_pages * a.page_size);
   const int L = clamp_len(a.kv_lens[b], cap);
@@ -289,14 +304,31 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_mla_kernel(AttnArgs a) {
   const char* qrow0 = reinterpret_cast<const char*>(a.q) + (int64_t)b * a.q_heads * kMlaD * 2;
   const int head0 = wid * 32;
 
-  // ---- Q^T fragments: lane holds head (head0+col), dims 16s + 8hf .. +8
-  bf16x8 qf[KSTEPS];
+  const uint32_t kv0 = (uint32_t)(uintptr_t)(lds_ptr_t)s_kv;
+  // One DMA instruction: LDS units ub .. ub+63 (u = row * 73 + slot) of
+  // the rows whose byte offsets rowoff(row) returns (negative: the row is
+  // filled from the first query row instead).  Pad units read a harmless
+  // 16 bytes of that row.  Every lane is in bounds; lanes past `units` do
+  // nothing, and there is always an active lane.
+  auto dma64 = [&](int ub, int units, const char* base, auto&& rowoff) {
+    const int rowA = ub / kMlaStride;            // the at most two rows it touches
+    const int64_t oA = rowoff(rowA), oB = rowoff(rowA + 1);
+    const int u = ub + lane;
+    const int row = u / kMlaStride, slot = u - row * kMlaStride;
+    const int64_t ro = row == rowA ? oA : oB;
+    const int sl = slot < kMlaUnits ? slot ^ mla_swz(row) : 0;  // data unit held at position `slot`
+    const char* src = ro >= 0 ? base + ro + sl * 16 : qrow0 + sl * 16;
+    if (u < units) __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(uintptr_t)(kv0 + 16u * ub), 16, 0, 0);
+  };
+
+  // ---- the block's query rows (heads 0 .. 32*NW-1) into LDS, same layout
+  // as the latent rows, while the row offsets are looked up
   {
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)b * a.q_heads + head0 + col) * kMlaD + 8 * hf;
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
+    constexpr int qunits = 32 * NW * kMlaStride;
+    auto qoff = [&](int h) -> int64_t { return h < 32 * NW ? (int64_t)h * kMlaD * 2 : -1; };
+    for (int i = wid; i < (qunits + 63) / 64; i += NW) dma64(64 * i, qunits, qrow0, qoff);
   }
-  // ---- byte offsets of rows lane and lane + 64 of the split (-1: not usable)
+  // byte offsets of rows lane and lane + 64 of the split (-1: not usable)
   int64_t off_lo, off_hi;
   {
     const int i0 = r0 + lane, i1 = r0 + 64 + lane;
@@ -307,80 +339,107 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_mla_kernel(AttnArgs a) {
     off_lo = e0 < 0 ? -1 : e0 * 2;
     off_hi = e1 < 0 ? -1 : e1 * 2;
   }
-  // every ordinary load is complete before the first DMA (see above)
-#pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) asm volatile("" : : "v"(qf[s]));
   asm volatile("" : : "v"(off_lo), "v"(off_hi));
+  mla_wait_vmcnt_barrier<0>();
+  // Q^T fragments from LDS: lane holds head (head0+col), dims 16s + 8hf .. +8
+  bf16x8 qf[KSTEPS];
+  {
+    const uint4* qs = s_kv + (head0 + col) * kMlaStride;
+    const int sw = mla_swz(head0 + col);
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) qf[s] = __builtin_bit_cast(bf16x8, qs[(2 * s + hf) ^ sw]);
+  }
+  // the latent rows overwrite the query rows: every wave has its fragments
+  __syncthreads();
   // usable-row masks, rows 0..63 and 64..127
   const uint64_t ok_lo = __ballot(off_lo >= 0), ok_hi = __ballot(off_hi >= 0);
 
-  // ---- DMA of the four chunks: LDS unit u = row * 73 + slot
-  const uint32_t kv0 = (uint32_t)(uintptr_t)(lds_ptr_t)s_kv;
+  // ---- DMA of the latent rows, 32-row chunks; wave w issues instructions
+  // w, w + NW, ... of each chunk: (38 - w + NW - 1) / NW of them
   auto row_off = [&](int row) -> int64_t {  // wave-uniform row
+    if (row >= kMlaSplitRows) return -1;
     const int64_t v = row < 64 ? off_lo : off_hi;
     const int ln = row & 63;
     const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)(uint64_t)v, ln);
     const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)v >> 32), ln);
     return (int64_t)(((uint64_t)hi << 32) | lo);
   };
-#pragma unroll
-  for (int j = 0; j < kMlaChunks; ++j) {
-    for (int i = wid; i < kMlaChunkInsts; i += NW) {
-      const int ub = j * kMlaChunkUnits + 64 * i;   // first unit of the instruction (uniform)
-      const int rowA = ub / kMlaStride;             // the at most two rows it touches
-      const int64_t oA = row_off(rowA);
-      const int64_t oB = rowA + 1 < kMlaSplitRows ? row_off(rowA + 1) : -1;
-      const int u = ub + lane;
-      const int row = u / kMlaStride, slot = u - row * kMlaStride;
-      const int64_t ro = row == rowA ? oA : oB;
-      // pad units and unusable rows read the first query row (finite, in bounds)
-      const char* src = (ro >= 0 && slot < kMlaUnits) ? kb + ro + slot * 16 : qrow0 + (slot < kMlaUnits ? slot : 0) * 16;
-      if (u < kMlaSplitRows * kMlaStride)
-        __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(uintptr_t)(kv0 + 16u * ub), 16, 0, 0);
-    }
-  }
+  auto issue_chunk = [&](int j) {
+    for (int i = wid; i < kMlaChunkInsts; i += NW)
+      dma64(j * kMlaChunkUnits + 64 * i, kMlaSplitRows * kMlaStride, kb, row_off);
+  };
+  issue_chunk(0);
+  issue_chunk(1);
 
-  // ---- S^T chunk by chunk as the chunks land.  This lane: head `col`,
-  // tokens 32j + 8*(r/4) + 4*hf + (r%4).
-  float sc[kMlaChunks][16];
-  float cmax = -__builtin_inff();
-  const uint32_t kaddr = kv0 + (uint32_t)(col * kMlaRowBytes + hf * 16);
+  // ---- S^T chunk by chunk as the chunks land; chunk j + 2 is issued once
+  // S of chunk j is done.  This lane: head `col`, tokens 32j + 8*(r/4) +
+  // 4*hf + (r%4).  Probabilities are formed chunk by chunk against a
+  // running reference m (the running max rounded up to an integer, -inf
+  // while no token is usable): when a chunk raises it, the probabilities
+  // already formed are scaled by 2^(m_old - m_new), an exact power of two,
+  // so the result equals forming them all against the final m.
+  uint32_t pw[kMlaChunks][8];  // bf16 P of each chunk, A-operand layout
+  float m_run = -__builtin_inff(), psum = 0.0f;
+  // K fragment bases: row col of the chunk, data unit 2t + hf (t = s & 3)
+  uint32_t kaddr[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) kaddr[t] = kv0 + (uint32_t)(col * kMlaRowBytes + 16 * ((2 * t + hf) ^ mla_swz(col)));
   mla_static_for<0, kMlaChunks>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
-    // wait for this wave's DMA of chunk j, then for everyone's
-    if (wid == 0) mla_wait_vmcnt_barrier<(kMlaChunks - 1 - j) * kInst0>();
-    else mla_wait_vmcnt_barrier<(kMlaChunks - 1 - j) * kInstN>();
+    // chunk j + 1 (if any) may still be in flight: wait for the rest, then
+    // for everyone's
+    constexpr int later = j + 1 < kMlaChunks ? 1 : 0;
+    mla_static_for<0, NW>([&](auto wc) {
+      constexpr int w = decltype(wc)::value;
+      if (wid == w) mla_wait_vmcnt_barrier<later * ((kMlaChunkInsts - w + NW - 1) / NW)>();
+    });
     floatx16 st = floatx16{};
     mla_static_for<0, KSTEPS / 6>([&](auto gc) {
       constexpr int g = decltype(gc)::value;
       u32x4 kf[6];
-      mla_kfrag6<6 * g>(kf, kaddr + (uint32_t)(j * kMlaChunkRows * kMlaRowBytes));
+      uint32_t ka[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) ka[t] = kaddr[t] + (uint32_t)(j * kMlaChunkRows * kMlaRowBytes);
+      mla_kfrag6<6 * g>(kf, ka);
 #pragma unroll
       for (int e = 0; e < 6; ++e)
         st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[e]), qf[6 * g + e], st, 0, 0, 0);
     });
+    if constexpr (j + 2 < kMlaChunks) issue_chunk(j + 2);
+    float cmax = -__builtin_inff();
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int tk = kMlaChunkRows * j + 8 * (r / 4) + 4 * hf + (r % 4);
       const bool ok = ((tk < 64 ? ok_lo : ok_hi) >> (tk & 63)) & 1;
-      sc[j][r] = ok ? st[r] * c : -__builtin_inff();
-      cmax = fmaxf(cmax, sc[j][r]);
+      st[r] = ok ? st[r] * c : -__builtin_inff();
+      cmax = fmaxf(cmax, st[r]);
     }
-  });
-  const float m_blk = fmaxf(cmax, __shfl_xor(cmax, 32));
-  // masked tokens: exp2(-inf - mref) = 0 (mref finite even with no token)
-  const float mref = m_blk == -__builtin_inff() ? 0.0f : m_blk;
-  float psum = 0.0f;
-  uint32_t pw[kMlaChunks][8];  // bf16 P of each chunk, A-operand layout
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));  // both token halves of head `col`
+    const float m_new = fmaxf(m_run, ceilf(cmax));
+    if constexpr (j > 0) {
+      // 2^(m_run - m_new): 1 while nothing changes, 0 before any usable token
+      const float f = m_new == -__builtin_inff() ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      psum *= f;
 #pragma unroll
-  for (int j = 0; j < kMlaChunks; ++j)
+      for (int jj = 0; jj < j; ++jj)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float lo = bf16_lo(pw[jj][e]) * f, hi = bf16_hi(pw[jj][e]) * f;
+          pw[jj][e] = __builtin_bit_cast(uint32_t, __builtin_convertvector((float2v){lo, hi}, bf16x2));
+        }
+    }
+    m_run = m_new;
+    // masked tokens: exp2(-inf - mref) = 0 (mref finite even with no token)
+    const float mref = m_new == -__builtin_inff() ? 0.0f : m_new;
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(sc[j][r] - mref);
-      const float p1 = __builtin_amdgcn_exp2f(sc[j][r + 1] - mref);
+      const float p0 = __builtin_amdgcn_exp2f(st[r] - mref);
+      const float p1 = __builtin_amdgcn_exp2f(st[r + 1] - mref);
       psum += p0 + p1;
       pw[j][r / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector((float2v){p0, p1}, bf16x2));
     }
+  });
+  const float m_blk = m_run;
 
   // ---- O[:, 256*half ...] += P_j V_j.  In k-step ks of chunk j the lane's
   // 8 P values are tokens 32j + 16ks + 4hf + e (e < 4) and 32j + 16ks + 8 +
@@ -388,31 +447,51 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_mla_kernel(AttnArgs a) {
   // the value column i of four rows, lane 4m + c of the group naming row m,
   // columns 4c .. 4c+3.  Group G of the wave covers value columns 16*(G%2) ..
   // +16 of the N tile for k half G/2 = hf.
+  // Row 32j + 16ks + 4hf + m (+8 for the second read) has swizzle
+  // (4ks + hf + 2*second) & 7 and value column dv = 256*half + 32*cc +
+  // 16*(G&1) + 4c lies in data unit 32*half + 4*cc + 2*(G&1) + c/2, byte
+  // 8*(c&1) of it.  The lane-dependent part of the position goes into two
+  // bases (second read or not); the rest is a constant offset.
   const int g16 = lane & 15, G = lane >> 4;
-  const uint32_t vaddr = kv0 + (uint32_t)((4 * hf + (g16 >> 2)) * kMlaRowBytes + (16 * (G & 1) + 4 * (g16 & 3)) * 2);
+  const int vm = g16 >> 2, vc = g16 & 3;
+  uint32_t vbase[2];
+#pragma unroll
+  for (int sec = 0; sec < 2; ++sec)
+    vbase[sec] = kv0 + (uint32_t)((4 * hf + vm + 8 * sec) * kMlaRowBytes +
+                                  16 * ((2 * ((G & 1) ^ sec)) | ((vc >> 1) ^ hf)) + 8 * (vc & 1));
   floatx16 acc[8];
   const int64_t blk = (int64_t)b * a.splits + split;
   uint16_t* po = reinterpret_cast<uint16_t*>(a.part_o) + ((blk * NW + wid) * 16) * (64 * 16);
+  // V fragments of one (chunk, k-step) and N tile: two transposed reads.
+  auto vload = [&](shortx4 (&v)[2], int half, int step, int cc) {
+    const int j = step >> 1, ks = step & 1;
+    const uint32_t off = (uint32_t)((32 * j + 16 * ks) * kMlaRowBytes + 16 * (8 * (4 * half + cc / 2) + 4 * ((cc & 1) ^ ks)));
+    v[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) shortx4*)(uintptr_t)(vbase[0] + off));
+    v[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) shortx4*)(uintptr_t)(vbase[1] + off));
+  };
+  // Each MFMA is followed by the two reads for the same N tile one step
+  // later, so every read has eight MFMAs of lead while at most 14 reads
+  // follow the one being waited for (the LDS counter holds 15).
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
 #pragma unroll
     for (int n = 0; n < 8; ++n) acc[n] = floatx16{};
+    shortx4 vb[2][8][2];
 #pragma unroll
-    for (int j = 0; j < kMlaChunks; ++j)
+    for (int cc = 0; cc < 8; ++cc) vload(vb[0][cc], half, 0, cc);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 pa = __builtin_bit_cast(bf16x8, u32x4{pw[j][4 * ks], pw[j][4 * ks + 1], pw[j][4 * ks + 2], pw[j][4 * ks + 3]});
-        const uint32_t rbase = vaddr + (uint32_t)((32 * j + 16 * ks) * kMlaRowBytes + 2 * 256 * half);
+    for (int step = 0; step < 2 * kMlaChunks; ++step) {
+      const int j = step >> 1, ks = step & 1;
+      const bf16x8 pa = __builtin_bit_cast(bf16x8, u32x4{pw[j][4 * ks], pw[j][4 * ks + 1], pw[j][4 * ks + 2], pw[j][4 * ks + 3]});
 #pragma unroll
-        for (int cc = 0; cc < 8; ++cc) {
-          const uint32_t ad = rbase + (uint32_t)(2 * 32 * cc);
-          const shortx4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) shortx4*)(uintptr_t)ad);
-          const shortx4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) shortx4*)(uintptr_t)(ad + 8 * kMlaRowBytes));
-          const bf16x8 vb = __builtin_bit_cast(bf16x8, (shortx8){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
-          acc[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, vb, acc[cc], 0, 0, 0);
-        }
+      for (int cc = 0; cc < 8; ++cc) {
+        const shortx4 v0 = vb[step & 1][cc][0], v1 = vb[step & 1][cc][1];
+        const bf16x8 vv = __builtin_bit_cast(bf16x8, (shortx8){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+        acc[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, vv, acc[cc], 0, 0, 0);
+        if (step + 1 < 2 * kMlaChunks) vload(vb[(step + 1) & 1][cc], half, step + 1, cc);
+        __builtin_amdgcn_sched_barrier(0);
       }
+    }
     // partials in register order, bf16: part_o[((b*splits+split)*NW + w)][n][lane][16]
     // (n < 8: dv 0..255, n >= 8: dv 256..511)
 #pragma unroll
@@ -580,7 +659,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
   hipError_t e;
   if (attn_mla_supported(a)) {
     if (a.chunk != kMlaSplitRows || a.splits > kMlaMaxSplits) return hipErrorInvalidValue;
-    dim3 grid(a.splits, a.batch);
+    dim3 grid(a.splits * a.batch);
     const int nw = a.q_heads / 32;
     switch (nw) {
       case 1: attn_mla_kernel<1><<<grid, 64, 0, st>>>(a); break;
