@@ -182,11 +182,17 @@ __device__ float exact_dsa_score(const ScoreArgs& sa, int b, int g, int t, float
     float term = 0.0f;
     if (h < G) {
       const uint16_t* qh = qb + (int64_t)h * 128;
+      // all 32 loads in flight at once, then the ordered dot product
+      uint4 kr[16], qr[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        kr[i] = *reinterpret_cast<const uint4*>(krow + 8 * i);
+        qr[i] = *reinterpret_cast<const uint4*>(qh + 8 * i);
+      }
       float acc = 0.0f;
-#pragma unroll 2
-      for (int d = 0; d < 128; d += 8) {
-        const uint4 kv = *reinterpret_cast<const uint4*>(krow + d);
-        const uint4 qv = *reinterpret_cast<const uint4*>(qh + d);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint4 kv = kr[i], qv = qr[i];
         acc = __builtin_fmaf(bf16_lo(qv.x), bf16_lo(kv.x), acc);
         acc = __builtin_fmaf(bf16_hi(qv.x), bf16_hi(kv.x), acc);
         acc = __builtin_fmaf(bf16_lo(qv.y), bf16_lo(kv.y), acc);
@@ -508,6 +514,7 @@ __device__ __noinline__ void select_row_block(const SelectArgs& a, int row, SelS
 // select_row_block (exact, slower).
 
 constexpr int kChunkThreads = 512;
+constexpr int kStageRows = kChunkThreads / 16;  // band K rows staged per pass
 constexpr int kPerThread = kSelChunk / kChunkThreads;  // 8 contiguous tokens
 
 struct RowView {
@@ -612,6 +619,17 @@ __device__ RowCut row_cut(const SelectArgs& a, int row, const RowView& v, ChunkS
   return c;
 }
 
+// The cut as the classify pass published it (stat slots 3..6).
+__device__ __forceinline__ RowCut stored_cut(const SelectArgs& a, int row) {
+  const int32_t* st = a.stats + (int64_t)row * kStatStride;
+  RowCut c;
+  c.bstar = st[3];
+  c.nfin = st[4];
+  c.band_lo = __int_as_float(st[5]);
+  c.band_hi = __int_as_float(st[6]);
+  return c;
+}
+
 // IN / OUT / BAND of one token (NaN = past kv_len -> kPad)
 __device__ __forceinline__ uint32_t classify(const RowView& v, const RowCut& c, float x, bool fast) {
   if (x != x) return kPad;
@@ -681,15 +699,24 @@ __global__ __launch_bounds__(kChunkThreads) void select_hist_kernel(SelectArgs a
 template <bool FAST>
 __global__ __launch_bounds__(kChunkThreads) void select_classify_kernel(SelectArgs a) {
   __shared__ ChunkShared sh;
-  __shared__ int s_band[kSelChunk];
-  __shared__ int s_nband;
+  __shared__ int s_band[kSelChunk];       // band positions of the chunk
+  __shared__ uint32_t s_bkey[kSelChunk];  // and their exact keys
+  __shared__ int s_nband, s_base;
   __shared__ __attribute__((aligned(16))) float s_terms[kSelWaves][kWave];
+  __shared__ uint4 s_krow[kStageRows][16];  // K rows of band tokens being re-scored
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int row = blockIdx.y, c = blockIdx.x;
   const RowView v = row_view(a, row);
   if (v.L <= a.k || c * kSelChunk >= v.L) return;
   const RowCut cut = row_cut(a, row, v, sh, FAST);
   if (tid == 0) s_nband = 0;
+  if (c == 0 && tid == 0) {  // for the emit kernel (identical in every block)
+    int32_t* stc = a.stats + (int64_t)row * kStatStride;
+    stc[3] = cut.bstar;
+    stc[4] = cut.nfin;
+    stc[5] = __float_as_int(cut.band_lo);
+    stc[6] = __float_as_int(cut.band_hi);
+  }
   __syncthreads();
   float x[kPerThread];
   const int t0 = c * kSelChunk + kPerThread * tid;
@@ -704,14 +731,9 @@ __global__ __launch_bounds__(kChunkThreads) void select_classify_kernel(SelectAr
     n_in += cl == kIn;
     n_neg += (x[e] == -__builtin_inff());
     if (cl == kBand) {
-      if (FAST && cut.bstar >= 0) {
-        s_band[atomicAdd(&s_nband, 1)] = t0 + e;  // re-scored below
-      } else {
-        const uint32_t key = score_key(x[e]);
-        keys[t0 + e] = key;
-        const int slot = atomicAdd(&st[2], 1);
-        if (slot < kBandCap) band[slot] = ((uint64_t)key << 32) | (uint32_t)~(uint32_t)(t0 + e);
-      }
+      const int i = atomicAdd(&s_nband, 1);
+      s_band[i] = t0 + e;
+      s_bkey[i] = score_key(x[e]);  // fast scores: replaced by the exact key below
     }
   }
   n_in = chunk_sum_i(n_in, sh.redi);
@@ -721,17 +743,87 @@ __global__ __launch_bounds__(kChunkThreads) void select_classify_kernel(SelectAr
     cc[0] = n_in;
     cc[1] = n_neg;
   }
-  if constexpr (FAST) {
-    const int nb = s_nband;
+  const int nb = s_nband;  // (visible: the barriers above)
+  if (FAST && cut.bstar >= 0 && nb > 0) {
+    // Exact re-score of the band: the K rows of up to kStageRows tokens at a
+    // time are staged in LDS (one round trip), each wave holds its lane's
+    // query row in registers, and a wave scores one token in the library's
+    // exact order (lane h: dot_h left to right; then the head terms in head
+    // order), bit-identical to the exact scorer.
+    const ScoreArgs& sa = a.score;
     const int g = row % a.groups, b = row / a.groups;
-    for (int i = wid; i < nb; i += kSelWaves) {
-      const int t = s_band[i];
-      const uint32_t key = score_key(exact_dsa_score(a.score, b, g, t, s_terms[wid]));
-      if (lane == 0) {
-        keys[t] = key;
-        const int slot = atomicAdd(&st[2], 1);
-        if (slot < kBandCap) band[slot] = ((uint64_t)key << 32) | (uint32_t)~(uint32_t)t;
+    const int G = sa.q_heads / sa.num_kv_heads;  // <= 64 on the fast path
+    const bool hact = lane < G;
+    uint4 qr[16];
+    float wh = 0.0f;
+    if (hact) {
+      const uint16_t* qh = reinterpret_cast<const uint16_t*>(sa.q) + ((int64_t)b * sa.q_heads + g * G + lane) * 128;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) qr[i] = *reinterpret_cast<const uint4*>(qh + 8 * i);
+      wh = sa.head_weights[(int64_t)b * sa.q_heads + g * G + lane];
+    }
+    for (int p0 = 0; p0 < nb; p0 += kStageRows) {
+      const int np = min(kStageRows, nb - p0);
+      {
+        const int i = tid >> 4, part = tid & 15;  // 16 threads per row
+        if (i < np) {
+          const int t = s_band[p0 + i];
+          const int page = sa.block_table[(int64_t)b * sa.max_pages + t / sa.page_size];
+          const uint16_t* krow = reinterpret_cast<const uint16_t*>(sa.k) + (int64_t)page * sa.page_stride +
+                                 (int64_t)g * sa.head_stride + (int64_t)(t % sa.page_size) * sa.token_stride;
+          s_krow[i][part] = *reinterpret_cast<const uint4*>(krow + 8 * part);
+        }
       }
+      __syncthreads();
+      for (int i = wid; i < np; i += kSelWaves) {
+        float term = 0.0f;
+        if (hact) {
+          float acc = 0.0f;
+#pragma unroll
+          for (int c8 = 0; c8 < 16; ++c8) {
+            const uint4 kv = s_krow[i][c8], qv = qr[c8];
+            acc = __builtin_fmaf(bf16_lo(qv.x), bf16_lo(kv.x), acc);
+            acc = __builtin_fmaf(bf16_hi(qv.x), bf16_hi(kv.x), acc);
+            acc = __builtin_fmaf(bf16_lo(qv.y), bf16_lo(kv.y), acc);
+            acc = __builtin_fmaf(bf16_hi(qv.y), bf16_hi(kv.y), acc);
+            acc = __builtin_fmaf(bf16_lo(qv.z), bf16_lo(kv.z), acc);
+            acc = __builtin_fmaf(bf16_hi(qv.z), bf16_hi(kv.z), acc);
+            acc = __builtin_fmaf(bf16_lo(qv.w), bf16_lo(kv.w), acc);
+            acc = __builtin_fmaf(bf16_hi(qv.w), bf16_hi(kv.w), acc);
+          }
+          term = __fmul_rn(wh, acc > 0.0f ? acc : 0.0f);
+        }
+        s_terms[wid][lane] = term;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        float total = 0.0f;
+        for (int j0 = 0; j0 < G; j0 += 16) {
+          float tv[16];
+#pragma unroll
+          for (int j = 0; j < 16; j += 4) {
+            const float4 q4 = *reinterpret_cast<const float4*>(&s_terms[wid][j0 + j]);
+            tv[j] = q4.x; tv[j + 1] = q4.y; tv[j + 2] = q4.z; tv[j + 3] = q4.w;
+          }
+#pragma unroll
+          for (int j = 0; j < 16; ++j) total = __fadd_rn(total, tv[j]);
+        }
+        if (lane == 0) s_bkey[p0 + i] = score_key(total);
+        __builtin_amdgcn_wave_barrier();
+      }
+      __syncthreads();  // keys visible; the staging rows may be reused
+    }
+  }
+  // the chunk's band entries: one slot reservation per block
+  if (nb > 0) {
+    if (tid == 0) s_base = atomicAdd(&st[2], nb);
+    __syncthreads();
+    for (int i = tid; i < nb; i += kChunkThreads) {
+      const int t = s_band[i];
+      const uint32_t key = s_bkey[i];
+      keys[t] = key;
+      const int slot = s_base + i;
+      if (slot < kBandCap) band[slot] = ((uint64_t)key << 32) | (uint32_t)~(uint32_t)t;
     }
   }
 }
@@ -740,7 +832,7 @@ struct EmitShared {
   ChunkShared cs;
   uint64_t band[kBandCap];
   uint32_t chosen[kSelChunk / 32];  // chunk-local bitmap of kept band tokens
-  int red2[kSelWaves];
+  int red2[4];
 };
 
 template <bool FAST>
@@ -771,55 +863,82 @@ __global__ __launch_bounds__(kChunkThreads) void select_emit_kernel(SelectArgs a
     if (c == 0) select_row_block<kMaxNI, false, FAST>(a, row, u.one, s_terms);
     return;
   }
-  const RowCut cut = row_cut(a, row, v, u.e.cs, FAST);
-  // per-chunk counts: kept-for-sure before this chunk and in total
+  const RowCut cut = stored_cut(a, row);
+  // per-chunk counts (kept-for-sure, -inf) before this chunk and in total:
+  // wave 0 reduces them, LDS hands them to the block
   const int nch = (v.L + kSelChunk - 1) / kSelChunk;
   const int32_t* cc = a.chunk_counts + (int64_t)row * a.nchunks * 2;
-  int in_before = 0, in_total = 0, neg_before = 0;
-  for (int i = tid; i < nch; i += kChunkThreads) {
-    in_total += cc[2 * i];
-    if (i < c) {
-      in_before += cc[2 * i];
-      neg_before += cc[2 * i + 1];
+  if (tid < kWave) {
+    int in_total = 0, in_before = 0, neg_before = 0;
+    for (int i = tid; i < nch; i += kWave) {
+      const int ci = cc[2 * i], cn = cc[2 * i + 1];
+      in_total += ci;
+      if (i < c) {
+        in_before += ci;
+        neg_before += cn;
+      }
+    }
+    in_total = wave_sum(in_total);
+    in_before = wave_sum(in_before);
+    neg_before = wave_sum(neg_before);
+    if (tid == 0) {
+      u.e.red2[0] = in_total;
+      u.e.red2[1] = in_before;
+      u.e.red2[2] = neg_before;
     }
   }
-  in_total = chunk_sum_i(in_total, u.e.cs.redi);
-  in_before = chunk_sum_i(in_before, u.e.cs.redi);
-  neg_before = chunk_sum_i(neg_before, u.e.cs.redi);
-  const int need = k - in_total;  // BAND tokens to keep (>= 1)
-
-  // band: sort (key desc, position asc) = descending 64-bit composite
-  int nb_pow = 1;
-  while (nb_pow < nband) nb_pow <<= 1;
-  for (int i = tid; i < nb_pow; i += kChunkThreads)
-    u.e.band[i] = i < nband ? a.band[(int64_t)row * kBandCap + i] : 0ull;
+  for (int i = tid; i < nband; i += kChunkThreads) u.e.band[i] = a.band[(int64_t)row * kBandCap + i];
   for (int i = tid; i < kSelChunk / 32; i += kChunkThreads) u.e.chosen[i] = 0u;
   __syncthreads();
-  for (int size = 2; size <= nb_pow; size <<= 1)
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < nb_pow / 2; i += kChunkThreads) {
-        const int lo = 2 * i - (i & (stride - 1));
-        const int hi = lo + stride;
-        const bool desc = (lo & size) == 0;
-        const uint64_t x0 = u.e.band[lo], x1 = u.e.band[hi];
-        if ((x0 < x1) == desc) {
-          u.e.band[lo] = x1;
-          u.e.band[hi] = x0;
-        }
-      }
-      __syncthreads();
-    }
-  // kept band entries: the first `need`; those of this chunk go to the
-  // bitmap, those before it shift the offset
+  const int in_total = u.e.red2[0], in_before = u.e.red2[1], neg_before = u.e.red2[2];
+  const int need = k - in_total;  // BAND tokens to keep (>= 1)
+
+  // Band entry i is kept iff fewer than `need` entries come before it in
+  // (key desc, position asc) order, i.e. have a larger composite
+  // (key << 32) | ~position.  Counting them is a pass over the list per
+  // entry (the list is short: tokens within a few error bounds of the
+  // threshold); long lists are sorted instead.
   int chosen_before = 0;
   if (cut.bstar >= 0) {
-    for (int i = tid; i < need && i < nband; i += kChunkThreads) {
-      const int t = (int)~(uint32_t)(u.e.band[i] & 0xFFFFFFFFull);
-      if (t < cstart) ++chosen_before;
-      else if (t < cstart + kSelChunk) atomicOr(&u.e.chosen[(t - cstart) >> 5], 1u << ((t - cstart) & 31));
+    if (nband <= 2 * kChunkThreads) {
+      for (int i = tid; i < nband; i += kChunkThreads) {
+        const uint64_t x = u.e.band[i];
+        int rank = 0;
+        for (int j = 0; j < nband; ++j) rank += u.e.band[j] > x;
+        if (rank < need) {
+          const int t = (int)~(uint32_t)(x & 0xFFFFFFFFull);
+          if (t < cstart) ++chosen_before;
+          else if (t < cstart + kSelChunk) atomicOr(&u.e.chosen[(t - cstart) >> 5], 1u << ((t - cstart) & 31));
+        }
+      }
+    } else {
+      // sort (key desc, position asc) = descending 64-bit composite
+      int nb_pow = 1;
+      while (nb_pow < nband) nb_pow <<= 1;
+      for (int i = nband + tid; i < nb_pow; i += kChunkThreads) u.e.band[i] = 0ull;
+      __syncthreads();
+      for (int size = 2; size <= nb_pow; size <<= 1)
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+          for (int i = tid; i < nb_pow / 2; i += kChunkThreads) {
+            const int lo = 2 * i - (i & (stride - 1));
+            const int hi = lo + stride;
+            const bool desc = (lo & size) == 0;
+            const uint64_t x0 = u.e.band[lo], x1 = u.e.band[hi];
+            if ((x0 < x1) == desc) {
+              u.e.band[lo] = x1;
+              u.e.band[hi] = x0;
+            }
+          }
+          __syncthreads();
+        }
+      for (int i = tid; i < need && i < nband; i += kChunkThreads) {
+        const int t = (int)~(uint32_t)(u.e.band[i] & 0xFFFFFFFFull);
+        if (t < cstart) ++chosen_before;
+        else if (t < cstart + kSelChunk) atomicOr(&u.e.chosen[(t - cstart) >> 5], 1u << ((t - cstart) & 31));
+      }
     }
   }
-  chosen_before = chunk_sum_i(chosen_before, u.e.red2);  // (barrier: bitmap complete)
+  chosen_before = chunk_sum_i(chosen_before, u.e.cs.redi);  // (barrier: bitmap complete)
 
   float x[kPerThread];
   const int t0 = cstart + kPerThread * tid;
