@@ -516,65 +516,84 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_mla_kernel(AttnArgs a) {
   }
 }
 
-// Combine of the MLA partials: one 512-thread block per (request, wave w,
-// value half): thread (tile n, lane l) owns heads 32w + 8(r/4) + 4(l/32) + r%4
-// (r < 16) at dv = 256*half + 32*(n%8) + l%32.  Split weights
-// 2^(m_s - M) / sum_s l_s 2^(m_s - M) are computed once per head into LDS; the
-// result is transposed through LDS so output rows are written contiguously.
+// Combine of the MLA partials: one 256-thread block per (request, wave w,
+// quarter of the value columns): thread (tile n, lane l) owns heads
+// 32w + 8(r/4) + 4(l/32) + r%4 (r < 16) at dv = 128*quarter + 32*(n%4) +
+// l%32.  Split weights 2^(m_s - M) / sum_s l_s 2^(m_s - M) are computed once
+// per head into LDS; each thread then has the partials of eight splits in
+// flight at a time; the result is transposed through LDS so output rows are
+// written contiguously.
 constexpr int kMlaMaxSplits = 64;
 
-__global__ __launch_bounds__(512) void attn_mla_combine_kernel(AttnArgs a, int nw) {
+__global__ __launch_bounds__(256) void attn_mla_combine_kernel(AttnArgs a, int nw) {
+  __shared__ float s_m[kMlaMaxSplits][32], s_l[kMlaMaxSplits][32];
   __shared__ float s_w[kMlaMaxSplits][32];   // weight of split s for head 32w + h
-  __shared__ float s_out[32][256 + 4];       // [head][dv in half], padded
+  __shared__ float s_out[32][128 + 4];       // [head][dv in the quarter], padded
   const int tid = threadIdx.x;
-  const int lane = tid & 63, n = tid >> 6;  // tile within the half: 0..7
-  const int half = blockIdx.x % 2, w = (blockIdx.x / 2) % nw, b = blockIdx.x / (2 * nw);
+  const int lane = tid & 63, n = tid >> 6;  // tile within the quarter: 0..3
+  const int quarter = blockIdx.x % 4, w = (blockIdx.x / 4) % nw, b = blockIdx.x / (4 * nw);
   const int col = lane & 31, hf = lane >> 5;
   const int S = a.splits;
-  // ---- weights: thread h < 32 handles head 32w + h
+  // ---- m and l of (split, head), all loads at once
+  for (int i = tid; i < S * 32; i += 256) {
+    const int sp = i >> 5, h = i & 31;
+    const float* ml = a.part_ml + (((int64_t)b * S + sp) * a.q_heads + 32 * w + h) * 2;
+    s_m[sp][h] = ml[0];
+    s_l[sp][h] = ml[1];
+  }
+  __syncthreads();
   if (tid < 32) {
-    const int h = 32 * w + tid;
     float mx = -__builtin_inff();
-    for (int s = 0; s < S; ++s) mx = fmaxf(mx, a.part_ml[(((int64_t)b * S + s) * a.q_heads + h) * 2]);
+    for (int sp = 0; sp < S; ++sp) mx = fmaxf(mx, s_m[sp][tid]);
     float Ls = 0.0f;
-    for (int s = 0; s < S; ++s) {
-      const float* ml = a.part_ml + (((int64_t)b * S + s) * a.q_heads + h) * 2;
-      const float e = ml[0] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(ml[0] - mx);
-      s_w[s][tid] = e;
-      Ls += ml[1] * e;
+    for (int sp = 0; sp < S; ++sp) {
+      const float m = s_m[sp][tid];
+      const float e = m == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m - mx);
+      s_w[sp][tid] = e;
+      Ls += s_l[sp][tid] * e;
     }
     const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
-    for (int s = 0; s < S; ++s) s_w[s][tid] *= inv;
+    for (int sp = 0; sp < S; ++sp) s_w[sp][tid] *= inv;
   }
   __syncthreads();
   // ---- weighted sum over splits of this thread's 16 partial values
   float o[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) o[r] = 0.0f;
-  const int tile = 8 * half + n;
-  for (int s = 0; s < S; ++s) {
-    const int64_t blk = (int64_t)b * S + s;
-    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.part_o) +
-                                                      (((blk * nw + w) * 16 + tile) * 64 + lane) * 16);
-    float v[16];
+  const int tile = 4 * quarter + n;  // N tile of the partial layout (0..15)
+  const uint16_t* pbase = reinterpret_cast<const uint16_t*>(a.part_o) + (((int64_t)w * 16 + tile) * 64 + lane) * 16;
+  const int64_t sstride = (int64_t)nw * 16 * 64 * 16;  // one split's partial, in elements
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    uint4 q[8][2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint4 q = src[j];
-      v[8 * j + 0] = bf16_lo(q.x); v[8 * j + 1] = bf16_hi(q.x);
-      v[8 * j + 2] = bf16_lo(q.y); v[8 * j + 3] = bf16_hi(q.y);
-      v[8 * j + 4] = bf16_lo(q.z); v[8 * j + 5] = bf16_hi(q.z);
-      v[8 * j + 6] = bf16_lo(q.w); v[8 * j + 7] = bf16_hi(q.w);
-    }
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u < S) {
+        const uint4* src = reinterpret_cast<const uint4*>(pbase + ((int64_t)b * S + s0 + u) * sstride);
+        q[u][0] = src[0];
+        q[u][1] = src[1];
+      }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[r] += v[r] * s_w[s][8 * (r / 4) + 4 * hf + (r % 4)];
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u < S) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const uint32_t wv[4] = {q[u][j].x, q[u][j].y, q[u][j].z, q[u][j].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r0 = 8 * j + 2 * e;
+            o[r0] += bf16_lo(wv[e]) * s_w[s0 + u][8 * (r0 / 4) + 4 * hf + (r0 % 4)];
+            o[r0 + 1] += bf16_hi(wv[e]) * s_w[s0 + u][8 * ((r0 + 1) / 4) + 4 * hf + ((r0 + 1) % 4)];
+          }
+        }
+      }
   }
   // ---- transpose to [head][dv] and write rows
 #pragma unroll
   for (int r = 0; r < 16; ++r) s_out[8 * (r / 4) + 4 * hf + (r % 4)][32 * n + col] = o[r];
   __syncthreads();
-  for (int i = tid; i < 32 * 256; i += 512) {
-    const int h = i / 256, d = i % 256;
-    const int64_t oi = ((int64_t)b * a.q_heads + 32 * w + h) * kMlaDv + 256 * half + d;
+  for (int i = tid; i < 32 * 128; i += 256) {
+    const int h = i / 128, d = i % 128;
+    const int64_t oi = ((int64_t)b * a.q_heads + 32 * w + h) * kMlaDv + 128 * quarter + d;
     if (a.out_dtype == 0)
       reinterpret_cast<float*>(a.out)[oi] = s_out[h][d];
     else
@@ -668,7 +687,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
       default: return hipErrorInvalidValue;
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    attn_mla_combine_kernel<<<a.batch * nw * 2, 512, 0, st>>>(a, nw);
+    attn_mla_combine_kernel<<<a.batch * nw * 4, 256, 0, st>>>(a, nw);
     return hipGetLastError();
   } else {
     dim3 grid(a.splits, a.batch * a.num_kv_heads);

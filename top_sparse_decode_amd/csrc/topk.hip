@@ -231,7 +231,7 @@ __device__ float exact_dsa_score(const ScoreArgs& sa, int b, int g, int t, float
 // fallback of the multi-block path when a row's band does not fit the band
 // list (e.g. long runs of equal scores).
 template <int NI, bool RESIDENT, bool FAST>
-__device__ __noinline__ void select_row_block(const SelectArgs& a, int row, SelShared& sh,
+__device__ __forceinline__ void select_row_block(const SelectArgs& a, int row, SelShared& sh,
                                  float (*s_terms)[kWave]) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int b = row / a.groups;
