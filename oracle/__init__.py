@@ -27,6 +27,7 @@ import ctypes
 import os
 import subprocess
 from dataclasses import dataclass
+from typing import Optional
 
 import numpy as np
 
@@ -34,7 +35,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-F32, BF16 = 0, 1
+F32, BF16, FP8 = 0, 1, 2
 GROUP_SUM, GROUP_MEAN, RELU_WEIGHTED = 0, 1, 2
 _MODES = {"group_sum": GROUP_SUM, "group_mean": GROUP_MEAN, "relu_weighted": RELU_WEIGHTED}
 _ERRORS = {1: "bad argument", 2: "page id out of range", 3: "NaN score", 4: "index out of range"}
@@ -62,6 +63,7 @@ class _Pool(ctypes.Structure):
         ("page_stride", ctypes.c_int64),
         ("head_stride", ctypes.c_int64),
         ("token_stride", ctypes.c_int64),
+        ("scale", ctypes.c_void_p),
     ]
 
 
@@ -96,7 +98,9 @@ def _dtype_code(a: np.ndarray) -> int:
         return F32
     if a.dtype == np.uint16:
         return BF16
-    raise TypeError(f"oracle takes float32 or bfloat16 bits (uint16), got {a.dtype}")
+    if a.dtype == np.uint8:
+        return FP8
+    raise TypeError(f"oracle takes float32, bfloat16 bits (uint16) or FP8 E4M3 codes (uint8), got {a.dtype}")
 
 
 @dataclass
@@ -106,6 +110,7 @@ class PoolView:
     head_dim] in any memory order, the element strides are taken from it."""
 
     data: np.ndarray
+    scale: Optional[np.ndarray] = None  # FP8 pools: [num_pages, num_kv_heads, page_size] float32
 
     def struct(self) -> _Pool:
         a = self.data
@@ -115,8 +120,14 @@ class PoolView:
         st = [s // es for s in a.strides]
         if st[3] != 1:
             raise ValueError("pool rows must be contiguous")
+        sc = None
+        if a.dtype == np.uint8:
+            if self.scale is None or self.scale.shape != (a.shape[0], a.shape[1], a.shape[2]):
+                raise ValueError("an FP8 pool needs scales [num_pages, num_kv_heads, page_size]")
+            self._scale_c = np.ascontiguousarray(self.scale, dtype=np.float32)  # kept alive with the view
+            sc = self._scale_c.ctypes.data
         return _Pool(a.ctypes.data, _dtype_code(a), a.shape[0], a.shape[2], a.shape[1],
-                     a.shape[3], st[0], st[1], st[2])
+                     a.shape[3], st[0], st[1], st[2], sc)
 
 
 def _c(a: np.ndarray, dtype) -> np.ndarray:
@@ -124,12 +135,14 @@ def _c(a: np.ndarray, dtype) -> np.ndarray:
 
 
 def score(block_table, kv_lens, k_pool: np.ndarray, q: np.ndarray, weights, mode: int,
-          head_scale: float, row_len: int) -> np.ndarray:
-    """Scores [batch, num_kv_heads, row_len] float32 (-inf past kv_len)."""
+          head_scale: float, row_len: int, k_scale: Optional[np.ndarray] = None) -> np.ndarray:
+    """Scores [batch, num_kv_heads, row_len] float32 (-inf past kv_len).  An
+    FP8 pool (uint8 codes) comes with its row scales ``k_scale``."""
     lib = _load()
     bt = _c(block_table, np.int32)
     kl = _c(kv_lens, np.int32)
-    pool = PoolView(k_pool).struct()
+    view = PoolView(k_pool, k_scale)
+    pool = view.struct()
     qa = np.ascontiguousarray(q)
     batch, q_heads = qa.shape[0], qa.shape[1]
     w = None if weights is None else _c(weights, np.float32)
@@ -192,7 +205,7 @@ def sparse_decode(w) -> dict:
     score -> top-k -> attention.  Returns scores, indices, counts and the
     float64 output."""
     s = score(w.block_table, w.kv_lens, w.score_k, w.score_q, w.head_weights, w.mode,
-              w.head_scale, w.max_kv_len)
+              w.head_scale, w.max_kv_len, getattr(w, "score_k_scale", None))
     idx, cnt = topk(s, w.kv_lens, w.topk)
     out = attention(w.block_table, w.kv_lens, w.q, w.k, w.v, w.v_dim, idx, w.softmax_scale)
     return {"scores": s, "indices": idx, "counts": cnt, "out": out}

@@ -25,8 +25,21 @@ static float bf16_bits_to_float(uint16_t b) {
   return f;
 }
 
+/* OCP FP8 E4M3 ("E4M3FN"): sign bit, 4 exponent bits with bias 7, 3
+ * mantissa bits.  Exponent field 0 holds the subnormals m * 2^-9; the two
+ * codes with every exponent and mantissa bit set are NaN; there is no
+ * infinity, the largest finite value is 448. */
+static float fp8_e4m3_to_float(uint8_t c) {
+  const int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  if (e == 15 && m == 7) return NAN;
+  /* (1 + m/8) * 2^(e-7) = (8 + m) * 2^(e-10) for normals */
+  const float v = e == 0 ? ldexpf((float)m, -9) : ldexpf((float)(8 + m), e - 10);
+  return s ? -v : v;
+}
+
 static float load_elem(const void* base, int32_t dtype, int64_t off) {
   if (dtype == ORC_F32) return ((const float*)base)[off];
+  if (dtype == ORC_FP8) return fp8_e4m3_to_float(((const uint8_t*)base)[off]);
   return bf16_bits_to_float(((const uint16_t*)base)[off]);
 }
 
@@ -44,6 +57,14 @@ static int64_t row_offset(const orc_pool* p, const int32_t* block_table, int32_t
   if (page < 0 || page >= p->num_pages) return -1;
   return (int64_t)page * p->page_stride + (int64_t)g * p->head_stride +
          (int64_t)slot * p->token_stride;
+}
+
+/* The FP8 row scale of token t (same page lookup as row_offset, which the
+ * caller has already checked). */
+static float row_scale(const orc_pool* p, const int32_t* block_table, int32_t max_pages, int32_t b,
+                       int32_t g, int32_t t) {
+  const int32_t page = block_table[(int64_t)b * max_pages + t / p->page_size];
+  return p->scale[((int64_t)page * p->num_kv_heads + g) * p->page_size + t % p->page_size];
 }
 
 /* q . k accumulated in binary32 in ascending d, each product and each sum
@@ -81,6 +102,7 @@ int orc_score(const int32_t* block_table, int32_t max_pages, const int32_t* kv_l
   if (Hkv <= 0 || D <= 0 || k->page_size <= 0 || q_heads % Hkv != 0) return ORC_EARG;
   if (mode == ORC_RELU_WEIGHTED && !weights) return ORC_EARG;
   if (mode < ORC_GROUP_SUM || mode > ORC_RELU_WEIGHTED) return ORC_EARG;
+  if (k->dtype == ORC_FP8 && !k->scale) return ORC_EARG;
   const int32_t G = q_heads / Hkv;
   const float inv_g = (float)(1.0 / (double)G);
 
@@ -101,6 +123,12 @@ int orc_score(const int32_t* block_table, int32_t max_pages, const int32_t* kv_l
         int64_t off = row_offset(k, block_table, max_pages, b, g, t);
         if (off < 0) { rc = ORC_EPAGE; break; }
         for (int32_t d = 0; d < D; ++d) kf[d] = load_elem(k->data, k->dtype, off + d);
+        if (k->dtype == ORC_FP8) {
+          /* dequantize first, one binary32 rounding per element, then score
+           * the binary32 row exactly as an F32 pool */
+          const float sc = row_scale(k, block_table, max_pages, b, g, t);
+          for (int32_t d = 0; d < D; ++d) kf[d] = kf[d] * sc;
+        }
         float s = 0.0f;
         for (int32_t j = 0; j < G; ++j) {
           int32_t h = g * G + j;
@@ -208,6 +236,7 @@ int orc_attention(const int32_t* block_table, int32_t max_pages, const int32_t* 
   if (batch < 0 || q_heads <= 0 || Hkv <= 0 || q_heads % Hkv != 0 || k_sel <= 0) return ORC_EARG;
   if (v->num_kv_heads != Hkv || v_dim <= 0 || v_dim > v->head_dim) return ORC_EARG;
   if (v->page_size != k->page_size) return ORC_EARG;
+  if (k->dtype == ORC_FP8 || v->dtype == ORC_FP8) return ORC_EARG;  /* indexer pools only */
   const int32_t G = q_heads / Hkv;
 
   double* x = (double*)malloc(sizeof(double) * (size_t)k_sel);

@@ -38,6 +38,7 @@ extern "C" {
 /* element types */
 #define ORC_F32 0   /* IEEE binary32                                  */
 #define ORC_BF16 1  /* bfloat16 bits stored as uint16 (upper half of f32) */
+#define ORC_FP8 2   /* OCP FP8 E4M3 byte codes with one binary32 scale per row */
 
 /* score modes */
 #define ORC_GROUP_SUM 0      /* s = sum_{h in group} (dot_h * head_scale)       */
@@ -56,12 +57,21 @@ typedef struct {
   int32_t dtype;     /* ORC_F32 or ORC_BF16                                  */
   int32_t num_pages, page_size, num_kv_heads, head_dim;
   int64_t page_stride, head_stride, token_stride;  /* in elements            */
+  /* ORC_FP8 only: the scale of each row, [num_pages][num_kv_heads][page_size]
+   * contiguous; row (page, g, slot) stands for the values
+   * decode(code) * scale[(page * num_kv_heads + g) * page_size + slot]. */
+  const float* scale;
 } orc_pool;
 
 /* Scores for every (request b, KV head g, token t < kv_lens[b]); entries
  * t >= kv_lens[b] of a row are set to -inf.  q is [batch][q_heads][head_dim],
  * query head h belongs to KV head h / (q_heads / num_kv_heads).  weights is
- * [batch][q_heads] (RELU_WEIGHTED only).  scores is [batch][num_kv_heads][row_len]. */
+ * [batch][q_heads] (RELU_WEIGHTED only).  scores is [batch][num_kv_heads][row_len].
+ * An ORC_FP8 pool is dequantized first (each element decoded and multiplied
+ * by its row scale, one binary32 rounding) and the binary32 row is then
+ * scored exactly as an ORC_F32 row: the block-scaled FP8 indexer cache of
+ * "Overlap DSA heuristic prev_topk write-back on the aux stream" (Test
+ * Coverage: the FP8 block-scale end-to-end test). */
 int orc_score(const int32_t* block_table, int32_t max_pages, const int32_t* kv_lens,
               int32_t batch, const orc_pool* k, const void* q, int32_t q_dtype,
               int32_t q_heads, const float* weights, int32_t mode, float head_scale,

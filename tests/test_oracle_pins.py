@@ -415,3 +415,81 @@ def test_local_to_global_by_hand():
     # request 1: t=1 -> 1, t=4 -> page 9 (out of pool) -> -1, 5 -> -1, 11 -> page 3 -> 15,
     #            t=12 -> past the table -> -1, t=2 -> 2
     assert got.tolist() == [[[20, 23, 8, 11, -1, -1]], [[1, -1, -1, 15, -1, 2]]]
+
+
+# ----------------------------------------------------------------- FP8 indexer pools
+
+def _fp8_values(codes):
+    """Score one-hot queries against one FP8 row of the given codes with unit
+    scale: dot = decode(code) exactly (one nonzero product, exact sums)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    D = len(codes)
+    pool = codes[None, None, None, :]
+    scale = np.ones((1, 1, 1), dtype=F32)
+    q = np.eye(D, dtype=F32)[None]                              # [1, D heads, D]
+    bt = np.zeros((1, 1), dtype=np.int32)
+    # group_sum with G = D heads on one KV head would add them up; score each
+    # head alone instead (one query head per call)
+    out = []
+    for d in range(D):
+        s = oracle.score(bt, [1], pool, q[:, d:d + 1, :], None, "group_sum", 1.0, 1, k_scale=scale)
+        out.append(s[0, 0, 0])
+    return np.array(out, dtype=np.float64)
+
+
+def test_fp8_e4m3_decode_facts():
+    # OCP FP8 E4M3: bias 7, 3 mantissa bits, subnormal step 2^-9, max 448,
+    # S.1111.111 is NaN.  Spot values, then the spacing inside every binade.
+    spot = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0,
+            0x3F: 1.875, 0x40: 2.0, 0x77: 240.0, 0x7D: 416.0, 0x7E: 448.0,
+            0xB8: -1.0, 0xFE: -448.0}
+    got = _fp8_values(list(spot))
+    assert list(got) == list(spot.values())
+    pos = _fp8_values(list(range(0x00, 0x7F)))       # every finite non-negative code
+    neg = _fp8_values(list(range(0x80, 0xFF)))
+    assert np.array_equal(neg, -pos)                  # sign-magnitude
+    steps = np.diff(pos)
+    assert np.all(steps[:8] == 2.0 ** -9)             # subnormals and the step into 2^-6
+    for e in range(1, 16):                            # binade e: codes 8e .. 8e+7 (8e+7 < 0x7F)
+        lo, hi = 8 * e, min(8 * e + 7, 0x7E)
+        assert np.all(np.diff(pos[lo:hi + 1]) == 2.0 ** (e - 10)), e
+    nan = _fp8_values([0x7F, 0xFF])
+    assert np.all(np.isnan(nan))
+
+
+def test_fp8_pool_scores_as_dequantized_f32_pool():
+    # dequantize-then-score: the FP8 row (codes c, scale s) scores exactly as
+    # the binary32 row decode(c) * s, one binary32 rounding per element
+    w = synth.make_workload(4, batch=2, kv_len=[300, 77], idx_heads=8, heads=4, topk=32,
+                            index_dtype="fp8")
+    s8 = oracle.score(w.block_table, w.kv_lens, w.score_k, w.score_q, w.head_weights, w.mode,
+                      1.0, w.max_kv_len, k_scale=w.score_k_scale)
+    # decode table from the one-hot scores (a NaN code in the row would turn
+    # every product with it into NaN, so the two NaN codes are left out)
+    fin = [c for c in range(256) if c not in (0x7F, 0xFF)]
+    table = np.full(256, np.nan, dtype=F32)
+    table[fin] = _fp8_values(fin).astype(F32)
+    deq = table[w.score_k] * w.score_k_scale[..., None].astype(F32)   # numpy float32 product
+    qf = synth.bf16_bits_to_f32(w.score_q)
+    s32 = oracle.score(w.block_table, w.kv_lens, deq.astype(F32), qf, w.head_weights, w.mode,
+                       1.0, w.max_kv_len)
+    assert np.array_equal(s8.view(np.uint32), s32.view(np.uint32))
+    # a dropped or misplaced scale would change the scores
+    s_unit = oracle.score(w.block_table, w.kv_lens, w.score_k, w.score_q, w.head_weights, w.mode,
+                          1.0, w.max_kv_len, k_scale=np.ones_like(w.score_k_scale))
+    assert not np.array_equal(s_unit, s8)
+
+
+def test_fp8_pool_scale_follows_the_page():
+    # permuting physical pages (codes and scales together) changes nothing
+    w = synth.make_workload(4, batch=2, kv_len=[500, 190], idx_heads=8, heads=4, topk=32,
+                            index_dtype="fp8")
+    base = oracle.score(w.block_table, w.kv_lens, w.score_k, w.score_q, w.head_weights, w.mode,
+                        1.0, w.max_kv_len, k_scale=w.score_k_scale)
+    perm = np.random.default_rng(7).permutation(w.score_k.shape[0])
+    inv = np.argsort(perm)
+    k2, s2 = w.score_k[perm], w.score_k_scale[perm]
+    bt2 = np.where(w.block_table >= 0, inv[np.maximum(w.block_table, 0)], -1).astype(np.int32)
+    got = oracle.score(bt2, w.kv_lens, k2, w.score_q, w.head_weights, w.mode, 1.0, w.max_kv_len,
+                       k_scale=s2)
+    assert np.array_equal(got.view(np.uint32), base.view(np.uint32))

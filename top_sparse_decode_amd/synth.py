@@ -64,6 +64,44 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
+FP8_NAN = np.uint8(0x7F)
+FP8_MAX = 448.0
+
+
+def to_fp8_e4m3(x: np.ndarray) -> np.ndarray:
+    """float32 -> OCP FP8 E4M3 codes (sign, 4 exponent bits with bias 7, 3
+    mantissa bits; subnormals m * 2^-9), round to nearest even, magnitudes
+    above 448 saturated to 448.  Finite inputs."""
+    x = np.asarray(x, dtype=np.float32)
+    sign = (np.signbit(x)).astype(np.uint8) << np.uint8(7)
+    a = np.abs(x).astype(np.float64)
+    frac, ex = np.frexp(a)                 # a = frac * 2^ex, frac in [0.5, 1)
+    e = ex.astype(np.int64) - 1            # a = (2 frac) * 2^e
+    normal = (e >= -6) & (a > 0)
+    # normals: 8 + mantissa = rne(a / 2^(e-3)) in [8, 16]; subnormals: rne(a / 2^-9)
+    m_norm = np.rint(np.where(normal, np.ldexp(a, -(e - 3)), 0.0)).astype(np.int64)
+    m_sub = np.rint(np.where(normal, 0.0, np.ldexp(a, 9))).astype(np.int64)
+    up = m_norm == 16                      # rounding carried into the next binade
+    e = np.where(up, e + 1, e)
+    m_norm = np.where(up, 8, m_norm)
+    be = np.where(normal, e + 7, np.where(m_sub == 8, 1, 0))
+    mant = np.where(normal, m_norm - 8, np.where(m_sub == 8, 0, m_sub))
+    over = (be > 15) | ((be == 15) & (mant > 6))
+    be = np.where(over, 15, be)
+    mant = np.where(over, 6, mant)
+    return sign | (be.astype(np.uint8) << np.uint8(3)) | mant.astype(np.uint8)
+
+
+def quantize_rows_fp8(rows_f32: np.ndarray):
+    """Per-row block scaling: scale = max|row| / 448 (1 for an all-zero row),
+    codes = E4M3(row / scale).  rows [..., D] -> (codes uint8 [..., D],
+    scales float32 [...])."""
+    amax = np.max(np.abs(rows_f32), axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(FP8_MAX), np.float32(1.0)).astype(np.float32)
+    codes = to_fp8_e4m3(rows_f32 / scale[..., None])
+    return codes, scale
+
+
 @dataclass
 class Workload:
     """One decode step's inputs.  Arrays are host numpy; bfloat16 as uint16 bits."""
@@ -89,6 +127,9 @@ class Workload:
     softmax_scale: float
     out_dtype: str                   # "f32" | "bf16"
     meta: dict = field(default_factory=dict)
+    # FP8 indexer pools: score_k holds E4M3 codes (uint8) and this the row
+    # scales [pages, Hs_kv, P] float32
+    score_k_scale: Optional[np.ndarray] = None
 
     @property
     def batch(self) -> int:
@@ -194,10 +235,10 @@ DEFAULTS = {
     3: dict(batch=32, q_heads=32, kv_heads=8, head_dim=128, kv_len=8192, page_size=64, topk=2048,
             num_pages=None),
     4: dict(batch=16, idx_heads=64, idx_dim=128, kv_len=65536, page_size=64, topk=2048,
-            heads=128, latent=576, v_dim=512, num_pages=None),
+            heads=128, latent=576, v_dim=512, num_pages=None, index_dtype="bf16"),
     5: dict(batch=64, idx_heads=64, idx_dim=128, min_len=4096, max_len=131072, page_size=64,
             topk=2048, heads=128, latent=576, v_dim=512, bias_frac=0.01, bias=4.0,
-            slack=1.25, kv_lens=None),
+            slack=1.25, kv_lens=None, index_dtype="bf16"),
 }
 
 NAMES = {1: "tiny_f32", 2: "mha_bf16", 3: "gqa_bf16", 4: "dsa_mla", 5: "dsa_mla_mixed"}
@@ -333,9 +374,20 @@ def _build_dsa(seed, p, kv_lens, name, max_len=None, num_pages=None):
     lat = _normal_pool(seed, _T_LAT, (num_pages, 1, P, Dl), True, used)
     _apply_canaries(ki, used, tails)
     _apply_canaries(lat, used, tails)
+    ki_scale = None
+    if p.get("index_dtype", "bf16") == "fp8":
+        # the same keys, block-scaled to FP8 E4M3 with one scale per token row
+        # (canary rows stay NaN: code 0x7F, scale NaN)
+        codes, ki_scale = quantize_rows_fp8(np.nan_to_num(bf16_bits_to_f32(ki), nan=0.0))
+        nanrow = np.isnan(bf16_bits_to_f32(ki)).any(axis=-1)
+        codes[nanrow] = FP8_NAN
+        ki_scale[nanrow] = np.float32(np.nan)
+        ki = codes
+    elif p.get("index_dtype", "bf16") != "bf16":
+        raise ValueError(f"index_dtype must be bf16 or fp8, got {p['index_dtype']}")
     return Workload(name, seed, P, bt, kv_lens, max_len, ki, qi, w, "relu_weighted", 1.0,
                     p["topk"], q, lat, lat, p["v_dim"], 1.0 / math.sqrt(192.0), "bf16",
-                    meta=dict(p))
+                    meta=dict(p), score_k_scale=ki_scale)
 
 
 def _build_dsa4(seed, p):
