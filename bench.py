@@ -44,17 +44,19 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-requests", type=int, default=16, help="requests in the oracle sample")
     p.add_argument("--cpu-repeats", type=int, default=2, help="passes of the oracle over the sample")
+    p.add_argument("--index-dtype", choices=["bf16", "fp8"], default="bf16",
+                   help="indexer K cache: bf16, or FP8 E4M3 codes with one float32 scale per row")
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="also run a plain device copy of this many bytes (3 launches) before the "
                         "steps: the reference kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE")
     return p.parse_args()
 
 
-def scorer_traffic(kernel_hash: str):
+def scorer_traffic(kernel_hash: str, fp8: bool):
     """HBM bytes per scorer launch from the committed rocprofv3 counter
     summary, or None when it is missing or was taken on another version of
     the scorer source."""
-    path = os.path.join(PROFILES, "score_dsa_traffic.json")
+    path = os.path.join(PROFILES, "score_dsa_fp8_traffic.json" if fp8 else "score_dsa_traffic.json")
     if not os.path.exists(path):
         return None
     try:
@@ -80,15 +82,17 @@ def main():
 
     torch.cuda.set_device(0)
     dev = "cuda:0"
-    say("[bench] generating dsa_mla workload (B16, L65536) ...")
+    fp8 = args.index_dtype == "fp8"
+    say(f"[bench] generating dsa_mla workload (B16, L65536, {args.index_dtype} indexer) ...")
     t0 = time.time()
-    w = synth.make_workload(4)
+    w = synth.make_workload(4, index_dtype=args.index_dtype)
     say(f"[bench] generated in {time.time() - t0:.1f}s; uploading {args.replicas} replicas")
     steps = [api.prepare(w, precision=api.FAST, device=dev) for _ in range(max(1, args.replicas))]
     torch.cuda.synchronize()
 
     B, L, P = w.batch, int(w.kv_lens[0]), w.page_size
-    k_scored = B * L * w.score_k.shape[-1] * 2            # bytes of indexer K read
+    # bytes of indexer K read (fp8: the codes and one float32 scale per row)
+    k_scored = B * L * (w.score_k.shape[-1] + 4 if fp8 else w.score_k.shape[-1] * 2)
     k_gathered = B * w.topk * w.k.shape[-1] * 2           # selected latent rows (V is inside them)
     alg_bytes = k_scored + k_gathered
 
@@ -155,11 +159,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) bf16 pools, U(0,1) head weights)",
+        "dtype": "fp8e4m3+bf16" if fp8 else "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 pools, U(0,1) head weights"
+                + (", indexer keys quantized to FP8 E4M3 per row)" if fp8 else ")"),
         "config": {
             "workload": "dsa_mla: batch 16, one decode query each, kv_len 65536, page 64, "
-                        "indexer 64 heads x 128 bf16 (ReLU-weighted), top-k 2048, sparse MLA "
+                        + ("indexer 64 heads x 128 fp8 e4m3 keys with a float32 scale per row"
+                           if fp8 else "indexer 64 heads x 128 bf16")
+                        + " (ReLU-weighted), top-k 2048, sparse MLA "
                         "128 heads over 576-dim latent rows (V = first 512), scale 1/sqrt(192)",
             "batch": B, "kv_len": L, "page_size": P, "topk": w.topk,
             "precision": "fast scores + exact band re-score (indices exact)",
@@ -169,13 +176,13 @@ def main():
         "step_gbps": round(alg_bytes / (ms_step * 1e-3) / 1e9, 1),
         "step_frac_of_hbm_peak": round(alg_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         "roofline": {
-            "kernel": "score_dsa_kernel<4, 4, 4, 32>",
+            "kernel": "score_dsa_fp8_kernel<4, 4, 6, 32>" if fp8 else "score_dsa_kernel<4, 4, 4, 32>",
             "bound": "hbm",
             "achieved": round(score_gbps, 1),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(score_gbps / PEAK_HBM_GBPS, 4),
-            "traffic": scorer_traffic(src_hash),
+            "traffic": scorer_traffic(src_hash, fp8),
             "avg_launch_us": round(score_ms * 1e3, 2),
             "bytes_per_launch": k_scored,
         },

@@ -46,6 +46,13 @@
  *     token whose page id is outside [0, num_pages) is treated as absent (it
  *     scores -inf, is never kept, and contributes nothing to attention).
  *   - bfloat16 data is passed as raw 16-bit patterns (SD_BF16).
+ *   - SD_FP8_E4M3 pools (indexer K only) hold OCP FP8 E4M3 byte codes (sign,
+ *     4 exponent bits with bias 7, 3 mantissa bits; no infinities, codes 0x7F
+ *     and 0xFF are NaN, largest finite 448) plus one binary32 scale per row:
+ *     row (page p, KV head g, slot s) stands for decode(code) * scale[(p *
+ *     num_kv_heads + g) * page_size + s] ("Overlap DSA heuristic prev_topk
+ *     write-back on the aux stream", Test Coverage: the block-scaled FP8
+ *     indexer cache).
  *   - Every entry point validates its host-visible arguments first and
  *     returns a non-SD_OK status without enqueuing anything when they are
  *     wrong; sd_last_error() then names the argument.  No exception crosses
@@ -63,7 +70,7 @@
 extern "C" {
 #endif
 
-#define SD_VERSION 1
+#define SD_VERSION 2
 
 typedef enum sd_status {
   SD_OK = 0,
@@ -73,7 +80,7 @@ typedef enum sd_status {
   SD_ERR_HIP = 4               /* a HIP launch or runtime call failed          */
 } sd_status;
 
-typedef enum sd_dtype { SD_F32 = 0, SD_BF16 = 1 } sd_dtype;
+typedef enum sd_dtype { SD_F32 = 0, SD_BF16 = 1, SD_FP8_E4M3 = 2 } sd_dtype;
 
 /* How the per-head dot products of one KV head's query heads become one
  * token score ("Add TriAttention ...", Summary: per-head reduction; the DSA
@@ -91,6 +98,10 @@ typedef enum sd_score_mode {
  * over the group's heads left to right in head order, with the mode's scale
  * applied as written above.  Two calls, or this library and any other
  * implementation of that order, agree bit for bit.
+ * An SD_FP8_E4M3 pool is scored as the binary32 pool of its dequantized
+ * rows: each element is decoded and multiplied by its row scale (one
+ * rounding), then the dot products follow the same order with every product
+ * rounded once.
  * SD_SCORE_FAST may evaluate in another order (bf16 matrix cores for the
  * DSA mode) and reports a per-row bound on its distance from the exact score.
  * Modes without a fast kernel compute the exact scores in both settings. */
@@ -107,6 +118,8 @@ typedef struct sd_pool {
   int64_t page_stride;     /* elements                                         */
   int64_t head_stride;     /* elements                                         */
   int64_t token_stride;    /* elements                                         */
+  const float* scale;      /* SD_FP8_E4M3 only (else NULL): device row scales  */
+                           /* [num_pages][num_kv_heads][page_size], contiguous */
 } sd_pool;
 
 /* The batch's page tables ("Add TriAttention ...", Key Design Decisions: a
@@ -123,7 +136,7 @@ typedef struct sd_pages {
 
 /* Score every token t < kv_len of every (request, KV head) of k_pool.
  *   q            device [batch][q_heads][k_pool->head_dim], dtype q_dtype
- *                (must equal k_pool->dtype)
+ *                (must equal k_pool->dtype; SD_BF16 for an SD_FP8_E4M3 pool)
  *   head_weights device [batch][q_heads] float, RELU_WEIGHTED only (else NULL)
  *   head_scale   GROUP_SUM factor (ignored by the other modes)
  *   scores       device [batch][num_kv_heads][max_kv_len] float; entries at
@@ -172,7 +185,8 @@ sd_status sd_topk_select(const float* scores, int32_t batch, int32_t groups, int
  *   sum_t e^{x_t - max x}, over the kept t of indices[b][g][0..k_sel).
  *   q        device [batch][q_heads][k_pool->head_dim], dtype q_dtype
  *   k_pool   key rows; v_pool value rows whose first v_dim elements are the
- *            value (MLA: pass the latent pool as both, v_dim = 512)
+ *            value (MLA: pass the latent pool as both, v_dim = 512); F32 or
+ *            BF16 (FP8 pools are scored, not attended)
  *   indices  device [batch][num_kv_heads][k_sel] int32 request-local
  *            positions, -1 = unused slot; a position >= kv_len or on an absent
  *            page is skipped

@@ -37,22 +37,24 @@ def test_library_exports_every_declared_symbol():
     lib = _lib()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.sd_version() == 1
+    assert lib.sd_version() == 2
     assert lib.sd_status_string(0) == b"ok"
     assert lib.sd_status_string(3) == b"workspace too small"
 
 
-def _pool(data=4096, dtype=api.BF16, pages=8, P=64, H=1, D=128):
-    return api.sd_pool(data, dtype, pages, P, H, D, H * P * D, P * D, D)
+def _pool(data=4096, dtype=api.BF16, pages=8, P=64, H=1, D=128, scale=None):
+    return api.sd_pool(data, dtype, pages, P, H, D, H * P * D, P * D, D, scale)
 
 
 def _pages(batch=2, max_pages=4, max_kv_len=256):
     return api.sd_pages(8192, 12288, batch, max_pages, max_kv_len)
 
 
-def _rc_score(pg, pool, q=16384, heads=64, w=20480, mode=api.RELU_WEIGHTED, scores=24576):
+def _rc_score(pg, pool, q=16384, heads=64, w=20480, mode=api.RELU_WEIGHTED, scores=24576, q_dtype=None):
     lib = _lib()
-    return lib.sd_sparse_score_paged(ctypes.byref(pg), ctypes.byref(pool), q, pool.dtype, heads, w,
+    if q_dtype is None:
+        q_dtype = api.BF16 if pool.dtype == api.FP8_E4M3 else pool.dtype
+    return lib.sd_sparse_score_paged(ctypes.byref(pg), ctypes.byref(pool), q, q_dtype, heads, w,
                                      mode, 1.0, api.FAST, scores, None, 0)
 
 
@@ -70,6 +72,37 @@ def test_score_argument_validation():
     assert _rc_score(_pages(), _pool(), scores=None) == api.ERR_INVALID_ARGUMENT
     # zero-size batch is a no-op that needs no GPU
     assert _rc_score(_pages(batch=0), _pool()) == api.OK
+
+
+def test_fp8_pool_validation():
+    lib = _lib()
+    fp8 = dict(dtype=api.FP8_E4M3)
+    assert _rc_score(_pages(), _pool(**fp8)) == api.ERR_INVALID_ARGUMENT          # no scales
+    assert b"scales" in lib.sd_last_error()
+    assert _rc_score(_pages(), _pool(scale=4104, **fp8)) == api.ERR_INVALID_ARGUMENT  # misaligned
+    assert _rc_score(_pages(), _pool(scale=8192)) == api.ERR_INVALID_ARGUMENT     # scales on a bf16 pool
+    assert _rc_score(_pages(), _pool(D=120, scale=8192, **fp8)) == api.ERR_INVALID_ARGUMENT  # 120-byte rows
+    assert _rc_score(_pages(), _pool(scale=8192, **fp8), q_dtype=api.F32) == api.ERR_UNSUPPORTED
+    assert _rc_score(_pages(), _pool(scale=8192, **fp8), q_dtype=api.FP8_E4M3) == api.ERR_UNSUPPORTED
+    assert _rc_score(_pages(batch=0), _pool(scale=8192, **fp8)) == api.OK
+    # FP8 pools are scored, never attended
+    n = ctypes.c_size_t(0)
+    kp = _pool(D=576, scale=8192, **fp8)
+    assert lib.sd_sparse_decode_attn_workspace_size(ctypes.byref(_pages()), 128, ctypes.byref(kp), 512,
+                                                     2048, ctypes.byref(n)) == api.ERR_UNSUPPORTED
+    # the fused step accepts an FP8 indexer pool beside a bf16 latent pool
+    a = api.sd_sparse_decode_args()
+    a.pages = _pages(batch=4, max_pages=64, max_kv_len=4096)
+    a.score_k = api.sd_pool(4096, api.FP8_E4M3, 512, 64, 1, 128, 64 * 128, 64 * 128, 128, 8192)
+    a.score_q_dtype, a.score_heads, a.mode, a.head_scale = api.BF16, 64, api.RELU_WEIGHTED, 1.0
+    a.precision, a.topk = api.FAST, 2048
+    a.q_dtype, a.q_heads = api.BF16, 128
+    a.k = api.sd_pool(8192, api.BF16, 512, 64, 1, 576, 64 * 576, 64 * 576, 576)
+    a.v = a.k
+    a.v_dim, a.softmax_scale, a.out_dtype = 512, 0.0721, api.BF16
+    assert lib.sd_sparse_decode_workspace_size(ctypes.byref(a), ctypes.byref(n)) == api.OK
+    a.score_q_dtype = api.FP8_E4M3
+    assert lib.sd_sparse_decode_workspace_size(ctypes.byref(a), ctypes.byref(n)) == api.ERR_UNSUPPORTED
 
 
 def test_topk_argument_validation():
@@ -117,11 +150,11 @@ def test_fused_workspace_and_validation():
     lib = _lib()
     a = api.sd_sparse_decode_args()
     a.pages = _pages(batch=16, max_pages=1024, max_kv_len=65536)
-    a.score_k = api.sd_pool(4096, api.BF16, 16384, 64, 1, 128, 64 * 128, 64 * 128, 128)
+    a.score_k = api.sd_pool(4096, api.BF16, 16384, 64, 1, 128, 64 * 128, 64 * 128, 128, None)
     a.score_q_dtype, a.score_heads, a.mode, a.head_scale = api.BF16, 64, api.RELU_WEIGHTED, 1.0
     a.precision, a.topk = api.FAST, 2048
     a.q_dtype, a.q_heads = api.BF16, 128
-    a.k = api.sd_pool(8192, api.BF16, 16384, 64, 1, 576, 64 * 576, 64 * 576, 576)
+    a.k = api.sd_pool(8192, api.BF16, 16384, 64, 1, 576, 64 * 576, 64 * 576, 576, None)
     a.v = a.k
     a.v_dim, a.softmax_scale, a.out_dtype = 512, 0.0721, api.BF16
     n = ctypes.c_size_t(0)

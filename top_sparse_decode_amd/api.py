@@ -21,7 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsparse_decode.so")
 
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = range(5)
-F32, BF16 = 0, 1
+F32, BF16, FP8_E4M3 = 0, 1, 2
 GROUP_SUM, GROUP_MEAN, RELU_WEIGHTED = 0, 1, 2
 EXACT, FAST = 0, 1
 MODES = {"group_sum": GROUP_SUM, "group_mean": GROUP_MEAN, "relu_weighted": RELU_WEIGHTED}
@@ -37,7 +37,8 @@ class sd_pool(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int), ("num_pages", ctypes.c_int32),
                 ("page_size", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("page_stride", ctypes.c_int64),
-                ("head_stride", ctypes.c_int64), ("token_stride", ctypes.c_int64)]
+                ("head_stride", ctypes.c_int64), ("token_stride", ctypes.c_int64),
+                ("scale", ctypes.c_void_p)]
 
 
 class sd_pages(ctypes.Structure):
@@ -132,18 +133,30 @@ def dtype_code(t) -> int:
         return F32
     if t.dtype == torch.bfloat16:
         return BF16
+    if t.dtype in (torch.uint8, getattr(torch, "float8_e4m3fn", None)):
+        return FP8_E4M3
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
 # ------------------------------------------------------------------ descriptors
 
-def pool(t, num_kv_heads_dim: int = 1) -> sd_pool:
+def pool(t, scale=None) -> sd_pool:
     """Describe a 4-D paged pool tensor [pages, kv_heads, page_size, head_dim]
-    (HND; any strides with a contiguous last dim)."""
+    (HND; any strides with a contiguous last dim).  An FP8 E4M3 pool (uint8
+    codes) takes its float32 row scales [pages, kv_heads, page_size]."""
     if t.dim() != 4 or t.stride(3) != 1:
         raise ValueError("pool must be 4-D [pages, kv_heads, page_size, head_dim] with contiguous rows")
-    return sd_pool(t.data_ptr(), dtype_code(t), t.shape[0], t.shape[2], t.shape[1], t.shape[3],
-                   t.stride(0), t.stride(1), t.stride(2))
+    code = dtype_code(t)
+    if code == FP8_E4M3:
+        import torch
+
+        if scale is None or scale.dtype != torch.float32 or tuple(scale.shape) != (t.shape[0], t.shape[1], t.shape[2]) \
+                or not scale.is_contiguous():
+            raise ValueError("an FP8 pool needs contiguous float32 scales [pages, kv_heads, page_size]")
+    elif scale is not None:
+        raise ValueError("scales are for FP8 pools only")
+    return sd_pool(t.data_ptr(), code, t.shape[0], t.shape[2], t.shape[1], t.shape[3],
+                   t.stride(0), t.stride(1), t.stride(2), None if scale is None else scale.data_ptr())
 
 
 def pages(block_table, kv_lens, max_kv_len: int) -> sd_pages:
@@ -225,7 +238,7 @@ def version() -> int:
 # ------------------------------------------------------------------ workloads on the device
 
 def to_device_array(a: np.ndarray, device="cuda"):
-    """numpy float32 / uint16 (bfloat16 bits) / int32 -> torch tensor on device."""
+    """numpy float32 / uint16 (bfloat16 bits) / uint8 (FP8 codes) / int32 -> torch tensor on device."""
     import torch
 
     if a.dtype == np.uint16:
@@ -240,6 +253,7 @@ class DeviceStep:
     block_table: object
     kv_lens: object
     score_k: object
+    score_k_scale: object
     score_q: object
     head_weights: object
     q: object
@@ -264,6 +278,7 @@ def prepare(w, precision: int = FAST, device="cuda", out_dtype=None) -> DeviceSt
     bt = to_device_array(w.block_table, device)
     kl = to_device_array(w.kv_lens, device)
     sk = to_device_array(w.score_k, device)
+    sks = None if getattr(w, "score_k_scale", None) is None else to_device_array(w.score_k_scale, device)
     sq = to_device_array(w.score_q, device)
     hw = None if w.head_weights is None else to_device_array(w.head_weights, device)
     if w.score_k is w.k:
@@ -280,7 +295,7 @@ def prepare(w, precision: int = FAST, device="cuda", out_dtype=None) -> DeviceSt
     pg = pages(bt, kl, w.max_kv_len)
     args = sd_sparse_decode_args()
     args.pages = pg
-    args.score_k = pool(sk)
+    args.score_k = pool(sk, sks)
     args.score_q = sq.data_ptr()
     args.score_q_dtype = dtype_code(sq)
     args.score_heads = w.score_q.shape[1]
@@ -302,4 +317,4 @@ def prepare(w, precision: int = FAST, device="cuda", out_dtype=None) -> DeviceSt
     args.counts_out = cnt.data_ptr()
     nbytes = sparse_decode_workspace_size(args)
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
-    return DeviceStep(bt, kl, sk, sq, hw, q, k, v, out, idx, cnt, ws, args, w)
+    return DeviceStep(bt, kl, sk, sks, sq, hw, q, k, v, out, idx, cnt, ws, args, w)

@@ -36,8 +36,9 @@ sd_status hip_status(hipError_t e, const char* what) {
   return fail(SD_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-int elem_size(sd_dtype t) { return t == SD_F32 ? 4 : 2; }
-bool dtype_ok(sd_dtype t) { return t == SD_F32 || t == SD_BF16; }
+int elem_size(sd_dtype t) { return t == SD_F32 ? 4 : (t == SD_BF16 ? 2 : 1); }
+bool dtype_ok(sd_dtype t) { return t == SD_F32 || t == SD_BF16 || t == SD_FP8_E4M3; }
+int dtype_code(sd_dtype t) { return t == SD_F32 ? 0 : (t == SD_BF16 ? 1 : 2); }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 constexpr size_t kAlign = 256;
@@ -68,6 +69,12 @@ sd_status check_pool(const sd_pool* k, const char* name) {
   if (!aligned16(k->data) || ((int64_t)k->head_dim * es) % 16 || (k->page_stride * es) % 16 ||
       (k->head_stride * es) % 16 || (k->token_stride * es) % 16)
     return fail(SD_ERR_INVALID_ARGUMENT, "%s: rows must be 16-byte aligned", name);
+  if (k->dtype == SD_FP8_E4M3) {
+    if (!k->scale) return fail(SD_ERR_INVALID_ARGUMENT, "%s: FP8 pool needs row scales", name);
+    if (!aligned16(k->scale)) return fail(SD_ERR_INVALID_ARGUMENT, "%s: scales must be 16-byte aligned", name);
+  } else if (k->scale) {
+    return fail(SD_ERR_INVALID_ARGUMENT, "%s: scales are for FP8 pools only", name);
+  }
   return SD_OK;
 }
 
@@ -81,7 +88,8 @@ sd::ScoreArgs make_score_args(const sd_pages* pg, const sd_pool* k, const void* 
   a.max_pages = pg->max_pages;
   a.max_kv_len = pg->max_kv_len;
   a.k = k->data;
-  a.dtype = k->dtype == SD_F32 ? 0 : 1;
+  a.dtype = dtype_code(k->dtype);
+  a.k_scale = k->scale;
   a.num_pages = k->num_pages;
   a.page_size = k->page_size;
   a.num_kv_heads = k->num_kv_heads;
@@ -108,7 +116,8 @@ sd_status check_score(const sd_pages* pg, const sd_pool* k, const void* q, sd_dt
   sd_status st = check_pool(k, "score k");
   if (st != SD_OK) return st;
   if ((st = check_pages(pg, k->page_size)) != SD_OK) return st;
-  if (q_dtype != k->dtype) return fail(SD_ERR_UNSUPPORTED, "score q dtype must equal the K pool dtype");
+  if (k->dtype == SD_FP8_E4M3 ? q_dtype != SD_BF16 : q_dtype != k->dtype)
+    return fail(SD_ERR_UNSUPPORTED, "score q dtype must equal the K pool dtype (BF16 for an FP8 pool)");
   if (need_ptrs) {
     if (!q) return fail(SD_ERR_INVALID_ARGUMENT, "score q is NULL");
     if (!aligned16(q)) return fail(SD_ERR_INVALID_ARGUMENT, "score q must be 16-byte aligned");
@@ -156,13 +165,15 @@ sd_status plan_attn(const sd_pages* pg, const void* q, sd_dtype q_dtype, int32_t
   if ((st = check_pages(pg, k->page_size)) != SD_OK) return st;
   if (v->page_size != k->page_size || v->num_kv_heads != k->num_kv_heads)
     return fail(SD_ERR_INVALID_ARGUMENT, "k and v pools must share page_size and num_kv_heads");
+  if (k->dtype == SD_FP8_E4M3 || v->dtype == SD_FP8_E4M3)
+    return fail(SD_ERR_UNSUPPORTED, "attention pools must be F32 or BF16 (FP8 pools are scored only)");
   if (k->dtype != v->dtype || q_dtype != k->dtype)
     return fail(SD_ERR_UNSUPPORTED, "q, k and v must have one dtype");
   if (q_heads <= 0 || q_heads % k->num_kv_heads)
     return fail(SD_ERR_INVALID_ARGUMENT, "q_heads %d is not a multiple of num_kv_heads", q_heads);
   if (v_dim <= 0 || v_dim > v->head_dim) return fail(SD_ERR_INVALID_ARGUMENT, "bad v_dim %d", v_dim);
   if (k_sel <= 0) return fail(SD_ERR_INVALID_ARGUMENT, "k_sel must be >= 1");
-  if (!dtype_ok(out_dtype)) return fail(SD_ERR_INVALID_ARGUMENT, "bad out dtype");
+  if (out_dtype != SD_F32 && out_dtype != SD_BF16) return fail(SD_ERR_INVALID_ARGUMENT, "bad out dtype");
   if (need_ptrs) {
     if (!q || !indices || !out) return fail(SD_ERR_INVALID_ARGUMENT, "q, indices or out is NULL");
     if (!aligned16(q)) return fail(SD_ERR_INVALID_ARGUMENT, "q must be 16-byte aligned");

@@ -22,6 +22,25 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
+// OCP FP8 E4M3 byte `B` of a 32-bit word -> binary32 (exact; codes 0x7F and
+// 0xFF decode to NaN).  gfx950's conversion implements the OCP encoding.
+template <int B>
+__device__ __forceinline__ float fp8_to_f32(uint32_t w) { return __builtin_amdgcn_cvt_f32_fp8((int)w, B); }
+
+// Four E4M3 codes -> their dequantized values decode(code) * scale, each
+// product rounded once (the library's dequantization).
+__device__ __forceinline__ void fp8x4_dequant(uint32_t w, float scale, float* v) {
+  v[0] = __fmul_rn(fp8_to_f32<0>(w), scale);
+  v[1] = __fmul_rn(fp8_to_f32<1>(w), scale);
+  v[2] = __fmul_rn(fp8_to_f32<2>(w), scale);
+  v[3] = __fmul_rn(fp8_to_f32<3>(w), scale);
+}
+
+// Offset of the row scale of (page, KV head g, slot) in an fp8 pool's scale array.
+__device__ __forceinline__ int64_t fp8_scale_index(int page, int g, int slot, int num_kv_heads, int page_size) {
+  return ((int64_t)page * num_kv_heads + g) * page_size + slot;
+}
+
 // binary32 -> bfloat16, round to nearest even (NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   uint32_t u = __float_as_uint(f);

@@ -12,7 +12,8 @@ struct ScoreArgs {
   const int32_t* kv_lens;
   int32_t batch, max_pages, max_kv_len;
   const void* k;
-  int32_t dtype;  // 0 f32, 1 bf16 (q has the same type)
+  int32_t dtype;  // 0 f32, 1 bf16 (q has the same type); 2 fp8 e4m3 codes (q bf16)
+  const float* k_scale;  // fp8: row scales [num_pages][num_kv_heads][page_size]
   int32_t num_pages, page_size, num_kv_heads, head_dim;
   int64_t page_stride, head_stride, token_stride;
   const void* q;

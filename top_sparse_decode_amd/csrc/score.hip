@@ -38,6 +38,10 @@ template <>
 struct Elems<uint16_t> {
   static constexpr int kPerUnit = 8;
 };
+template <>
+struct Elems<uint8_t> {  // fp8 codes; the query stays bf16
+  static constexpr int kPerUnit = 16;
+};
 
 __device__ __forceinline__ void unpack_unit(const uint4& u, float (&v)[4]) {
   v[0] = __uint_as_float(u.x);
@@ -52,12 +56,50 @@ __device__ __forceinline__ void unpack_unit(const uint4& u, float (&v)[8]) {
   v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
 }
 
+// One 16-byte unit of a K row as binary32 values; an fp8 unit is dequantized
+// with its row scale.
+template <typename KT>
+__device__ __forceinline__ void load_k_unit(const KT* p, float scale, float (&v)[Elems<KT>::kPerUnit]) {
+  unpack_unit(*reinterpret_cast<const uint4*>(p), v);
+}
+template <>
+__device__ __forceinline__ void load_k_unit<uint8_t>(const uint8_t* p, float scale, float (&v)[16]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  fp8x4_dequant(u.x, scale, v);
+  fp8x4_dequant(u.y, scale, v + 4);
+  fp8x4_dequant(u.z, scale, v + 8);
+  fp8x4_dequant(u.w, scale, v + 12);
+}
+// The query elements that meet one K unit (bf16 for an fp8 pool).
+template <typename KT>
+__device__ __forceinline__ void load_q_unit(const void* p, float (&v)[Elems<KT>::kPerUnit]) {
+  unpack_unit(*reinterpret_cast<const uint4*>(p), v);
+}
+template <>
+__device__ __forceinline__ void load_q_unit<uint8_t>(const void* p, float (&v)[16]) {
+  const uint4* u = reinterpret_cast<const uint4*>(p);
+  float lo[8], hi[8];
+  unpack_unit(u[0], lo);
+  unpack_unit(u[1], hi);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    v[e] = lo[e];
+    v[8 + e] = hi[e];
+  }
+}
+template <typename KT>
+struct QElem {
+  typedef KT type;
+};
+template <>
+struct QElem<uint8_t> {
+  typedef uint16_t type;
+};
+
 // acc + q*k with the product rounded, then the sum rounded.  For bf16 q and
 // k the product is exact in binary32, so the fused form is the same value.
 template <typename KT>
-__device__ __forceinline__ float dot_step(float acc, float q, float k);
-template <>
-__device__ __forceinline__ float dot_step<float>(float acc, float q, float k) {
+__device__ __forceinline__ float dot_step(float acc, float q, float k) {
   return __fadd_rn(acc, __fmul_rn(q, k));
 }
 template <>
@@ -92,28 +134,31 @@ __global__ __launch_bounds__(256) void score_exact_kernel(ScoreArgs a) {
   float* row = a.scores + (int64_t)blockIdx.y * a.max_kv_len;
   const bool in_row = t < a.max_kv_len;
   bool ok = in_row && t < L;
-  int64_t off = 0;
+  int64_t off = 0, scale_idx = 0;
   if (ok) {
     const int page = a.block_table[(int64_t)b * a.max_pages + t / a.page_size];
     ok = page >= 0 && page < a.num_pages;
     off = (int64_t)page * a.page_stride + (int64_t)g * a.head_stride +
           (int64_t)(t % a.page_size) * a.token_stride;
+    scale_idx = fp8_scale_index(page, g, t % a.page_size, a.num_kv_heads, a.page_size);
   }
   float s = -__builtin_inff();
   if (ok) {
+    typedef typename QElem<KT>::type QT;
     const KT* krow = reinterpret_cast<const KT*>(a.k) + off;
-    const KT* qbase = reinterpret_cast<const KT*>(a.q) + ((int64_t)b * a.q_heads + g * G) * a.head_dim;
+    const QT* qbase = reinterpret_cast<const QT*>(a.q) + ((int64_t)b * a.q_heads + g * G) * a.head_dim;
+    const float ksc = std::is_same<KT, uint8_t>::value ? a.k_scale[scale_idx] : 1.0f;
     float acc[G];
 #pragma unroll
     for (int j = 0; j < G; ++j) acc[j] = 0.0f;
     const int units = a.head_dim / EPU;
     for (int u = 0; u < units; ++u) {
       float kv[EPU];
-      unpack_unit(*reinterpret_cast<const uint4*>(krow + u * EPU), kv);
+      load_k_unit<KT>(krow + u * EPU, ksc, kv);
 #pragma unroll
       for (int j = 0; j < G; ++j) {
         float qv[EPU];
-        unpack_unit(*reinterpret_cast<const uint4*>(qbase + (int64_t)j * a.head_dim + u * EPU), qv);
+        load_q_unit<KT>(qbase + (int64_t)j * a.head_dim + u * EPU, qv);
 #pragma unroll
         for (int e = 0; e < EPU; ++e) acc[j] = dot_step<KT>(acc[j], qv[e], kv[e]);
       }
@@ -200,6 +245,47 @@ __device__ __forceinline__ void lds_store_f32(uint32_t addr, float v) {
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "i"(N) : "memory");
+}
+
+// End of a fast-scorer block: the block's min / max finite score keys and
+// its bound (one atomic each), then the span's scores from the LDS staging
+// row (every token below L lies in a scored tile; the rest is -inf).
+template <int NW>
+__device__ __forceinline__ void finish_span(const ScoreArgs& a, uint32_t (*s_red)[3], const float* s_out,
+                                            float* row, int tb0, int tend, int L, float smin, float smax,
+                                            float dmax) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  uint32_t kmin = smin <= smax ? score_key(smin) : 0xFFFFFFFFu;
+  uint32_t kmax = smin <= smax ? score_key(smax) : 0u;
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
+  dmax = wave_max(dmax);
+  if (lane == 0) {
+    s_red[wid][0] = kmin;
+    s_red[wid][1] = kmax;
+    s_red[wid][2] = __float_as_uint(dmax);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t bmin = s_red[0][0], bmax = s_red[0][1];
+    float bd = __uint_as_float(s_red[0][2]);
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      bmin = min(bmin, s_red[w][0]);
+      bmax = max(bmax, s_red[w][1]);
+      bd = fmaxf(bd, __uint_as_float(s_red[w][2]));
+    }
+    if (a.row_stats && bmin <= bmax) {
+      int32_t* stat = a.row_stats + (int64_t)blockIdx.y * kStatStride;
+      atomicMin(reinterpret_cast<unsigned int*>(stat), bmin);
+      atomicMax(reinterpret_cast<unsigned int*>(stat + 1), bmax);
+    }
+    // 1e-3 relative slack covers the rounding of the bound's own evaluation,
+    // the absolute term any flushed subnormal.
+    if (a.row_bound)
+      atomicMax(reinterpret_cast<unsigned int*>(a.row_bound + blockIdx.y), __float_as_uint(bd * 1.001f + 1e-30f));
+  }
+  for (int t = tb0 + threadIdx.x; t < tend; t += NW * 64) row[t] = t < L ? s_out[t - tb0] : -__builtin_inff();
 }
 
 // MT = query heads / 16, NW waves per block, S ring stages per wave.
@@ -418,39 +504,261 @@ __global__ __launch_bounds__(NW * 64) void score_dsa_kernel(ScoreArgs a, int ite
   // scores are written
   wait_vmcnt<0>();
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  // the block's min / max finite score keys and its bound: one atomic each
-  uint32_t kmin = smin <= smax ? score_key(smin) : 0xFFFFFFFFu;
-  uint32_t kmax = smin <= smax ? score_key(smax) : 0u;
-  kmin = wave_min_u32(kmin);
-  kmax = wave_max_u32(kmax);
-  dmax = wave_max(dmax);
-  if (lane == 0) {
-    s_red[wid][0] = kmin;
-    s_red[wid][1] = kmax;
-    s_red[wid][2] = __float_as_uint(dmax);
+  finish_span<NW>(a, s_red, s_out, row, tb0, tend, L, smin, smax, dmax);
+}
+
+// ------------------------------------------------------------------ fast DSA, fp8 K
+
+// The same score over an FP8 E4M3 indexer cache with one binary32 scale per
+// row ("Overlap DSA heuristic prev_topk write-back on the aux stream", Test
+// Coverage: the block-scaled FP8 indexer cache).  Each code widens exactly to
+// bf16 (3 mantissa bits, exponents 2^-9 .. 2^8), so the matrix cores form
+// t~_h = sum_d q_hd code_d, and the head's dot product is sigma_t * t~_h.
+constexpr int kTileBytes8 = kTileTok * 128;      // a tile's fp8 K rows (D = 128)
+constexpr int kStageBytes8 = kTileBytes8 + 256;  // + its 32 row scales (one 256-byte DMA)
+
+// Eight E4M3 codes (two words) -> bf16, exact.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// A tile's fragment reads as one asm block (see ring_read8): two 16-byte
+// units (64 head dims each) of each 16-token half, the halves 2048 bytes
+// apart, and the scales of this lane's two tokens.
+template <int OFF>
+__device__ __forceinline__ void ring_read_fp8(u32x4 (&f)[4], float (&sc)[2], const uint32_t (&addr)[2],
+                                              uint32_t saddr) {
+  asm volatile(
+      "ds_read_b128 %0, %6 offset:%8\n\t"
+      "ds_read_b128 %1, %7 offset:%8\n\t"
+      "ds_read_b128 %2, %6 offset:%9\n\t"
+      "ds_read_b128 %3, %7 offset:%9\n\t"
+      "ds_read_b32 %4, %10 offset:%11\n\t"
+      "ds_read_b32 %5, %10 offset:%12\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3]), "=&v"(sc[0]), "=&v"(sc[1])
+      : "v"(addr[0]), "v"(addr[1]), "i"(OFF), "i"(OFF + 2048), "v"(saddr), "i"(OFF + kTileBytes8),
+        "i"(OFF + kTileBytes8 + 64)
+      : "memory");
+}
+
+// Tiles, waves and the MFMA layout as in score_dsa_kernel; what differs:
+//  * a tile is 32 x 128 bytes, four 1 KB DMA instructions of eight rows
+//    each, plus one 4-byte-per-lane DMA of the 32 row scales (lanes 32..63
+//    repeat lanes 0..31);
+//  * 16-byte units are swizzled as unit ^ ((row >> 1) & 7): two 128-byte rows
+//    share one 256-byte bank line, and 16 rows read at one unit then hit 16
+//    different bank groups;
+//  * the 8 k-values of lane group l/16 at k-step ks are head dims
+//    64 (ks/2) + 16 (l/16) + 8 (ks%2) .. +8, so one 16-byte read serves two
+//    k-steps.
+// Error bound: the exact score dequantizes (one rounding), rounds every
+// product and every sum, so each head's dot differs from sigma sum_d q_d c_d
+// by at most gamma_{D+1} sigma sum_d |q_d c_d|; the matrix-core value
+// fl(sigma t~) by at most (gamma_D (1 + u) + u) times the same.  Both are
+// below gamma_{D+2} (unit 2^-23) times sigma sum_d |q_d||c_d|, and with
+// B_t = |sigma| sum_d a_d |c_d| the score bound keeps the bf16 form.
+template <int MT, int NW, int S, int MAXIT>
+__global__ __launch_bounds__(NW * 64) void score_dsa_fp8_kernel(ScoreArgs a, int iters) {
+  constexpr int D = 128;
+  constexpr int KS = D / 32;
+  constexpr int G = 16 * MT;
+  __shared__ __attribute__((aligned(1024))) uint4 s_ring[NW * S * kStageBytes8 / 16];
+  __shared__ float s_out[NW * kTileTok * MAXIT];
+  __shared__ uint32_t s_red[NW][3];
+
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int b = blockIdx.y / a.num_kv_heads, g = blockIdx.y % a.num_kv_heads;
+  const int cap = min(a.max_kv_len, a.max_pages * a.page_size);
+  const int L = clamp_len(a.kv_lens[b], cap);
+  const int span = NW * kTileTok * iters;
+  const int tb0 = blockIdx.x * span;
+  float* row = a.scores + (int64_t)blockIdx.y * a.max_kv_len;
+  if (tb0 >= a.max_kv_len) return;
+  const int tend = min(tb0 + span, a.max_kv_len);
+  if (tb0 >= L) {
+    for (int t = tb0 + threadIdx.x; t < tend; t += NW * 64) row[t] = -__builtin_inff();
+    return;
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t bmin = s_red[0][0], bmax = s_red[0][1];
-    float bd = __uint_as_float(s_red[0][2]);
+  const int ps = a.page_size;
+  const int p0 = tb0 / ps;
+  const int n_it = min(iters, max(0, (L - tb0 - wid * kTileTok + NW * kTileTok - 1) / (NW * kTileTok)));
+
+  const int lp = p0 + lane;
+  const int pg_raw = a.block_table[(int64_t)b * a.max_pages + min(lp, a.max_pages - 1)];
+  const uint16_t* qb = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)b * a.q_heads + g * G) * D;
+  const float* wb = a.head_weights + (int64_t)b * a.q_heads + g * G;
+  bf16x8 qf[MT][KS];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) {
-      bmin = min(bmin, s_red[w][0]);
-      bmax = max(bmax, s_red[w][1]);
-      bd = fmaxf(bd, __uint_as_float(s_red[w][2]));
-    }
-    if (a.row_stats && bmin <= bmax) {
-      int32_t* stat = a.row_stats + (int64_t)blockIdx.y * kStatStride;
-      atomicMin(reinterpret_cast<unsigned int*>(stat), bmin);
-      atomicMax(reinterpret_cast<unsigned int*>(stat + 1), bmax);
-    }
-    // 1e-3 relative slack covers the rounding of the bound's own evaluation,
-    // the absolute term any flushed subnormal.
-    if (a.row_bound)
-      atomicMax(reinterpret_cast<unsigned int*>(a.row_bound + blockIdx.y), __float_as_uint(bd * 1.001f + 1e-30f));
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[mt][ks] = *reinterpret_cast<const bf16x8*>(qb + (16 * mt + col) * D + 64 * (ks >> 1) + 16 * grp +
+                                                    8 * (ks & 1));
+  float wv[MT][4], wa[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) wv[mt][r] = wb[16 * mt + 4 * grp + r];
+    wa[mt] = fabsf(wb[16 * mt + col]);
   }
-  // every token below L lies in a scored tile; the rest of the span is -inf
-  for (int t = tb0 + threadIdx.x; t < tend; t += NW * 64) row[t] = t < L ? s_out[t - tb0] : -__builtin_inff();
+  // ordinary loads complete before the first DMA (see score_dsa_kernel)
+  asm volatile("" : : "v"(pg_raw));
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" : : "v"(qf[mt][ks]));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) asm volatile("" : : "v"(wv[mt][r]));
+    asm volatile("" : : "v"(wa[mt]));
+  }
+  const int mypage = (lp < a.max_pages && lp * ps < L && pg_raw >= 0 && pg_raw < a.num_pages) ? pg_raw : -1;
+
+  // K DMA lane layout: chunk c of a 16-token half moves rows 8c + l/8, unit
+  // (l%8) ^ swz(row); the scale DMA gives lane l the scale of token l%16 of
+  // half (l/16)%2.
+  const int64_t ts = a.token_stride;  // fp8: elements are bytes
+  uint32_t vofs[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int r = 8 * c + (lane >> 3);
+    vofs[c] = (uint32_t)(r * ts + 16 * ((lane & 7) ^ ((r >> 1) & 7)));
+  }
+  const int shalf = (lane >> 4) & 1;
+  const char* kbase = reinterpret_cast<const char*>(a.k) + (int64_t)g * a.head_stride;
+  const uint32_t ring0 = (uint32_t)(uintptr_t)(lds_ptr)s_ring + (uint32_t)(wid * S * kStageBytes8);
+  auto tile_t0 = [&](int it) { return tb0 + (it * NW + wid) * kTileTok; };
+  auto half_page = [&](int t) { return __builtin_amdgcn_readlane(mypage, min(t / ps - p0, 63)); };
+  auto issue = [&](int it, int stage) {
+    const int t0 = tile_t0(it);
+    const uint32_t dst = ring0 + (uint32_t)(stage * kStageBytes8);
+    int pgh[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int t = t0 + 16 * h;
+      pgh[h] = max(half_page(t), 0);  // an absent page reads page 0 (masked)
+      const char* hb = kbase + (int64_t)pgh[h] * a.page_stride + (int64_t)(t % ps) * ts;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        __builtin_amdgcn_global_load_lds(hb + vofs[c], (lds_ptr)(uintptr_t)(dst + h * 2048 + c * 1024), 16, 0, 0);
+    }
+    const int spg = shalf ? pgh[1] : pgh[0];
+    const float* sp = a.k_scale + fp8_scale_index(spg, g, (t0 + 16 * shalf) % ps + col, a.num_kv_heads, ps);
+    __builtin_amdgcn_global_load_lds(sp, (lds_ptr)(uintptr_t)(dst + kTileBytes8), 4, 0, 0);
+  };
+  static_for<0, S - 1>([&](auto j) { issue(decltype(j)::value, decltype(j)::value); });
+
+  // a_d = sum_h |w_h| |q_hd|, rounded up to bf16, as the bound tile's row 0
+  bf16x8 af[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    float part[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) part[j] = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const u32x4 w4 = __builtin_bit_cast(u32x4, qf[mt][ks]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        part[2 * e] += wa[mt] * fabsf(bf16_lo(w4[e]));
+        part[2 * e + 1] += wa[mt] * fabsf(bf16_hi(w4[e]));
+      }
+    }
+    u32x4 p4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float lo = row16_sum(part[2 * e]), hi = row16_sum(part[2 * e + 1]);
+      p4[e] = col == 0 ? (bf16_round_up(lo) | (bf16_round_up(hi) << 16)) : 0u;
+    }
+    af[ks] = __builtin_bit_cast(bf16x8, p4);
+  }
+  const float u24 = 5.9604644775390625e-8f, u23 = 1.1920928955078125e-7f;
+  const float gD = gamma_n((float)(D + 2), u23), gH = gamma_n((float)(G + 1), u24);
+  const float bcoef = 2.0f * gH * (1.0f + gD) + 2.0f * gD;
+  float dmax = 0.0f;
+  float smin = __builtin_inff(), smax = -__builtin_inff();
+
+  uint32_t raddr[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) raddr[j] = ring0 + col * 128 + 16 * ((4 * j + grp) ^ ((col >> 1) & 7));
+  const uint32_t saddr = ring0 + 4 * col;
+  const uint32_t out0 = (uint32_t)(uintptr_t)(lds_ptr)s_out;
+
+  auto compute = [&](int it, auto sc) {
+    constexpr int s = decltype(sc)::value;
+    u32x4 kr[4];
+    float sig[2];
+    ring_read_fp8<s * kStageBytes8>(kr, sig, raddr, saddr);
+    const int t0 = tile_t0(it);
+    float sv[2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      bf16x8 kb[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 w = kr[2 * n + (ks >> 1)];
+        kb[ks] = fp8x8_to_bf16(w[2 * (ks & 1)], w[2 * (ks & 1) + 1]);
+      }
+      floatx4 acc[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        acc[mt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[mt][ks], kb[ks], acc[mt], 0, 0, 0);
+      }
+      floatx4 accb = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        accb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            af[ks], __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, kb[ks]) & 0x7FFF7FFFu), accb, 0, 0, 0);
+      float sum = 0.0f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sum = __builtin_fmaf(wv[mt][r], relu_bits(__fmul_rn(sig[n], acc[mt][r])), sum);
+      sum += __shfl_xor(sum, 16);
+      sum += __shfl_xor(sum, 32);
+      const int t = t0 + 16 * n + col;
+      const bool ok = t < L && half_page(t0 + 16 * n) >= 0;
+      if (ok) {
+        if (grp == 0) dmax = fmaxf(dmax, fabsf(sig[n]) * accb[0] * bcoef);
+        smin = fminf(smin, sum);
+        smax = fmaxf(smax, sum);
+      }
+      sv[n] = ok ? sum : -__builtin_inff();
+    }
+    if (lane < 32) lds_store_f32(out0 + 4 * (t0 - tb0 + lane), lane < 16 ? sv[0] : sv[1]);
+  };
+
+  constexpr int kPerTile = 5;  // DMA instructions per tile
+  for (int it0 = 0; it0 < n_it; it0 += S) {
+    static_for<0, S>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      const int it = it0 + s;
+      if (it < n_it) {
+        const int ahead = min(n_it - 1 - it, S - 1);
+        if (ahead == S - 1) {
+          issue(it + S - 1, (s + S - 1) % S);
+          wait_vmcnt<kPerTile * (S - 1)>();
+        } else {
+          static_for<0, S - 1>([&](auto j) {
+            if (ahead == decltype(j)::value) wait_vmcnt<kPerTile * decltype(j)::value>();
+          });
+        }
+        compute(it, sc);
+      }
+    });
+  }
+  wait_vmcnt<0>();
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  finish_span<NW>(a, s_red, s_out, row, tb0, tend, L, smin, smax, dmax);
 }
 
 // ------------------------------------------------------------------ launch
@@ -478,41 +786,58 @@ bool score_exact_supported(int G) {
 
 hipError_t launch_score_exact(const ScoreArgs& a, hipStream_t st) {
   if (a.batch == 0 || a.max_kv_len == 0) return hipSuccess;
-  return a.dtype == 0 ? launch_exact_t<float>(a, st) : launch_exact_t<uint16_t>(a, st);
+  if (a.dtype == 0) return launch_exact_t<float>(a, st);
+  if (a.dtype == 1) return launch_exact_t<uint16_t>(a, st);
+  return launch_exact_t<uint8_t>(a, st);
 }
 
 bool score_fast_supported(const ScoreArgs& a) {
   const int G = a.q_heads / a.num_kv_heads;
-  return a.dtype == 1 && a.mode == 2 && a.head_dim == 128 && (G == 16 || G == 32 || G == 64) &&
-         (a.page_size % 16) == 0 && (a.token_stride % 8) == 0 && (a.page_stride % 8) == 0 &&
-         (a.head_stride % 8) == 0;
+  const int es = a.dtype == 1 ? 2 : 1;  // bytes per K element (bf16, fp8)
+  return (a.dtype == 1 || (a.dtype == 2 && a.k_scale)) && a.mode == 2 && a.head_dim == 128 &&
+         (G == 16 || G == 32 || G == 64) && (a.page_size % 16) == 0 && (a.token_stride * es) % 16 == 0 &&
+         (a.page_stride * es) % 16 == 0 && (a.head_stride * es) % 16 == 0;
 }
 
 namespace {
-constexpr int kScoreNW = 4, kScoreStages = 4, kScoreMaxIt = 32, kScoreBlocksPerCU = 1;
+// waves per block, ring stages, tiles per wave at most, blocks per CU
+constexpr int kScoreNW = 4, kScoreStages = 4, kScoreMaxIt = 32, kScoreBlocksPerCU = 1;      // bf16 K
+constexpr int kScore8NW = 4, kScore8Stages = 6, kScore8MaxIt = 32, kScore8BlocksPerCU = 1;  // fp8 K
 
-template <int MT>
-hipError_t launch_dsa(const ScoreArgs& a, hipStream_t st) {
+// Tiles per wave: enough blocks to fill the chip once, and a span that
+// overlaps at most 64 logical pages (their ids ride in one register per
+// lane): span / page_size pages when the span is a whole number of pages,
+// else up to two more.
+int score_iters(const ScoreArgs& a, int nw, int maxit, int bpc) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
-  // tiles per wave: enough blocks to fill the chip once, and a span that
-  // overlaps at most 64 logical pages (their ids ride in one register per
-  // lane): span / page_size pages when the span is a whole number of pages,
-  // else up to two more.
   const int64_t rows = (int64_t)a.batch * a.num_kv_heads;
   const int64_t tiles = rows * ((a.max_kv_len + kTileTok - 1) / kTileTok);
-  const int64_t per_block = (tiles + (int64_t)cus * kScoreBlocksPerCU - 1) / ((int64_t)cus * kScoreBlocksPerCU);
-  int iters = (int)std::min<int64_t>((per_block + kScoreNW - 1) / kScoreNW, kScoreMaxIt);
+  const int64_t per_block = (tiles + (int64_t)cus * bpc - 1) / ((int64_t)cus * bpc);
+  int iters = (int)std::min<int64_t>((per_block + nw - 1) / nw, maxit);
   auto pages_spanned = [&](int it) {
-    const int span = kScoreNW * kTileTok * it;
+    const int span = nw * kTileTok * it;
     return span % a.page_size == 0 ? span / a.page_size : (span - 1) / a.page_size + 2;
   };
   while (iters > 1 && pages_spanned(iters) > 64) --iters;
-  iters = std::max(iters, 1);
-  const int span = kScoreNW * kTileTok * iters;
-  dim3 grid((a.max_kv_len + span - 1) / span, (unsigned)rows);
-  score_dsa_kernel<MT, kScoreNW, kScoreStages, kScoreMaxIt><<<grid, kScoreNW * 64, 0, st>>>(a, iters);
+  return std::max(iters, 1);
+}
+
+template <int MT>
+hipError_t launch_dsa(const ScoreArgs& a, hipStream_t st) {
+  const unsigned rows = (unsigned)(a.batch * a.num_kv_heads);
+  if (a.dtype == 2) {
+    const int iters = score_iters(a, kScore8NW, kScore8MaxIt, kScore8BlocksPerCU);
+    const int span = kScore8NW * kTileTok * iters;
+    dim3 grid((a.max_kv_len + span - 1) / span, rows);
+    score_dsa_fp8_kernel<MT, kScore8NW, kScore8Stages, kScore8MaxIt><<<grid, kScore8NW * 64, 0, st>>>(a, iters);
+  } else {
+    const int iters = score_iters(a, kScoreNW, kScoreMaxIt, kScoreBlocksPerCU);
+    const int span = kScoreNW * kTileTok * iters;
+    dim3 grid((a.max_kv_len + span - 1) / span, rows);
+    score_dsa_kernel<MT, kScoreNW, kScoreStages, kScoreMaxIt><<<grid, kScoreNW * 64, 0, st>>>(a, iters);
+  }
   return hipGetLastError();
 }
 }  // namespace

@@ -165,42 +165,81 @@ __device__ __forceinline__ void find_bin_n(const int* hist, int* tmp, int* win, 
   __syncthreads();
 }
 
+// acc + q * k over eight (bf16 q, binary32 k) pairs in order, each product
+// and each sum rounded once (k is a dequantized fp8 element).
+__device__ __forceinline__ float dot8_f32k(float acc, uint4 qv, const float* k) {
+  acc = __fadd_rn(acc, __fmul_rn(bf16_lo(qv.x), k[0]));
+  acc = __fadd_rn(acc, __fmul_rn(bf16_hi(qv.x), k[1]));
+  acc = __fadd_rn(acc, __fmul_rn(bf16_lo(qv.y), k[2]));
+  acc = __fadd_rn(acc, __fmul_rn(bf16_hi(qv.y), k[3]));
+  acc = __fadd_rn(acc, __fmul_rn(bf16_lo(qv.z), k[4]));
+  acc = __fadd_rn(acc, __fmul_rn(bf16_hi(qv.z), k[5]));
+  acc = __fadd_rn(acc, __fmul_rn(bf16_lo(qv.w), k[6]));
+  acc = __fadd_rn(acc, __fmul_rn(bf16_hi(qv.w), k[7]));
+  return acc;
+}
+// acc + q * k over eight bf16 pairs in order (the products are exact, so a
+// fused multiply-add per step rounds only the sum, as the exact order asks).
+__device__ __forceinline__ float dot8_bf16(float acc, uint4 qv, uint4 kv) {
+  acc = __builtin_fmaf(bf16_lo(qv.x), bf16_lo(kv.x), acc);
+  acc = __builtin_fmaf(bf16_hi(qv.x), bf16_hi(kv.x), acc);
+  acc = __builtin_fmaf(bf16_lo(qv.y), bf16_lo(kv.y), acc);
+  acc = __builtin_fmaf(bf16_hi(qv.y), bf16_hi(kv.y), acc);
+  acc = __builtin_fmaf(bf16_lo(qv.z), bf16_lo(kv.z), acc);
+  acc = __builtin_fmaf(bf16_hi(qv.z), bf16_hi(kv.z), acc);
+  acc = __builtin_fmaf(bf16_lo(qv.w), bf16_lo(kv.w), acc);
+  acc = __builtin_fmaf(bf16_hi(qv.w), bf16_hi(kv.w), acc);
+  return acc;
+}
+
 // Exact score of one token, evaluated by a whole wave in the library's exact
-// order (DSA mode, bf16, head_dim 128): lane h forms dot_h left to right,
-// then the terms w_h * relu(dot_h) are added in head order.
+// order (DSA mode, bf16 or fp8 K, head_dim 128): lane h forms dot_h left to
+// right, then the terms w_h * relu(dot_h) are added in head order.
 __device__ float exact_dsa_score(const ScoreArgs& sa, int b, int g, int t, float* lds_terms) {
   const int lane = threadIdx.x & 63;
   const int G = sa.q_heads / sa.num_kv_heads;
   const uint16_t* qb = reinterpret_cast<const uint16_t*>(sa.q) + ((int64_t)b * sa.q_heads + g * G) * 128;
   const float* wb = sa.head_weights + (int64_t)b * sa.q_heads + g * G;
   const int page = sa.block_table[(int64_t)b * sa.max_pages + t / sa.page_size];
-  const uint16_t* krow = reinterpret_cast<const uint16_t*>(sa.k) + (int64_t)page * sa.page_stride +
-                         (int64_t)g * sa.head_stride + (int64_t)(t % sa.page_size) * sa.token_stride;
+  const int slot = t % sa.page_size;
+  const int64_t koff = (int64_t)page * sa.page_stride + (int64_t)g * sa.head_stride + (int64_t)slot * sa.token_stride;
+  const bool fp8 = sa.dtype == 2;
   float total = 0.0f;
   for (int h0 = 0; h0 < G; h0 += kWave) {
     const int h = h0 + lane;
     float term = 0.0f;
     if (h < G) {
       const uint16_t* qh = qb + (int64_t)h * 128;
-      // all 32 loads in flight at once, then the ordered dot product
+      // all loads in flight at once, then the ordered dot product
       uint4 kr[16], qr[16];
+      float ksc = 1.0f;
+      if (fp8) {
+        const uint8_t* krow = reinterpret_cast<const uint8_t*>(sa.k) + koff;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        kr[i] = *reinterpret_cast<const uint4*>(krow + 8 * i);
-        qr[i] = *reinterpret_cast<const uint4*>(qh + 8 * i);
+        for (int i = 0; i < 8; ++i) kr[i] = *reinterpret_cast<const uint4*>(krow + 16 * i);
+        ksc = sa.k_scale[fp8_scale_index(page, g, slot, sa.num_kv_heads, sa.page_size)];
+      } else {
+        const uint16_t* krow = reinterpret_cast<const uint16_t*>(sa.k) + koff;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) kr[i] = *reinterpret_cast<const uint4*>(krow + 8 * i);
       }
-      float acc = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint4 kv = kr[i], qv = qr[i];
-        acc = __builtin_fmaf(bf16_lo(qv.x), bf16_lo(kv.x), acc);
-        acc = __builtin_fmaf(bf16_hi(qv.x), bf16_hi(kv.x), acc);
-        acc = __builtin_fmaf(bf16_lo(qv.y), bf16_lo(kv.y), acc);
-        acc = __builtin_fmaf(bf16_hi(qv.y), bf16_hi(kv.y), acc);
-        acc = __builtin_fmaf(bf16_lo(qv.z), bf16_lo(kv.z), acc);
-        acc = __builtin_fmaf(bf16_hi(qv.z), bf16_hi(kv.z), acc);
-        acc = __builtin_fmaf(bf16_lo(qv.w), bf16_lo(kv.w), acc);
-        acc = __builtin_fmaf(bf16_hi(qv.w), bf16_hi(kv.w), acc);
+      for (int i = 0; i < 16; ++i) qr[i] = *reinterpret_cast<const uint4*>(qh + 8 * i);
+      float acc = 0.0f;
+      if (fp8) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float kd[16];
+          fp8x4_dequant(kr[i].x, ksc, kd);
+          fp8x4_dequant(kr[i].y, ksc, kd + 4);
+          fp8x4_dequant(kr[i].z, ksc, kd + 8);
+          fp8x4_dequant(kr[i].w, ksc, kd + 12);
+          acc = dot8_f32k(acc, qr[2 * i], kd);
+          acc = dot8_f32k(acc, qr[2 * i + 1], kd + 8);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc = dot8_bf16(acc, qr[i], kr[i]);
       }
       const float r = acc > 0.0f ? acc : 0.0f;
       term = __fmul_rn(wb[h], r);
@@ -703,7 +742,9 @@ __global__ __launch_bounds__(kChunkThreads) void select_classify_kernel(SelectAr
   __shared__ uint32_t s_bkey[kSelChunk];  // and their exact keys
   __shared__ int s_nband, s_base;
   __shared__ __attribute__((aligned(16))) float s_terms[kSelWaves][kWave];
-  __shared__ uint4 s_krow[kStageRows][16];  // K rows of band tokens being re-scored
+  // K rows of band tokens being re-scored: bf16 rows as they are (256 bytes),
+  // fp8 rows dequantized to binary32 (512 bytes)
+  __shared__ __attribute__((aligned(16))) float s_krow[kStageRows][128];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int row = blockIdx.y, c = blockIdx.x;
   const RowView v = row_view(a, row);
@@ -762,6 +803,7 @@ __global__ __launch_bounds__(kChunkThreads) void select_classify_kernel(SelectAr
       for (int i = 0; i < 16; ++i) qr[i] = *reinterpret_cast<const uint4*>(qh + 8 * i);
       wh = sa.head_weights[(int64_t)b * sa.q_heads + g * G + lane];
     }
+    const bool fp8 = sa.dtype == 2;
     for (int p0 = 0; p0 < nb; p0 += kStageRows) {
       const int np = min(kStageRows, nb - p0);
       {
@@ -769,9 +811,21 @@ __global__ __launch_bounds__(kChunkThreads) void select_classify_kernel(SelectAr
         if (i < np) {
           const int t = s_band[p0 + i];
           const int page = sa.block_table[(int64_t)b * sa.max_pages + t / sa.page_size];
-          const uint16_t* krow = reinterpret_cast<const uint16_t*>(sa.k) + (int64_t)page * sa.page_stride +
-                                 (int64_t)g * sa.head_stride + (int64_t)(t % sa.page_size) * sa.token_stride;
-          s_krow[i][part] = *reinterpret_cast<const uint4*>(krow + 8 * part);
+          const int slot = t % sa.page_size;
+          const int64_t koff = (int64_t)page * sa.page_stride + (int64_t)g * sa.head_stride +
+                               (int64_t)slot * sa.token_stride;
+          if (fp8) {  // 8 codes per thread, dequantized once here
+            const uint2 c = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(sa.k) + koff + 8 * part);
+            const float ksc = sa.k_scale[fp8_scale_index(page, g, slot, sa.num_kv_heads, sa.page_size)];
+            float kd[8];
+            fp8x4_dequant(c.x, ksc, kd);
+            fp8x4_dequant(c.y, ksc, kd + 4);
+            *reinterpret_cast<float4*>(&s_krow[i][8 * part]) = make_float4(kd[0], kd[1], kd[2], kd[3]);
+            *reinterpret_cast<float4*>(&s_krow[i][8 * part + 4]) = make_float4(kd[4], kd[5], kd[6], kd[7]);
+          } else {
+            reinterpret_cast<uint4*>(s_krow[i])[part] =
+                *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(sa.k) + koff + 8 * part);
+          }
         }
       }
       __syncthreads();
@@ -779,17 +833,19 @@ __global__ __launch_bounds__(kChunkThreads) void select_classify_kernel(SelectAr
         float term = 0.0f;
         if (hact) {
           float acc = 0.0f;
+          if (fp8) {
 #pragma unroll
-          for (int c8 = 0; c8 < 16; ++c8) {
-            const uint4 kv = s_krow[i][c8], qv = qr[c8];
-            acc = __builtin_fmaf(bf16_lo(qv.x), bf16_lo(kv.x), acc);
-            acc = __builtin_fmaf(bf16_hi(qv.x), bf16_hi(kv.x), acc);
-            acc = __builtin_fmaf(bf16_lo(qv.y), bf16_lo(kv.y), acc);
-            acc = __builtin_fmaf(bf16_hi(qv.y), bf16_hi(kv.y), acc);
-            acc = __builtin_fmaf(bf16_lo(qv.z), bf16_lo(kv.z), acc);
-            acc = __builtin_fmaf(bf16_hi(qv.z), bf16_hi(kv.z), acc);
-            acc = __builtin_fmaf(bf16_lo(qv.w), bf16_lo(kv.w), acc);
-            acc = __builtin_fmaf(bf16_hi(qv.w), bf16_hi(kv.w), acc);
+            for (int c8 = 0; c8 < 16; ++c8) {
+              float kd[8];
+              const float4 lo = *reinterpret_cast<const float4*>(&s_krow[i][8 * c8]);
+              const float4 hi = *reinterpret_cast<const float4*>(&s_krow[i][8 * c8 + 4]);
+              kd[0] = lo.x; kd[1] = lo.y; kd[2] = lo.z; kd[3] = lo.w;
+              kd[4] = hi.x; kd[5] = hi.y; kd[6] = hi.z; kd[7] = hi.w;
+              acc = dot8_f32k(acc, qr[c8], kd);
+            }
+          } else {
+#pragma unroll
+            for (int c8 = 0; c8 < 16; ++c8) acc = dot8_bf16(acc, qr[c8], reinterpret_cast<const uint4*>(s_krow[i])[c8]);
           }
           term = __fmul_rn(wh, acc > 0.0f ? acc : 0.0f);
         }

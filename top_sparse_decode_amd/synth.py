@@ -71,35 +71,46 @@ FP8_MAX = 448.0
 def to_fp8_e4m3(x: np.ndarray) -> np.ndarray:
     """float32 -> OCP FP8 E4M3 codes (sign, 4 exponent bits with bias 7, 3
     mantissa bits; subnormals m * 2^-9), round to nearest even, magnitudes
-    above 448 saturated to 448.  Finite inputs."""
-    x = np.asarray(x, dtype=np.float32)
-    sign = (np.signbit(x)).astype(np.uint8) << np.uint8(7)
-    a = np.abs(x).astype(np.float64)
-    frac, ex = np.frexp(a)                 # a = frac * 2^ex, frac in [0.5, 1)
-    e = ex.astype(np.int64) - 1            # a = (2 frac) * 2^e
-    normal = (e >= -6) & (a > 0)
-    # normals: 8 + mantissa = rne(a / 2^(e-3)) in [8, 16]; subnormals: rne(a / 2^-9)
-    m_norm = np.rint(np.where(normal, np.ldexp(a, -(e - 3)), 0.0)).astype(np.int64)
-    m_sub = np.rint(np.where(normal, 0.0, np.ldexp(a, 9))).astype(np.int64)
-    up = m_norm == 16                      # rounding carried into the next binade
-    e = np.where(up, e + 1, e)
-    m_norm = np.where(up, 8, m_norm)
-    be = np.where(normal, e + 7, np.where(m_sub == 8, 1, 0))
-    mant = np.where(normal, m_norm - 8, np.where(m_sub == 8, 0, m_sub))
-    over = (be > 15) | ((be == 15) & (mant > 6))
-    be = np.where(over, 15, be)
-    mant = np.where(over, 6, mant)
-    return sign | (be.astype(np.uint8) << np.uint8(3)) | mant.astype(np.uint8)
+    above 448 saturated to 448.  Finite inputs.  Normals round the binary32
+    mantissa to 3 bits on the bit pattern (a carry moves into the exponent);
+    below 2^-6 the code is rne(|x| * 2^9) itself (8 is the smallest normal)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, np.uint8)
+    xf, of = x.reshape(-1), out.reshape(-1)
+    step = 1 << 22
+    for s in range(0, xf.size, step):
+        u = xf[s:s + step].view(np.uint32)
+        a = u & np.uint32(0x7FFFFFFF)
+        r = (a + np.uint32(0x7FFFF) + ((a >> np.uint32(20)) & np.uint32(1))) >> np.uint32(20)
+        code_n = r.astype(np.int32) - (120 << 3)          # binary32 bias 127 -> E4M3 bias 7
+        code_s = np.rint(a.view(np.float32) * np.float32(512.0)).astype(np.int32)
+        code = np.minimum(np.where(a >= np.uint32(0x3C800000), code_n, code_s), 0x7E)  # 2^-6
+        of[s:s + step] = ((u >> np.uint32(24)) & np.uint32(0x80)).astype(np.uint8) | code.astype(np.uint8)
+    return out
 
 
 def quantize_rows_fp8(rows_f32: np.ndarray):
     """Per-row block scaling: scale = max|row| / 448 (1 for an all-zero row),
     codes = E4M3(row / scale).  rows [..., D] -> (codes uint8 [..., D],
-    scales float32 [...])."""
-    amax = np.max(np.abs(rows_f32), axis=-1)
-    scale = np.where(amax > 0, amax / np.float32(FP8_MAX), np.float32(1.0)).astype(np.float32)
-    codes = to_fp8_e4m3(rows_f32 / scale[..., None])
-    return codes, scale
+    scales float32 [...]).  Rows holding a NaN get code 0x7F and scale NaN."""
+    rows = np.asarray(rows_f32, dtype=np.float32)
+    D = rows.shape[-1]
+    flat = rows.reshape(-1, D)
+    codes = np.empty(flat.shape, np.uint8)
+    scale = np.empty(flat.shape[0], np.float32)
+    step = max(1, (1 << 22) // D)
+    for s in range(0, flat.shape[0], step):
+        r = flat[s:s + step]
+        nan = np.isnan(r).any(axis=-1)
+        r = np.where(nan[:, None], np.float32(0.0), r)
+        amax = np.max(np.abs(r), axis=-1)
+        sc = np.where(amax > 0, amax / np.float32(FP8_MAX), np.float32(1.0)).astype(np.float32)
+        c = to_fp8_e4m3(r / sc[:, None])
+        c[nan] = FP8_NAN
+        sc[nan] = np.float32(np.nan)
+        codes[s:s + step] = c
+        scale[s:s + step] = sc
+    return codes.reshape(rows.shape), scale.reshape(rows.shape[:-1])
 
 
 @dataclass
@@ -378,11 +389,7 @@ def _build_dsa(seed, p, kv_lens, name, max_len=None, num_pages=None):
     if p.get("index_dtype", "bf16") == "fp8":
         # the same keys, block-scaled to FP8 E4M3 with one scale per token row
         # (canary rows stay NaN: code 0x7F, scale NaN)
-        codes, ki_scale = quantize_rows_fp8(np.nan_to_num(bf16_bits_to_f32(ki), nan=0.0))
-        nanrow = np.isnan(bf16_bits_to_f32(ki)).any(axis=-1)
-        codes[nanrow] = FP8_NAN
-        ki_scale[nanrow] = np.float32(np.nan)
-        ki = codes
+        ki, ki_scale = quantize_rows_fp8(bf16_bits_to_f32(ki))
     elif p.get("index_dtype", "bf16") != "bf16":
         raise ValueError(f"index_dtype must be bf16 or fp8, got {p['index_dtype']}")
     return Workload(name, seed, P, bt, kv_lens, max_len, ki, qi, w, "relu_weighted", 1.0,
