@@ -176,7 +176,7 @@ def main():
         "step_gbps": round(alg_bytes / (ms_step * 1e-3) / 1e9, 1),
         "step_frac_of_hbm_peak": round(alg_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         "roofline": {
-            "kernel": "score_dsa_fp8_kernel<4, 4, 6, 32>" if fp8 else "score_dsa_kernel<4, 4, 4, 32>",
+            "kernel": "score_dsa_fp8_kernel<4, 8, 3, 16>" if fp8 else "score_dsa_kernel<4, 4, 4, 32>",
             "bound": "hbm",
             "achieved": round(score_gbps, 1),
             "peak": PEAK_HBM_GBPS,

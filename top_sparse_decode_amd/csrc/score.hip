@@ -555,13 +555,19 @@ __device__ __forceinline__ void ring_read_fp8(u32x4 (&f)[4], float (&sc)[2], con
 //    different bank groups;
 //  * the 8 k-values of lane group l/16 at k-step ks are head dims
 //    64 (ks/2) + 16 (l/16) + 8 (ks%2) .. +8, so one 16-byte read serves two
-//    k-steps.
+//    k-steps;
+//  * the scale is applied once per token: for sigma >= 0,
+//    sum_h w_h relu(sigma t~_h) = sigma sum_h w_h relu(t~_h) (a tile with a
+//    negative scale takes the per-head form).
 // Error bound: the exact score dequantizes (one rounding), rounds every
 // product and every sum, so each head's dot differs from sigma sum_d q_d c_d
-// by at most gamma_{D+1} sigma sum_d |q_d c_d|; the matrix-core value
-// fl(sigma t~) by at most (gamma_D (1 + u) + u) times the same.  Both are
-// below gamma_{D+2} (unit 2^-23) times sigma sum_d |q_d||c_d|, and with
-// B_t = |sigma| sum_d a_d |c_d| the score bound keeps the bf16 form.
+// by at most gamma_{D+1} |sigma| sum_d |q_d c_d|; the matrix-core value
+// sigma t~ by at most gamma_D times the same (its final scaling counts with
+// the head sum's roundings).  Both are below gamma_{D+2} (unit 2^-23).  No
+// finite E4M3 code exceeds 448 in magnitude, so
+// B_t = |sigma_t| sum_h |w_h| sum_d |q_hd| |c_td| <= 448 |sigma_t| sum_d a_d,
+// and the row bound is max_t |sigma_t| times a per-row constant: no bound
+// tile on the matrix cores.
 template <int MT, int NW, int S, int MAXIT>
 __global__ __launch_bounds__(NW * 64) void score_dsa_fp8_kernel(ScoreArgs a, int iters) {
   constexpr int D = 128;
@@ -654,34 +660,26 @@ __global__ __launch_bounds__(NW * 64) void score_dsa_fp8_kernel(ScoreArgs a, int
   };
   static_for<0, S - 1>([&](auto j) { issue(decltype(j)::value, decltype(j)::value); });
 
-  // a_d = sum_h |w_h| |q_hd|, rounded up to bf16, as the bound tile's row 0
-  bf16x8 af[KS];
+  // sum_d a_d = sum_h |w_h| sum_d |q_hd|: this lane's 4 MT heads x 32 dims,
+  // then the whole wave (all 64 heads x 128 dims), times 448 and the
+  // rounding coefficient; 1e-3 covers the rounding of these 8192 sums
+  float asum = 0.0f;
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    float part[8];
+  for (int mt = 0; mt < MT; ++mt) {
+    float part = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) part[j] = 0.0f;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
+    for (int ks = 0; ks < KS; ++ks) {
       const u32x4 w4 = __builtin_bit_cast(u32x4, qf[mt][ks]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        part[2 * e] += wa[mt] * fabsf(bf16_lo(w4[e]));
-        part[2 * e + 1] += wa[mt] * fabsf(bf16_hi(w4[e]));
-      }
+      for (int e = 0; e < 4; ++e) part += fabsf(bf16_lo(w4[e])) + fabsf(bf16_hi(w4[e]));
     }
-    u32x4 p4;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float lo = row16_sum(part[2 * e]), hi = row16_sum(part[2 * e + 1]);
-      p4[e] = col == 0 ? (bf16_round_up(lo) | (bf16_round_up(hi) << 16)) : 0u;
-    }
-    af[ks] = __builtin_bit_cast(bf16x8, p4);
+    asum += wa[mt] * part;
   }
+  asum = wave_sum(asum);
   const float u24 = 5.9604644775390625e-8f, u23 = 1.1920928955078125e-7f;
   const float gD = gamma_n((float)(D + 2), u23), gH = gamma_n((float)(G + 1), u24);
-  const float bcoef = 2.0f * gH * (1.0f + gD) + 2.0f * gD;
-  float dmax = 0.0f;
+  const float acoef = 448.0f * asum * (2.0f * gH * (1.0f + gD) + 2.0f * gD) * 1.001f;
+  float smax_sig = 0.0f;  // max |sigma| over this lane's scored tokens
   float smin = __builtin_inff(), smax = -__builtin_inff();
 
   uint32_t raddr[2];
@@ -696,6 +694,8 @@ __global__ __launch_bounds__(NW * 64) void score_dsa_fp8_kernel(ScoreArgs a, int
     float sig[2];
     ring_read_fp8<s * kStageBytes8>(kr, sig, raddr, saddr);
     const int t0 = tile_t0(it);
+    // one uniform test per tile: any negative scale (sign bit) among its tokens
+    const bool neg = __builtin_amdgcn_ballot_w64((__float_as_uint(sig[0]) | __float_as_uint(sig[1])) >> 31) != 0;
     float sv[2];
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
@@ -713,22 +713,27 @@ __global__ __launch_bounds__(NW * 64) void score_dsa_fp8_kernel(ScoreArgs a, int
         for (int ks = 0; ks < KS; ++ks)
           acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[mt][ks], kb[ks], acc[mt], 0, 0, 0);
       }
-      floatx4 accb = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        accb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            af[ks], __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, kb[ks]) & 0x7FFF7FFFu), accb, 0, 0, 0);
       float sum = 0.0f;
+      if (!neg) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sum = __builtin_fmaf(wv[mt][r], relu_bits(__fmul_rn(sig[n], acc[mt][r])), sum);
-      sum += __shfl_xor(sum, 16);
-      sum += __shfl_xor(sum, 32);
+          for (int r = 0; r < 4; ++r) sum = __builtin_fmaf(wv[mt][r], relu_bits(acc[mt][r]), sum);
+        sum += __shfl_xor(sum, 16);
+        sum += __shfl_xor(sum, 32);
+        sum = __fmul_rn(sig[n], sum);
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sum = __builtin_fmaf(wv[mt][r], relu_bits(__fmul_rn(sig[n], acc[mt][r])), sum);
+        sum += __shfl_xor(sum, 16);
+        sum += __shfl_xor(sum, 32);
+      }
       const int t = t0 + 16 * n + col;
       const bool ok = t < L && half_page(t0 + 16 * n) >= 0;
       if (ok) {
-        if (grp == 0) dmax = fmaxf(dmax, fabsf(sig[n]) * accb[0] * bcoef);
+        smax_sig = fmaxf(smax_sig, fabsf(sig[n]));
         smin = fminf(smin, sum);
         smax = fmaxf(smax, sum);
       }
@@ -758,7 +763,7 @@ __global__ __launch_bounds__(NW * 64) void score_dsa_fp8_kernel(ScoreArgs a, int
   }
   wait_vmcnt<0>();
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  finish_span<NW>(a, s_red, s_out, row, tb0, tend, L, smin, smax, dmax);
+  finish_span<NW>(a, s_red, s_out, row, tb0, tend, L, smin, smax, smax_sig * acoef);
 }
 
 // ------------------------------------------------------------------ launch
@@ -802,7 +807,7 @@ bool score_fast_supported(const ScoreArgs& a) {
 namespace {
 // waves per block, ring stages, tiles per wave at most, blocks per CU
 constexpr int kScoreNW = 4, kScoreStages = 4, kScoreMaxIt = 32, kScoreBlocksPerCU = 1;      // bf16 K
-constexpr int kScore8NW = 4, kScore8Stages = 6, kScore8MaxIt = 32, kScore8BlocksPerCU = 1;  // fp8 K
+constexpr int kScore8NW = 8, kScore8Stages = 3, kScore8MaxIt = 16, kScore8BlocksPerCU = 1;  // fp8 K
 
 // Tiles per wave: enough blocks to fill the chip once, and a span that
 // overlaps at most 64 logical pages (their ids ride in one register per
