@@ -191,9 +191,11 @@ __global__ __launch_bounds__(256) void attn_vec_kernel(AttnArgs a) {
 // (global_load_lds) in four 32-row chunks and stay resident (147 KB):
 //   S^T[token][head] = K_chunk (A operand, 32 tokens x 16 dims per step) *
 //     Q^T (B operand, the wave's 32 heads over all 36 steps of the 576 dims,
-//     held in registers), chunk by chunk as each chunk lands; the block max
-//     is then exact, P = 2^(x - max) is formed once (bf16, in registers) and
-//     never rescaled;
+//     held in registers), chunk by chunk as each chunk lands, the chunk
+//     after next issued as soon as a chunk's S is done; P = 2^(x - m) is
+//     formed per chunk (bf16, in registers) against a running reference m,
+//     the running max rounded up to an integer, and earlier chunks' P are
+//     rescaled by the exact power of two 2^(m_old - m_new) when m rises;
 //   O[:, 0:256] += P * V[:, 0:256], then O[:, 256:512] += P * V[:, 256:512],
 //     the V operand fetched with the transposing LDS read (ds_read_b64_tr_b16)
 //     that hands each lane one value column of four rows.

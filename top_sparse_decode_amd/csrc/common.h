@@ -16,6 +16,7 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float float2v __attribute__((ext_vector_type(2)));
+typedef int intx8 __attribute__((ext_vector_type(8)));
 
 // bfloat16 is the upper half of a binary32: widening is exact.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -34,6 +35,16 @@ __device__ __forceinline__ void fp8x4_dequant(uint32_t w, float scale, float* v)
   v[1] = __fmul_rn(fp8_to_f32<1>(w), scale);
   v[2] = __fmul_rn(fp8_to_f32<2>(w), scale);
   v[3] = __fmul_rn(fp8_to_f32<3>(w), scale);
+}
+
+// Smallest E4M3 code whose value is >= x, for finite 0 <= x <= 448.
+__device__ __forceinline__ uint32_t fp8_round_up(float x) {
+  if (!(x > 0.0f)) return 0u;
+  if (x < 0.015625f) return (uint32_t)__builtin_ceilf(x * 512.0f);  // subnormals m * 2^-9 (8 = 2^-6)
+  const uint32_t u = __float_as_uint(x);
+  uint32_t r = (u >> 20) - (120u << 3);  // biased exponent and top 3 mantissa bits
+  if (u & 0xFFFFFu) ++r;                 // round up (a carry moves into the exponent)
+  return r < 0x7Eu ? r : 0x7Eu;
 }
 
 // Offset of the row scale of (page, KV head g, slot) in an fp8 pool's scale array.

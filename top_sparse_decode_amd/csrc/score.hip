@@ -563,11 +563,11 @@ __device__ __forceinline__ void ring_read_fp8(u32x4 (&f)[4], float (&sc)[2], con
 // product and every sum, so each head's dot differs from sigma sum_d q_d c_d
 // by at most gamma_{D+1} |sigma| sum_d |q_d c_d|; the matrix-core value
 // sigma t~ by at most gamma_D times the same (its final scaling counts with
-// the head sum's roundings).  Both are below gamma_{D+2} (unit 2^-23).  No
-// finite E4M3 code exceeds 448 in magnitude, so
-// B_t = |sigma_t| sum_h |w_h| sum_d |q_hd| |c_td| <= 448 |sigma_t| sum_d a_d,
-// and the row bound is max_t |sigma_t| times a per-row constant: no bound
-// tile on the matrix cores.
+// the head sum's roundings).  Both are below gamma_{D+2} (unit 2^-23), so the
+// bf16 form holds with B_t = |sigma_t| sum_d a_d |c_td|.  B_t comes from one
+// fp8 MFMA per 16 tokens: a_d scaled by a power of two and rounded up to
+// E4M3 against the codes' magnitudes (products of two E4M3 values are exact
+// in binary32).
 template <int MT, int NW, int S, int MAXIT>
 __global__ __launch_bounds__(NW * 64) void score_dsa_fp8_kernel(ScoreArgs a, int iters) {
   constexpr int D = 128;
@@ -660,26 +660,52 @@ __global__ __launch_bounds__(NW * 64) void score_dsa_fp8_kernel(ScoreArgs a, int
   };
   static_for<0, S - 1>([&](auto j) { issue(decltype(j)::value, decltype(j)::value); });
 
-  // sum_d a_d = sum_h |w_h| sum_d |q_hd|: this lane's 4 MT heads x 32 dims,
-  // then the whole wave (all 64 heads x 128 dims), times 448 and the
-  // rounding coefficient; 1e-3 covers the rounding of these 8192 sums
-  float asum = 0.0f;
+  // a_d = sum_h |w_h| |q_hd| for the bound, on this lane's 32 dims (those of
+  // its B fragment: k-steps 0..3 = dims 16 grp + [0, 16), 64 + 16 grp +
+  // [0, 16)), summed over its MT heads and then the 16 lanes of its column
+  // group.  Row 0 of the bound tile (lanes with col 0) holds a_d * 2^-e
+  // rounded up to E4M3, with 2^e a power of two that keeps max_d a_d * 2^-e
+  // in [128, 256); the other rows are zero.
+  float ad[KS][8];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    float part = 0.0f;
+  for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int j = 0; j < 8; ++j) ad[ks][j] = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
       const u32x4 w4 = __builtin_bit_cast(u32x4, qf[mt][ks]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) part += fabsf(bf16_lo(w4[e])) + fabsf(bf16_hi(w4[e]));
+      for (int e = 0; e < 4; ++e) {
+        ad[ks][2 * e] += wa[mt] * fabsf(bf16_lo(w4[e]));
+        ad[ks][2 * e + 1] += wa[mt] * fabsf(bf16_hi(w4[e]));
+      }
     }
-    asum += wa[mt] * part;
   }
-  asum = wave_sum(asum);
+  float amax = 0.0f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      ad[ks][j] = row16_sum(ad[ks][j]);
+      amax = fmaxf(amax, ad[ks][j]);
+    }
+  amax = wave_max(amax);
+  // 2^-e with max_d a_d * 2^-e in [128, 256) (e = 0 for an all-zero tile)
+  const int ebits = (int)((__float_as_uint(amax) >> 23) & 0xFF);
+  const int e2 = amax > 0.0f ? ebits - 127 - 7 : 0;
+  const float down = __uint_as_float((uint32_t)(127 - e2) << 23), up = __uint_as_float((uint32_t)(127 + e2) << 23);
+  intx8 af8;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) word |= fp8_round_up(ad[2 * (w >> 2) + ((w >> 1) & 1)][4 * (w & 1) + j] * down) << (8 * j);
+    af8[w] = col == 0 ? (int)word : 0;
+  }
   const float u24 = 5.9604644775390625e-8f, u23 = 1.1920928955078125e-7f;
   const float gD = gamma_n((float)(D + 2), u23), gH = gamma_n((float)(G + 1), u24);
-  const float acoef = 448.0f * asum * (2.0f * gH * (1.0f + gD) + 2.0f * gD) * 1.001f;
-  float smax_sig = 0.0f;  // max |sigma| over this lane's scored tokens
+  const float bcoef = (2.0f * gH * (1.0f + gD) + 2.0f * gD) * up;
+  float dmax = 0.0f;
   float smin = __builtin_inff(), smax = -__builtin_inff();
 
   uint32_t raddr[2];
@@ -713,6 +739,14 @@ __global__ __launch_bounds__(NW * 64) void score_dsa_fp8_kernel(ScoreArgs a, int
         for (int ks = 0; ks < KS; ++ks)
           acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[mt][ks], kb[ks], acc[mt], 0, 0, 0);
       }
+      // the bound tile: sum_d (a_d 2^-e)^ |c_d| on the fp8 matrix cores, |c| by
+      // clearing the code sign bits (E4M3 A and B, unit block scales)
+      const u32x4 c0 = kr[2 * n], c1 = kr[2 * n + 1];
+      const intx8 cabs = intx8{(int)(c0[0] & 0x7F7F7F7Fu), (int)(c0[1] & 0x7F7F7F7Fu), (int)(c0[2] & 0x7F7F7F7Fu),
+                               (int)(c0[3] & 0x7F7F7F7Fu), (int)(c1[0] & 0x7F7F7F7Fu), (int)(c1[1] & 0x7F7F7F7Fu),
+                               (int)(c1[2] & 0x7F7F7F7Fu), (int)(c1[3] & 0x7F7F7F7Fu)};
+      const floatx4 accb = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          af8, cabs, floatx4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 127, 0, 127);
       float sum = 0.0f;
       if (!neg) {
 #pragma unroll
@@ -732,11 +766,11 @@ __global__ __launch_bounds__(NW * 64) void score_dsa_fp8_kernel(ScoreArgs a, int
       }
       const int t = t0 + 16 * n + col;
       const bool ok = t < L && half_page(t0 + 16 * n) >= 0;
-      if (ok) {
-        smax_sig = fmaxf(smax_sig, fabsf(sig[n]));
-        smin = fminf(smin, sum);
-        smax = fmaxf(smax, sum);
-      }
+      // selects, not a branch: the bound MFMA stays in straight-line code
+      const float bt = fabsf(sig[n]) * accb[0];
+      dmax = (ok && grp == 0) ? fmaxf(dmax, bt) : dmax;
+      smin = ok ? fminf(smin, sum) : smin;
+      smax = ok ? fmaxf(smax, sum) : smax;
       sv[n] = ok ? sum : -__builtin_inff();
     }
     if (lane < 32) lds_store_f32(out0 + 4 * (t0 - tb0 + lane), lane < 16 ? sv[0] : sv[1]);
@@ -763,7 +797,7 @@ __global__ __launch_bounds__(NW * 64) void score_dsa_fp8_kernel(ScoreArgs a, int
   }
   wait_vmcnt<0>();
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  finish_span<NW>(a, s_red, s_out, row, tb0, tend, L, smin, smax, smax_sig * acoef);
+  finish_span<NW>(a, s_red, s_out, row, tb0, tend, L, smin, smax, dmax * bcoef);
 }
 
 // ------------------------------------------------------------------ launch
