@@ -46,6 +46,9 @@ def parse():
     p.add_argument("--cpu-repeats", type=int, default=2, help="passes of the oracle over the sample")
     p.add_argument("--index-dtype", choices=["bf16", "fp8"], default="bf16",
                    help="indexer K cache: bf16, or FP8 E4M3 codes with one float32 scale per row")
+    p.add_argument("--hint", action="store_true",
+                   help="feed each step the previous step's selection as its top-k hint (written back "
+                        "by the selection itself)")
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="also run a plain device copy of this many bytes (3 launches) before the "
                         "steps: the reference kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -87,7 +90,7 @@ def main():
     t0 = time.time()
     w = synth.make_workload(4, index_dtype=args.index_dtype)
     say(f"[bench] generated in {time.time() - t0:.1f}s; uploading {args.replicas} replicas")
-    steps = [api.prepare(w, precision=api.FAST, device=dev) for _ in range(max(1, args.replicas))]
+    steps = [api.prepare(w, precision=api.FAST, device=dev, hint=args.hint) for _ in range(max(1, args.replicas))]
     torch.cuda.synchronize()
 
     B, L, P = w.batch, int(w.kv_lens[0]), w.page_size
@@ -171,6 +174,7 @@ def main():
             "batch": B, "kv_len": L, "page_size": P, "topk": w.topk,
             "precision": "fast scores + exact band re-score (indices exact)",
             "input_replicas": args.replicas,
+            "topk_hint": "previous step's selection, written back in place" if args.hint else None,
         },
         "algorithmic_bytes_per_step": alg_bytes,
         "step_gbps": round(alg_bytes / (ms_step * 1e-3) / 1e9, 1),

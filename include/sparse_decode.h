@@ -175,6 +175,30 @@ sd_status sd_topk_select(const float* scores, int32_t batch, int32_t groups, int
                          const int32_t* kv_lens, int32_t k, int32_t* indices, int32_t* counts,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Top-k with a previous step's selection as a hint, and its write-back ("Overlap
+ * DSA heuristic prev_topk write-back on the aux stream", Description: each
+ * decode step's top-k is written back as the next step's hint).  The result
+ * is exactly sd_topk_select's for any hint contents: the hint only narrows
+ * the search.  A hint entry counts when it is a position in [0, kv_len)
+ * larger than every counted entry before it (an ascending hint, as the
+ * write-back produces, counts in full); when at least k entries of a row
+ * count, the smallest of their scores is a floor under the k-th largest and
+ * no token below it is examined further.  A row whose hint certifies
+ * nothing is selected without a floor.
+ *   hint       device [batch][groups][hint_stride] int32 request-local
+ *              positions (may be NULL: no hint); the first hint_len of each
+ *              row are read (hint_stride >= hint_len >= 0)
+ *   writeback  device [batch][groups][writeback_stride] int32 or NULL: gets
+ *              the same k entries as indices (writeback_stride >= k), from
+ *              the same kernel stores.  It may be the hint buffer itself:
+ *              the hint is read completely before any write-back store.
+ * Other arguments, workspace and errors as sd_topk_select. */
+sd_status sd_topk_select_hinted(const float* scores, int32_t batch, int32_t groups, int32_t row_stride,
+                                const int32_t* kv_lens, int32_t k, const int32_t* hint, int32_t hint_len,
+                                int64_t hint_stride, int32_t* indices, int32_t* counts,
+                                int32_t* writeback, int64_t writeback_stride, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------ step 3 */
 
 /* Softmax attention of every query head over its KV head's selected rows
@@ -239,6 +263,14 @@ typedef struct sd_sparse_decode_args {
   /* optional outputs (NULL to skip) */
   int32_t* indices_out;          /* device [batch][groups][topk]               */
   int32_t* counts_out;           /* device [batch][groups]                     */
+  /* optional hint and write-back, as sd_topk_select_hinted (NULL to skip);
+   * with fast scores the floor is the hint's smallest fast score minus twice
+   * the row bound, so selection stays exact */
+  const int32_t* topk_hint;      /* device [batch][groups][hint_stride]        */
+  int32_t hint_len;
+  int64_t hint_stride;
+  int32_t* topk_writeback;       /* device [batch][groups][writeback_stride]   */
+  int64_t writeback_stride;
 } sd_sparse_decode_args;
 
 sd_status sd_sparse_decode_workspace_size(const sd_sparse_decode_args* args, size_t* bytes);

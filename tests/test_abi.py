@@ -105,6 +105,24 @@ def test_fp8_pool_validation():
     assert lib.sd_sparse_decode_workspace_size(ctypes.byref(a), ctypes.byref(n)) == api.ERR_UNSUPPORTED
 
 
+def test_hinted_topk_argument_validation():
+    lib = _lib()
+    f = lib.sd_topk_select_hinted
+    # (scores, batch, groups, row_stride, kv_lens, k, hint, hint_len, hint_stride, indices, counts,
+    #  writeback, writeback_stride, workspace, workspace_bytes, stream)
+    n = ctypes.c_size_t(0)
+    assert lib.sd_topk_workspace_size(2, 1, 100, 8, ctypes.byref(n)) == api.OK
+    def call(h=32, hl=8, hs=8, wb=48, wbs=8):
+        return f(16, 2, 1, 100, 64, 8, h, hl, hs, 80, None, wb, wbs, 4096, n.value, 0)
+    assert call(hl=-1) == api.ERR_INVALID_ARGUMENT          # negative hint length
+    assert call(hl=9, hs=8) == api.ERR_INVALID_ARGUMENT     # stride below the length
+    assert call(wbs=7) == api.ERR_INVALID_ARGUMENT          # write-back row shorter than k
+    assert b"write-back" in lib.sd_last_error()
+    # batch 0 is a no-op that needs no GPU, with or without a hint
+    assert f(None, 0, 1, 100, None, 8, 32, 8, 8, None, None, 48, 8, None, 0, 0) == api.OK
+    assert f(None, 0, 1, 100, None, 8, None, 0, 0, None, None, None, 0, None, 0, 0) == api.OK
+
+
 def test_topk_argument_validation():
     lib = _lib()
     f = lib.sd_topk_select

@@ -56,10 +56,13 @@ class sd_sparse_decode_args(ctypes.Structure):
                 ("q_heads", ctypes.c_int32), ("k", sd_pool), ("v", sd_pool),
                 ("v_dim", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
                 ("out", ctypes.c_void_p), ("out_dtype", ctypes.c_int),
-                ("indices_out", ctypes.c_void_p), ("counts_out", ctypes.c_void_p)]
+                ("indices_out", ctypes.c_void_p), ("counts_out", ctypes.c_void_p),
+                ("topk_hint", ctypes.c_void_p), ("hint_len", ctypes.c_int32),
+                ("hint_stride", ctypes.c_int64), ("topk_writeback", ctypes.c_void_p),
+                ("writeback_stride", ctypes.c_int64)]
 
 
-EXPORTS = ["sd_sparse_score_paged", "sd_topk_workspace_size", "sd_topk_select",
+EXPORTS = ["sd_sparse_score_paged", "sd_topk_workspace_size", "sd_topk_select", "sd_topk_select_hinted",
            "sd_sparse_decode_attn_workspace_size", "sd_sparse_decode_attn",
            "sd_sparse_decode_workspace_size", "sd_sparse_decode", "sd_local_to_global",
            "sd_status_string", "sd_last_error", "sd_version"]
@@ -84,6 +87,8 @@ def load(path: str = LIB_PATH):
         "sd_sparse_score_paged": [PP, PL, P, E, I32, P, E, F, E, P, P, P],
         "sd_topk_workspace_size": [I32, I32, I32, I32, ctypes.POINTER(SZ)],
         "sd_topk_select": [P, I32, I32, I32, P, I32, P, P, P, SZ, P],
+        "sd_topk_select_hinted": [P, I32, I32, I32, P, I32, P, I32, ctypes.c_int64, P, P, P, ctypes.c_int64,
+                                  P, SZ, P],
         "sd_sparse_decode_attn_workspace_size": [PP, I32, PL, I32, I32, ctypes.POINTER(SZ)],
         "sd_sparse_decode_attn": [PP, P, E, I32, PL, PL, I32, P, I32, F, P, E, P, SZ, P],
         "sd_sparse_decode_workspace_size": [PA, ctypes.POINTER(SZ)],
@@ -190,6 +195,19 @@ def topk_select(scores, batch: int, groups: int, row_stride: int, kv_lens, k: in
     _check(rc, "sd_topk_select")
 
 
+def topk_select_hinted(scores, batch: int, groups: int, row_stride: int, kv_lens, k: int, hint,
+                       indices, counts=None, writeback=None, workspace=None, workspace_bytes: int = 0,
+                       stream=None):
+    """hint and writeback are [batch, groups, n] int32 tensors (or None)."""
+    hl = 0 if hint is None else int(hint.shape[-1])
+    hs = 0 if hint is None else int(hint.stride(1))
+    ws_ = 0 if writeback is None else int(writeback.stride(1))
+    rc = load().sd_topk_select_hinted(_ptr(scores), batch, groups, row_stride, _ptr(kv_lens), k, _ptr(hint), hl,
+                                      hs, _ptr(indices), _ptr(counts), _ptr(writeback), ws_, _ptr(workspace),
+                                      workspace_bytes, _stream(stream))
+    _check(rc, "sd_topk_select_hinted")
+
+
 def sparse_decode_attn_workspace_size(pg: sd_pages, q_heads: int, k_pool: sd_pool, v_dim: int,
                                       k_sel: int) -> int:
     n = ctypes.c_size_t(0)
@@ -265,14 +283,18 @@ class DeviceStep:
     workspace: object
     args: sd_sparse_decode_args
     workload: object
+    hint: object = None
 
     def run(self, stream=None):
         sparse_decode(self.args, self.workspace, stream=stream)
 
 
-def prepare(w, precision: int = FAST, device="cuda", out_dtype=None) -> DeviceStep:
+def prepare(w, precision: int = FAST, device="cuda", out_dtype=None, hint: bool = False) -> DeviceStep:
     """Upload a host workload (see synth.Workload) and build the fused-step
-    arguments, output buffers and workspace."""
+    arguments, output buffers and workspace.  hint=True adds a persistent
+    [batch, groups, topk] buffer that each step reads as its hint and
+    overwrites with its own selection (the next step's hint); it starts at -1
+    (no hint)."""
     import torch
 
     bt = to_device_array(w.block_table, device)
@@ -315,6 +337,14 @@ def prepare(w, precision: int = FAST, device="cuda", out_dtype=None) -> DeviceSt
     args.out_dtype = dtype_code(out)
     args.indices_out = idx.data_ptr()
     args.counts_out = cnt.data_ptr()
+    hbuf = None
+    if hint:
+        hbuf = torch.full((B, groups, w.topk), -1, dtype=torch.int32, device=device)
+        args.topk_hint = hbuf.data_ptr()
+        args.hint_len = w.topk
+        args.hint_stride = w.topk
+        args.topk_writeback = hbuf.data_ptr()
+        args.writeback_stride = w.topk
     nbytes = sparse_decode_workspace_size(args)
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
-    return DeviceStep(bt, kl, sk, sks, sq, hw, q, k, v, out, idx, cnt, ws, args, w)
+    return DeviceStep(bt, kl, sk, sks, sq, hw, q, k, v, out, idx, cnt, ws, args, w, hbuf)

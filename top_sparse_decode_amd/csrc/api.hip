@@ -240,6 +240,55 @@ struct FusedPlan {
   size_t off_scores, off_bound, off_keys, off_idx, off_attn, total;
 };
 
+sd_status check_hint(const int32_t* hint, int32_t hint_len, int64_t hint_stride, const int32_t* writeback,
+                     int64_t wb_stride, int32_t k) {
+  if (hint && (hint_len < 0 || hint_stride < hint_len))
+    return fail(SD_ERR_INVALID_ARGUMENT, "bad hint length %d / stride %lld", hint_len, (long long)hint_stride);
+  if (writeback && wb_stride < k)
+    return fail(SD_ERR_INVALID_ARGUMENT, "write-back stride %lld below k %d", (long long)wb_stride, k);
+  return SD_OK;
+}
+
+sd_status topk_select_impl(const float* scores, int32_t batch, int32_t groups, int32_t row_stride,
+                           const int32_t* kv_lens, int32_t k, const int32_t* hint, int32_t hint_len,
+                           int64_t hint_stride, int32_t* indices, int32_t* counts, int32_t* writeback,
+                           int64_t wb_stride, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_err.clear();
+  if (batch < 0 || groups <= 0 || row_stride < 0 || k <= 0)
+    return fail(SD_ERR_INVALID_ARGUMENT, "bad sizes (batch %d, groups %d, row_stride %d, k %d)", batch,
+                groups, row_stride, k);
+  if (row_stride > sd::select_max_row())
+    return fail(SD_ERR_UNSUPPORTED, "rows longer than %d tokens", sd::select_max_row());
+  if (batch > 0 && (!scores || !kv_lens || !indices))
+    return fail(SD_ERR_INVALID_ARGUMENT, "scores, kv_lens or indices is NULL");
+  sd_status s = check_hint(hint, hint_len, hint_stride, writeback, wb_stride, k);
+  if (s != SD_OK) return s;
+  const size_t need = align_up(sd::select_workspace_bytes(batch * groups, row_stride));
+  if (batch > 0 && (workspace_bytes < need || !workspace))
+    return fail(SD_ERR_WORKSPACE_TOO_SMALL, "topk needs %zu workspace bytes", need);
+  if (batch > 0 && !aligned16(workspace)) return fail(SD_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  if (batch == 0) return SD_OK;
+  sd::SelectArgs a{};
+  a.scores = scores;
+  a.batch = batch;
+  a.groups = groups;
+  a.row_stride = row_stride;
+  a.kv_lens = kv_lens;
+  a.k = k;
+  a.indices = indices;
+  a.counts = counts;
+  a.row_bound = nullptr;
+  a.hint = hint;
+  a.hint_len = hint ? hint_len : 0;
+  a.hint_stride = hint_stride;
+  a.writeback = writeback;
+  a.wb_stride = wb_stride;
+  sd::select_bind_workspace(&a, workspace);
+  if ((s = hip_status(sd::launch_select_init(a, stream), "select_init")) != SD_OK) return s;
+  if ((s = hip_status(sd::launch_select_stats(a, stream), "select_stats")) != SD_OK) return s;
+  return hip_status(sd::launch_select(a, stream), "select");
+}
+
 sd_status plan_fused(const sd_sparse_decode_args* x, bool need_ptrs, FusedPlan* f) {
   if (!x) return fail(SD_ERR_INVALID_ARGUMENT, "args is NULL");
   // the fused call scores into its own workspace: no scores pointer to check
@@ -248,6 +297,9 @@ sd_status plan_fused(const sd_sparse_decode_args* x, bool need_ptrs, FusedPlan* 
                              x->head_weights, x->mode, &kNonNull, need_ptrs);
   if (st != SD_OK) return st;
   if (x->topk <= 0) return fail(SD_ERR_INVALID_ARGUMENT, "topk must be >= 1");
+  if ((st = check_hint(x->topk_hint, x->hint_len, x->hint_stride, x->topk_writeback, x->writeback_stride,
+                       x->topk)) != SD_OK)
+    return st;
   if (x->pages.max_kv_len > sd::select_max_row())
     return fail(SD_ERR_UNSUPPORTED, "max_kv_len above %d tokens", sd::select_max_row());
   if (x->precision != SD_SCORE_EXACT && x->precision != SD_SCORE_FAST)
@@ -325,37 +377,21 @@ sd_status sd_topk_workspace_size(int32_t batch, int32_t groups, int32_t row_stri
   return SD_OK;
 }
 
+
 sd_status sd_topk_select(const float* scores, int32_t batch, int32_t groups, int32_t row_stride,
                          const int32_t* kv_lens, int32_t k, int32_t* indices, int32_t* counts,
                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  g_err.clear();
-  if (batch < 0 || groups <= 0 || row_stride < 0 || k <= 0)
-    return fail(SD_ERR_INVALID_ARGUMENT, "bad sizes (batch %d, groups %d, row_stride %d, k %d)", batch,
-                groups, row_stride, k);
-  if (row_stride > sd::select_max_row())
-    return fail(SD_ERR_UNSUPPORTED, "rows longer than %d tokens", sd::select_max_row());
-  if (batch > 0 && (!scores || !kv_lens || !indices))
-    return fail(SD_ERR_INVALID_ARGUMENT, "scores, kv_lens or indices is NULL");
-  const size_t need = align_up(sd::select_workspace_bytes(batch * groups, row_stride));
-  if (batch > 0 && (workspace_bytes < need || !workspace))
-    return fail(SD_ERR_WORKSPACE_TOO_SMALL, "topk needs %zu workspace bytes", need);
-  if (batch > 0 && !aligned16(workspace)) return fail(SD_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
-  if (batch == 0) return SD_OK;
-  sd::SelectArgs a{};
-  a.scores = scores;
-  a.batch = batch;
-  a.groups = groups;
-  a.row_stride = row_stride;
-  a.kv_lens = kv_lens;
-  a.k = k;
-  a.indices = indices;
-  a.counts = counts;
-  a.row_bound = nullptr;
-  sd::select_bind_workspace(&a, workspace);
-  sd_status s;
-  if ((s = hip_status(sd::launch_select_init(a, stream), "select_init")) != SD_OK) return s;
-  if ((s = hip_status(sd::launch_select_stats(a, stream), "select_stats")) != SD_OK) return s;
-  return hip_status(sd::launch_select(a, stream), "select");
+  return topk_select_impl(scores, batch, groups, row_stride, kv_lens, k, nullptr, 0, 0, indices, counts,
+                          nullptr, 0, workspace, workspace_bytes, stream);
+}
+
+sd_status sd_topk_select_hinted(const float* scores, int32_t batch, int32_t groups, int32_t row_stride,
+                                const int32_t* kv_lens, int32_t k, const int32_t* hint, int32_t hint_len,
+                                int64_t hint_stride, int32_t* indices, int32_t* counts,
+                                int32_t* writeback, int64_t writeback_stride, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  return topk_select_impl(scores, batch, groups, row_stride, kv_lens, k, hint, hint_len, hint_stride, indices,
+                          counts, writeback, writeback_stride, workspace, workspace_bytes, stream);
 }
 
 sd_status sd_sparse_decode_attn_workspace_size(const sd_pages* pages, int32_t q_heads,
@@ -424,6 +460,11 @@ sd_status sd_sparse_decode(const sd_sparse_decode_args* x, void* workspace, size
   t.indices = idx;
   t.counts = x->counts_out;
   t.row_bound = f.fast ? bound : nullptr;
+  t.hint = x->topk_hint;
+  t.hint_len = x->topk_hint ? x->hint_len : 0;
+  t.hint_stride = x->hint_stride;
+  t.writeback = x->topk_writeback;
+  t.wb_stride = x->writeback_stride;
   sd::select_bind_workspace(&t, ws + f.off_keys);
   if ((st = hip_status(sd::launch_select_init(t, stream), "select_init")) != SD_OK) return st;
   f.score.scores = scores;

@@ -27,7 +27,8 @@ struct ScoreArgs {
   int32_t* row_stats;  // selection statistics (min/max keys of finite scores) or null
 };
 
-// Per-row selection statistics: [kmin key, kmax key, band count, 5 spare,
+// Per-row selection statistics: [kmin key, kmax key, band count, cut (4
+// slots), score floor certified by the hint (float bits, -inf = none),
 // 2048-bin histogram].
 constexpr int kStatStride = 8 + 2048;
 constexpr int kSelChunk = 4096;   // tokens per block in the multi-block selection
@@ -47,6 +48,14 @@ struct SelectArgs {
   int32_t* chunk_counts;  // [rows][nchunks][2]: kept-for-sure count, -inf count
   uint64_t* band;       // [rows][kBandCap]: (key << 32) | ~position
   int32_t nchunks;      // ceil(row_stride / kSelChunk)
+  // optional hint: a previous selection per row (request-local positions),
+  // used only to certify a lower score floor for the histogram range
+  const int32_t* hint;  // [rows][hint_stride] or null
+  int32_t hint_len;
+  int64_t hint_stride;
+  // optional copy of this selection (the next step's hint), written by emit
+  int32_t* writeback;   // [rows][wb_stride] or null
+  int64_t wb_stride;
 };
 
 struct AttnArgs {

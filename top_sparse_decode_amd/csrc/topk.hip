@@ -47,6 +47,14 @@ constexpr int kMaxNI = 32;              // tiles held in registers: rows up to 6
 constexpr int kMaxChunks = 4;           // longer rows: up to 4 super-chunks, re-read per pass
 enum : uint32_t { kOut = 0, kIn = 1, kBand = 2, kPad = 3 };
 
+// Slot i of a row's output, and of its copy for the next step's hint when
+// the caller asked for one (the write-back rides along with the output
+// stores instead of a copy kernel after them).
+__device__ __forceinline__ void put_index(const SelectArgs& a, int row, int i, int v) {
+  a.indices[(int64_t)row * a.k + i] = v;
+  if (a.writeback) a.writeback[(int64_t)row * a.wb_stride + i] = v;
+}
+
 struct SelShared {
   int hist[kBins];
   int tmp[kSelWaves];
@@ -276,9 +284,8 @@ __device__ __forceinline__ void select_row_block(const SelectArgs& a, int row, S
   const int b = row / a.groups;
   const int L = clamp_len(a.kv_lens[b], a.row_stride);
   const int k = a.k;
-  int32_t* out = a.indices + (int64_t)row * k;
   if (L <= k) {  // every token is kept
-    for (int i = tid; i < k; i += kSelThreads) out[i] = i < L ? i : -1;
+    for (int i = tid; i < k; i += kSelThreads) put_index(a, row, i, i < L ? i : -1);
     if (a.counts && tid == 0) a.counts[row] = L;
     return;
   }
@@ -525,7 +532,7 @@ __device__ __forceinline__ void select_row_block(const SelectArgs& a, int row, S
       for (int e = 0; e < 4; ++e) {
         const bool keep = (flags & (1u << e)) || ((flags & (16u << e)) && take > 0);
         if (!(flags & (1u << e)) && keep) --take;
-        if (keep && pos < k) out[pos] = t0 + e;
+        if (keep && pos < k) put_index(a, row, pos, t0 + e);
         pos += keep;
       }
       const int took = min(max(need, 0), tot_eq);
@@ -562,7 +569,9 @@ struct RowView {
   float lo, hi, fscale;
 };
 
-__device__ __forceinline__ RowView row_view(const SelectArgs& a, int row) {
+// The row's histogram range [lo, hi]: the min / max finite score, with lo
+// raised to the floor a hint certified (no token below it can be selected).
+__device__ __forceinline__ RowView make_view(const SelectArgs& a, int row, float floor) {
   const int b = row / a.groups;
   RowView v;
   v.L = clamp_len(a.kv_lens[b], a.row_stride);
@@ -571,9 +580,13 @@ __device__ __forceinline__ RowView row_view(const SelectArgs& a, int row) {
   v.any_finite = kmin <= kmax;
   v.lo = v.any_finite ? key_to_score(kmin) : 0.0f;
   v.hi = v.any_finite ? key_to_score(kmax) : 0.0f;
-  // identical to the one-block path: same bins, same classes
+  if (v.any_finite && floor > v.lo) v.lo = fminf(floor, v.hi);
+  // identical to the one-block path when there is no floor: same bins, same classes
   v.fscale = v.hi > v.lo ? (float)((double)kBins / ((double)v.hi - (double)v.lo)) : 0.0f;
   return v;
+}
+__device__ __forceinline__ RowView row_view(const SelectArgs& a, int row) {
+  return make_view(a, row, __int_as_float(a.stats[(int64_t)row * kStatStride + 7]));
 }
 
 __device__ __forceinline__ int bin_of_v(const RowView& v, float x) {
@@ -673,7 +686,7 @@ __device__ __forceinline__ RowCut stored_cut(const SelectArgs& a, int row) {
 __device__ __forceinline__ uint32_t classify(const RowView& v, const RowCut& c, float x, bool fast) {
   if (x != x) return kPad;
   if (c.bstar < 0) return __builtin_isfinite(x) ? kIn : kBand;  // -inf tokens fill the quota
-  if (!__builtin_isfinite(x)) return kOut;
+  if (!__builtin_isfinite(x) || x < v.lo) return kOut;  // below the hint's floor: never selected
   if (fast) return x > c.band_hi ? kIn : (x < c.band_lo ? kOut : kBand);
   const int bn = bin_of_v(v, x);
   return bn > c.bstar ? kIn : (bn < c.bstar ? kOut : kBand);
@@ -684,6 +697,7 @@ __global__ __launch_bounds__(256) void select_init_kernel(SelectArgs a) {
   int32_t* st = a.stats + (int64_t)row * kStatStride;
   for (int i = threadIdx.x; i < kStatStride; i += 256) st[i] = 0;
   if (threadIdx.x == 0) st[0] = (int32_t)0xFFFFFFFFu;  // kmin starts at the largest key
+  if (threadIdx.x == 0) st[7] = (int32_t)0xFF800000u;  // no floor (-inf)
   // the fast scorer max-accumulates its error bound into row_bound
   if (threadIdx.x == 0 && a.row_bound) a.row_bound[row] = 0.0f;
 }
@@ -714,11 +728,86 @@ __global__ __launch_bounds__(kChunkThreads) void select_stats_kernel(SelectArgs 
   }
 }
 
+// Exclusive max over the threads of a chunk block (-1 for thread 0); `red`
+// needs kSelWaves ints.  Contains __syncthreads.
+__device__ __forceinline__ int chunk_excl_max(int v, int* red) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int w = __shfl_up(inc, o);
+    if (lane >= o) inc = max(inc, w);
+  }
+  if (lane == 63) red[wid] = inc;
+  __syncthreads();
+  int before = -1;
+  for (int w = 0; w < wid; ++w) before = max(before, red[w]);
+  const int excl = max(before, __shfl_up(inc, 1));
+  __syncthreads();
+  return lane == 0 ? before : excl;
+}
+
+// Floor certified by a hint: when the hint names at least k distinct
+// positions below L, the k-th largest score is at least the smallest of
+// their scores (exact scores), or that minus the row bound d (fast scores,
+// whose exact values differ by at most d); a token whose score is below
+// min - 2d (fast) or min (exact) is then below the k-th largest exact score
+// and is never selected.  -inf when the hint certifies nothing.  Distinct
+// positions are counted without a set: an entry counts when it is valid and
+// larger than every valid entry before it, so an ascending hint (what the
+// write-back produces) counts in full and any other hint counts a subset of
+// distinct positions.  Every block of the row computes the same value.
+__device__ float hint_floor(const SelectArgs& a, int row, int L, int* red) {
+  const int tid = threadIdx.x;
+  const int n = a.hint_len;
+  const int per = (n + kChunkThreads - 1) / kChunkThreads;  // a contiguous run per thread
+  const int i0 = min(n, tid * per), i1 = min(n, i0 + per);
+  const int32_t* h = a.hint + (int64_t)row * a.hint_stride;
+  const float* s = a.scores + (int64_t)row * a.row_stride;
+  int lmax = -1;
+  for (int i = i0; i < i1; ++i) {
+    const int p = h[i];
+    if (p >= 0 && p < L) lmax = max(lmax, p);
+  }
+  int run = chunk_excl_max(lmax, red);
+  int distinct = 0;
+  float vmin = __builtin_inff();
+  for (int i = i0; i < i1; ++i) {
+    const int p = h[i];
+    if (p >= 0 && p < L && p > run) {
+      run = p;
+      ++distinct;
+      vmin = fminf(vmin, s[p]);
+    }
+  }
+  distinct = chunk_sum_i(distinct, red);
+  vmin = fminf(vmin, __shfl_xor(vmin, 32)); vmin = fminf(vmin, __shfl_xor(vmin, 16));
+  vmin = fminf(vmin, __shfl_xor(vmin, 8)); vmin = fminf(vmin, __shfl_xor(vmin, 4));
+  vmin = fminf(vmin, __shfl_xor(vmin, 2)); vmin = fminf(vmin, __shfl_xor(vmin, 1));
+  if ((tid & 63) == 0) red[tid >> 6] = __float_as_int(vmin);
+  __syncthreads();
+  float m = __int_as_float(red[0]);
+  for (int w = 1; w < kSelWaves; ++w) m = fminf(m, __int_as_float(red[w]));
+  __syncthreads();
+  if (distinct < a.k || !__builtin_isfinite(m)) return -__builtin_inff();
+  if (!a.row_bound) return m;
+  const double f = (double)m - 2.0 * (double)a.row_bound[row];
+  float fl = (float)f;
+  if ((double)fl > f) fl = next_down(fl);
+  return fl;
+}
+
 __global__ __launch_bounds__(kChunkThreads) void select_hist_kernel(SelectArgs a) {
   __shared__ int hist[kBins];
+  __shared__ int red[kSelWaves];
   const int row = blockIdx.y, c = blockIdx.x;
-  const RowView v = row_view(a, row);
+  RowView v = row_view(a, row);
   if (v.L <= a.k || c * kSelChunk >= v.L || !v.any_finite) return;
+  if (a.hint) {
+    const float floor = hint_floor(a, row, v.L, red);
+    v = make_view(a, row, floor);
+    if (c == 0 && threadIdx.x == 0) a.stats[(int64_t)row * kStatStride + 7] = __float_as_int(floor);
+  }
   for (int i = threadIdx.x; i < kBins; i += kChunkThreads) hist[i] = 0;
   __syncthreads();
   float x[kPerThread];
@@ -726,7 +815,7 @@ __global__ __launch_bounds__(kChunkThreads) void select_hist_kernel(SelectArgs a
   load8(a.scores + (int64_t)row * a.row_stride, t0, v.L, x);
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
-    const bool fin = __builtin_isfinite(x[e]);
+    const bool fin = __builtin_isfinite(x[e]) && x[e] >= v.lo;
     hist_add(hist, fin ? bin_of_v(v, x[e]) : 0, fin);
   }
   __syncthreads();
@@ -902,12 +991,11 @@ __global__ __launch_bounds__(kChunkThreads) void select_emit_kernel(SelectArgs a
   const int row = blockIdx.y, c = blockIdx.x;
   const RowView v = row_view(a, row);
   const int k = a.k;
-  int32_t* out = a.indices + (int64_t)row * k;
   const int cstart = c * kSelChunk;
   if (v.L <= k) {  // every token kept (dense-equivalent)
-    for (int t = cstart + tid; t < min(v.L, cstart + kSelChunk); t += kChunkThreads) out[t] = t;
+    for (int t = cstart + tid; t < min(v.L, cstart + kSelChunk); t += kChunkThreads) put_index(a, row, t, t);
     if (c == 0) {
-      for (int i = v.L + tid; i < k; i += kChunkThreads) out[i] = -1;
+      for (int i = v.L + tid; i < k; i += kChunkThreads) put_index(a, row, i, -1);
       if (a.counts && tid == 0) a.counts[row] = v.L;
     }
     return;
@@ -1043,7 +1131,7 @@ __global__ __launch_bounds__(kChunkThreads) void select_emit_kernel(SelectArgs a
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e)
     if ((keep >> e) & 1u) {
-      if (offset < k) out[offset] = t0 + e;
+      if (offset < k) put_index(a, row, offset, t0 + e);
       ++offset;
     }
   if (a.counts && c == 0 && tid == 0) a.counts[row] = k;
