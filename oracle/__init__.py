@@ -82,7 +82,8 @@ def _load():
         lib.orc_topk.argtypes = [P, I32, I32, I32, P, I32, P, P]
         lib.orc_attention.argtypes = [P, I32, P, I32, P, I32, I32, PP, PP, I32, P, I32, F, P]
         lib.orc_local_to_global.argtypes = [P, I32, I32, I32, I32, P, I32, I32, P]
-        for f in (lib.orc_score, lib.orc_topk, lib.orc_attention, lib.orc_local_to_global):
+        lib.orc_tri_select.argtypes = [P, I32, I32, I32, I32, P, I32, I32, P, P, P, P]
+        for f in (lib.orc_score, lib.orc_topk, lib.orc_attention, lib.orc_local_to_global, lib.orc_tri_select):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -198,6 +199,30 @@ def local_to_global(block_table, page_size: int, num_pages: int, local: np.ndarr
                                  loc.ctypes.data, groups, k, out.ctypes.data)
     _check(rc, "local_to_global")
     return out
+
+
+TRI_MODES = {"per_layer_perhead": 0, "per_head": 1, "union": 2}
+
+
+def tri_select(scores: np.ndarray, kv_lens, mode, k: int) -> dict:
+    """TriAttention normalize -> reduce -> top-k (see oracle.h).  scores is
+    [layers, batch, groups, row_len] float32; returns z (same shape), the
+    reduced rows, indices and counts ([out_rows, k] / [out_rows] with
+    out_rows = layers*batch*groups, batch*groups or batch by mode)."""
+    lib = _load()
+    s = _c(scores, np.float32)
+    kl = _c(kv_lens, np.int32)
+    layers, batch, groups, row_len = s.shape
+    m = TRI_MODES[mode] if isinstance(mode, str) else int(mode)
+    out_rows = {0: layers * batch * groups, 1: batch * groups, 2: batch}[m]
+    z = np.empty(s.shape, dtype=np.float32)
+    red = np.empty((out_rows, row_len), dtype=np.float32)
+    idx = np.empty((out_rows, k), dtype=np.int32)
+    cnt = np.empty((out_rows,), dtype=np.int32)
+    rc = lib.orc_tri_select(s.ctypes.data, layers, batch, groups, row_len, kl.ctypes.data, m, k,
+                            z.ctypes.data, red.ctypes.data, idx.ctypes.data, cnt.ctypes.data)
+    _check(rc, "tri_select")
+    return {"z": z, "reduced": red, "indices": idx, "counts": cnt}
 
 
 def sparse_decode(w) -> dict:

@@ -324,3 +324,94 @@ int orc_local_to_global(const int32_t* block_table, int32_t max_pages, int32_t b
       }
   return ORC_OK;
 }
+
+/* ------------------------------------------------------------------ TriAttention modes */
+
+/* Normalization of one member row (see oracle.h): strided binary64 partial
+ * sums in token order, then the partials in order. */
+static void tri_normalize_row(const float* row, int32_t L, int32_t row_len, float* z) {
+  double part[256];
+  int64_t n = 0;
+  for (int c = 0; c < 256; ++c) part[c] = 0.0;
+  for (int32_t t = 0; t < L; ++t)
+    if (isfinite(row[t])) {
+      part[t % 256] = part[t % 256] + (double)row[t];
+      ++n;
+    }
+  double s1 = 0.0;
+  for (int c = 0; c < 256; ++c) s1 = s1 + part[c];
+  const double mu = n > 0 ? s1 / (double)n : 0.0;
+  for (int c = 0; c < 256; ++c) part[c] = 0.0;
+  for (int32_t t = 0; t < L; ++t)
+    if (isfinite(row[t])) {
+      const double d = (double)row[t] - mu;
+      part[t % 256] = part[t % 256] + d * d;
+    }
+  double s2 = 0.0;
+  for (int c = 0; c < 256; ++c) s2 = s2 + part[c];
+  const double sigma = n > 0 ? sqrt(s2 / (double)n) : 0.0;
+  for (int32_t t = 0; t < row_len; ++t) {
+    if (t >= L || !isfinite(row[t])) {
+      z[t] = -INFINITY;
+    } else if (sigma == 0.0) {
+      z[t] = 0.0f;
+    } else {
+      z[t] = (float)(((double)row[t] - mu) / sigma);
+    }
+  }
+}
+
+int orc_tri_select(const float* scores, int32_t layers, int32_t batch, int32_t groups, int32_t row_len,
+                   const int32_t* kv_lens, int32_t mode, int32_t k, float* z, float* reduced,
+                   int32_t* indices, int32_t* counts) {
+  if (!scores || !kv_lens || !indices || layers <= 0 || batch < 0 || groups <= 0 || row_len < 0 || k <= 0)
+    return ORC_EARG;
+  if (mode != ORC_PER_LAYER_PERHEAD && mode != ORC_PER_HEAD && mode != ORC_UNION) return ORC_EARG;
+  const int64_t members = (int64_t)layers * batch * groups;
+  for (int32_t b = 0; b < batch; ++b)
+    if (kv_lens[b] < 0 || kv_lens[b] > row_len) return ORC_EARG;
+  for (int64_t m = 0; m < members; ++m) {
+    const int32_t b = (int32_t)((m / groups) % batch);
+    for (int32_t t = 0; t < kv_lens[b]; ++t)
+      if (isnan(scores[m * row_len + t])) return ORC_ENAN;
+  }
+  float* zz = (float*)malloc(sizeof(float) * (size_t)(members * row_len > 0 ? members * row_len : 1));
+  if (!zz) return ORC_EARG;
+  for (int64_t m = 0; m < members; ++m) {
+    const int32_t b = (int32_t)((m / groups) % batch);
+    tri_normalize_row(scores + m * row_len, kv_lens[b], row_len, zz + m * row_len);
+  }
+  if (z) memcpy(z, zz, sizeof(float) * (size_t)(members * row_len));
+
+  /* reduced rows and the batch / group shape the top-k sees */
+  int32_t out_batch, out_groups;
+  int32_t* lens;
+  if (mode == ORC_PER_LAYER_PERHEAD) { out_batch = layers * batch; out_groups = groups; }
+  else if (mode == ORC_PER_HEAD) { out_batch = batch; out_groups = groups; }
+  else { out_batch = batch; out_groups = 1; }
+  const int64_t out_rows = (int64_t)out_batch * out_groups;
+  float* r = (float*)malloc(sizeof(float) * (size_t)(out_rows * row_len > 0 ? out_rows * row_len : 1));
+  lens = (int32_t*)malloc(sizeof(int32_t) * (size_t)(out_batch > 0 ? out_batch : 1));
+  if (!r || !lens) { free(zz); free(r); free(lens); return ORC_EARG; }
+  for (int32_t ob = 0; ob < out_batch; ++ob) lens[ob] = kv_lens[ob % batch];
+  for (int64_t o = 0; o < out_rows; ++o)
+    for (int32_t t = 0; t < row_len; ++t) r[o * row_len + t] = -INFINITY;
+  for (int32_t l = 0; l < layers; ++l)
+    for (int32_t b = 0; b < batch; ++b)
+      for (int32_t g = 0; g < groups; ++g) {
+        const float* src = zz + (((int64_t)l * batch + b) * groups + g) * row_len;
+        int64_t o;
+        if (mode == ORC_PER_LAYER_PERHEAD) o = ((int64_t)l * batch + b) * groups + g;
+        else if (mode == ORC_PER_HEAD) o = (int64_t)b * groups + g;
+        else o = b;
+        float* dst = r + o * row_len;
+        for (int32_t t = 0; t < row_len; ++t)
+          if (src[t] > dst[t]) dst[t] = src[t];
+      }
+  if (reduced) memcpy(reduced, r, sizeof(float) * (size_t)(out_rows * row_len));
+  const int rc = orc_topk(r, out_batch, out_groups, row_len, lens, k, indices, counts);
+  free(zz);
+  free(r);
+  free(lens);
+  return rc;
+}

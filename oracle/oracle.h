@@ -102,6 +102,37 @@ int orc_local_to_global(const int32_t* block_table, int32_t max_pages, int32_t b
                         int32_t page_size, int32_t num_pages, const int32_t* local,
                         int32_t groups, int32_t k, int64_t* global_out);
 
+/* TriAttention selection modes ("Add TriAttention KV-cache compression
+ * method", Summary: a normalize/reduce step between paged-K scoring and
+ * TopK / tie settlement, with union, per_head and per_layer_perhead eviction
+ * modes; Main Files: score normalization and union reduction).  The pages
+ * name these steps only; the arithmetic below is this oracle's reading of
+ * them, written out in full.
+ *
+ * scores is [layers][batch][groups][row_len].  Normalization, per member row
+ * (layer, b, g), over its finite scores at t < kv_lens[b] (n of them):
+ *   P_c = sum over those t with t % 256 == c, t ascending, of (double)s_t
+ *         (each addition rounded in binary64), c = 0..255;
+ *   mu  = (sum of P_0 .. P_255 in order, binary64) / n;
+ *   Q_c, var likewise from d_t * d_t with d_t = (double)s_t - mu; var = sum / n;
+ *   sigma = sqrt(var);
+ *   z_t = (float)(((double)s_t - mu) / sigma)  (0 when sigma == 0),
+ *   z_t = -inf for a non-finite score and for t >= kv_lens[b].
+ * Reduction: r_t = max over the mode's members of z_t (binary32 max).
+ *   ORC_PER_LAYER_PERHEAD: one output row per (layer, b, g), its own z;
+ *   ORC_PER_HEAD:          one row per (b, g), the max over layers;
+ *   ORC_UNION:             one row per b, the max over layers and groups.
+ * Selection: orc_topk on the reduced rows with kv_lens[b].
+ * z (optional) receives every member's z, shape of scores; reduced
+ * (optional) the reduced rows [out_rows][row_len]; indices [out_rows][k],
+ * counts [out_rows] (may be NULL). */
+#define ORC_PER_LAYER_PERHEAD 0
+#define ORC_PER_HEAD 1
+#define ORC_UNION 2
+int orc_tri_select(const float* scores, int32_t layers, int32_t batch, int32_t groups, int32_t row_len,
+                   const int32_t* kv_lens, int32_t mode, int32_t k, float* z, float* reduced,
+                   int32_t* indices, int32_t* counts);
+
 #ifdef __cplusplus
 }
 #endif

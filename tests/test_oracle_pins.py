@@ -493,3 +493,96 @@ def test_fp8_pool_scale_follows_the_page():
     got = oracle.score(bt2, w.kv_lens, k2, w.score_q, w.head_weights, w.mode, 1.0, w.max_kv_len,
                        k_scale=s2)
     assert np.array_equal(got.view(np.uint32), base.view(np.uint32))
+
+
+# ---------------------------------------------------------------- TriAttention modes
+
+def test_tri_normalize_is_the_population_zscore_of_finite_scores():
+    # against numpy's float64 mean / population std over the finite scores
+    rs = np.random.default_rng(31)
+    s = (rs.standard_normal((1, 2, 3, 5000)) * 7 + 40).astype(F32)
+    s[0, 1, 2, 100:140] = -np.inf                      # absent tokens: left out of the statistics
+    kv = np.array([5000, 3001], np.int32)
+    z = oracle.tri_select(s, kv, "per_layer_perhead", 16)["z"]
+    for b in range(2):
+        L = int(kv[b])
+        for g in range(3):
+            row = s[0, b, g, :L].astype(np.float64)
+            fin = np.isfinite(row)
+            ref = (row - row[fin].mean()) / row[fin].std()   # ddof=0: population
+            got = z[0, b, g, :L]
+            assert np.allclose(got[fin], ref[fin], rtol=2e-7, atol=2e-7)
+            assert np.all(got[~fin] == -np.inf)
+            assert np.all(z[0, b, g, L:] == -np.inf)
+
+
+def test_tri_normalize_bitwise_where_every_order_is_exact():
+    # small integers over a power-of-two length: the mean and the squared
+    # deviations are exact dyadic sums in any order, so numpy's float64
+    # result, rounded once to float32, is the exact definition
+    rs = np.random.default_rng(32)
+    s = rs.integers(-8, 9, size=(2, 1, 2, 512)).astype(F32)
+    kv = np.array([512], np.int32)
+    z = oracle.tri_select(s, kv, "per_layer_perhead", 8)["z"]
+    x = s.astype(np.float64)
+    mu = x.mean(axis=-1, keepdims=True)
+    sd = np.sqrt(((x - mu) ** 2).mean(axis=-1, keepdims=True))
+    ref = ((x - mu) / sd).astype(F32)
+    assert np.array_equal(z.view(np.uint32), ref.view(np.uint32))
+    # scaling every score by 4 scales mean and deviation exactly: same z bits
+    z4 = oracle.tri_select(s * F32(4), kv, "per_layer_perhead", 8)["z"]
+    assert np.array_equal(z4.view(np.uint32), z.view(np.uint32))
+
+
+def test_tri_constant_row_and_empty_row():
+    s = np.full((1, 2, 1, 300), 3.25, F32)
+    kv = np.array([300, 0], np.int32)
+    r = oracle.tri_select(s, kv, "union", 10)
+    assert np.all(r["z"][0, 0, 0] == 0.0)
+    assert list(r["indices"][0]) == list(range(10))        # all tie: lowest positions
+    assert np.all(r["indices"][1] == -1) and r["counts"][1] == 0
+
+
+def test_tri_per_layer_perhead_matches_raw_topk_on_separated_scores():
+    # z is increasing in s, so with well-separated distinct scores the
+    # selection on z is the selection on the raw scores
+    rs = np.random.default_rng(33)
+    L = 4000
+    s = np.stack([rs.permutation(L).astype(F32) * F32(0.5) for _ in range(2 * 3 * 2)]).reshape(2, 3, 2, L)
+    kv = np.array([4000, 2500, 999], np.int32)
+    r = oracle.tri_select(s, kv, "per_layer_perhead", 300)
+    raw_i, raw_c = oracle.topk(s.reshape(6, 2, L), np.tile(kv, 2), 300)
+    assert np.array_equal(r["indices"], raw_i.reshape(-1, 300))
+    assert np.array_equal(r["counts"], raw_c.reshape(-1))
+
+
+def test_tri_modes_reduce_over_the_right_members():
+    rs = np.random.default_rng(34)
+    one = rs.standard_normal((1, 2, 1, 3000)).astype(F32)
+    kv = np.array([3000, 2000], np.int32)
+    base = oracle.tri_select(one, kv, "per_layer_perhead", 128)
+    # identical layers and groups reduce to the single row
+    same = np.broadcast_to(one, (3, 2, 4, 3000)).copy()
+    for mode, rows in (("per_head", 8), ("union", 2)):
+        r = oracle.tri_select(same, kv, mode, 128)
+        assert r["indices"].shape[0] == rows
+        want = base["indices"] if mode == "union" else np.repeat(base["indices"], 4, axis=0)
+        assert np.array_equal(r["indices"], want)
+    # union's reduced row is the max of per_head's reduced rows over groups,
+    # per_head's the max over layers of the per-layer z
+    s = rs.standard_normal((3, 2, 4, 3000)).astype(F32)
+    ph = oracle.tri_select(s, kv, "per_head", 64)
+    un = oracle.tri_select(s, kv, "union", 64)
+    assert np.array_equal(un["reduced"], ph["reduced"].reshape(2, 4, 3000).max(axis=1))
+    assert np.array_equal(ph["reduced"], ph["z"].max(axis=0).reshape(8, 3000))
+
+
+def test_tri_union_keeps_a_token_one_head_alone_wants():
+    # the reduction is a max: a spike in one head survives the union even when
+    # every other head scores the token at the bottom (a mean would drop it)
+    rs = np.random.default_rng(35)
+    s = rs.standard_normal((1, 1, 8, 2000)).astype(F32)
+    s[0, 0, 1:, 777] = -5.0
+    s[0, 0, 0, 777] = 40.0
+    r = oracle.tri_select(s, np.array([2000], np.int32), "union", 16)
+    assert 777 in r["indices"][0]
