@@ -44,6 +44,11 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-requests", type=int, default=16, help="requests in the oracle sample")
     p.add_argument("--cpu-repeats", type=int, default=2, help="passes of the oracle over the sample")
+    p.add_argument("--workload", choices=["dsa_mla", "triattention"], default="dsa_mla",
+                   help="dsa_mla: the fused decode step (default); triattention: one eviction-time "
+                        "selection (normalize, reduce, top-k) over 36 layers x 32 requests x 8 KV heads "
+                        "x 4096 tokens, keeping 2048")
+    p.add_argument("--tri-mode", choices=["union", "per_head", "per_layer_perhead"], default="union")
     p.add_argument("--index-dtype", choices=["bf16", "fp8"], default="bf16",
                    help="indexer K cache: bf16, or FP8 E4M3 codes with one float32 scale per row")
     p.add_argument("--hint", action="store_true",
@@ -71,11 +76,63 @@ def scorer_traffic(kernel_hash: str, fp8: bool):
     return d.get("hbm_bytes_per_launch")
 
 
+def bench_triattention(args, api, torch, dev):
+    """One TriAttention eviction-time selection: the stacked per-layer score
+    rows of a 36-layer, 8-KV-head model for 32 requests at 4096 tokens
+    (budget 2048 + window 2048), normalized, reduced by mode, top 2048 kept.
+    The rows are seeded synthetic scores (per-row location and spread drawn
+    once, then N(0,1) tokens), generated on the device."""
+    layers, B, G, S, k = 36, 32, 8, 4096, 2048
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(2048)
+    loc = torch.rand((layers, B, G, 1), generator=gen, device=dev) * 100 - 50
+    spread = torch.exp(torch.rand((layers, B, G, 1), generator=gen, device=dev) * 4 - 2)
+    scores = [torch.randn((layers, B, G, S), generator=gen, device=dev) * spread + loc
+              for _ in range(max(1, args.replicas))]
+    kv = torch.full((B,), S, dtype=torch.int32, device=dev)
+    out_rows = {"per_layer_perhead": layers * B * G, "per_head": B * G, "union": B}[args.tri_mode]
+    idx = torch.empty((out_rows, k), dtype=torch.int32, device=dev)
+    ws = torch.empty(api.triattention_select_workspace_size(layers, B, G, S, args.tri_mode, k),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        api.triattention_select(scores[i % len(scores)], kv, args.tri_mode, k, idx, None, None, ws,
+                                stream=stream)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    score_bytes = layers * B * G * S * 4
+    gbps = score_bytes / (ms * 1e-3) / 1e9
+    result = {
+        "metric": "TriAttention selections/s (normalize + reduce + top-k)",
+        "value": round(1000.0 / ms, 2), "unit": "selections/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32 scores, f64 statistics", "data": "synthetic (seeded per-row "
+        "location U(-50,50), spread exp(U(-2,2)), N(0,1) tokens, generated on the device)",
+        "config": {"workload": f"triattention {args.tri_mode}: 36 layers x 32 requests x 8 KV heads x "
+                               f"4096 tokens, keep 2048", "layers": layers, "batch": B, "kv_heads": G,
+                   "kv_len": S, "topk": k, "mode": args.tri_mode, "input_replicas": len(scores)},
+        "roofline": {"kernel": "whole call (tri_stats, tri_reduce, selection)", "bound": "hbm",
+                     "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": score_bytes},
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards by "
-              "request across GPUs with no exchange, see DESIGN.md.", file=sys.stderr)
+              "request across GPUs with no exchange between them.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -85,6 +142,8 @@ def main():
 
     torch.cuda.set_device(0)
     dev = "cuda:0"
+    if args.workload == "triattention":
+        return bench_triattention(args, api, torch, dev)
     fp8 = args.index_dtype == "fp8"
     say(f"[bench] generating dsa_mla workload (B16, L65536, {args.index_dtype} indexer) ...")
     t0 = time.time()

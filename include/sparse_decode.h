@@ -199,6 +199,44 @@ sd_status sd_topk_select_hinted(const float* scores, int32_t batch, int32_t grou
                                 int32_t* writeback, int64_t writeback_stride, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------ modes */
+
+/* TriAttention selection modes ("Add TriAttention KV-cache compression
+ * method", Summary: normalize/reduce before TopK / tie settlement; union,
+ * per_head and per_layer_perhead eviction modes; Main Files: score
+ * normalization and union reduction).  The pages give no formula; the
+ * library's evaluation, bit-identical on every call:
+ *   per member row (layer l, request b, KV head g), over its finite scores
+ *   at t < kv_len[b] (n of them), binary64 statistics summed in a fixed
+ *   order -- 256 partials P_c over t % 256 == c (t ascending), then
+ *   P_0..P_255 in order -- mu = sum / n, var = (the same sums of
+ *   ((double)s_t - mu)^2) / n, and z_t = (float)(((double)s_t - mu) /
+ *   sqrt(var)) (0 when var == 0; -inf for a non-finite score or t >= kv_len);
+ *   reduced row r_t = max of z_t over the mode's members (layers, then
+ *   heads, ascending; a later member wins only when strictly larger);
+ *   then the top-k of sd_topk_select on each reduced row. */
+typedef enum sd_select_mode {
+  SD_SELECT_PER_LAYER_PERHEAD = 0, /* one row per (layer, b, g): its own z      */
+  SD_SELECT_PER_HEAD = 1,          /* one row per (b, g): max over layers       */
+  SD_SELECT_UNION = 2              /* one row per b: max over layers and heads  */
+} sd_select_mode;
+
+/*   scores      device [layers][batch][groups][row_stride] float (the
+ *               scorer's output for each layer, stacked)
+ *   indices     device [out_rows][k] int32, out_rows = layers*batch*groups,
+ *               batch*groups or batch by mode; ascending, -1 padded
+ *   counts      device [out_rows] int32 or NULL
+ *   reduced_out device [out_rows][row_stride] float or NULL: the reduced rows
+ *   workspace   device, at least sd_triattention_select_workspace_size() bytes
+ * NaN scores inside kv_len are outside the contract. */
+sd_status sd_triattention_select_workspace_size(int32_t layers, int32_t batch, int32_t groups,
+                                                int32_t row_stride, sd_select_mode mode, int32_t k,
+                                                size_t* bytes);
+sd_status sd_triattention_select(const float* scores, int32_t layers, int32_t batch, int32_t groups,
+                                 int32_t row_stride, const int32_t* kv_lens, sd_select_mode mode,
+                                 int32_t k, int32_t* indices, int32_t* counts, float* reduced_out,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------ step 3 */
 
 /* Softmax attention of every query head over its KV head's selected rows

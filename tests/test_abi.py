@@ -123,6 +123,23 @@ def test_hinted_topk_argument_validation():
     assert f(None, 0, 1, 100, None, 8, None, 0, 0, None, None, None, 0, None, 0, 0) == api.OK
 
 
+def test_triattention_select_validation():
+    lib = _lib()
+    n = ctypes.c_size_t(0)
+    ws = lib.sd_triattention_select_workspace_size
+    assert ws(4, 2, 8, 4096, 2, 2048, ctypes.byref(n)) == api.OK
+    assert n.value >= 2 * 4096 * 4            # the two reduced union rows at least
+    assert ws(0, 2, 8, 4096, 2, 2048, ctypes.byref(n)) == api.ERR_INVALID_ARGUMENT   # no layers
+    assert ws(4, 2, 8, 4096, 3, 2048, ctypes.byref(n)) == api.ERR_INVALID_ARGUMENT   # bad mode
+    assert ws(4, 2, 8, 4096, 2, 0, ctypes.byref(n)) == api.ERR_INVALID_ARGUMENT      # k = 0
+    assert ws(4, 2, 8, 300000, 2, 16, ctypes.byref(n)) == api.ERR_UNSUPPORTED        # row too long
+    f = lib.sd_triattention_select
+    assert ws(4, 2, 8, 4096, 1, 2048, ctypes.byref(n)) == api.OK
+    assert f(16, 4, 2, 8, 4096, 32, 1, 2048, 48, None, None, 4096, n.value - 1, 0) == api.ERR_WORKSPACE_TOO_SMALL
+    assert f(None, 4, 2, 8, 4096, 32, 1, 2048, 48, None, None, 4096, n.value, 0) == api.ERR_INVALID_ARGUMENT
+    assert f(None, 4, 0, 8, 4096, None, 1, 2048, None, None, None, None, 0, 0) == api.OK  # empty batch
+
+
 def test_topk_argument_validation():
     lib = _lib()
     f = lib.sd_topk_select

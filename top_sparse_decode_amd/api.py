@@ -24,6 +24,7 @@ OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = ra
 F32, BF16, FP8_E4M3 = 0, 1, 2
 GROUP_SUM, GROUP_MEAN, RELU_WEIGHTED = 0, 1, 2
 EXACT, FAST = 0, 1
+SELECT_MODES = {"per_layer_perhead": 0, "per_head": 1, "union": 2}
 MODES = {"group_sum": GROUP_SUM, "group_mean": GROUP_MEAN, "relu_weighted": RELU_WEIGHTED}
 
 
@@ -65,6 +66,7 @@ class sd_sparse_decode_args(ctypes.Structure):
 EXPORTS = ["sd_sparse_score_paged", "sd_topk_workspace_size", "sd_topk_select", "sd_topk_select_hinted",
            "sd_sparse_decode_attn_workspace_size", "sd_sparse_decode_attn",
            "sd_sparse_decode_workspace_size", "sd_sparse_decode", "sd_local_to_global",
+           "sd_triattention_select_workspace_size", "sd_triattention_select",
            "sd_status_string", "sd_last_error", "sd_version"]
 
 _lib = None
@@ -94,6 +96,8 @@ def load(path: str = LIB_PATH):
         "sd_sparse_decode_workspace_size": [PA, ctypes.POINTER(SZ)],
         "sd_sparse_decode": [PA, P, SZ, P],
         "sd_local_to_global": [PP, I32, I32, P, I32, I32, P, P],
+        "sd_triattention_select_workspace_size": [I32, I32, I32, I32, E, I32, ctypes.POINTER(SZ)],
+        "sd_triattention_select": [P, I32, I32, I32, I32, P, E, I32, P, P, P, P, SZ, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -247,6 +251,31 @@ def local_to_global(pg: sd_pages, page_size: int, num_pages: int, local, out, st
     rc = load().sd_local_to_global(ctypes.byref(pg), page_size, num_pages, _ptr(local), g, k,
                                    _ptr(out), _stream(stream))
     _check(rc, "sd_local_to_global")
+
+
+def _select_mode(mode) -> int:
+    return SELECT_MODES[mode] if isinstance(mode, str) else int(mode)
+
+
+def triattention_select_workspace_size(layers: int, batch: int, groups: int, row_stride: int, mode,
+                                       k: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().sd_triattention_select_workspace_size(layers, batch, groups, row_stride, _select_mode(mode),
+                                                        k, ctypes.byref(n)),
+           "sd_triattention_select_workspace_size")
+    return n.value
+
+
+def triattention_select(scores, kv_lens, mode, k: int, indices, counts=None, reduced=None, workspace=None,
+                        workspace_bytes: Optional[int] = None, stream=None):
+    """scores: [layers, batch, groups, row_stride] float32 tensor."""
+    layers, batch, groups, row_stride = scores.shape
+    wb = (0 if workspace is None else workspace.numel() * workspace.element_size()) \
+        if workspace_bytes is None else workspace_bytes
+    rc = load().sd_triattention_select(_ptr(scores), layers, batch, groups, row_stride, _ptr(kv_lens),
+                                       _select_mode(mode), k, _ptr(indices), _ptr(counts), _ptr(reduced),
+                                       _ptr(workspace), wb, _stream(stream))
+    _check(rc, "sd_triattention_select")
 
 
 def version() -> int:

@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libsparse_decode.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("SD_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["api.hip", "score.hip", "topk.hip", "attn.hip"]
+SOURCES = ["api.hip", "score.hip", "topk.hip", "attn.hip", "tri.hip"]
 
 # Per-source options.  The scorer keeps its matrix-core accumulators in
 # ordinary VGPRs (its epilogue reads every one of them on the VALU; AGPR

@@ -289,6 +289,32 @@ sd_status topk_select_impl(const float* scores, int32_t batch, int32_t groups, i
   return hip_status(sd::launch_select(a, stream), "select");
 }
 
+struct TriPlan {
+  int out_rows, out_batch, out_groups;
+  size_t off_stats, off_lens, off_reduced, off_select, total;
+};
+sd_status plan_tri(int32_t layers, int32_t batch, int32_t groups, int32_t row_stride, sd_select_mode mode,
+                   int32_t k, bool own_reduced, TriPlan* p) {
+  if (layers <= 0 || batch < 0 || groups <= 0 || row_stride < 0 || k <= 0)
+    return fail(SD_ERR_INVALID_ARGUMENT, "bad sizes (layers %d, batch %d, groups %d, row_stride %d, k %d)",
+                layers, batch, groups, row_stride, k);
+  if (mode != SD_SELECT_PER_LAYER_PERHEAD && mode != SD_SELECT_PER_HEAD && mode != SD_SELECT_UNION)
+    return fail(SD_ERR_INVALID_ARGUMENT, "bad selection mode %d", (int)mode);
+  if (row_stride > sd::select_max_row())
+    return fail(SD_ERR_UNSUPPORTED, "rows longer than %d tokens", sd::select_max_row());
+  if ((int64_t)layers * batch * groups > INT32_MAX / 2) return fail(SD_ERR_UNSUPPORTED, "too many rows");
+  p->out_rows = sd::tri_out_rows(layers, batch, groups, (int)mode);
+  p->out_batch = mode == SD_SELECT_PER_LAYER_PERHEAD ? layers * batch : batch;
+  p->out_groups = mode == SD_SELECT_UNION ? 1 : groups;
+  size_t off = 0;
+  p->off_stats = off; off += align_up((size_t)layers * batch * groups * 16);
+  p->off_lens = off; off += align_up((size_t)layers * batch * 4);
+  p->off_reduced = off; off += own_reduced ? 0 : align_up((size_t)p->out_rows * row_stride * 4);
+  p->off_select = off; off += align_up(sd::select_workspace_bytes(p->out_rows, row_stride));
+  p->total = off;
+  return SD_OK;
+}
+
 sd_status plan_fused(const sd_sparse_decode_args* x, bool need_ptrs, FusedPlan* f) {
   if (!x) return fail(SD_ERR_INVALID_ARGUMENT, "args is NULL");
   // the fused call scores into its own workspace: no scores pointer to check
@@ -377,6 +403,63 @@ sd_status sd_topk_workspace_size(int32_t batch, int32_t groups, int32_t row_stri
   return SD_OK;
 }
 
+
+
+sd_status sd_triattention_select_workspace_size(int32_t layers, int32_t batch, int32_t groups,
+                                                int32_t row_stride, sd_select_mode mode, int32_t k,
+                                                size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(SD_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  TriPlan p;
+  sd_status st = plan_tri(layers, batch, groups, row_stride, mode, k, false, &p);
+  if (st != SD_OK) return st;
+  *bytes = p.total;
+  return SD_OK;
+}
+
+sd_status sd_triattention_select(const float* scores, int32_t layers, int32_t batch, int32_t groups,
+                                 int32_t row_stride, const int32_t* kv_lens, sd_select_mode mode,
+                                 int32_t k, int32_t* indices, int32_t* counts, float* reduced_out,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_err.clear();
+  TriPlan p;
+  sd_status st = plan_tri(layers, batch, groups, row_stride, mode, k, reduced_out != nullptr, &p);
+  if (st != SD_OK) return st;
+  if (batch > 0 && (!scores || !kv_lens || !indices))
+    return fail(SD_ERR_INVALID_ARGUMENT, "scores, kv_lens or indices is NULL");
+  if (batch > 0 && (workspace_bytes < p.total || !workspace))
+    return fail(SD_ERR_WORKSPACE_TOO_SMALL, "triattention select needs %zu workspace bytes", p.total);
+  if (batch > 0 && !aligned16(workspace)) return fail(SD_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  if (reduced_out && !aligned16(reduced_out))
+    return fail(SD_ERR_INVALID_ARGUMENT, "reduced_out must be 16-byte aligned");
+  if (batch == 0 || row_stride == 0) return SD_OK;
+  char* ws = static_cast<char*>(workspace);
+  sd::TriArgs t{};
+  t.scores = scores;
+  t.layers = layers;
+  t.batch = batch;
+  t.groups = groups;
+  t.row_stride = row_stride;
+  t.kv_lens = kv_lens;
+  t.mode = (int32_t)mode;
+  t.stats = reinterpret_cast<double*>(ws + p.off_stats);
+  t.lens = mode == SD_SELECT_PER_LAYER_PERHEAD ? reinterpret_cast<int32_t*>(ws + p.off_lens) : nullptr;
+  t.reduced = reduced_out ? reduced_out : reinterpret_cast<float*>(ws + p.off_reduced);
+  if ((st = hip_status(sd::launch_tri(t, stream), "triattention normalize/reduce")) != SD_OK) return st;
+  sd::SelectArgs a{};
+  a.scores = t.reduced;
+  a.batch = p.out_batch;
+  a.groups = p.out_groups;
+  a.row_stride = row_stride;
+  a.kv_lens = t.lens ? t.lens : kv_lens;
+  a.k = k;
+  a.indices = indices;
+  a.counts = counts;
+  sd::select_bind_workspace(&a, ws + p.off_select);
+  if ((st = hip_status(sd::launch_select_init(a, stream), "select_init")) != SD_OK) return st;
+  if ((st = hip_status(sd::launch_select_stats(a, stream), "select_stats")) != SD_OK) return st;
+  return hip_status(sd::launch_select(a, stream), "select");
+}
 
 sd_status sd_topk_select(const float* scores, int32_t batch, int32_t groups, int32_t row_stride,
                          const int32_t* kv_lens, int32_t k, int32_t* indices, int32_t* counts,

@@ -82,6 +82,19 @@ struct AttnArgs {
   int32_t out_dtype;
 };
 
+// TriAttention normalize + reduce (tri.hip)
+struct TriArgs {
+  const float* scores;     // [layers][batch][groups][row_stride]
+  int32_t layers, batch, groups, row_stride;
+  const int32_t* kv_lens;  // [batch]
+  int32_t mode;            // 0 per layer per head, 1 per head, 2 union
+  double* stats;           // [layers*batch*groups][2]: mu, sigma
+  int32_t* lens;           // [layers*batch]: kv_lens repeated per layer (mode 0), or null
+  float* reduced;          // [out_rows][row_stride]
+};
+int tri_out_rows(int layers, int batch, int groups, int mode);
+hipError_t launch_tri(const TriArgs& a, hipStream_t st);
+
 bool score_exact_supported(int G);
 bool score_fast_supported(const ScoreArgs& a);
 hipError_t launch_score_exact(const ScoreArgs& a, hipStream_t st);

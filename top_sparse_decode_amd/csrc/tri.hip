@@ -1,0 +1,170 @@
+// tri.hip -- TriAttention selection modes: normalize the per-head score rows,
+// reduce them by mode, then the library's top-k.
+//
+// "Add TriAttention KV-cache compression method" (Summary) puts a
+// normalize/reduce step between paged-K scoring and TopK / tie settlement and
+// names three eviction modes (union, per_head, per_layer_perhead); its Main
+// Files name score normalization and union reduction.  The pages give no
+// formula, so the library fixes one evaluation and keeps to it bit for bit:
+//
+//   per member row m = (layer, request b, KV head g), over its finite scores
+//   at t < kv_len[b] (n of them):
+//     P_c  = sum_{t % 256 == c} (double)s_t, t ascending, binary64 adds;
+//     mu   = (P_0 + P_1 + ... + P_255, in order) / n;
+//     var  = (the same sums of d_t * d_t, d_t = (double)s_t - mu) / n;
+//     z_t  = (float)(((double)s_t - mu) / sqrt(var)), 0 when var == 0,
+//            -inf for a non-finite score or t >= kv_len[b];
+//   reduced row: r_t = max over the mode's members of z_t, members visited
+//   layer by layer and head by head, a later member replacing the running
+//   value only when strictly larger.
+//
+// Kernels: tri_stats_kernel (one 256-thread block per member row: thread c
+// owns the tokens t = c + 256 i, so its partial is exactly P_c and the loads
+// are coalesced; rows up to 4096 tokens stay in registers between the two
+// passes) and tri_reduce_kernel (one thread per token of an output row, the
+// members in the stated order).  Selection then runs on the reduced rows.
+#include "common.h"
+#include "kernels.h"
+
+#include <math.h>
+
+namespace sd {
+
+constexpr int kTriThreads = 256;
+constexpr int kTriRegs = 16;  // tokens per thread kept in registers (rows up to 4096)
+
+__global__ __launch_bounds__(kTriThreads) void tri_stats_kernel(TriArgs a) {
+  __shared__ double s_part[kTriThreads];
+  __shared__ double s_mu;
+  const int m = blockIdx.x;  // member row (layer, b, g)
+  const int tid = threadIdx.x;
+  const int b = (m / a.groups) % a.batch;
+  const int L = clamp_len(a.kv_lens[b], a.row_stride);
+  const float* row = a.scores + (int64_t)m * a.row_stride;
+  if (a.lens && (m % a.groups) == 0 && tid == 0) a.lens[m / a.groups] = a.kv_lens[b];
+  const bool resident = L <= kTriThreads * kTriRegs;
+  float x[kTriRegs];
+  double part = 0.0;
+  int n = 0;
+  if (resident) {
+#pragma unroll
+    for (int i = 0; i < kTriRegs; ++i) {
+      const int t = tid + kTriThreads * i;
+      x[i] = t < L ? row[t] : -__builtin_inff();
+    }
+#pragma unroll
+    for (int i = 0; i < kTriRegs; ++i)
+      if (__builtin_isfinite(x[i])) {
+        part = __dadd_rn(part, (double)x[i]);
+        ++n;
+      }
+  } else {
+    for (int t = tid; t < L; t += kTriThreads) {
+      const float v = row[t];
+      if (__builtin_isfinite(v)) {
+        part = __dadd_rn(part, (double)v);
+        ++n;
+      }
+    }
+  }
+  s_part[tid] = part;
+  // n over the block (exact integer sum)
+  int nn = wave_sum(n);
+  __shared__ int s_n[kTriThreads / 64];
+  if ((tid & 63) == 0) s_n[tid >> 6] = nn;
+  __syncthreads();
+  const int total = s_n[0] + s_n[1] + s_n[2] + s_n[3];
+  if (tid == 0) {
+    double s1 = 0.0;
+    for (int c = 0; c < kTriThreads; ++c) s1 = __dadd_rn(s1, s_part[c]);
+    s_mu = total > 0 ? __ddiv_rn(s1, (double)total) : 0.0;
+  }
+  __syncthreads();
+  const double mu = s_mu;
+  part = 0.0;
+  if (resident) {
+#pragma unroll
+    for (int i = 0; i < kTriRegs; ++i)
+      if (__builtin_isfinite(x[i])) {
+        const double d = __dsub_rn((double)x[i], mu);
+        part = __dadd_rn(part, __dmul_rn(d, d));
+      }
+  } else {
+    for (int t = tid; t < L; t += kTriThreads) {
+      const float v = row[t];
+      if (__builtin_isfinite(v)) {
+        const double d = __dsub_rn((double)v, mu);
+        part = __dadd_rn(part, __dmul_rn(d, d));
+      }
+    }
+  }
+  __syncthreads();  // every thread has read s_mu
+  s_part[tid] = part;
+  __syncthreads();
+  if (tid == 0) {
+    double s2 = 0.0;
+    for (int c = 0; c < kTriThreads; ++c) s2 = __dadd_rn(s2, s_part[c]);
+    const double sigma = total > 0 ? __dsqrt_rn(__ddiv_rn(s2, (double)total)) : 0.0;
+    a.stats[2 * (int64_t)m] = mu;
+    a.stats[2 * (int64_t)m + 1] = sigma;
+  }
+}
+
+__device__ __forceinline__ float tri_z(float s, double mu, double sigma) {
+  if (!__builtin_isfinite(s)) return -__builtin_inff();
+  if (sigma == 0.0) return 0.0f;
+  return __double2float_rn(__ddiv_rn(__dsub_rn((double)s, mu), sigma));
+}
+
+__global__ __launch_bounds__(kTriThreads) void tri_reduce_kernel(TriArgs a) {
+  const int o = blockIdx.y;  // output row
+  const int t = blockIdx.x * kTriThreads + threadIdx.x;
+  if (t >= a.row_stride) return;
+  // members of output row o, in the stated order
+  int b, g0, ng, nl, l0;
+  if (a.mode == 0) {        // per layer, per head: the member itself
+    l0 = o / (a.batch * a.groups);
+    b = (o / a.groups) % a.batch;
+    g0 = o % a.groups;
+    ng = 1;
+    nl = 1;
+  } else if (a.mode == 1) {  // per head: over layers
+    l0 = 0;
+    b = o / a.groups;
+    g0 = o % a.groups;
+    ng = 1;
+    nl = a.layers;
+  } else {                   // union: over layers and heads
+    l0 = 0;
+    b = o;
+    g0 = 0;
+    ng = a.groups;
+    nl = a.layers;
+  }
+  const int L = clamp_len(a.kv_lens[b], a.row_stride);
+  float r = -__builtin_inff();
+  if (t < L) {
+    for (int l = l0; l < l0 + nl; ++l)
+      for (int g = g0; g < g0 + ng; ++g) {
+        const int64_t m = ((int64_t)l * a.batch + b) * a.groups + g;
+        const float z = tri_z(a.scores[m * a.row_stride + t], a.stats[2 * m], a.stats[2 * m + 1]);
+        if (z > r) r = z;
+      }
+  }
+  a.reduced[(int64_t)o * a.row_stride + t] = r;
+}
+
+int tri_out_rows(int layers, int batch, int groups, int mode) {
+  return mode == 0 ? layers * batch * groups : (mode == 1 ? batch * groups : batch);
+}
+
+hipError_t launch_tri(const TriArgs& a, hipStream_t st) {
+  const int members = a.layers * a.batch * a.groups;
+  const int out_rows = tri_out_rows(a.layers, a.batch, a.groups, a.mode);
+  if (members == 0 || a.row_stride == 0) return hipSuccess;
+  tri_stats_kernel<<<members, kTriThreads, 0, st>>>(a);
+  tri_reduce_kernel<<<dim3((a.row_stride + kTriThreads - 1) / kTriThreads, out_rows), kTriThreads, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace sd
