@@ -240,6 +240,16 @@ struct FusedPlan {
   size_t off_scores, off_bound, off_keys, off_idx, off_attn, total;
 };
 
+// Selection over finished scores: one launch for short exact rows, else
+// statistics, histogram, classification and emission.
+sd_status run_select(const sd::SelectArgs& a, hipStream_t stream) {
+  if (sd::select_short_path(a)) return hip_status(sd::launch_select_short(a, stream), "select_short");
+  sd_status s;
+  if ((s = hip_status(sd::launch_select_init(a, stream), "select_init")) != SD_OK) return s;
+  if ((s = hip_status(sd::launch_select_stats(a, stream), "select_stats")) != SD_OK) return s;
+  return hip_status(sd::launch_select(a, stream), "select");
+}
+
 sd_status check_hint(const int32_t* hint, int32_t hint_len, int64_t hint_stride, const int32_t* writeback,
                      int64_t wb_stride, int32_t k) {
   if (hint && (hint_len < 0 || hint_stride < hint_len))
@@ -284,9 +294,7 @@ sd_status topk_select_impl(const float* scores, int32_t batch, int32_t groups, i
   a.writeback = writeback;
   a.wb_stride = wb_stride;
   sd::select_bind_workspace(&a, workspace);
-  if ((s = hip_status(sd::launch_select_init(a, stream), "select_init")) != SD_OK) return s;
-  if ((s = hip_status(sd::launch_select_stats(a, stream), "select_stats")) != SD_OK) return s;
-  return hip_status(sd::launch_select(a, stream), "select");
+  return run_select(a, stream);
 }
 
 struct TriPlan {
@@ -456,9 +464,7 @@ sd_status sd_triattention_select(const float* scores, int32_t layers, int32_t ba
   a.indices = indices;
   a.counts = counts;
   sd::select_bind_workspace(&a, ws + p.off_select);
-  if ((st = hip_status(sd::launch_select_init(a, stream), "select_init")) != SD_OK) return st;
-  if ((st = hip_status(sd::launch_select_stats(a, stream), "select_stats")) != SD_OK) return st;
-  return hip_status(sd::launch_select(a, stream), "select");
+  return run_select(a, stream);
 }
 
 sd_status sd_topk_select(const float* scores, int32_t batch, int32_t groups, int32_t row_stride,
@@ -549,15 +555,19 @@ sd_status sd_sparse_decode(const sd_sparse_decode_args* x, void* workspace, size
   t.writeback = x->topk_writeback;
   t.wb_stride = x->writeback_stride;
   sd::select_bind_workspace(&t, ws + f.off_keys);
-  if ((st = hip_status(sd::launch_select_init(t, stream), "select_init")) != SD_OK) return st;
+  // short exact rows are selected in one launch that needs no statistics
+  const bool short_rows = sd::select_short_path(t);
+  if (!short_rows && (st = hip_status(sd::launch_select_init(t, stream), "select_init")) != SD_OK) return st;
   f.score.scores = scores;
   f.score.row_bound = f.fast ? bound : nullptr;
-  f.score.row_stats = t.stats;
+  f.score.row_stats = short_rows ? nullptr : t.stats;
   st = run_score(f.score, f.fast ? SD_SCORE_FAST : SD_SCORE_EXACT, stream);
   if (st != SD_OK) return st;
   // 2. select (exactly, also from fast scores)
   t.score = f.score;
-  if ((st = hip_status(sd::launch_select(t, stream), "select")) != SD_OK) return st;
+  st = short_rows ? hip_status(sd::launch_select_short(t, stream), "select_short")
+                  : hip_status(sd::launch_select(t, stream), "select");
+  if (st != SD_OK) return st;
   // 3. attend
   f.attn.a.indices = idx;
   bind_attn_ws(&f.attn, ws + f.off_attn);

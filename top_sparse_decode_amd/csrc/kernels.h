@@ -107,6 +107,10 @@ void select_bind_workspace(SelectArgs* a, void* ws);
 hipError_t launch_select_init(const SelectArgs& a, hipStream_t st);
 hipError_t launch_select_stats(const SelectArgs& a, hipStream_t st);
 hipError_t launch_select(const SelectArgs& a, hipStream_t st);
+// exact scores, rows up to 16384 tokens: the whole selection in one launch
+// (needs neither init nor statistics; hints are not used)
+bool select_short_path(const SelectArgs& a);
+hipError_t launch_select_short(const SelectArgs& a, hipStream_t st);
 
 bool attn_mla_supported(const AttnArgs& a);
 bool attn_vec_supported(const AttnArgs& a);

@@ -55,16 +55,20 @@ __device__ __forceinline__ void put_index(const SelectArgs& a, int row, int i, i
   if (a.writeback) a.writeback[(int64_t)row * a.wb_stride + i] = v;
 }
 
-struct SelShared {
+template <int NCLS>
+struct SelSharedN {
   int hist[kBins];
   int tmp[kSelWaves];
   int win[2];
   float redf[2][kSelWaves];
   int redi[kSelWaves];
-  uint8_t cls[kMaxChunks * kMaxNI * kSelThreads];  // 4 x 2-bit classes per byte
+  uint8_t cls[NCLS];  // 4 x 2-bit classes per byte
 };
+// the whole-row path at the longest rows; shorter rows need NI * kSelThreads bytes of classes
+using SelShared = SelSharedN<kMaxChunks * kMaxNI * kSelThreads>;
 
-__device__ __forceinline__ float block_min_f(float v, SelShared& sh) {
+template <typename SH>
+__device__ __forceinline__ float block_min_f(float v, SH& sh) {
   v = fminf(v, __shfl_xor(v, 32)); v = fminf(v, __shfl_xor(v, 16)); v = fminf(v, __shfl_xor(v, 8));
   v = fminf(v, __shfl_xor(v, 4)); v = fminf(v, __shfl_xor(v, 2)); v = fminf(v, __shfl_xor(v, 1));
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -75,7 +79,8 @@ __device__ __forceinline__ float block_min_f(float v, SelShared& sh) {
   __syncthreads();
   return r;
 }
-__device__ __forceinline__ float block_max_f(float v, SelShared& sh) {
+template <typename SH>
+__device__ __forceinline__ float block_max_f(float v, SH& sh) {
   v = fmaxf(v, __shfl_xor(v, 32)); v = fmaxf(v, __shfl_xor(v, 16)); v = fmaxf(v, __shfl_xor(v, 8));
   v = fmaxf(v, __shfl_xor(v, 4)); v = fmaxf(v, __shfl_xor(v, 2)); v = fmaxf(v, __shfl_xor(v, 1));
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -86,7 +91,8 @@ __device__ __forceinline__ float block_max_f(float v, SelShared& sh) {
   __syncthreads();
   return r;
 }
-__device__ __forceinline__ int block_sum_i(int v, SelShared& sh) {
+template <typename SH>
+__device__ __forceinline__ int block_sum_i(int v, SH& sh) {
   v = wave_sum(v);
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   if (lane == 0) sh.redi[wid] = v;
@@ -121,7 +127,8 @@ __device__ __forceinline__ void hist_add(int* hist, int bin, bool active) {
 
 // Find, over bins in descending order, the bin holding the `want`-th
 // element (1-based); returns (bin, count strictly above it) via sh.win.
-__device__ __forceinline__ void find_bin(SelShared& sh, int nb, int want) {
+template <typename SH>
+__device__ __forceinline__ void find_bin(SH& sh, int nb, int want) {
   constexpr int BPT = kBins / kSelThreads;  // bins per thread
   const int tid = threadIdx.x;
   int c[BPT];
@@ -277,8 +284,8 @@ __device__ float exact_dsa_score(const ScoreArgs& sa, int b, int g, int t, float
 // The whole selection of one row by one 512-thread block.  Used as the
 // fallback of the multi-block path when a row's band does not fit the band
 // list (e.g. long runs of equal scores).
-template <int NI, bool RESIDENT, bool FAST>
-__device__ __forceinline__ void select_row_block(const SelectArgs& a, int row, SelShared& sh,
+template <int NI, bool RESIDENT, bool FAST, typename SH>
+__device__ __forceinline__ void select_row_block(const SelectArgs& a, int row, SH& sh,
                                  float (*s_terms)[kWave]) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int b = row / a.groups;
@@ -1160,6 +1167,30 @@ void select_bind_workspace(SelectArgs* a, void* ws) {
   a->chunk_counts = reinterpret_cast<int32_t*>(p);
   p += align256((size_t)rows * a->nchunks * 2 * 4);
   a->band = reinterpret_cast<uint64_t*>(p);
+}
+
+// Rows of at most NI * kTile tokens with exact scores: one block per row
+// holds the row in registers and does the whole selection (no statistics,
+// histogram or band passes between launches).
+template <int NI>
+__global__ __launch_bounds__(kSelThreads) void select_rows_kernel(SelectArgs a) {
+  __shared__ SelSharedN<NI * kSelThreads> sh;
+  __shared__ __attribute__((aligned(16))) float s_terms[kSelWaves][kWave];
+  select_row_block<NI, true, false>(a, blockIdx.x, sh, s_terms);
+}
+
+constexpr int kShortRow = 8 * kTile;  // 16384 tokens
+
+bool select_short_path(const SelectArgs& a) { return !a.row_bound && a.row_stride <= kShortRow; }
+
+hipError_t launch_select_short(const SelectArgs& a, hipStream_t st) {
+  const int rows = a.batch * a.groups;
+  if (rows == 0) return hipSuccess;
+  if (a.row_stride <= kTile) select_rows_kernel<1><<<rows, kSelThreads, 0, st>>>(a);
+  else if (a.row_stride <= 2 * kTile) select_rows_kernel<2><<<rows, kSelThreads, 0, st>>>(a);
+  else if (a.row_stride <= 4 * kTile) select_rows_kernel<4><<<rows, kSelThreads, 0, st>>>(a);
+  else select_rows_kernel<8><<<rows, kSelThreads, 0, st>>>(a);
+  return hipGetLastError();
 }
 
 hipError_t launch_select_init(const SelectArgs& a, hipStream_t st) {

@@ -21,8 +21,8 @@
 // Kernels: tri_stats_kernel (one 256-thread block per member row: thread c
 // owns the tokens t = c + 256 i, so its partial is exactly P_c and the loads
 // are coalesced; rows up to 4096 tokens stay in registers between the two
-// passes) and tri_reduce_kernel (one thread per token of an output row, the
-// members in the stated order).  Selection then runs on the reduced rows.
+// passes) and tri_reduce_kernel (a token per lane, the members split into
+// four ordered quarters).  Selection then runs on the reduced rows.
 #include "common.h"
 #include "kernels.h"
 
@@ -32,6 +32,7 @@ namespace sd {
 
 constexpr int kTriThreads = 256;
 constexpr int kTriRegs = 16;  // tokens per thread kept in registers (rows up to 4096)
+constexpr int kTriSpan = 4096;  // tokens per block of the one-slice reduce
 
 __global__ __launch_bounds__(kTriThreads) void tri_stats_kernel(TriArgs a) {
   __shared__ double s_part[kTriThreads];
@@ -116,11 +117,19 @@ __device__ __forceinline__ float tri_z(float s, double mu, double sigma) {
   return __double2float_rn(__ddiv_rn(__dsub_rn((double)s, mu), sigma));
 }
 
+// Lane = token.  SLICES = 4 (rows with many members): one block per
+// (64-token tile, output row), wave j takes the j-th quarter of the row's
+// members (in order), and the four partial maxima are combined in wave
+// order.  SLICES = 1: each wave takes its own 64 tokens and all members.  A
+// later value replaces the running one only when strictly larger, within a
+// wave and across waves, so the result is the first member attaining the
+// maximum, as in a single pass over the members.
+template <int SLICES>
 __global__ __launch_bounds__(kTriThreads) void tri_reduce_kernel(TriArgs a) {
+  __shared__ float s_part[kTriThreads / 64][64];
   const int o = blockIdx.y;  // output row
-  const int t = blockIdx.x * kTriThreads + threadIdx.x;
-  if (t >= a.row_stride) return;
-  // members of output row o, in the stated order
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  // members of output row o: (layer l, head g), l in [l0, l0 + nl), g in [g0, g0 + ng)
   int b, g0, ng, nl, l0;
   if (a.mode == 0) {        // per layer, per head: the member itself
     l0 = o / (a.batch * a.groups);
@@ -141,17 +150,57 @@ __global__ __launch_bounds__(kTriThreads) void tri_reduce_kernel(TriArgs a) {
     ng = a.groups;
     nl = a.layers;
   }
+  const int nm = nl * ng;
+  const int per = (nm + SLICES - 1) / SLICES;
+  const int j0 = SLICES == 1 ? 0 : min(nm, wid * per), j1 = SLICES == 1 ? nm : min(nm, j0 + per);
   const int L = clamp_len(a.kv_lens[b], a.row_stride);
-  float r = -__builtin_inff();
-  if (t < L) {
-    for (int l = l0; l < l0 + nl; ++l)
-      for (int g = g0; g < g0 + ng; ++g) {
-        const int64_t m = ((int64_t)l * a.batch + b) * a.groups + g;
-        const float z = tri_z(a.scores[m * a.row_stride + t], a.stats[2 * m], a.stats[2 * m + 1]);
+  // running max of z over members [j0, j1) at token t
+  auto reduce = [&](int t) {
+    float r = -__builtin_inff();
+    if (t >= L) return r;
+    int j = j0;
+    // eight members at a time: their loads are in flight together
+    for (; j + 8 <= j1; j += 8) {
+      float x[8];
+      int64_t m[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int jj = j + u;
+        m[u] = ((int64_t)(l0 + jj / ng) * a.batch + b) * a.groups + g0 + jj % ng;
+        x[u] = a.scores[m[u] * a.row_stride + t];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float z = tri_z(x[u], a.stats[2 * m[u]], a.stats[2 * m[u] + 1]);
         if (z > r) r = z;
       }
+    }
+    for (; j < j1; ++j) {
+      const int64_t m = ((int64_t)(l0 + j / ng) * a.batch + b) * a.groups + g0 + j % ng;
+      const float z = tri_z(a.scores[m * a.row_stride + t], a.stats[2 * m], a.stats[2 * m + 1]);
+      if (z > r) r = z;
+    }
+    return r;
+  };
+  float* out = a.reduced + (int64_t)o * a.row_stride;
+  if constexpr (SLICES == 1) {
+    // the block covers kTriSpan tokens, kTriThreads apart per thread
+    const int tend = min(a.row_stride, (int)(blockIdx.x + 1) * kTriSpan);
+    for (int t = blockIdx.x * kTriSpan + threadIdx.x; t < tend; t += kTriThreads) out[t] = reduce(t);
+  } else {
+    const int t = blockIdx.x * 64 + lane;
+    s_part[wid][lane] = reduce(t);
+    __syncthreads();
+    if (wid == 0 && t < a.row_stride) {
+      float v = s_part[0][lane];
+#pragma unroll
+      for (int w = 1; w < SLICES; ++w) {
+        const float z = s_part[w][lane];
+        if (z > v) v = z;
+      }
+      out[t] = v;
+    }
   }
-  a.reduced[(int64_t)o * a.row_stride + t] = r;
 }
 
 int tri_out_rows(int layers, int batch, int groups, int mode) {
@@ -163,7 +212,11 @@ hipError_t launch_tri(const TriArgs& a, hipStream_t st) {
   const int out_rows = tri_out_rows(a.layers, a.batch, a.groups, a.mode);
   if (members == 0 || a.row_stride == 0) return hipSuccess;
   tri_stats_kernel<<<members, kTriThreads, 0, st>>>(a);
-  tri_reduce_kernel<<<dim3((a.row_stride + kTriThreads - 1) / kTriThreads, out_rows), kTriThreads, 0, st>>>(a);
+  const int nm = a.mode == 0 ? 1 : (a.mode == 1 ? a.layers : a.layers * a.groups);
+  if (nm >= 16)
+    tri_reduce_kernel<4><<<dim3((a.row_stride + 63) / 64, out_rows), kTriThreads, 0, st>>>(a);
+  else
+    tri_reduce_kernel<1><<<dim3((a.row_stride + kTriSpan - 1) / kTriSpan, out_rows), kTriThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 
