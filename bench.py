@@ -49,6 +49,8 @@ def parse():
                         "selection (normalize, reduce, top-k) over 36 layers x 32 requests x 8 KV heads "
                         "x 4096 tokens, keeping 2048")
     p.add_argument("--tri-mode", choices=["union", "per_head", "per_layer_perhead"], default="union")
+    p.add_argument("--next-n", type=int, default=1,
+                   help="query tokens per request (multi-query decode: a token and its drafts)")
     p.add_argument("--index-dtype", choices=["bf16", "fp8"], default="bf16",
                    help="indexer K cache: bf16, or FP8 E4M3 codes with one float32 scale per row")
     p.add_argument("--hint", action="store_true",
@@ -147,7 +149,7 @@ def main():
     fp8 = args.index_dtype == "fp8"
     say(f"[bench] generating dsa_mla workload (B16, L65536, {args.index_dtype} indexer) ...")
     t0 = time.time()
-    w = synth.make_workload(4, index_dtype=args.index_dtype)
+    w = synth.make_workload(4, index_dtype=args.index_dtype, next_n=args.next_n)
     say(f"[bench] generated in {time.time() - t0:.1f}s; uploading {args.replicas} replicas")
     steps = [api.prepare(w, precision=api.FAST, device=dev, hint=args.hint) for _ in range(max(1, args.replicas))]
     torch.cuda.synchronize()
@@ -155,7 +157,8 @@ def main():
     B, L, P = w.batch, int(w.kv_lens[0]), w.page_size
     # bytes of indexer K read (fp8: the codes and one float32 scale per row)
     k_scored = B * L * (w.score_k.shape[-1] + 4 if fp8 else w.score_k.shape[-1] * 2)
-    k_gathered = B * w.topk * w.k.shape[-1] * 2           # selected latent rows (V is inside them)
+    # selected latent rows (V is inside them), per query token
+    k_gathered = B * args.next_n * w.topk * w.k.shape[-1] * 2
     alg_bytes = k_scored + k_gathered
 
     stream = torch.cuda.current_stream()
@@ -233,6 +236,7 @@ def main():
             "batch": B, "kv_len": L, "page_size": P, "topk": w.topk,
             "precision": "fast scores + exact band re-score (indices exact)",
             "input_replicas": args.replicas,
+            "next_n": args.next_n,
             "topk_hint": "previous step's selection, written back in place" if args.hint else None,
         },
         "algorithmic_bytes_per_step": alg_bytes,
@@ -258,9 +262,11 @@ def main():
         reqs = list(range(n))
         import dataclasses
 
+        nq = args.next_n
+        rows = [b * nq + j for b in reqs for j in range(nq)]   # the requests' query rows
         ws = dataclasses.replace(w, block_table=w.block_table[reqs], kv_lens=w.kv_lens[reqs],
-                                 score_q=w.score_q[reqs], head_weights=w.head_weights[reqs],
-                                 q=w.q[reqs])
+                                 score_q=w.score_q[rows], head_weights=w.head_weights[rows],
+                                 q=w.q[rows])
         reps = max(1, args.cpu_repeats)
         say(f"[bench] oracle on {n} request(s) x {reps} ...")
         t0 = time.perf_counter()
@@ -278,8 +284,8 @@ def main():
                       f"single-threaded, scaled to one step",
         }
         s0 = steps[(args.steps - 1) % len(steps)]
-        idx = s0.indices.cpu().numpy()[reqs]
-        got = s0.out.float().cpu().numpy()[reqs].astype(np.float64)
+        idx = s0.indices.cpu().numpy()[rows]
+        got = s0.out.float().cpu().numpy()[rows].astype(np.float64)
         err = np.linalg.norm(got - ref["out"], axis=-1) / np.linalg.norm(ref["out"], axis=-1)
         result["parity_sample"] = {"requests": reqs,
                                    "indices_equal": bool(np.array_equal(idx, ref["indices"])),

@@ -309,6 +309,16 @@ typedef struct sd_sparse_decode_args {
   int64_t hint_stride;
   int32_t* topk_writeback;       /* device [batch][groups][writeback_stride]   */
   int64_t writeback_stride;
+  /* multi-query decode (0 or 1: one query per request).  With next_n > 1
+   * every request carries next_n consecutive query tokens (a decode token
+   * and its draft tokens), the last next_n positions of its kv_len tokens;
+   * query j (0-based) sees tokens t < kv_len - (next_n - 1 - j) (causal).
+   * Each query token is scored, selected and attended on its own: score_q,
+   * head_weights, q, out, indices_out, counts_out, topk_hint and
+   * topk_writeback gain a next_n dimension after batch ([batch][next_n]...).
+   * ("Overlap DSA heuristic prev_topk write-back on the aux stream",
+   * Performance: the MTP=3 end-to-end setting; next_n <= 64.) */
+  int32_t next_n;
 } sd_sparse_decode_args;
 
 sd_status sd_sparse_decode_workspace_size(const sd_sparse_decode_args* args, size_t* bytes);

@@ -225,10 +225,28 @@ def tri_select(scores: np.ndarray, kv_lens, mode, k: int) -> dict:
     return {"z": z, "reduced": red, "indices": idx, "counts": cnt}
 
 
+def multi_query_rows(block_table, kv_lens, next_n: int):
+    """Multi-query decode as single-query rows: request b's query j (of
+    next_n, the last next_n positions of its kv_len tokens) is row
+    b*next_n + j, with request b's page table and the causal length
+    kv_len - (next_n - 1 - j) ("Overlap DSA heuristic prev_topk write-back on
+    the aux stream", Performance: the MTP decode setting)."""
+    bt = np.repeat(np.asarray(block_table), next_n, axis=0)
+    j = np.tile(np.arange(next_n), len(kv_lens))
+    kl = np.maximum(np.repeat(np.asarray(kv_lens, dtype=np.int64), next_n) - (next_n - 1 - j), 0)
+    return bt.astype(np.int32), kl.astype(np.int32)
+
+
 def sparse_decode(w) -> dict:
     """The whole path on a workload object (see top_sparse_decode_amd.synth):
     score -> top-k -> attention.  Returns scores, indices, counts and the
-    float64 output."""
+    float64 output.  A multi-query workload (next_n > 1) runs as its
+    single-query rows (multi_query_rows); outputs are request-major rows."""
+    n = int(getattr(w, "next_n", 1))
+    if n > 1:
+        import dataclasses
+        bt, kl = multi_query_rows(w.block_table, w.kv_lens, n)
+        w = dataclasses.replace(w, block_table=bt, kv_lens=kl, next_n=1)
     s = score(w.block_table, w.kv_lens, w.score_k, w.score_q, w.head_weights, w.mode,
               w.head_scale, w.max_kv_len, getattr(w, "score_k_scale", None))
     idx, cnt = topk(s, w.kv_lens, w.topk)

@@ -12,9 +12,11 @@ TOL = {"f32": 1e-5, "bf16": 2e-2}
 def subset(w, reqs):
     """The same workload restricted to requests `reqs` (pools shared)."""
     reqs = list(reqs)
+    n = int(getattr(w, "next_n", 1))
+    rows = [b * n + j for b in reqs for j in range(n)]   # query rows of the requests
     return dataclasses.replace(
-        w, block_table=w.block_table[reqs], kv_lens=w.kv_lens[reqs], score_q=w.score_q[reqs],
-        head_weights=None if w.head_weights is None else w.head_weights[reqs], q=w.q[reqs])
+        w, block_table=w.block_table[reqs], kv_lens=w.kv_lens[reqs], score_q=w.score_q[rows],
+        head_weights=None if w.head_weights is None else w.head_weights[rows], q=w.q[rows])
 
 
 def oracle_run(w, reqs=None):

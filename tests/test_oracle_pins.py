@@ -586,3 +586,44 @@ def test_tri_union_keeps_a_token_one_head_alone_wants():
     s[0, 0, 0, 777] = 40.0
     r = oracle.tri_select(s, np.array([2000], np.int32), "union", 16)
     assert 777 in r["indices"][0]
+
+
+# ---------------------------------------------------------------- multi-query decode
+
+def test_multi_query_last_row_is_single_query_decode_and_rows_are_causal():
+    import dataclasses
+    n = 3
+    w = synth.make_workload(4, batch=2, kv_len=[300, 130], topk=64, idx_heads=8, heads=4, next_n=n)
+    assert w.score_q.shape[0] == 2 * n and w.q.shape[0] == 2 * n
+    ref = oracle.sparse_decode(w)
+    # the last query token of each request sees the whole cache: it is the
+    # single-query decode of that request with its own query
+    last = [b * n + n - 1 for b in range(2)]
+    w1 = dataclasses.replace(w, score_q=w.score_q[last], head_weights=w.head_weights[last], q=w.q[last],
+                             next_n=1)
+    one = oracle.sparse_decode(w1)
+    assert np.array_equal(ref["indices"][last], one["indices"])
+    assert np.array_equal(ref["out"][last], one["out"])
+    # query j never selects a token at or past kv_len - (n - 1 - j) (its own
+    # later draft positions), and selects every token when that length <= k
+    for b, L in enumerate(w.kv_lens):
+        for j in range(n):
+            lim = int(L) - (n - 1 - j)
+            idx = ref["indices"][b * n + j, 0]
+            kept = idx[idx >= 0]
+            assert kept.max() < lim
+            assert ref["counts"][b * n + j, 0] == min(lim, 64)
+            if lim <= 64:
+                assert list(kept) == list(range(lim))
+
+
+def test_multi_query_rows_past_the_cache_are_empty():
+    n = 4
+    w = synth.make_workload(4, batch=2, kv_len=[2, 50], topk=16, idx_heads=8, heads=4, next_n=n)
+    ref = oracle.sparse_decode(w)
+    # request 0 has 2 tokens: its queries 0 and 1 see -1 and 0 tokens
+    for j, lim in enumerate([0, 0, 1, 2]):
+        assert ref["counts"][j, 0] == lim
+        if lim == 0:
+            assert np.all(ref["indices"][j] == -1)
+            assert np.all(ref["out"][j] == 0.0)

@@ -60,7 +60,7 @@ class sd_sparse_decode_args(ctypes.Structure):
                 ("indices_out", ctypes.c_void_p), ("counts_out", ctypes.c_void_p),
                 ("topk_hint", ctypes.c_void_p), ("hint_len", ctypes.c_int32),
                 ("hint_stride", ctypes.c_int64), ("topk_writeback", ctypes.c_void_p),
-                ("writeback_stride", ctypes.c_int64)]
+                ("writeback_stride", ctypes.c_int64), ("next_n", ctypes.c_int32)]
 
 
 EXPORTS = ["sd_sparse_score_paged", "sd_topk_workspace_size", "sd_topk_select", "sd_topk_select_hinted",
@@ -338,7 +338,8 @@ def prepare(w, precision: int = FAST, device="cuda", out_dtype=None, hint: bool 
         k, q = to_device_array(w.k, device), to_device_array(w.q, device)
     v = k if w.v is w.k else to_device_array(w.v, device)
     odt = out_dtype or (torch.float32 if w.out_dtype == "f32" else torch.bfloat16)
-    B, Hq = w.q.shape[0], w.q.shape[1]
+    n = int(getattr(w, "next_n", 1))
+    B, Hq = w.q.shape[0], w.q.shape[1]   # B = requests * next_n decode rows
     groups = w.score_k.shape[1]
     out = torch.empty((B, Hq, w.v_dim), dtype=odt, device=device)
     idx = torch.empty((B, groups, w.topk), dtype=torch.int32, device=device)
@@ -366,6 +367,7 @@ def prepare(w, precision: int = FAST, device="cuda", out_dtype=None, hint: bool 
     args.out_dtype = dtype_code(out)
     args.indices_out = idx.data_ptr()
     args.counts_out = cnt.data_ptr()
+    args.next_n = n
     hbuf = None
     if hint:
         hbuf = torch.full((B, groups, w.topk), -1, dtype=torch.int32, device=device)

@@ -365,6 +365,37 @@ sd_status plan_fused(const sd_sparse_decode_args* x, bool need_ptrs, FusedPlan* 
   return SD_OK;
 }
 
+// Multi-query decode: next_n query tokens per request become next_n decode
+// rows of one request each, row (b, j) seeing the first kv_len - (next_n - 1
+// - j) tokens through request b's page table.  *y is the single-query call
+// over those rows; with `expand` NULL its tables are placeholders (sizing).
+// *mq = the bytes of the expanded tables, placed after f->total.
+sd_status plan_multi_query(const sd_sparse_decode_args* x, bool need_ptrs, char* expand,
+                           sd_sparse_decode_args* y, FusedPlan* f, size_t* mq) {
+  if (!x) return fail(SD_ERR_INVALID_ARGUMENT, "args is NULL");
+  if (x->next_n < 0 || x->next_n > 64) return fail(SD_ERR_INVALID_ARGUMENT, "next_n %d outside [0, 64]", x->next_n);
+  *y = *x;
+  *mq = 0;
+  if (x->next_n <= 1) return plan_fused(y, need_ptrs, f);
+  sd_status st = check_pages(&x->pages, x->score_k.page_size);
+  if (st != SD_OK) return st;
+  if (need_ptrs && x->pages.batch > 0 && (!x->pages.block_table || !x->pages.kv_lens))
+    return fail(SD_ERR_INVALID_ARGUMENT, "block_table or kv_lens is NULL");
+  const int64_t rows = (int64_t)x->pages.batch * x->next_n;
+  if (rows > INT32_MAX / 2) return fail(SD_ERR_UNSUPPORTED, "too many decode rows");
+  static const int32_t kPlaceholder[1] = {0};
+  const size_t bt_bytes = align_up((size_t)rows * x->pages.max_pages * 4);
+  y->pages.batch = (int32_t)rows;
+  y->pages.block_table = expand ? reinterpret_cast<const int32_t*>(expand) : kPlaceholder;
+  y->pages.kv_lens = expand ? reinterpret_cast<const int32_t*>(expand + bt_bytes) : kPlaceholder;
+  y->next_n = 1;
+  st = plan_fused(y, need_ptrs, f);
+  if (st != SD_OK) return st;
+  *mq = bt_bytes + align_up((size_t)rows * 4);
+  return SD_OK;
+}
+
+
 }  // namespace
 
 // ====================================================================== ABI
@@ -516,24 +547,41 @@ sd_status sd_sparse_decode_attn(const sd_pages* pages, const void* q, sd_dtype q
 sd_status sd_sparse_decode_workspace_size(const sd_sparse_decode_args* args, size_t* bytes) {
   g_err.clear();
   if (!bytes) return fail(SD_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  sd_sparse_decode_args y;
   FusedPlan f;
-  sd_status st = plan_fused(args, false, &f);
+  size_t mq = 0;
+  sd_status st = plan_multi_query(args, false, nullptr, &y, &f, &mq);
   if (st != SD_OK) return st;
-  *bytes = f.total;
+  *bytes = f.total + mq;
   return SD_OK;
 }
 
-sd_status sd_sparse_decode(const sd_sparse_decode_args* x, void* workspace, size_t workspace_bytes,
+sd_status sd_sparse_decode(const sd_sparse_decode_args* args, void* workspace, size_t workspace_bytes,
                            hipStream_t stream) {
   g_err.clear();
+  sd_sparse_decode_args y;
   FusedPlan f;
-  sd_status st = plan_fused(x, true, &f);
+  size_t mq = 0;
+  sd_status st = plan_multi_query(args, true, nullptr, &y, &f, &mq);
   if (st != SD_OK) return st;
-  if (workspace_bytes < f.total || (f.total && !workspace))
-    return fail(SD_ERR_WORKSPACE_TOO_SMALL, "sparse_decode needs %zu workspace bytes", f.total);
+  if (workspace_bytes < f.total + mq || (f.total + mq && !workspace))
+    return fail(SD_ERR_WORKSPACE_TOO_SMALL, "sparse_decode needs %zu workspace bytes", f.total + mq);
   if (!aligned16(workspace)) return fail(SD_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
-  if (x->pages.batch == 0) return SD_OK;
+  if (args->pages.batch == 0) return SD_OK;
   char* ws = static_cast<char*>(workspace);
+  if (mq) {
+    // one decode row per (request, query token): the page tables repeated
+    // and the causal lengths, at the end of the workspace; then plan again
+    // with those pointers
+    if ((st = plan_multi_query(args, true, ws + f.total, &y, &f, &mq)) != SD_OK) return st;
+    const int n = args->next_n;
+    st = hip_status(sd::launch_mq_expand(args->pages.block_table, args->pages.kv_lens, args->pages.batch,
+                                         args->pages.max_pages, n, const_cast<int32_t*>(y.pages.block_table),
+                                         const_cast<int32_t*>(y.pages.kv_lens), stream),
+                    "multi-query expand");
+    if (st != SD_OK) return st;
+  }
+  const sd_sparse_decode_args* x = &y;
   float* scores = reinterpret_cast<float*>(ws + f.off_scores);
   float* bound = reinterpret_cast<float*>(ws + f.off_bound);
   int32_t* idx = x->indices_out ? x->indices_out : reinterpret_cast<int32_t*>(ws + f.off_idx);
@@ -597,6 +645,21 @@ namespace sd {
 __global__ void fill_f32_kernel(float* p, int64_t n, float v) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
+}
+
+__global__ void mq_expand_kernel(const int32_t* bt, const int32_t* kv_lens, int32_t max_pages, int32_t n,
+                                 int32_t* bt_out, int32_t* kv_out) {
+  const int r = blockIdx.x, b = r / n, j = r % n;
+  for (int i = threadIdx.x; i < max_pages; i += blockDim.x)
+    bt_out[(int64_t)r * max_pages + i] = bt[(int64_t)b * max_pages + i];
+  if (threadIdx.x == 0) kv_out[r] = max(kv_lens[b] - (n - 1 - j), 0);
+}
+
+hipError_t launch_mq_expand(const int32_t* bt, const int32_t* kv_lens, int32_t batch, int32_t max_pages,
+                            int32_t n, int32_t* bt_out, int32_t* kv_out, hipStream_t st) {
+  if (batch == 0) return hipSuccess;
+  mq_expand_kernel<<<batch * n, 256, 0, st>>>(bt, kv_lens, max_pages, n, bt_out, kv_out);
+  return hipGetLastError();
 }
 
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t st) {

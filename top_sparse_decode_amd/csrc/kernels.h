@@ -118,6 +118,9 @@ int attn_rows_per_split(const AttnArgs& a, bool mla);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
 
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t st);
+// multi-query decode: row b*n + j <- block-table row b, kv_len max(kv_lens[b] - (n - 1 - j), 0)
+hipError_t launch_mq_expand(const int32_t* bt, const int32_t* kv_lens, int32_t batch, int32_t max_pages,
+                            int32_t n, int32_t* bt_out, int32_t* kv_out, hipStream_t st);
 hipError_t launch_local_to_global(const int32_t* bt, int32_t max_pages, int32_t batch,
                                   int32_t page_size, int32_t num_pages, const int32_t* local,
                                   int32_t groups, int32_t k, int64_t* out, hipStream_t st);

@@ -141,6 +141,9 @@ class Workload:
     # FP8 indexer pools: score_k holds E4M3 codes (uint8) and this the row
     # scales [pages, Hs_kv, P] float32
     score_k_scale: Optional[np.ndarray] = None
+    # multi-query decode: next_n query tokens per request; score_q,
+    # head_weights and q then hold batch * next_n rows (request-major)
+    next_n: int = 1
 
     @property
     def batch(self) -> int:
@@ -246,10 +249,10 @@ DEFAULTS = {
     3: dict(batch=32, q_heads=32, kv_heads=8, head_dim=128, kv_len=8192, page_size=64, topk=2048,
             num_pages=None),
     4: dict(batch=16, idx_heads=64, idx_dim=128, kv_len=65536, page_size=64, topk=2048,
-            heads=128, latent=576, v_dim=512, num_pages=None, index_dtype="bf16"),
+            heads=128, latent=576, v_dim=512, num_pages=None, index_dtype="bf16", next_n=1),
     5: dict(batch=64, idx_heads=64, idx_dim=128, min_len=4096, max_len=131072, page_size=64,
             topk=2048, heads=128, latent=576, v_dim=512, bias_frac=0.01, bias=4.0,
-            slack=1.25, kv_lens=None, index_dtype="bf16"),
+            slack=1.25, kv_lens=None, index_dtype="bf16", next_n=1),
 }
 
 NAMES = {1: "tiny_f32", 2: "mha_bf16", 3: "gqa_bf16", 4: "dsa_mla", 5: "dsa_mla_mixed"}
@@ -367,8 +370,9 @@ def _build_dsa(seed, p, kv_lens, name, max_len=None, num_pages=None):
     if num_pages is not None:
         p["num_pages"] = num_pages
     P, B, max_len, max_pages, num_pages, bt, used, tails = _paged_common(seed, p, kv_lens, max_len)
-    qi = to_bf16_bits(rng(seed, _T_QI).standard_normal((B, Hi, Di), dtype=np.float32))
-    w = rng(seed, _T_W).random((B, Hi), dtype=np.float32)
+    n = int(p.get("next_n", 1))
+    qi = to_bf16_bits(rng(seed, _T_QI).standard_normal((B * n, Hi, Di), dtype=np.float32))
+    w = rng(seed, _T_W).random((B * n, Hi), dtype=np.float32)
     ki = _normal_pool(seed, _T_KI, (num_pages, 1, P, Di), True, used)
     if p.get("bias_frac"):
         # +bias on every indexer-key channel for a Bernoulli(bias_frac) subset of tokens
@@ -381,7 +385,7 @@ def _build_dsa(seed, p, kv_lens, name, max_len=None, num_pages=None):
             pg, sl = bt[b, hit // P], hit % P
             rows = bf16_bits_to_f32(ki[pg, 0, sl, :]) + np.float32(p["bias"])
             ki[pg, 0, sl, :] = to_bf16_bits(rows)
-    q = to_bf16_bits(rng(seed, _T_Q).standard_normal((B, H, Dl), dtype=np.float32))
+    q = to_bf16_bits(rng(seed, _T_Q).standard_normal((B * n, H, Dl), dtype=np.float32))
     lat = _normal_pool(seed, _T_LAT, (num_pages, 1, P, Dl), True, used)
     _apply_canaries(ki, used, tails)
     _apply_canaries(lat, used, tails)
@@ -394,7 +398,7 @@ def _build_dsa(seed, p, kv_lens, name, max_len=None, num_pages=None):
         raise ValueError(f"index_dtype must be bf16 or fp8, got {p['index_dtype']}")
     return Workload(name, seed, P, bt, kv_lens, max_len, ki, qi, w, "relu_weighted", 1.0,
                     p["topk"], q, lat, lat, p["v_dim"], 1.0 / math.sqrt(192.0), "bf16",
-                    meta=dict(p), score_k_scale=ki_scale)
+                    meta=dict(p), score_k_scale=ki_scale, next_n=n)
 
 
 def _build_dsa4(seed, p):
