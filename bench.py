@@ -44,10 +44,11 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-requests", type=int, default=16, help="requests in the oracle sample")
     p.add_argument("--cpu-repeats", type=int, default=2, help="passes of the oracle over the sample")
-    p.add_argument("--workload", choices=["dsa_mla", "triattention"], default="dsa_mla",
+    p.add_argument("--workload", choices=["dsa_mla", "triattention", "blocks"], default="dsa_mla",
                    help="dsa_mla: the fused decode step (default); triattention: one eviction-time "
                         "selection (normalize, reduce, top-k) over 36 layers x 32 requests x 8 KV heads "
-                        "x 4096 tokens, keeping 2048")
+                        "x 4096 tokens, keeping 2048; blocks: sparse MLA attention at 64K over 128 "
+                        "selected 16-token blocks per request")
     p.add_argument("--tri-mode", choices=["union", "per_head", "per_layer_perhead"], default="union")
     p.add_argument("--next-n", type=int, default=1,
                    help="query tokens per request (multi-query decode: a token and its drafts)")
@@ -130,6 +131,59 @@ def bench_triattention(args, api, torch, dev):
     print(json.dumps(result), flush=True)
 
 
+def bench_blocks(args, api, torch, dev, synth, np):
+    """Sparse MLA attention over block-granular selections: the config-4
+    latent cache (16 requests, 64K tokens), 128 distinct random 16-token
+    blocks per request (2048 tokens), against the same tokens given as a
+    token list."""
+    w = synth.make_workload(4)
+    step = api.prepare(w, precision=api.EXACT, device=dev)
+    kb, bs = 128, 16
+    rs = np.random.default_rng(16)
+    B = w.batch
+    blocks = np.stack([np.sort(rs.permutation(int(L) // bs)[:kb]) for L in w.kv_lens]).astype(np.int32)[:, None, :]
+    d_blk = torch.from_numpy(blocks).to(dev)
+    tok = torch.from_numpy((blocks[..., None] * bs + np.arange(bs)).reshape(B, 1, kb * bs).astype(np.int32)).to(dev)
+    Hq = w.q.shape[1]
+    nb = api.sparse_decode_attn_blocks_workspace_size(step.args.pages, Hq, step.args.k, w.v_dim, kb, bs)
+    nt = api.sparse_decode_attn_workspace_size(step.args.pages, Hq, step.args.k, w.v_dim, kb * bs)
+    wsb = torch.empty(nb, dtype=torch.uint8, device=dev)
+    wst = torch.empty(nt, dtype=torch.uint8, device=dev)
+    out = torch.empty_like(step.out)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+    ms_b = timed(lambda: api.sparse_decode_attn_blocks(step.args.pages, step.q, Hq, step.args.k, step.args.v,
+                                                       w.v_dim, d_blk, kb, bs, w.softmax_scale, out, wsb,
+                                                       stream=stream))
+    ms_t = timed(lambda: api.sparse_decode_attn(step.args.pages, step.q, Hq, step.args.k, step.args.v, w.v_dim,
+                                                tok, kb * bs, w.softmax_scale, out, wst, stream=stream))
+    gathered = B * kb * bs * w.k.shape[-1] * 2
+    gbps = gathered / (ms_b * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "block-granular sparse MLA attention calls/s",
+        "value": round(1000.0 / ms_b, 2), "unit": "calls/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_b, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (config-4 latent pool, seeded random blocks)",
+        "config": {"workload": "sparse MLA 128 heads x 576/512 over 128 blocks of 16 tokens per request, "
+                               "16 requests at 64K", "batch": B, "k_blocks": kb, "block_size": bs},
+        "token_list_ms": round(ms_t, 5),
+        "roofline": {"kernel": "whole call (block expansion, attention, combine)", "bound": "hbm",
+                     "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None, "bytes_per_launch": gathered},
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -146,6 +200,8 @@ def main():
     dev = "cuda:0"
     if args.workload == "triattention":
         return bench_triattention(args, api, torch, dev)
+    if args.workload == "blocks":
+        return bench_blocks(args, api, torch, dev, synth, np)
     fp8 = args.index_dtype == "fp8"
     say(f"[bench] generating dsa_mla workload (B16, L65536, {args.index_dtype} indexer) ...")
     t0 = time.time()

@@ -264,6 +264,27 @@ sd_status sd_sparse_decode_attn(const sd_pages* pages, const void* q, sd_dtype q
                                 float softmax_scale, void* out, sd_dtype out_dtype,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Attention over block-granular selections ("Unify sparse attention
+ * framework with clean backend interfaces", review of the runtime carrier:
+ * the indices travel with an indices block size).  Entry e >= 0 of a row
+ * names the tokens [e*block_size, (e+1)*block_size) that lie below kv_len;
+ * a negative entry names none.  The result is sd_sparse_decode_attn over the
+ * token list the entries name, in order (an entry given twice counts twice).
+ *   block_indices device [batch][num_kv_heads][k_blocks] int32
+ *   block_size    >= 1; k_blocks * block_size <= 2^24
+ *   workspace     device, at least sd_sparse_decode_attn_blocks_workspace_size()
+ * Other arguments and errors as sd_sparse_decode_attn. */
+sd_status sd_sparse_decode_attn_blocks_workspace_size(const sd_pages* pages, int32_t q_heads,
+                                                      const sd_pool* k_pool, int32_t v_dim,
+                                                      int32_t k_blocks, int32_t block_size,
+                                                      size_t* bytes);
+sd_status sd_sparse_decode_attn_blocks(const sd_pages* pages, const void* q, sd_dtype q_dtype,
+                                       int32_t q_heads, const sd_pool* k_pool, const sd_pool* v_pool,
+                                       int32_t v_dim, const int32_t* block_indices, int32_t k_blocks,
+                                       int32_t block_size, float softmax_scale, void* out,
+                                       sd_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
+
 /* ------------------------------------------------------------------ fused */
 
 /* One whole decode step: score -> top-k -> attention on one stream, with no

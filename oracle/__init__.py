@@ -201,6 +201,21 @@ def local_to_global(block_table, page_size: int, num_pages: int, local: np.ndarr
     return out
 
 
+def expand_blocks(block_indices: np.ndarray, kv_lens, block_size: int) -> np.ndarray:
+    """Block-granular selections as token lists: entry e >= 0 of a row
+    names tokens e*block_size .. e*block_size + block_size - 1 that lie below
+    the request's kv_len, -1 stands for the others and for negative entries
+    ("Unify sparse attention framework with clean backend interfaces": the
+    runtime carrier's indices block size).  [batch, groups, k_blocks] ->
+    [batch, groups, k_blocks * block_size]."""
+    bi = np.asarray(block_indices, dtype=np.int64)
+    B, G, kb = bi.shape
+    tok = bi[..., None] * block_size + np.arange(block_size)
+    L = np.asarray(kv_lens, dtype=np.int64)[:, None, None, None]
+    ok = (bi[..., None] >= 0) & (tok < L)
+    return np.where(ok, tok, -1).reshape(B, G, kb * block_size).astype(np.int32)
+
+
 TRI_MODES = {"per_layer_perhead": 0, "per_head": 1, "union": 2}
 
 

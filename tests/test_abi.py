@@ -140,6 +140,23 @@ def test_triattention_select_validation():
     assert f(None, 4, 0, 8, 4096, None, 1, 2048, None, None, None, None, 0, 0) == api.OK  # empty batch
 
 
+def test_block_attention_validation():
+    lib = _lib()
+    n = ctypes.c_size_t(0)
+    kp = _pool(D=576)
+    f = lib.sd_sparse_decode_attn_blocks_workspace_size
+    assert f(ctypes.byref(_pages()), 128, ctypes.byref(kp), 512, 64, 32, ctypes.byref(n)) == api.OK
+    assert n.value >= 2 * 64 * 32 * 4                                  # the expanded token lists
+    assert f(ctypes.byref(_pages()), 128, ctypes.byref(kp), 512, 64, 0, ctypes.byref(n)) == api.ERR_INVALID_ARGUMENT
+    assert f(ctypes.byref(_pages()), 128, ctypes.byref(kp), 512, 0, 32, ctypes.byref(n)) == api.ERR_INVALID_ARGUMENT
+    assert f(ctypes.byref(_pages()), 128, ctypes.byref(kp), 512, 1 << 13, 1 << 12, ctypes.byref(n)) == api.ERR_INVALID_ARGUMENT
+    g = lib.sd_sparse_decode_attn_blocks
+    assert f(ctypes.byref(_pages()), 128, ctypes.byref(kp), 512, 64, 32, ctypes.byref(n)) == api.OK
+    args = (ctypes.byref(_pages(max_kv_len=256)), 16384, api.BF16, 128, ctypes.byref(kp), ctypes.byref(kp), 512)
+    assert g(*args, None, 64, 32, 0.07, 24576, api.BF16, 4096, n.value, 0) == api.ERR_INVALID_ARGUMENT
+    assert g(*args, 20480, 64, 32, 0.07, 24576, api.BF16, 4096, n.value - 1, 0) == api.ERR_WORKSPACE_TOO_SMALL
+
+
 def test_topk_argument_validation():
     lib = _lib()
     f = lib.sd_topk_select

@@ -627,3 +627,26 @@ def test_multi_query_rows_past_the_cache_are_empty():
         if lim == 0:
             assert np.all(ref["indices"][j] == -1)
             assert np.all(ref["out"][j] == 0.0)
+
+
+# ---------------------------------------------------------------- block-granular indices
+
+def test_block_expansion_by_hand():
+    # block size 4, kv_len 10: entry 2 -> tokens 8, 9 (10, 11 lie past the
+    # cache), -1 -> nothing, entry 0 -> 0..3, entry 3 -> nothing (12..15)
+    tok = oracle.expand_blocks(np.array([[[2, -1, 0, 3]]]), np.array([10]), 4)
+    assert tok.tolist() == [[[8, 9, -1, -1, -1, -1, -1, -1, 0, 1, 2, 3, -1, -1, -1, -1]]]
+    # block size 1 is the token list itself, with the past-L entries dropped
+    one = oracle.expand_blocks(np.array([[[5, 0, 12, -3]]]), np.array([10]), 1)
+    assert one.tolist() == [[[5, 0, -1, -1]]]
+
+
+def test_block_attention_of_one_covering_block_is_dense_attention():
+    w = synth.make_workload(3, batch=2, kv_len=[70, 33], topk=16)
+    G = w.k.shape[1]
+    full = np.tile(np.arange(70, dtype=np.int32), (2, G, 1))
+    full[1, :, 33:] = -1
+    dense = oracle.attention(w.block_table, w.kv_lens, w.q, w.k, w.v, w.v_dim, full, w.softmax_scale)
+    blk = oracle.expand_blocks(np.zeros((2, G, 1), np.int32), w.kv_lens, 128)   # one block of 128
+    got = oracle.attention(w.block_table, w.kv_lens, w.q, w.k, w.v, w.v_dim, blk, w.softmax_scale)
+    assert np.array_equal(got, dense)

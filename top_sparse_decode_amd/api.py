@@ -67,6 +67,7 @@ EXPORTS = ["sd_sparse_score_paged", "sd_topk_workspace_size", "sd_topk_select", 
            "sd_sparse_decode_attn_workspace_size", "sd_sparse_decode_attn",
            "sd_sparse_decode_workspace_size", "sd_sparse_decode", "sd_local_to_global",
            "sd_triattention_select_workspace_size", "sd_triattention_select",
+           "sd_sparse_decode_attn_blocks_workspace_size", "sd_sparse_decode_attn_blocks",
            "sd_status_string", "sd_last_error", "sd_version"]
 
 _lib = None
@@ -97,6 +98,8 @@ def load(path: str = LIB_PATH):
         "sd_sparse_decode": [PA, P, SZ, P],
         "sd_local_to_global": [PP, I32, I32, P, I32, I32, P, P],
         "sd_triattention_select_workspace_size": [I32, I32, I32, I32, E, I32, ctypes.POINTER(SZ)],
+        "sd_sparse_decode_attn_blocks_workspace_size": [PP, I32, PL, I32, I32, I32, ctypes.POINTER(SZ)],
+        "sd_sparse_decode_attn_blocks": [PP, P, E, I32, PL, PL, I32, P, I32, I32, F, P, E, P, SZ, P],
         "sd_triattention_select": [P, I32, I32, I32, I32, P, E, I32, P, P, P, P, SZ, P],
     }
     for name, args in sig.items():
@@ -230,6 +233,26 @@ def sparse_decode_attn(pg: sd_pages, q, q_heads: int, k_pool: sd_pool, v_pool: s
                                       _ptr(indices), k_sel, softmax_scale, _ptr(out), dtype_code(out),
                                       _ptr(workspace), wb, _stream(stream))
     _check(rc, "sd_sparse_decode_attn")
+
+
+def sparse_decode_attn_blocks_workspace_size(pg: sd_pages, q_heads: int, k_pool: sd_pool, v_dim: int,
+                                             k_blocks: int, block_size: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().sd_sparse_decode_attn_blocks_workspace_size(ctypes.byref(pg), q_heads, ctypes.byref(k_pool),
+                                                               v_dim, k_blocks, block_size, ctypes.byref(n)),
+           "sd_sparse_decode_attn_blocks_workspace_size")
+    return n.value
+
+
+def sparse_decode_attn_blocks(pg: sd_pages, q, q_heads: int, k_pool: sd_pool, v_pool: sd_pool, v_dim: int,
+                              block_indices, k_blocks: int, block_size: int, softmax_scale: float, out,
+                              workspace, workspace_bytes: Optional[int] = None, stream=None):
+    wb = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
+    rc = load().sd_sparse_decode_attn_blocks(ctypes.byref(pg), _ptr(q), dtype_code(q), q_heads,
+                                             ctypes.byref(k_pool), ctypes.byref(v_pool), v_dim,
+                                             _ptr(block_indices), k_blocks, block_size, softmax_scale, _ptr(out),
+                                             dtype_code(out), _ptr(workspace), wb, _stream(stream))
+    _check(rc, "sd_sparse_decode_attn_blocks")
 
 
 def sparse_decode_workspace_size(args: sd_sparse_decode_args) -> int:

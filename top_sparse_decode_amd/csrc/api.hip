@@ -544,6 +544,55 @@ sd_status sd_sparse_decode_attn(const sd_pages* pages, const void* q, sd_dtype q
   return hip_status(sd::launch_attn(p.a, stream), "attention");
 }
 
+sd_status sd_sparse_decode_attn_blocks_workspace_size(const sd_pages* pages, int32_t q_heads,
+                                                      const sd_pool* k_pool, int32_t v_dim, int32_t k_blocks,
+                                                      int32_t block_size, size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(SD_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  if (k_blocks <= 0 || block_size <= 0 || (int64_t)k_blocks * block_size > (1 << 24))
+    return fail(SD_ERR_INVALID_ARGUMENT, "bad k_blocks %d / block_size %d", k_blocks, block_size);
+  if (!pages || !k_pool) return fail(SD_ERR_INVALID_ARGUMENT, "pages or k_pool is NULL");
+  AttnPlan p;
+  sd_status st = plan_attn(pages, nullptr, k_pool->dtype, q_heads, k_pool, k_pool, v_dim, nullptr,
+                           k_blocks * block_size, 1.0f, nullptr, SD_F32, false, &p);
+  if (st != SD_OK) return st;
+  *bytes = align_up((size_t)pages->batch * k_pool->num_kv_heads * k_blocks * block_size * 4) + p.ws_bytes;
+  return SD_OK;
+}
+
+sd_status sd_sparse_decode_attn_blocks(const sd_pages* pages, const void* q, sd_dtype q_dtype,
+                                       int32_t q_heads, const sd_pool* k_pool, const sd_pool* v_pool,
+                                       int32_t v_dim, const int32_t* block_indices, int32_t k_blocks,
+                                       int32_t block_size, float softmax_scale, void* out, sd_dtype out_dtype,
+                                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_err.clear();
+  if (k_blocks <= 0 || block_size <= 0 || (int64_t)k_blocks * block_size > (1 << 24))
+    return fail(SD_ERR_INVALID_ARGUMENT, "bad k_blocks %d / block_size %d", k_blocks, block_size);
+  if (!pages || !k_pool) return fail(SD_ERR_INVALID_ARGUMENT, "pages or k_pool is NULL");
+  if (pages->batch > 0 && !block_indices) return fail(SD_ERR_INVALID_ARGUMENT, "block_indices is NULL");
+  const int32_t k_sel = k_blocks * block_size;
+  const size_t tok_bytes = align_up((size_t)pages->batch * k_pool->num_kv_heads * k_sel * 4);
+  static const int32_t kIdx = 0;
+  AttnPlan p;
+  sd_status st = plan_attn(pages, q, q_dtype, q_heads, k_pool, v_pool, v_dim, &kIdx, k_sel, softmax_scale,
+                           out, out_dtype, true, &p);
+  if (st != SD_OK) return st;
+  if (workspace_bytes < tok_bytes + p.ws_bytes || !workspace)
+    return fail(SD_ERR_WORKSPACE_TOO_SMALL, "block attention needs %zu workspace bytes", tok_bytes + p.ws_bytes);
+  if (!aligned16(workspace)) return fail(SD_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  if (pages->batch == 0) return SD_OK;
+  // block entry i -> its tokens i*block_size + r (those below kv_len), -1 otherwise
+  char* ws = static_cast<char*>(workspace);
+  int32_t* tok = reinterpret_cast<int32_t*>(ws);
+  st = hip_status(sd::launch_expand_blocks(block_indices, pages->kv_lens, pages->batch, k_pool->num_kv_heads,
+                                           k_blocks, block_size, pages->max_kv_len, tok, stream),
+                  "block expand");
+  if (st != SD_OK) return st;
+  p.a.indices = tok;
+  bind_attn_ws(&p, ws + tok_bytes);
+  return hip_status(sd::launch_attn(p.a, stream), "attention");
+}
+
 sd_status sd_sparse_decode_workspace_size(const sd_sparse_decode_args* args, size_t* bytes) {
   g_err.clear();
   if (!bytes) return fail(SD_ERR_INVALID_ARGUMENT, "bytes is NULL");
@@ -659,6 +708,29 @@ hipError_t launch_mq_expand(const int32_t* bt, const int32_t* kv_lens, int32_t b
                             int32_t n, int32_t* bt_out, int32_t* kv_out, hipStream_t st) {
   if (batch == 0) return hipSuccess;
   mq_expand_kernel<<<batch * n, 256, 0, st>>>(bt, kv_lens, max_pages, n, bt_out, kv_out);
+  return hipGetLastError();
+}
+
+__global__ void expand_blocks_kernel(const int32_t* blocks, const int32_t* kv_lens, int32_t groups,
+                                     int32_t k_blocks, int32_t bs, int32_t cap, int64_t total, int32_t* tok) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // token slot
+  if (i >= total) return;
+  const int64_t per_row = (int64_t)k_blocks * bs;
+  const int64_t row = i / per_row;
+  const int slot = (int)(i % per_row);
+  const int b = (int)(row / groups);
+  const int L = clamp_len(kv_lens[b], cap);
+  const int e = blocks[row * k_blocks + slot / bs];
+  const int64_t t = (int64_t)e * bs + slot % bs;
+  tok[i] = (e >= 0 && t < L) ? (int32_t)t : -1;
+}
+
+hipError_t launch_expand_blocks(const int32_t* blocks, const int32_t* kv_lens, int32_t batch, int32_t groups,
+                                int32_t k_blocks, int32_t block_size, int32_t cap, int32_t* tok, hipStream_t st) {
+  const int64_t total = (int64_t)batch * groups * k_blocks * block_size;
+  if (total == 0) return hipSuccess;
+  expand_blocks_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(blocks, kv_lens, groups, k_blocks,
+                                                                        block_size, cap, total, tok);
   return hipGetLastError();
 }
 

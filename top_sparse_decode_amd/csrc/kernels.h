@@ -118,6 +118,9 @@ int attn_rows_per_split(const AttnArgs& a, bool mla);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
 
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t st);
+// block-granular selections: entry e of a row -> tokens e*bs .. e*bs+bs-1 below kv_len, else -1
+hipError_t launch_expand_blocks(const int32_t* blocks, const int32_t* kv_lens, int32_t batch, int32_t groups,
+                                int32_t k_blocks, int32_t block_size, int32_t cap, int32_t* tok, hipStream_t st);
 // multi-query decode: row b*n + j <- block-table row b, kv_len max(kv_lens[b] - (n - 1 - j), 0)
 hipError_t launch_mq_expand(const int32_t* bt, const int32_t* kv_lens, int32_t batch, int32_t max_pages,
                             int32_t n, int32_t* bt_out, int32_t* kv_out, hipStream_t st);
