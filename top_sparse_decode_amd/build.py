@@ -54,6 +54,13 @@ def build(verbose: bool = False) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
+    # every kernel the library launches must be defined in it (a template
+    # whose host side failed to instantiate leaves an undefined launch stub)
+    undef = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True).stdout
+    missing = [ln.split()[-1] for ln in undef.splitlines() if ln.split() and ln.split()[-1].startswith("_ZN2sd")]
+    if missing:
+        os.remove(tmp)
+        raise RuntimeError(f"libsparse_decode.so leaves library symbols undefined: {missing}")
     os.replace(tmp, LIB)
     for o in objs:
         os.remove(o)

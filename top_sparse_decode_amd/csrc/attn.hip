@@ -14,8 +14,6 @@
 #include "common.h"
 #include "kernels.h"
 
-#include <type_traits>
-
 namespace sd {
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -312,7 +310,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_mla_kernel(AttnArgs a) {
   // filled from the first query row instead).  Pad units read a harmless
   // 16 bytes of that row.  Every lane is in bounds; lanes past `units` do
   // nothing, and there is always an active lane.
-  auto dma64 = [&](int ub, int units, const char* base, auto&& rowoff) {
+  auto dma64 = [&](int ub, int units, const char* base, auto&& rowoff, bool stream) {
     const int rowA = ub / kMlaStride;            // the at most two rows it touches
     const int64_t oA = rowoff(rowA), oB = rowoff(rowA + 1);
     const int u = ub + lane;
@@ -320,7 +318,12 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_mla_kernel(AttnArgs a) {
     const int64_t ro = row == rowA ? oA : oB;
     const int sl = slot < kMlaUnits ? slot ^ mla_swz(row) : 0;  // data unit held at position `slot`
     const char* src = ro >= 0 ? base + ro + sl * 16 : qrow0 + sl * 16;
-    if (u < units) __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(uintptr_t)(kv0 + 16u * ub), 16, 0, 0);
+    if (u < units) {
+      if (stream)
+        __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(uintptr_t)(kv0 + 16u * ub), 16, 0, kLoadStream);
+      else
+        __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(uintptr_t)(kv0 + 16u * ub), 16, 0, kLoadReuse);
+    }
   };
 
   // ---- the block's query rows (heads 0 .. 32*NW-1) into LDS, same layout
@@ -328,7 +331,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_mla_kernel(AttnArgs a) {
   {
     constexpr int qunits = 32 * NW * kMlaStride;
     auto qoff = [&](int h) -> int64_t { return h < 32 * NW ? (int64_t)h * kMlaD * 2 : -1; };
-    for (int i = wid; i < (qunits + 63) / 64; i += NW) dma64(64 * i, qunits, qrow0, qoff);
+    for (int i = wid; i < (qunits + 63) / 64; i += NW)
+      dma64(64 * i, qunits, qrow0, qoff, false);
   }
   // byte offsets of rows lane and lane + 64 of the split (-1: not usable)
   int64_t off_lo, off_hi;
@@ -368,7 +372,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_mla_kernel(AttnArgs a) {
   };
   auto issue_chunk = [&](int j) {
     for (int i = wid; i < kMlaChunkInsts; i += NW)
-      dma64(j * kMlaChunkUnits + 64 * i, kMlaSplitRows * kMlaStride, kb, row_off);
+      dma64(j * kMlaChunkUnits + 64 * i, kMlaSplitRows * kMlaStride, kb, row_off, true);
   };
   issue_chunk(0);
   issue_chunk(1);

@@ -23,6 +23,14 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
+// Cache policy of global_load_lds for data read once per call (indexer K,
+// gathered latent rows): the non-temporal hint.  Those streams then do not
+// displace what is reused (queries, partials, scores) from the caches, and
+// dirty partial results of the previous step are not written back while the
+// next step streams.
+constexpr int kLoadStream = 2;
+constexpr int kLoadReuse = 0;
+
 // OCP FP8 E4M3 byte `B` of a 32-bit word -> binary32 (exact; codes 0x7F and
 // 0xFF decode to NaN).  gfx950's conversion implements the OCP encoding.
 template <int B>

@@ -388,7 +388,7 @@ __global__ __launch_bounds__(NW * 64) void score_dsa_kernel(ScoreArgs a, int ite
       const uint32_t dst = ring0 + (uint32_t)(stage * kTileBytes + h * 4096);
 #pragma unroll
       for (int c = 0; c < 4; ++c)
-        __builtin_amdgcn_global_load_lds(hb + vofs[c], (lds_ptr)(uintptr_t)(dst + c * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(hb + vofs[c], (lds_ptr)(uintptr_t)(dst + c * 1024), 16, 0, kLoadStream);
     }
   };
   // The first S - 1 tiles go out before the per-wave set-up below, whether
@@ -652,11 +652,12 @@ __global__ __launch_bounds__(NW * 64) void score_dsa_fp8_kernel(ScoreArgs a, int
       const char* hb = kbase + (int64_t)pgh[h] * a.page_stride + (int64_t)(t % ps) * ts;
 #pragma unroll
       for (int c = 0; c < 2; ++c)
-        __builtin_amdgcn_global_load_lds(hb + vofs[c], (lds_ptr)(uintptr_t)(dst + h * 2048 + c * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(hb + vofs[c], (lds_ptr)(uintptr_t)(dst + h * 2048 + c * 1024), 16, 0,
+                                         kLoadStream);
     }
     const int spg = shalf ? pgh[1] : pgh[0];
     const float* sp = a.k_scale + fp8_scale_index(spg, g, (t0 + 16 * shalf) % ps + col, a.num_kv_heads, ps);
-    __builtin_amdgcn_global_load_lds(sp, (lds_ptr)(uintptr_t)(dst + kTileBytes8), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(sp, (lds_ptr)(uintptr_t)(dst + kTileBytes8), 4, 0, kLoadStream);
   };
   static_for<0, S - 1>([&](auto j) { issue(decltype(j)::value, decltype(j)::value); });
 
