@@ -237,7 +237,7 @@ struct FusedPlan {
   bool fast;
   AttnPlan attn;
   int32_t groups;
-  size_t off_scores, off_bound, off_keys, off_idx, off_attn, total;
+  size_t off_scores, off_bound, off_slots, off_keys, off_idx, off_attn, total;
 };
 
 // Selection over finished scores: one launch for short exact rows, else
@@ -358,6 +358,8 @@ sd_status plan_fused(const sd_sparse_decode_args* x, bool need_ptrs, FusedPlan* 
   size_t off = 0;
   f->off_scores = off; off += sc;
   f->off_bound = off; off += align_up(rows * 4);
+  f->off_slots = off;
+  off += f->fast ? align_up(rows * (size_t)sd::score_fast_max_spans(x->pages.max_kv_len) * 16) : 0;
   f->off_keys = off; off += align_up(sd::select_workspace_bytes((int)rows, x->pages.max_kv_len));
   f->off_idx = off; off += x->indices_out ? 0 : align_up(rows * (size_t)x->topk * 4);
   f->off_attn = off; off += f->attn.ws_bytes;
@@ -635,7 +637,8 @@ sd_status sd_sparse_decode(const sd_sparse_decode_args* args, void* workspace, s
   float* bound = reinterpret_cast<float*>(ws + f.off_bound);
   int32_t* idx = x->indices_out ? x->indices_out : reinterpret_cast<int32_t*>(ws + f.off_idx);
 
-  // 0. selection statistics zeroed; 1. score (also the row min / max keys)
+  // 1. score (also the row min / max keys and the selection statistics
+  // cleared: by the fast scorer's blocks, else a small init pass first)
   sd::SelectArgs t{};
   t.scores = scores;
   t.batch = x->pages.batch;
@@ -654,10 +657,19 @@ sd_status sd_sparse_decode(const sd_sparse_decode_args* args, void* workspace, s
   sd::select_bind_workspace(&t, ws + f.off_keys);
   // short exact rows are selected in one launch that needs no statistics
   const bool short_rows = sd::select_short_path(t);
-  if (!short_rows && (st = hip_status(sd::launch_select_init(t, stream), "select_init")) != SD_OK) return st;
   f.score.scores = scores;
-  f.score.row_bound = f.fast ? bound : nullptr;
+  f.score.row_bound = nullptr;
   f.score.row_stats = short_rows ? nullptr : t.stats;
+  f.score.span_slots = nullptr;
+  if (f.fast && x->pages.max_kv_len > 0) {
+    // per-block slots that the histogram pass reduces into the row's keys and bound
+    f.score.span_slots = reinterpret_cast<int32_t*>(ws + f.off_slots);
+    t.span_slots = f.score.span_slots;
+    t.nspans = sd::score_fast_spans(f.score);
+  } else if (!short_rows) {
+    if ((st = hip_status(sd::launch_select_init(t, stream), "select_init")) != SD_OK) return st;
+    f.score.row_bound = f.fast ? bound : nullptr;
+  }
   st = run_score(f.score, f.fast ? SD_SCORE_FAST : SD_SCORE_EXACT, stream);
   if (st != SD_OK) return st;
   // 2. select (exactly, also from fast scores)

@@ -25,6 +25,11 @@ struct ScoreArgs {
   float* scores;     // [batch][num_kv_heads][max_kv_len]
   float* row_bound;  // [batch][num_kv_heads] or null
   int32_t* row_stats;  // selection statistics (min/max keys of finite scores) or null
+  // fused path (fast scorers): each block writes (kmin key, kmax key, bound
+  // bits, 0) to span_slots[row][blockIdx.x] instead of the row_stats / row_bound
+  // atomics, and clears its share of the row's row_stats (so no separate
+  // initialisation pass is needed)
+  int32_t* span_slots;
 };
 
 // Per-row selection statistics: [kmin key, kmax key, band count, cut (4
@@ -56,6 +61,10 @@ struct SelectArgs {
   // optional copy of this selection (the next step's hint), written by emit
   int32_t* writeback;   // [rows][wb_stride] or null
   int64_t wb_stride;
+  // fast scores from the fused path: the scorer's per-block slots; the
+  // histogram pass reduces them into stats[0..1] and row_bound
+  const int32_t* span_slots;  // [rows][nspans][4] or null
+  int32_t nspans;
 };
 
 struct AttnArgs {
@@ -99,6 +108,9 @@ bool score_exact_supported(int G);
 bool score_fast_supported(const ScoreArgs& a);
 hipError_t launch_score_exact(const ScoreArgs& a, hipStream_t st);
 hipError_t launch_score_fast(const ScoreArgs& a, hipStream_t st);
+// blocks per row of the fast scorer's grid, and an upper bound for any device
+int score_fast_spans(const ScoreArgs& a);
+int score_fast_max_spans(int max_kv_len);
 
 int select_max_row();
 size_t select_workspace_bytes(int rows, int row_stride);

@@ -247,9 +247,30 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "i"(N) : "memory");
 }
 
+// Fused-path bookkeeping of a fast-scorer block: its slot (min / max finite
+// score keys, bound) and its share of the row's selection statistics,
+// cleared (slot 7, the hint floor, to -inf).  Nothing else touches those
+// statistics until the histogram pass, a later launch.
+__device__ __forceinline__ void span_bookkeeping(const ScoreArgs& a, int nthreads, uint32_t kmin, uint32_t kmax,
+                                                 float bound, bool leader) {
+  int32_t* st = a.row_stats + (int64_t)blockIdx.y * kStatStride;
+  const int nx = gridDim.x;
+  const int per = (kStatStride + nx - 1) / nx;
+  const int i0 = blockIdx.x * per, i1 = min(kStatStride, i0 + per);
+  for (int i = i0 + threadIdx.x; i < i1; i += nthreads) st[i] = i == 7 ? (int32_t)0xFF800000u : 0;
+  if (leader) {
+    int32_t* sl = a.span_slots + ((int64_t)blockIdx.y * nx + blockIdx.x) * 4;
+    sl[0] = (int32_t)kmin;
+    sl[1] = (int32_t)kmax;
+    sl[2] = __float_as_int(bound);
+    sl[3] = 0;
+  }
+}
+
 // End of a fast-scorer block: the block's min / max finite score keys and
-// its bound (one atomic each), then the span's scores from the LDS staging
-// row (every token below L lies in a scored tile; the rest is -inf).
+// its bound (one atomic each, or the block's slot on the fused path), then
+// the span's scores from the LDS staging row (every token below L lies in a
+// scored tile; the rest is -inf).
 template <int NW>
 __device__ __forceinline__ void finish_span(const ScoreArgs& a, uint32_t (*s_red)[3], const float* s_out,
                                             float* row, int tb0, int tend, int L, float smin, float smax,
@@ -275,15 +296,22 @@ __device__ __forceinline__ void finish_span(const ScoreArgs& a, uint32_t (*s_red
       bmax = max(bmax, s_red[w][1]);
       bd = fmaxf(bd, __uint_as_float(s_red[w][2]));
     }
-    if (a.row_stats && bmin <= bmax) {
+    // 1e-3 relative slack covers the rounding of the bound's own evaluation,
+    // the absolute term any flushed subnormal.
+    bd = bd * 1.001f + 1e-30f;
+    if (!a.span_slots && a.row_stats && bmin <= bmax) {
       int32_t* stat = a.row_stats + (int64_t)blockIdx.y * kStatStride;
       atomicMin(reinterpret_cast<unsigned int*>(stat), bmin);
       atomicMax(reinterpret_cast<unsigned int*>(stat + 1), bmax);
     }
-    // 1e-3 relative slack covers the rounding of the bound's own evaluation,
-    // the absolute term any flushed subnormal.
-    if (a.row_bound)
-      atomicMax(reinterpret_cast<unsigned int*>(a.row_bound + blockIdx.y), __float_as_uint(bd * 1.001f + 1e-30f));
+    if (a.row_bound) atomicMax(reinterpret_cast<unsigned int*>(a.row_bound + blockIdx.y), __float_as_uint(bd));
+    s_red[0][0] = bmin;
+    s_red[0][1] = bmax;
+    s_red[0][2] = __float_as_uint(bd);
+  }
+  if (a.span_slots) {
+    __syncthreads();
+    span_bookkeeping(a, NW * 64, s_red[0][0], s_red[0][1], __uint_as_float(s_red[0][2]), threadIdx.x == 0);
   }
   for (int t = tb0 + threadIdx.x; t < tend; t += NW * 64) row[t] = t < L ? s_out[t - tb0] : -__builtin_inff();
 }
@@ -321,10 +349,10 @@ __global__ __launch_bounds__(NW * 64) void score_dsa_kernel(ScoreArgs a, int ite
   const int span = NW * kTileTok * iters;
   const int tb0 = blockIdx.x * span;
   float* row = a.scores + (int64_t)blockIdx.y * a.max_kv_len;
-  if (tb0 >= a.max_kv_len) return;
   const int tend = min(tb0 + span, a.max_kv_len);
   if (tb0 >= L) {  // nothing to score: fill -inf
     for (int t = tb0 + threadIdx.x; t < tend; t += NW * 64) row[t] = -__builtin_inff();
+    if (a.span_slots) span_bookkeeping(a, NW * 64, 0xFFFFFFFFu, 0u, 0.0f, threadIdx.x == 0);
     return;
   }
   const int ps = a.page_size;
@@ -586,10 +614,10 @@ __global__ __launch_bounds__(NW * 64) void score_dsa_fp8_kernel(ScoreArgs a, int
   const int span = NW * kTileTok * iters;
   const int tb0 = blockIdx.x * span;
   float* row = a.scores + (int64_t)blockIdx.y * a.max_kv_len;
-  if (tb0 >= a.max_kv_len) return;
   const int tend = min(tb0 + span, a.max_kv_len);
   if (tb0 >= L) {
     for (int t = tb0 + threadIdx.x; t < tend; t += NW * 64) row[t] = -__builtin_inff();
+    if (a.span_slots) span_bookkeeping(a, NW * 64, 0xFFFFFFFFu, 0u, 0.0f, threadIdx.x == 0);
     return;
   }
   const int ps = a.page_size;
@@ -864,6 +892,23 @@ int score_iters(const ScoreArgs& a, int nw, int maxit, int bpc) {
   return std::max(iters, 1);
 }
 
+}  // namespace
+
+int score_fast_spans(const ScoreArgs& a) {
+  const bool fp8 = a.dtype == 2;
+  const int nw = fp8 ? kScore8NW : kScoreNW;
+  const int iters = fp8 ? score_iters(a, kScore8NW, kScore8MaxIt, kScore8BlocksPerCU)
+                        : score_iters(a, kScoreNW, kScoreMaxIt, kScoreBlocksPerCU);
+  const int span = nw * kTileTok * iters;
+  return (a.max_kv_len + span - 1) / span;
+}
+
+int score_fast_max_spans(int max_kv_len) {  // one tile per wave, the smaller block
+  const int span = std::min(kScoreNW, kScore8NW) * kTileTok;
+  return (max_kv_len + span - 1) / span;
+}
+
+namespace {
 template <int MT>
 hipError_t launch_dsa(const ScoreArgs& a, hipStream_t st) {
   const unsigned rows = (unsigned)(a.batch * a.num_kv_heads);

@@ -578,12 +578,11 @@ struct RowView {
 
 // The row's histogram range [lo, hi]: the min / max finite score, with lo
 // raised to the floor a hint certified (no token below it can be selected).
-__device__ __forceinline__ RowView make_view(const SelectArgs& a, int row, float floor) {
+__device__ __forceinline__ RowView view_of_keys(const SelectArgs& a, int row, uint32_t kmin, uint32_t kmax,
+                                                float floor) {
   const int b = row / a.groups;
   RowView v;
   v.L = clamp_len(a.kv_lens[b], a.row_stride);
-  const int32_t* st = a.stats + (int64_t)row * kStatStride;
-  const uint32_t kmin = (uint32_t)st[0], kmax = (uint32_t)st[1];
   v.any_finite = kmin <= kmax;
   v.lo = v.any_finite ? key_to_score(kmin) : 0.0f;
   v.hi = v.any_finite ? key_to_score(kmax) : 0.0f;
@@ -591,6 +590,10 @@ __device__ __forceinline__ RowView make_view(const SelectArgs& a, int row, float
   // identical to the one-block path when there is no floor: same bins, same classes
   v.fscale = v.hi > v.lo ? (float)((double)kBins / ((double)v.hi - (double)v.lo)) : 0.0f;
   return v;
+}
+__device__ __forceinline__ RowView make_view(const SelectArgs& a, int row, float floor) {
+  const int32_t* st = a.stats + (int64_t)row * kStatStride;
+  return view_of_keys(a, row, (uint32_t)st[0], (uint32_t)st[1], floor);
 }
 __device__ __forceinline__ RowView row_view(const SelectArgs& a, int row) {
   return make_view(a, row, __int_as_float(a.stats[(int64_t)row * kStatStride + 7]));
@@ -764,7 +767,7 @@ __device__ __forceinline__ int chunk_excl_max(int v, int* red) {
 // larger than every valid entry before it, so an ascending hint (what the
 // write-back produces) counts in full and any other hint counts a subset of
 // distinct positions.  Every block of the row computes the same value.
-__device__ float hint_floor(const SelectArgs& a, int row, int L, int* red) {
+__device__ float hint_floor(const SelectArgs& a, int row, int L, float bound, int* red) {
   const int tid = threadIdx.x;
   const int n = a.hint_len;
   const int per = (n + kChunkThreads - 1) / kChunkThreads;  // a contiguous run per thread
@@ -798,21 +801,72 @@ __device__ float hint_floor(const SelectArgs& a, int row, int L, int* red) {
   __syncthreads();
   if (distinct < a.k || !__builtin_isfinite(m)) return -__builtin_inff();
   if (!a.row_bound) return m;
-  const double f = (double)m - 2.0 * (double)a.row_bound[row];
+  const double f = (double)m - 2.0 * (double)bound;
   float fl = (float)f;
   if ((double)fl > f) fl = next_down(fl);
   return fl;
 }
 
+// The fused path's fast scorer leaves per-block slots instead of the row's
+// min / max keys and bound: every block reduces them (a few dozen at most)
+// and block 0 publishes the result for the later passes.
+struct RowKeys {
+  uint32_t kmin, kmax;
+  float bound;
+};
+__device__ RowKeys reduce_span_slots(const SelectArgs& a, int row, uint32_t (*red)[kSelWaves]) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u, bd = 0u;  // bound bits: non-negative floats order as integers
+  const int32_t* sl = a.span_slots + (int64_t)row * a.nspans * 4;
+  for (int i = tid; i < a.nspans; i += kChunkThreads) {
+    const int4 e = *reinterpret_cast<const int4*>(sl + 4 * i);
+    kmin = min(kmin, (uint32_t)e.x);
+    kmax = max(kmax, (uint32_t)e.y);
+    bd = max(bd, (uint32_t)e.z);
+  }
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
+  bd = wave_max_u32(bd);
+  if (lane == 0) {
+    red[0][wid] = kmin;
+    red[1][wid] = kmax;
+    red[2][wid] = bd;
+  }
+  __syncthreads();
+  RowKeys r{red[0][0], red[1][0], 0.0f};
+  bd = red[2][0];
+  for (int w = 1; w < kSelWaves; ++w) {
+    r.kmin = min(r.kmin, red[0][w]);
+    r.kmax = max(r.kmax, red[1][w]);
+    bd = max(bd, red[2][w]);
+  }
+  r.bound = __uint_as_float(bd);
+  __syncthreads();
+  return r;
+}
+
 __global__ __launch_bounds__(kChunkThreads) void select_hist_kernel(SelectArgs a) {
   __shared__ int hist[kBins];
   __shared__ int red[kSelWaves];
+  __shared__ uint32_t red3[3][kSelWaves];
   const int row = blockIdx.y, c = blockIdx.x;
-  RowView v = row_view(a, row);
+  int32_t* st = a.stats + (int64_t)row * kStatStride;
+  RowKeys r;
+  if (a.span_slots) {
+    r = reduce_span_slots(a, row, red3);
+    if (c == 0 && threadIdx.x == 0) {
+      st[0] = (int32_t)r.kmin;
+      st[1] = (int32_t)r.kmax;
+      a.row_bound[row] = r.bound;
+    }
+  } else {
+    r = RowKeys{(uint32_t)st[0], (uint32_t)st[1], a.row_bound ? a.row_bound[row] : 0.0f};
+  }
+  RowView v = view_of_keys(a, row, r.kmin, r.kmax, __int_as_float(st[7]));
   if (v.L <= a.k || c * kSelChunk >= v.L || !v.any_finite) return;
   if (a.hint) {
-    const float floor = hint_floor(a, row, v.L, red);
-    v = make_view(a, row, floor);
+    const float floor = hint_floor(a, row, v.L, r.bound, red);
+    v = view_of_keys(a, row, r.kmin, r.kmax, floor);
     if (c == 0 && threadIdx.x == 0) a.stats[(int64_t)row * kStatStride + 7] = __float_as_int(floor);
   }
   for (int i = threadIdx.x; i < kBins; i += kChunkThreads) hist[i] = 0;
