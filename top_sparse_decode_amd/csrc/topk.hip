@@ -604,6 +604,28 @@ __device__ __forceinline__ int bin_of_v(const RowView& v, float x) {
   return (f >= (float)(kBins - 1) || f != f) ? kBins - 1 : (int)f;
 }
 
+// The passes below issue every load that does not depend on the row's
+// statistics first (scores, histogram, ...), so a block waits on memory once
+// rather than once per dependent step: load8_raw reads this thread's 8
+// tokens within the row's stride before kv_len is known, mask8 then marks
+// those past kv_len NaN.
+__device__ __forceinline__ void load8_raw(const float* s, int t0, int n, float (&x)[kPerThread]) {
+  if (t0 + kPerThread <= n && ((reinterpret_cast<uintptr_t>(s + t0) & 15) == 0)) {
+    const float4 p = *reinterpret_cast<const float4*>(s + t0);
+    const float4 q = *reinterpret_cast<const float4*>(s + t0 + 4);
+    x[0] = p.x; x[1] = p.y; x[2] = p.z; x[3] = p.w;
+    x[4] = q.x; x[5] = q.y; x[6] = q.z; x[7] = q.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) x[e] = t0 + e < n ? s[t0 + e] : __builtin_nanf("");
+  }
+}
+__device__ __forceinline__ void mask8(int t0, int L, float (&x)[kPerThread]) {
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e)
+    if (t0 + e >= L) x[e] = __builtin_nanf("");
+}
+
 // this thread's 8 contiguous tokens of chunk c (NaN past kv_len)
 __device__ __forceinline__ void load8(const float* s, int t0, int L, float (&x)[kPerThread]) {
   if (t0 + kPerThread <= L && ((reinterpret_cast<uintptr_t>(s + t0) & 15) == 0)) {
@@ -645,12 +667,17 @@ struct RowCut {
   float band_lo, band_hi;
 };
 
-__device__ RowCut row_cut(const SelectArgs& a, int row, const RowView& v, ChunkShared& sh, bool fast) {
-  const int32_t* gh = a.stats + (int64_t)row * kStatStride + 8;
+constexpr int kBinsPerThread = kBins / kChunkThreads;
+static_assert(kBins % kChunkThreads == 0, "histogram bins per thread");
+
+// hb: this thread's bins tid + j * kChunkThreads of the row's histogram
+__device__ RowCut row_cut(const SelectArgs& a, int row, const RowView& v, ChunkShared& sh, bool fast,
+                          const int (&hb)[kBinsPerThread]) {
   int part = 0;
-  for (int i = threadIdx.x; i < kBins; i += kChunkThreads) {
-    const int h = v.any_finite ? gh[i] : 0;
-    sh.hist[i] = h;
+#pragma unroll
+  for (int j = 0; j < kBinsPerThread; ++j) {
+    const int h = v.any_finite ? hb[j] : 0;
+    sh.hist[threadIdx.x + j * kChunkThreads] = h;
     part += h;
   }
   RowCut c;
@@ -851,6 +878,9 @@ __global__ __launch_bounds__(kChunkThreads) void select_hist_kernel(SelectArgs a
   __shared__ uint32_t red3[3][kSelWaves];
   const int row = blockIdx.y, c = blockIdx.x;
   int32_t* st = a.stats + (int64_t)row * kStatStride;
+  float x[kPerThread];
+  const int t0 = c * kSelChunk + kPerThread * threadIdx.x;
+  load8_raw(a.scores + (int64_t)row * a.row_stride, t0, a.row_stride, x);
   RowKeys r;
   if (a.span_slots) {
     r = reduce_span_slots(a, row, red3);
@@ -871,9 +901,7 @@ __global__ __launch_bounds__(kChunkThreads) void select_hist_kernel(SelectArgs a
   }
   for (int i = threadIdx.x; i < kBins; i += kChunkThreads) hist[i] = 0;
   __syncthreads();
-  float x[kPerThread];
-  const int t0 = c * kSelChunk + kPerThread * threadIdx.x;
-  load8(a.scores + (int64_t)row * a.row_stride, t0, v.L, x);
+  mask8(t0, v.L, x);
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
     const bool fin = __builtin_isfinite(x[e]) && x[e] >= v.lo;
@@ -895,11 +923,34 @@ __global__ __launch_bounds__(kChunkThreads) void select_classify_kernel(SelectAr
   // K rows of band tokens being re-scored: bf16 rows as they are (256 bytes),
   // fp8 rows dequantized to binary32 (512 bytes)
   __shared__ __attribute__((aligned(16))) float s_krow[kStageRows][128];
+  __shared__ int s_bpage[FAST ? kSelChunk : 1];      // page of each band token
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int row = blockIdx.y, c = blockIdx.x;
+  const int g = row % a.groups, b = row / a.groups;
+  const ScoreArgs& sa = a.score;
+  const int G = FAST ? sa.q_heads / sa.num_kv_heads : 0;  // <= 64 on the fast path
+  // loads that do not depend on the cut, all in flight together
+  float x[kPerThread];
+  const int t0 = c * kSelChunk + kPerThread * tid;
+  load8_raw(a.scores + (int64_t)row * a.row_stride, t0, a.row_stride, x);
+  int hb[kBinsPerThread];
+  {
+    const int32_t* gh = a.stats + (int64_t)row * kStatStride + 8;
+#pragma unroll
+    for (int j = 0; j < kBinsPerThread; ++j) hb[j] = gh[tid + j * kChunkThreads];
+  }
+  // fast scores: the page of this thread's eight tokens (one page: the fast
+  // path's page size is a multiple of 16)
+  int tpage = -1;
+  if constexpr (FAST) {
+    const int pi = t0 / sa.page_size;
+    if (t0 < a.row_stride && pi < sa.max_pages) tpage = sa.block_table[(int64_t)b * sa.max_pages + pi];
+  }
   const RowView v = row_view(a, row);
   if (v.L <= a.k || c * kSelChunk >= v.L) return;
-  const RowCut cut = row_cut(a, row, v, sh, FAST);
+  mask8(t0, v.L, x);
+  const RowCut cut = row_cut(a, row, v, sh, FAST, hb);
+
   if (tid == 0) s_nband = 0;
   if (c == 0 && tid == 0) {  // for the emit kernel (identical in every block)
     int32_t* stc = a.stats + (int64_t)row * kStatStride;
@@ -909,9 +960,6 @@ __global__ __launch_bounds__(kChunkThreads) void select_classify_kernel(SelectAr
     stc[6] = __float_as_int(cut.band_hi);
   }
   __syncthreads();
-  float x[kPerThread];
-  const int t0 = c * kSelChunk + kPerThread * tid;
-  load8(a.scores + (int64_t)row * a.row_stride, t0, v.L, x);
   int n_in = 0, n_neg = 0;
   uint32_t* keys = reinterpret_cast<uint32_t*>(a.keys) + (int64_t)row * a.row_stride;
   int32_t* st = a.stats + (int64_t)row * kStatStride;
@@ -925,6 +973,7 @@ __global__ __launch_bounds__(kChunkThreads) void select_classify_kernel(SelectAr
       const int i = atomicAdd(&s_nband, 1);
       s_band[i] = t0 + e;
       s_bkey[i] = score_key(x[e]);  // fast scores: replaced by the exact key below
+      if constexpr (FAST) s_bpage[i] = tpage;
     }
   }
   n_in = chunk_sum_i(n_in, sh.redi);
@@ -941,16 +990,12 @@ __global__ __launch_bounds__(kChunkThreads) void select_classify_kernel(SelectAr
     // query row in registers, and a wave scores one token in the library's
     // exact order (lane h: dot_h left to right; then the head terms in head
     // order), bit-identical to the exact scorer.
-    const ScoreArgs& sa = a.score;
-    const int g = row % a.groups, b = row / a.groups;
-    const int G = sa.q_heads / sa.num_kv_heads;  // <= 64 on the fast path
     const bool hact = lane < G;
     uint4 qr[16];
     float wh = 0.0f;
     if (hact) {
-      const uint16_t* qh = reinterpret_cast<const uint16_t*>(sa.q) + ((int64_t)b * sa.q_heads + g * G + lane) * 128;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) qr[i] = *reinterpret_cast<const uint4*>(qh + 8 * i);
+      for (int i = 0; i < 16; ++i) qr[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(sa.q) + ((int64_t)b * sa.q_heads + g * G + lane) * 128 + 8 * i);
       wh = sa.head_weights[(int64_t)b * sa.q_heads + g * G + lane];
     }
     const bool fp8 = sa.dtype == 2;
@@ -960,7 +1005,7 @@ __global__ __launch_bounds__(kChunkThreads) void select_classify_kernel(SelectAr
         const int i = tid >> 4, part = tid & 15;  // 16 threads per row
         if (i < np) {
           const int t = s_band[p0 + i];
-          const int page = sa.block_table[(int64_t)b * sa.max_pages + t / sa.page_size];
+          const int page = s_bpage[p0 + i];
           const int slot = t % sa.page_size;
           const int64_t koff = (int64_t)page * sa.page_stride + (int64_t)g * sa.head_stride +
                                (int64_t)slot * sa.token_stride;
@@ -1050,9 +1095,20 @@ __global__ __launch_bounds__(kChunkThreads) void select_emit_kernel(SelectArgs a
   __shared__ __attribute__((aligned(16))) float s_terms[kSelWaves][kWave];
   const int tid = threadIdx.x;
   const int row = blockIdx.y, c = blockIdx.x;
+  const int cstart = c * kSelChunk;
+  // loads that do not depend on the row's statistics, in flight together
+  float x[kPerThread];
+  const int t0 = cstart + kPerThread * tid;
+  load8_raw(a.scores + (int64_t)row * a.row_stride, t0, a.row_stride, x);
+  const int32_t* cc = a.chunk_counts + (int64_t)row * a.nchunks * 2;
+  int2 ccv[2] = {};  // chunk tid and tid + 64 (wave 0)
+  if (tid < kWave) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      if (tid + kWave * j < a.nchunks) ccv[j] = *reinterpret_cast<const int2*>(cc + 2 * (tid + kWave * j));
+  }
   const RowView v = row_view(a, row);
   const int k = a.k;
-  const int cstart = c * kSelChunk;
   if (v.L <= k) {  // every token kept (dense-equivalent)
     for (int t = cstart + tid; t < min(v.L, cstart + kSelChunk); t += kChunkThreads) put_index(a, row, t, t);
     if (c == 0) {
@@ -1072,17 +1128,19 @@ __global__ __launch_bounds__(kChunkThreads) void select_emit_kernel(SelectArgs a
   // per-chunk counts (kept-for-sure, -inf) before this chunk and in total:
   // wave 0 reduces them, LDS hands them to the block
   const int nch = (v.L + kSelChunk - 1) / kSelChunk;
-  const int32_t* cc = a.chunk_counts + (int64_t)row * a.nchunks * 2;
   if (tid < kWave) {
     int in_total = 0, in_before = 0, neg_before = 0;
-    for (int i = tid; i < nch; i += kWave) {
-      const int ci = cc[2 * i], cn = cc[2 * i + 1];
-      in_total += ci;
+    auto add = [&](int i, int2 e) {
+      in_total += e.x;
       if (i < c) {
-        in_before += ci;
-        neg_before += cn;
+        in_before += e.x;
+        neg_before += e.y;
       }
-    }
+    };
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      if (tid + kWave * j < nch) add(tid + kWave * j, ccv[j]);
+    for (int i = tid + 2 * kWave; i < nch; i += kWave) add(i, *reinterpret_cast<const int2*>(cc + 2 * i));
     in_total = wave_sum(in_total);
     in_before = wave_sum(in_before);
     neg_before = wave_sum(neg_before);
@@ -1145,9 +1203,7 @@ __global__ __launch_bounds__(kChunkThreads) void select_emit_kernel(SelectArgs a
   }
   chosen_before = chunk_sum_i(chosen_before, u.e.cs.redi);  // (barrier: bitmap complete)
 
-  float x[kPerThread];
-  const int t0 = cstart + kPerThread * tid;
-  load8(a.scores + (int64_t)row * a.row_stride, t0, v.L, x);
+  mask8(t0, v.L, x);
   uint32_t keep = 0;
   int nkeep = 0, nneg = 0;
 #pragma unroll
