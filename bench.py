@@ -44,11 +44,13 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-requests", type=int, default=16, help="requests in the oracle sample")
     p.add_argument("--cpu-repeats", type=int, default=2, help="passes of the oracle over the sample")
-    p.add_argument("--workload", choices=["dsa_mla", "triattention", "blocks"], default="dsa_mla",
+    p.add_argument("--workload", choices=["dsa_mla", "triattention", "blocks", "gqa"], default="dsa_mla",
                    help="dsa_mla: the fused decode step (default); triattention: one eviction-time "
                         "selection (normalize, reduce, top-k) over 36 layers x 32 requests x 8 KV heads "
                         "x 4096 tokens, keeping 2048; blocks: sparse MLA attention at 64K over 128 "
-                        "selected 16-token blocks per request")
+                        "selected 16-token blocks per request; gqa: the fused step on the Qwen3-8B-shaped "
+                        "GQA workload (32 requests, 32 query / 8 KV heads x 128, 8192 tokens, top-k 2048 "
+                        "per KV head, exact scores)")
     p.add_argument("--tri-mode", choices=["union", "per_head", "per_layer_perhead"], default="union")
     p.add_argument("--next-n", type=int, default=1,
                    help="query tokens per request (multi-query decode: a token and its drafts)")
@@ -184,6 +186,61 @@ def bench_blocks(args, api, torch, dev, synth, np):
     }), flush=True)
 
 
+def bench_gqa(args, api, torch, dev, synth):
+    """The fused step on the Qwen3-8B-shaped GQA workload: 32 requests, 32
+    query heads over 8 KV heads of 128 dims, 8192 tokens in 64-token pages,
+    score = mean over the 4 query heads of a KV head, top 2048 per KV head,
+    softmax attention per query head over the selected K/V rows.  Scores are
+    computed in the exact order (the vector scorer: one lane per token); the
+    roofline entry is that scorer alone."""
+    say("[bench] generating gqa workload (B32, 32q/8kv x 128, L8192) ...")
+    w = synth.make_workload(3)
+    step = api.prepare(w, precision=api.EXACT, device=dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    B, Hq = w.q.shape[0], w.q.shape[1]
+    Hkv, D = w.k.shape[1], w.k.shape[-1]
+    L = int(w.kv_lens[0])
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+    ms = timed(lambda: step.run(stream))
+    sc = torch.empty((B, Hkv, w.max_kv_len), dtype=torch.float32, device=dev)
+    bound = torch.zeros((B, Hkv), dtype=torch.float32, device=dev)
+    ms_sc = timed(lambda: api.sparse_score_paged(step.args.pages, step.args.score_k, step.score_q, Hq, None,
+                                                 api.MODES[w.mode], w.head_scale, api.EXACT, sc, bound, stream))
+    k_scored = B * Hkv * L * D * 2
+    gathered = B * Hkv * w.topk * D * 2 * 2  # selected K and V rows
+    alg = k_scored + gathered
+    sc_gbps = k_scored / (ms_sc * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "sparse decode steps/s, Qwen3-8B-shaped GQA 8K ctx top-k 2048 per KV head",
+        "value": round(1000.0 / ms, 2), "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) K/V with log-uniform "
+        "per-channel scales, one replica: 537 MB of K per step exceeds the last-level cache)",
+        "config": {"workload": "gqa: 32 requests, 32 query heads over 8 KV heads x 128, kv_len 8192, page 64, "
+                               "score = mean over a KV head's 4 query heads, top-k 2048 per KV head, exact "
+                               "scores", "batch": B, "kv_len": L, "page_size": w.page_size, "topk": w.topk},
+        "algorithmic_bytes_per_step": alg,
+        "step_gbps": round(alg / (ms * 1e-3) / 1e9, 1),
+        "step_frac_of_hbm_peak": round(alg / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "roofline": {"kernel": "score_exact_kernel (GROUP_MEAN, bf16)", "bound": "hbm",
+                     "achieved": round(sc_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(sc_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "avg_launch_us": round(ms_sc * 1e3, 2), "bytes_per_launch": k_scored},
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -202,6 +259,8 @@ def main():
         return bench_triattention(args, api, torch, dev)
     if args.workload == "blocks":
         return bench_blocks(args, api, torch, dev, synth, np)
+    if args.workload == "gqa":
+        return bench_gqa(args, api, torch, dev, synth)
     fp8 = args.index_dtype == "fp8"
     say(f"[bench] generating dsa_mla workload (B16, L65536, {args.index_dtype} indexer) ...")
     t0 = time.time()

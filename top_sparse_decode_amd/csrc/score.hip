@@ -59,16 +59,19 @@ __device__ __forceinline__ void unpack_unit(const uint4& u, float (&v)[8]) {
 // One 16-byte unit of a K row as binary32 values; an fp8 unit is dequantized
 // with its row scale.
 template <typename KT>
-__device__ __forceinline__ void load_k_unit(const KT* p, float scale, float (&v)[Elems<KT>::kPerUnit]) {
-  unpack_unit(*reinterpret_cast<const uint4*>(p), v);
+__device__ __forceinline__ void cvt_k_unit(const uint4& u, float scale, float (&v)[Elems<KT>::kPerUnit]) {
+  unpack_unit(u, v);
 }
 template <>
-__device__ __forceinline__ void load_k_unit<uint8_t>(const uint8_t* p, float scale, float (&v)[16]) {
-  const uint4 u = *reinterpret_cast<const uint4*>(p);
+__device__ __forceinline__ void cvt_k_unit<uint8_t>(const uint4& u, float scale, float (&v)[16]) {
   fp8x4_dequant(u.x, scale, v);
   fp8x4_dequant(u.y, scale, v + 4);
   fp8x4_dequant(u.z, scale, v + 8);
   fp8x4_dequant(u.w, scale, v + 12);
+}
+template <typename KT>
+__device__ __forceinline__ void load_k_unit(const KT* p, float scale, float (&v)[Elems<KT>::kPerUnit]) {
+  cvt_k_unit<KT>(*reinterpret_cast<const uint4*>(p), scale, v);
 }
 // The query elements that meet one K unit (bf16 for an fp8 pool).
 template <typename KT>
@@ -123,6 +126,55 @@ __device__ __forceinline__ void note_minmax(int32_t* stat, float s, bool finite)
   }
 }
 
+// The score of one token from its K row, in the exact order: the G dot
+// products left to right over the head dimension, then the group reduction
+// in head order.  kunit(u, v) yields K unit u and qunit(j, u, v) the query
+// elements of head j that meet it, as binary32 values; UNITS > 0 fixes the
+// number of units at compile time (else head_dim / units per element).
+template <typename KT, int G, int UNITS, typename KUnit, typename QUnit>
+__device__ __forceinline__ float exact_token_score(const ScoreArgs& a, int b, int g, KUnit&& kunit, QUnit&& qunit) {
+  constexpr int EPU = Elems<KT>::kPerUnit;
+  float acc[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) acc[j] = 0.0f;
+  auto step = [&](int u) {
+    float kv[EPU];
+    kunit(u, kv);
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      float qv[EPU];
+      qunit(j, u, qv);
+#pragma unroll
+      for (int e = 0; e < EPU; ++e) acc[j] = dot_step<KT>(acc[j], qv[e], kv[e]);
+    }
+  };
+  if constexpr (UNITS > 0) {
+#pragma unroll
+    for (int u = 0; u < UNITS; ++u) step(u);
+  } else {
+    const int units = a.head_dim / EPU;
+    for (int u = 0; u < units; ++u) step(u);
+  }
+  float s = 0.0f;
+  if (a.mode == 0) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) s = __fadd_rn(s, __fmul_rn(acc[j], a.head_scale));
+  } else if (a.mode == 1) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) s = __fadd_rn(s, acc[j]);
+    s = __fmul_rn(s, a.inv_g);
+  } else {
+    const float* w = a.head_weights + (int64_t)b * a.q_heads + g * G;
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const float r = acc[j] > 0.0f ? acc[j] : 0.0f;
+      s = __fadd_rn(s, __fmul_rn(w[j], r));
+    }
+  }
+  return s;
+}
+
+// Each lane reads its own K row from memory (any layout).
 template <typename KT, int G>
 __global__ __launch_bounds__(256) void score_exact_kernel(ScoreArgs a) {
   constexpr int EPU = Elems<KT>::kPerUnit;
@@ -146,39 +198,94 @@ __global__ __launch_bounds__(256) void score_exact_kernel(ScoreArgs a) {
   if (ok) {
     typedef typename QElem<KT>::type QT;
     const KT* krow = reinterpret_cast<const KT*>(a.k) + off;
-    const QT* qbase = reinterpret_cast<const QT*>(a.q) + ((int64_t)b * a.q_heads + g * G) * a.head_dim;
     const float ksc = std::is_same<KT, uint8_t>::value ? a.k_scale[scale_idx] : 1.0f;
-    float acc[G];
+    const QT* qbase = reinterpret_cast<const QT*>(a.q) + ((int64_t)b * a.q_heads + g * G) * a.head_dim;
+    s = exact_token_score<KT, G, 0>(
+        a, b, g, [&](int u, float (&kv)[EPU]) { load_k_unit<KT>(krow + u * EPU, ksc, kv); },
+        [&](int j, int u, float (&qv)[EPU]) { load_q_unit<KT>(qbase + (int64_t)j * a.head_dim + u * EPU, qv); });
+  }
+  if (in_row) row[t] = s;
+  if (a.row_stats) note_minmax(a.row_stats + (int64_t)blockIdx.y * kStatStride, s, ok && __builtin_isfinite(s));
+}
+
+// The same scores with the K rows staged through LDS.  A lane reading its
+// own row straight from memory touches a different 128-byte line in every
+// lane of every load; here a wave's 64 rows arrive with whole-row loads
+// (each instruction covers UPR * 16 / ... one kilobyte: 64 / UPR complete
+// rows) and each lane then reads its row from LDS.  Rows of UPR 16-byte
+// units; unit p of row r sits at position p ^ ((r / (16 / UPR)) & (UPR - 1)),
+// so the 16 lanes of each read phase hit 64 different banks (rows of 256 bytes
+// lie 64 banks apart, rows of 128 bytes 32).
+template <typename KT, int G, int UPR>
+__global__ __launch_bounds__(256) void score_exact_staged_kernel(ScoreArgs a) {
+  constexpr int EPU = Elems<KT>::kPerUnit;
+  typedef typename QElem<KT>::type QT;
+  // the group's G query rows: UPR units of K meet UPR * EPU query elements each
+  constexpr int kQUnits = G * UPR * EPU * (int)sizeof(QT) / 16;
+  __shared__ uint4 s_rows[4][64 * UPR];
+  __shared__ uint4 s_q[kQUnits];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int b = blockIdx.y / a.num_kv_heads, g = blockIdx.y % a.num_kv_heads;
+  const int cap = min(a.max_kv_len, a.max_pages * a.page_size);
+  const int L = clamp_len(a.kv_lens[b], cap);
+  const int t = (blockIdx.x * 4 + wid) * kWave + lane;
+  float* row = a.scores + (int64_t)blockIdx.y * a.max_kv_len;
+  const bool in_row = t < a.max_kv_len;
+  bool ok = in_row && t < L;
+  int64_t off = 0, scale_idx = 0;
+  if (ok) {
+    const int page = a.block_table[(int64_t)b * a.max_pages + t / a.page_size];
+    ok = page >= 0 && page < a.num_pages;
+    off = (int64_t)page * a.page_stride + (int64_t)g * a.head_stride +
+          (int64_t)(t % a.page_size) * a.token_stride;
+    scale_idx = fp8_scale_index(page, g, t % a.page_size, a.num_kv_heads, a.page_size);
+  }
+  // the query rows (contiguous: heads g*G .. g*G+G-1 of request b), loaded
+  // with the K rows below and written to LDS after them
+  constexpr int kQPerThread = (kQUnits + 255) / 256;
+  uint4 qreg[kQPerThread];
+  {
+    const uint4* qsrc = reinterpret_cast<const uint4*>(reinterpret_cast<const QT*>(a.q) +
+                                                       ((int64_t)b * a.q_heads + g * G) * a.head_dim);
 #pragma unroll
-    for (int j = 0; j < G; ++j) acc[j] = 0.0f;
-    const int units = a.head_dim / EPU;
-    for (int u = 0; u < units; ++u) {
-      float kv[EPU];
-      load_k_unit<KT>(krow + u * EPU, ksc, kv);
+    for (int k = 0; k < kQPerThread; ++k) qreg[k] = qsrc[min((int)threadIdx.x + 256 * k, kQUnits - 1)];
+  }
+  // byte offset of this lane's row, -1 when it is not read
+  const int64_t rb = ok ? off * (int64_t)sizeof(KT) : -1;
+  const uint32_t rb_lo = (uint32_t)(uint64_t)rb, rb_hi = (uint32_t)((uint64_t)rb >> 32);
+  const char* kb = reinterpret_cast<const char*>(a.k);
+  constexpr int kRowsPerRead = 64 / UPR;
+  auto swz = [](int r) { return (r / (16 / UPR)) & (UPR - 1); };
+  uint4 v[UPR];
 #pragma unroll
-      for (int j = 0; j < G; ++j) {
-        float qv[EPU];
-        load_q_unit<KT>(qbase + (int64_t)j * a.head_dim + u * EPU, qv);
+  for (int c = 0; c < UPR; ++c) {
+    const int r = c * kRowsPerRead + lane / UPR, p = lane % UPR;
+    const uint32_t lo = (uint32_t)__shfl((int)rb_lo, r), hi = (uint32_t)__shfl((int)rb_hi, r);
+    const int64_t src = (int64_t)(((uint64_t)hi << 32) | lo);
+    // rows not read load the pool's first unit instead (branch-free, so all
+    // UPR loads are in flight together); their values are never used
+    v[c] = *reinterpret_cast<const uint4*>(kb + (src >= 0 ? src + 16 * p : 0));
+  }
 #pragma unroll
-        for (int e = 0; e < EPU; ++e) acc[j] = dot_step<KT>(acc[j], qv[e], kv[e]);
-      }
-    }
-    s = 0.0f;
-    if (a.mode == 0) {
+  for (int c = 0; c < UPR; ++c) {
+    const int r = c * kRowsPerRead + lane / UPR, p = lane % UPR;
+    s_rows[wid][r * UPR + (p ^ swz(r))] = v[c];
+  }
+  // (threads past the last unit all write the last one, the same value)
 #pragma unroll
-      for (int j = 0; j < G; ++j) s = __fadd_rn(s, __fmul_rn(acc[j], a.head_scale));
-    } else if (a.mode == 1) {
-#pragma unroll
-      for (int j = 0; j < G; ++j) s = __fadd_rn(s, acc[j]);
-      s = __fmul_rn(s, a.inv_g);
-    } else {
-      const float* w = a.head_weights + (int64_t)b * a.q_heads + g * G;
-#pragma unroll
-      for (int j = 0; j < G; ++j) {
-        const float r = acc[j] > 0.0f ? acc[j] : 0.0f;
-        s = __fadd_rn(s, __fmul_rn(w[j], r));
-      }
-    }
+  for (int k = 0; k < kQPerThread; ++k) s_q[min((int)threadIdx.x + 256 * k, kQUnits - 1)] = qreg[k];
+  __syncthreads();
+  float s = -__builtin_inff();
+  if (ok) {
+    const float ksc = std::is_same<KT, uint8_t>::value ? a.k_scale[scale_idx] : 1.0f;
+    const uint4* mine = &s_rows[wid][lane * UPR];
+    const int sw = swz(lane);
+    // query units: QT elements u*EPU .. of head j (one 16-byte unit for bf16 or
+    // f32 K, two for fp8 K), the same address in every lane
+    constexpr int kQPerK = EPU * (int)sizeof(QT) / 16;
+    s = exact_token_score<KT, G, UPR>(
+        a, b, g, [&](int u, float (&kv)[EPU]) { cvt_k_unit<KT>(mine[u ^ sw], ksc, kv); },
+        [&](int j, int u, float (&qv)[EPU]) { load_q_unit<KT>(&s_q[(j * UPR + u) * kQPerK], qv); });
   }
   if (in_row) row[t] = s;
   if (a.row_stats) note_minmax(a.row_stats + (int64_t)blockIdx.y * kStatStride, s, ok && __builtin_isfinite(s));
@@ -831,10 +938,31 @@ __global__ __launch_bounds__(NW * 64) void score_dsa_fp8_kernel(ScoreArgs a, int
 
 // ------------------------------------------------------------------ launch
 
+template <typename KT, int UPR>
+static hipError_t launch_exact_g(const ScoreArgs& a, dim3 grid, hipStream_t st) {
+  switch (a.q_heads / a.num_kv_heads) {
+    case 1: score_exact_staged_kernel<KT, 1, UPR><<<grid, 256, 0, st>>>(a); break;
+    case 2: score_exact_staged_kernel<KT, 2, UPR><<<grid, 256, 0, st>>>(a); break;
+    case 4: score_exact_staged_kernel<KT, 4, UPR><<<grid, 256, 0, st>>>(a); break;
+    case 8: score_exact_staged_kernel<KT, 8, UPR><<<grid, 256, 0, st>>>(a); break;
+    case 16: score_exact_staged_kernel<KT, 16, UPR><<<grid, 256, 0, st>>>(a); break;
+    case 32: score_exact_staged_kernel<KT, 32, UPR><<<grid, 256, 0, st>>>(a); break;
+    case 64: score_exact_staged_kernel<KT, 64, UPR><<<grid, 256, 0, st>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <typename KT>
 static hipError_t launch_exact_t(const ScoreArgs& a, hipStream_t st) {
   const int G = a.q_heads / a.num_kv_heads;
   dim3 grid((a.max_kv_len + 255) / 256, a.batch * a.num_kv_heads);
+  // rows of 128 or 256 bytes starting on 16-byte boundaries are staged through LDS
+  const int64_t es = (int64_t)sizeof(KT), rbytes = (int64_t)a.head_dim * es;
+  const bool aligned = (reinterpret_cast<uintptr_t>(a.k) & 15) == 0 && (a.token_stride * es) % 16 == 0 &&
+                       (a.page_stride * es) % 16 == 0 && (a.head_stride * es) % 16 == 0;
+  if (aligned && a.num_pages > 0 && rbytes == 256) return launch_exact_g<KT, 16>(a, grid, st);
+  if (aligned && a.num_pages > 0 && rbytes == 128) return launch_exact_g<KT, 8>(a, grid, st);
   switch (G) {
     case 1: score_exact_kernel<KT, 1><<<grid, 256, 0, st>>>(a); break;
     case 2: score_exact_kernel<KT, 2><<<grid, 256, 0, st>>>(a); break;
