@@ -103,34 +103,83 @@ __global__ __launch_bounds__(256) void attn_vec_kernel(AttnArgs a) {
   }
   const T* kb = reinterpret_cast<const T*>(a.k);
   const T* vb = reinterpret_cast<const T*>(a.v);
-  for (int i0 = r0 + wid * RPW; i0 < r1; i0 += 4 * RPW) {
-    const int i = i0 + slot;
-    const int t = i < r1 ? sel[i] : -1;
-    const int64_t ko = sel_row(a, bt, L, t, g, a.k_page_stride, a.k_head_stride, a.k_token_stride, a.k_num_pages);
-    const int64_t vo = sel_row(a, bt, L, t, g, a.v_page_stride, a.v_head_stride, a.v_token_stride, a.v_num_pages);
-    const bool ok = ko >= 0 && vo >= 0;
-    float kv[EPL], vv[EPL];
-    if (ok) {
-      Vec<T>::unpack(*reinterpret_cast<const uint4*>(kb + ko + sub * EPL), kv);
-      Vec<T>::unpack(*reinterpret_cast<const uint4*>(vb + vo + sub * EPL), vv);
+  // Batches of 64 selected rows per wave, four batches resolved at once:
+  // lane l looks up row base + l of each (position, then its page: two
+  // rounds of independent loads for 256 rows), then the rows go through the
+  // wave RPW at a time with kPF groups' K and V loads in flight together.
+  // Rows that are not usable load the pool's first row instead (branch-free)
+  // and are skipped.
+  constexpr int kPF = LPR < 8 ? LPR : 8;
+  constexpr int kSB = 4;
+  // (an empty pool has no first row: nothing is usable then)
+  const int r_end = a.k_num_pages > 0 && a.v_num_pages > 0 ? r1 : r0;
+  for (int sbase = r0 + wid * kWave * kSB; sbase < r_end; sbase += 4 * kWave * kSB) {
+    int tsel[kSB], pg[kSB];
+#pragma unroll
+    for (int bi = 0; bi < kSB; ++bi) {
+      const int row = sbase + bi * kWave + lane;
+      tsel[bi] = row < r1 ? sel[row] : -1;
     }
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-      float x = 0.0f;
-      if (ok) {
+    for (int bi = 0; bi < kSB; ++bi) {
+      const bool in = tsel[bi] >= 0 && tsel[bi] < L;
+      const int p = bt[in ? tsel[bi] / a.page_size : 0];
+      pg[bi] = in ? p : -1;
+    }
+    uint32_t k_lo[kSB], k_hi[kSB], v_lo[kSB], v_hi[kSB];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) x = __builtin_fmaf(qf[j][e], kv[e], x);
-      }
+    for (int bi = 0; bi < kSB; ++bi) {
+      const int t = tsel[bi], p = pg[bi];
+      const bool ok = p >= 0 && p < a.k_num_pages && p < a.v_num_pages;
+      const int slot_t = ok ? t % a.page_size : 0;
+      const int64_t ko = ok ? (int64_t)p * a.k_page_stride + (int64_t)g * a.k_head_stride + (int64_t)slot_t * a.k_token_stride : -1;
+      const int64_t vo = ok ? (int64_t)p * a.v_page_stride + (int64_t)g * a.v_head_stride + (int64_t)slot_t * a.v_token_stride : -1;
+      k_lo[bi] = (uint32_t)(uint64_t)ko;
+      k_hi[bi] = (uint32_t)((uint64_t)ko >> 32);
+      v_lo[bi] = (uint32_t)(uint64_t)vo;
+      v_hi[bi] = (uint32_t)((uint64_t)vo >> 32);
+    }
 #pragma unroll
-      for (int off = LPR / 2; off > 0; off >>= 1) x += __shfl_xor(x, off);
-      if (ok) {
-        const float mn = fmaxf(m[j], x);
-        const float al = exp2f(m[j] - mn);
-        const float p = exp2f(x - mn);
-        l[j] = l[j] * al + p;
+    for (int bi = 0; bi < kSB; ++bi) {
+      const int base = sbase + bi * kWave;
+      if (base >= r1) break;
+      const int ngrp = min(LPR, (r1 - base + RPW - 1) / RPW);  // groups holding a row below r1
+      for (int q0 = 0; q0 < ngrp; q0 += kPF) {
+        uint4 kbuf[kPF], vbuf[kPF];
+        bool okb[kPF];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) o[j][e] = o[j][e] * al + p * vv[e];
-        m[j] = mn;
+        for (int q = 0; q < kPF; ++q) {
+          const int src = ((q0 + q) * RPW + slot) & 63;  // the lane that resolved this row
+          const int64_t k_o = (int64_t)(((uint64_t)(uint32_t)__shfl((int)k_hi[bi], src) << 32) | (uint32_t)__shfl((int)k_lo[bi], src));
+          const int64_t v_o = (int64_t)(((uint64_t)(uint32_t)__shfl((int)v_hi[bi], src) << 32) | (uint32_t)__shfl((int)v_lo[bi], src));
+          okb[q] = q0 + q < ngrp && k_o >= 0;
+          kbuf[q] = *reinterpret_cast<const uint4*>(kb + (okb[q] ? k_o : 0) + sub * EPL);
+          vbuf[q] = *reinterpret_cast<const uint4*>(vb + (okb[q] ? v_o : 0) + sub * EPL);
+        }
+#pragma unroll
+        for (int q = 0; q < kPF; ++q) {
+          const bool ok = okb[q];
+          float kv[EPL], vv[EPL];
+          Vec<T>::unpack(kbuf[q], kv);
+          Vec<T>::unpack(vbuf[q], vv);
+#pragma unroll
+          for (int j = 0; j < G; ++j) {
+            float x = 0.0f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) x = __builtin_fmaf(qf[j][e], kv[e], x);
+#pragma unroll
+            for (int off = LPR / 2; off > 0; off >>= 1) x += __shfl_xor(x, off);
+            if (ok) {
+              const float mn = fmaxf(m[j], x);
+              const float al = exp2f(m[j] - mn);
+              const float p = exp2f(x - mn);
+              l[j] = l[j] * al + p;
+#pragma unroll
+              for (int e = 0; e < EPL; ++e) o[j][e] = o[j][e] * al + p * vv[e];
+              m[j] = mn;
+            }
+          }
+        }
       }
     }
   }
