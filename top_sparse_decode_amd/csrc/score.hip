@@ -998,16 +998,25 @@ bool score_fast_supported(const ScoreArgs& a) {
 namespace {
 // waves per block, ring stages, tiles per wave at most, blocks per CU
 constexpr int kScoreNW = 4, kScoreStages = 4, kScoreMaxIt = 32, kScoreBlocksPerCU = 1;      // bf16 K
+// bf16 K when the grid needs several rounds of blocks: two smaller blocks per
+// CU, so that one block's start and drain overlap the other's stream, and
+// shorter spans (rows of different lengths balance better)
+constexpr int kScoreMNW = 4, kScoreMStages = 2, kScoreMMaxIt = 16, kScoreMBlocksPerCU = 2;
 constexpr int kScore8NW = 8, kScore8Stages = 3, kScore8MaxIt = 16, kScore8BlocksPerCU = 1;  // fp8 K
+
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  return cus;
+}
 
 // Tiles per wave: enough blocks to fill the chip once, and a span that
 // overlaps at most 64 logical pages (their ids ride in one register per
 // lane): span / page_size pages when the span is a whole number of pages,
 // else up to two more.
 int score_iters(const ScoreArgs& a, int nw, int maxit, int bpc) {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    cus = 256;
+  const int cus = device_cus();
   const int64_t rows = (int64_t)a.batch * a.num_kv_heads;
   const int64_t tiles = rows * ((a.max_kv_len + kTileTok - 1) / kTileTok);
   const int64_t per_block = (tiles + (int64_t)cus * bpc - 1) / ((int64_t)cus * bpc);
@@ -1020,37 +1029,46 @@ int score_iters(const ScoreArgs& a, int nw, int maxit, int bpc) {
   return std::max(iters, 1);
 }
 
+// Launch shape of the fast scorer: 0 = one round of large bf16 blocks,
+// 1 = several rounds (two blocks per CU), 2 = fp8.
+struct FastShape {
+  int kind, nw, iters;
+};
+FastShape fast_shape(const ScoreArgs& a) {
+  if (a.dtype == 2) return {2, kScore8NW, score_iters(a, kScore8NW, kScore8MaxIt, kScore8BlocksPerCU)};
+  const int64_t rows = (int64_t)a.batch * a.num_kv_heads;
+  const int64_t tiles = rows * ((a.max_kv_len + kTileTok - 1) / kTileTok);
+  if (tiles <= (int64_t)device_cus() * kScoreBlocksPerCU * kScoreNW * kScoreMaxIt)
+    return {0, kScoreNW, score_iters(a, kScoreNW, kScoreMaxIt, kScoreBlocksPerCU)};
+  return {1, kScoreMNW, score_iters(a, kScoreMNW, kScoreMMaxIt, kScoreMBlocksPerCU)};
+}
+
 }  // namespace
 
 int score_fast_spans(const ScoreArgs& a) {
-  const bool fp8 = a.dtype == 2;
-  const int nw = fp8 ? kScore8NW : kScoreNW;
-  const int iters = fp8 ? score_iters(a, kScore8NW, kScore8MaxIt, kScore8BlocksPerCU)
-                        : score_iters(a, kScoreNW, kScoreMaxIt, kScoreBlocksPerCU);
-  const int span = nw * kTileTok * iters;
+  const FastShape f = fast_shape(a);
+  const int span = f.nw * kTileTok * f.iters;
   return (a.max_kv_len + span - 1) / span;
 }
 
-int score_fast_max_spans(int max_kv_len) {  // one tile per wave, the smaller block
-  const int span = std::min(kScoreNW, kScore8NW) * kTileTok;
+int score_fast_max_spans(int max_kv_len) {  // one tile per wave, the smallest block
+  const int span = std::min(std::min(kScoreNW, kScoreMNW), kScore8NW) * kTileTok;
   return (max_kv_len + span - 1) / span;
 }
 
 namespace {
 template <int MT>
 hipError_t launch_dsa(const ScoreArgs& a, hipStream_t st) {
+  const FastShape f = fast_shape(a);
   const unsigned rows = (unsigned)(a.batch * a.num_kv_heads);
-  if (a.dtype == 2) {
-    const int iters = score_iters(a, kScore8NW, kScore8MaxIt, kScore8BlocksPerCU);
-    const int span = kScore8NW * kTileTok * iters;
-    dim3 grid((a.max_kv_len + span - 1) / span, rows);
-    score_dsa_fp8_kernel<MT, kScore8NW, kScore8Stages, kScore8MaxIt><<<grid, kScore8NW * 64, 0, st>>>(a, iters);
-  } else {
-    const int iters = score_iters(a, kScoreNW, kScoreMaxIt, kScoreBlocksPerCU);
-    const int span = kScoreNW * kTileTok * iters;
-    dim3 grid((a.max_kv_len + span - 1) / span, rows);
-    score_dsa_kernel<MT, kScoreNW, kScoreStages, kScoreMaxIt><<<grid, kScoreNW * 64, 0, st>>>(a, iters);
-  }
+  const int span = f.nw * kTileTok * f.iters;
+  const dim3 grid((a.max_kv_len + span - 1) / span, rows);
+  if (f.kind == 2)
+    score_dsa_fp8_kernel<MT, kScore8NW, kScore8Stages, kScore8MaxIt><<<grid, kScore8NW * 64, 0, st>>>(a, f.iters);
+  else if (f.kind == 1)
+    score_dsa_kernel<MT, kScoreMNW, kScoreMStages, kScoreMMaxIt><<<grid, kScoreMNW * 64, 0, st>>>(a, f.iters);
+  else
+    score_dsa_kernel<MT, kScoreNW, kScoreStages, kScoreMaxIt><<<grid, kScoreNW * 64, 0, st>>>(a, f.iters);
   return hipGetLastError();
 }
 }  // namespace
