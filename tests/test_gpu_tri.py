@@ -96,3 +96,13 @@ def test_tri_from_paged_group_mean_scores():
     assert np.array_equal(stacked.view(np.uint32), np.stack(ref).view(np.uint32))
     for mode in MODES:
         check(stacked, layers[0].kv_lens, mode, 256, "paged")
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("S", [3000, 3001])
+def test_tri_many_members_both_reduce_paths(mode, S):
+    # 20 members per union row (the sliced reduce); a row stride that is a
+    # multiple of four takes the 16-byte-load reduce, an odd one the scalar one
+    s = random_scores(44, 5, 2, 4, S)
+    kv = np.array([S, 1234], np.int32)
+    check(s, kv, mode, 256, f"members S={S}")

@@ -203,6 +203,103 @@ __global__ __launch_bounds__(kTriThreads) void tri_reduce_kernel(TriArgs a) {
   }
 }
 
+// The same reduction with four consecutive tokens per lane and 16-byte loads
+// (rows whose stride is a multiple of four floats): a wave reads a member's
+// 256 tokens with one instruction.  SLICES = 4: one block per (256-token
+// tile, output row), wave j takes the j-th quarter of the members, partial
+// maxima combined in wave order; SLICES = 1: a block covers kTriSpan tokens.
+// Per token the arithmetic and the order are those of tri_reduce_kernel.
+template <int SLICES>
+__global__ __launch_bounds__(kTriThreads) void tri_reduce4_kernel(TriArgs a) {
+  __shared__ float4 s_part[kTriThreads / 64][64];
+  const int o = blockIdx.y;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int b, g0, ng, nl, l0;
+  if (a.mode == 0) {
+    l0 = o / (a.batch * a.groups);
+    b = (o / a.groups) % a.batch;
+    g0 = o % a.groups;
+    ng = 1;
+    nl = 1;
+  } else if (a.mode == 1) {
+    l0 = 0;
+    b = o / a.groups;
+    g0 = o % a.groups;
+    ng = 1;
+    nl = a.layers;
+  } else {
+    l0 = 0;
+    b = o;
+    g0 = 0;
+    ng = a.groups;
+    nl = a.layers;
+  }
+  const int nm = nl * ng;
+  const int per = (nm + SLICES - 1) / SLICES;
+  const int j0 = SLICES == 1 ? 0 : min(nm, wid * per), j1 = SLICES == 1 ? nm : min(nm, j0 + per);
+  const int L = clamp_len(a.kv_lens[b], a.row_stride);
+  auto member = [&](int j) { return ((int64_t)(l0 + j / ng) * a.batch + b) * a.groups + g0 + j % ng; };
+  // running max of z over members [j0, j1) at tokens t0 .. t0 + 3 (t0 + 3 < row_stride)
+  auto reduce4 = [&](int t0) {
+    float r[4] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+    if (t0 >= L) return make_float4(r[0], r[1], r[2], r[3]);
+    int j = j0;
+    for (; j + 4 <= j1; j += 4) {
+      float4 x[4];
+      int64_t m[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        m[u] = member(j + u);
+        x[u] = *reinterpret_cast<const float4*>(a.scores + m[u] * a.row_stride + t0);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const double mu = a.stats[2 * m[u]], sg = a.stats[2 * m[u] + 1];
+        const float xs[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float z = t0 + e < L ? tri_z(xs[e], mu, sg) : -__builtin_inff();
+          if (z > r[e]) r[e] = z;
+        }
+      }
+    }
+    for (; j < j1; ++j) {
+      const int64_t m = member(j);
+      const float4 x = *reinterpret_cast<const float4*>(a.scores + m * a.row_stride + t0);
+      const double mu = a.stats[2 * m], sg = a.stats[2 * m + 1];
+      const float xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float z = t0 + e < L ? tri_z(xs[e], mu, sg) : -__builtin_inff();
+        if (z > r[e]) r[e] = z;
+      }
+    }
+    return make_float4(r[0], r[1], r[2], r[3]);
+  };
+  float* out = a.reduced + (int64_t)o * a.row_stride;
+  if constexpr (SLICES == 1) {
+    const int tend = min(a.row_stride, (int)(blockIdx.x + 1) * kTriSpan);
+    for (int t0 = blockIdx.x * kTriSpan + 4 * threadIdx.x; t0 < tend; t0 += 4 * kTriThreads)
+      *reinterpret_cast<float4*>(out + t0) = reduce4(t0);
+  } else {
+    const int t0 = blockIdx.x * 256 + 4 * lane;
+    s_part[wid][lane] = t0 < a.row_stride ? reduce4(t0) : make_float4(0.f, 0.f, 0.f, 0.f);
+    __syncthreads();
+    if (wid == 0 && t0 < a.row_stride) {
+      float4 v = s_part[0][lane];
+#pragma unroll
+      for (int w = 1; w < SLICES; ++w) {
+        const float4 z = s_part[w][lane];
+        if (z.x > v.x) v.x = z.x;
+        if (z.y > v.y) v.y = z.y;
+        if (z.z > v.z) v.z = z.z;
+        if (z.w > v.w) v.w = z.w;
+      }
+      *reinterpret_cast<float4*>(out + t0) = v;
+    }
+  }
+}
+
 int tri_out_rows(int layers, int batch, int groups, int mode) {
   return mode == 0 ? layers * batch * groups : (mode == 1 ? batch * groups : batch);
 }
@@ -213,7 +310,13 @@ hipError_t launch_tri(const TriArgs& a, hipStream_t st) {
   if (members == 0 || a.row_stride == 0) return hipSuccess;
   tri_stats_kernel<<<members, kTriThreads, 0, st>>>(a);
   const int nm = a.mode == 0 ? 1 : (a.mode == 1 ? a.layers : a.layers * a.groups);
-  if (nm >= 16)
+  const bool vec = (a.row_stride % 4) == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(a.reduced) & 15) == 0;
+  if (vec && nm >= 16)
+    tri_reduce4_kernel<4><<<dim3((a.row_stride + 255) / 256, out_rows), kTriThreads, 0, st>>>(a);
+  else if (vec)
+    tri_reduce4_kernel<1><<<dim3((a.row_stride + kTriSpan - 1) / kTriSpan, out_rows), kTriThreads, 0, st>>>(a);
+  else if (nm >= 16)
     tri_reduce_kernel<4><<<dim3((a.row_stride + 63) / 64, out_rows), kTriThreads, 0, st>>>(a);
   else
     tri_reduce_kernel<1><<<dim3((a.row_stride + kTriSpan - 1) / kTriSpan, out_rows), kTriThreads, 0, st>>>(a);
