@@ -434,7 +434,9 @@ __device__ __forceinline__ void select_row_block(const SelectArgs& a, int row, S
           c = bn > bstar ? kIn : (bn < bstar ? kOut : kBand);
         }
         n_in += c == kIn;
-        if (c == kBand && (!FAST || bstar < 0)) keys[t0 + e] = score_key(val);
+        // band keys: exact scores are re-derived from the scores themselves
+        // below (no memory round trip); fast rows store the -inf fillers'
+        if (c == kBand && FAST && bstar < 0) keys[t0 + e] = score_key(val);
         byte |= c << (2 * e);
       }
       sh.cls[(sc * NI + i) * kSelThreads + tid] = (uint8_t)byte;
@@ -466,6 +468,23 @@ __device__ __forceinline__ void select_row_block(const SelectArgs& a, int row, S
     }
   }
 
+  // Keys of this thread's band tokens in tile (sc, i): exact scores give
+  // them from the scores (registers when the row is resident); re-scored
+  // fast rows read them back from the key array.
+  auto band_keys = [&](int sc, int i, uint32_t byte, uint32_t (&k4)[4]) {
+    if constexpr (FAST) {
+      const int t0 = tok(sc, i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) k4[e] = ((byte >> (2 * e)) & 3u) == kBand ? keys[t0 + e] : 0u;
+    } else {
+      const float4 x = get(sc, i);
+      k4[0] = score_key(x.x);
+      k4[1] = score_key(x.y);
+      k4[2] = score_key(x.z);
+      k4[3] = score_key(x.w);
+    }
+  };
+
   // ---- 4. radix select over the band keys
   int remaining = k - n_in;  // band tokens to keep (>= 1)
   uint32_t prefix = 0, pmask = 0;
@@ -480,15 +499,13 @@ __device__ __forceinline__ void select_row_block(const SelectArgs& a, int row, S
       for (int sc = 0; sc < nsc; ++sc)
         for (int i = 0; i < NI; ++i) {
           const uint32_t byte = sh.cls[(sc * NI + i) * kSelThreads + tid];
-          const int t0 = tok(sc, i);
+          uint32_t k4[4];
+          band_keys(sc, i, byte, k4);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             bool act = ((byte >> (2 * e)) & 3u) == kBand;
-            uint32_t key = 0;
-            if (act) {
-              key = keys[t0 + e];
-              act = (key & pmask) == prefix;
-            }
+            const uint32_t key = act ? k4[e] : 0u;
+            act = act && (key & pmask) == prefix;
             hist_add(sh.hist, (int)((key >> shifts[p]) & (uint32_t)(nb - 1)), act);
           }
         }
@@ -511,6 +528,8 @@ __device__ __forceinline__ void select_row_block(const SelectArgs& a, int row, S
       const int t0 = tok(sc, i);
       int gt = 0, eq = 0;
       uint32_t flags = 0;  // bit e: strictly kept, bit 4+e: tie
+      uint32_t k4[4];
+      band_keys(sc, i, byte, k4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t c = (byte >> (2 * e)) & 3u;
@@ -518,7 +537,7 @@ __device__ __forceinline__ void select_row_block(const SelectArgs& a, int row, S
           flags |= 1u << e;
           ++gt;
         } else if (c == kBand) {
-          const uint32_t key = keys[t0 + e];
+          const uint32_t key = k4[e];
           if (key > kth) {
             flags |= 1u << e;
             ++gt;
