@@ -55,6 +55,7 @@ __device__ __forceinline__ void put_index(const SelectArgs& a, int row, int i, i
   if (a.writeback) a.writeback[(int64_t)row * a.wb_stride + i] = v;
 }
 
+constexpr int kRankMax = 512;  // band sizes the one-block path ranks directly
 template <int NCLS>
 struct SelSharedN {
   int hist[kBins];
@@ -63,6 +64,10 @@ struct SelSharedN {
   float redf[2][kSelWaves];
   int redi[kSelWaves];
   uint8_t cls[NCLS];  // 4 x 2-bit classes per byte
+  // a short band: (key << 32) | ~position per entry and whether it is kept
+  uint64_t rkey[kRankMax];
+  uint8_t rkeep[kRankMax];
+  int rcount;
 };
 // the whole-row path at the longest rows; shorter rows need NI * kSelThreads bytes of classes
 using SelShared = SelSharedN<kMaxChunks * kMaxNI * kSelThreads>;
@@ -409,7 +414,7 @@ __device__ __forceinline__ void select_row_block(const SelectArgs& a, int row, S
       if ((double)band_hi < bhi) band_hi = next_up(band_hi);
     }
   }
-  int n_in = 0;
+  int n_in = 0, n_band = 0;
   for (int sc = 0; sc < nsc; ++sc) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -434,6 +439,7 @@ __device__ __forceinline__ void select_row_block(const SelectArgs& a, int row, S
           c = bn > bstar ? kIn : (bn < bstar ? kOut : kBand);
         }
         n_in += c == kIn;
+        n_band += c == kBand;
         // band keys: exact scores are re-derived from the scores themselves
         // below (no memory round trip); fast rows store the -inf fillers'
         if (c == kBand && FAST && bstar < 0) keys[t0 + e] = score_key(val);
@@ -443,6 +449,7 @@ __device__ __forceinline__ void select_row_block(const SelectArgs& a, int row, S
     }
   }
   n_in = block_sum_i(n_in, sh);  // (has __syncthreads: classes visible)
+  n_band = block_sum_i(n_band, sh);
 
   // ---- FAST: exact scores of the band tokens (each wave re-scores the band
   // tokens among its own 64 threads' positions)
@@ -485,8 +492,70 @@ __device__ __forceinline__ void select_row_block(const SelectArgs& a, int row, S
     }
   };
 
-  // ---- 4. radix select over the band keys
   int remaining = k - n_in;  // band tokens to keep (>= 1)
+
+  // ---- 4'. a short band of a resident row: each entry is ranked against the
+  // others in (key desc, position asc) order and kept when fewer than
+  // `remaining` entries come before it; then the ordered emission
+  if constexpr (RESIDENT) {
+    if (n_band <= kRankMax) {
+      if (tid == 0) sh.rcount = 0;
+      __syncthreads();
+      int bidx[NI][4];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const uint32_t byte = sh.cls[i * kSelThreads + tid];
+        const int t0 = tok(0, i);
+        uint32_t k4[4];
+        band_keys(0, i, byte, k4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          bidx[i][e] = -1;
+          if (((byte >> (2 * e)) & 3u) == kBand) {
+            const int j = atomicAdd(&sh.rcount, 1);
+            sh.rkey[j] = ((uint64_t)k4[e] << 32) | (uint32_t)~(uint32_t)(t0 + e);
+            bidx[i][e] = j;
+          }
+        }
+      }
+      __syncthreads();
+      for (int j = tid; j < n_band; j += kSelThreads) {
+        const uint64_t x = sh.rkey[j];
+        int rank = 0;
+        for (int m = 0; m < n_band; ++m) rank += sh.rkey[m] > x;
+        sh.rkeep[j] = rank < remaining;
+      }
+      __syncthreads();
+      int base = 0;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const uint32_t byte = sh.cls[i * kSelThreads + tid];
+        const int t0 = tok(0, i);
+        uint32_t keepm = 0;
+        int kept = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t c = (byte >> (2 * e)) & 3u;
+          const bool kp = c == kIn || (c == kBand && sh.rkeep[bidx[i][e]]);
+          keepm |= (uint32_t)kp << e;
+          kept += kp;
+        }
+        int total;
+        int pos = base + block_excl_scan<kSelThreads>(kept, sh.tmp, &total);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if ((keepm >> e) & 1u) {
+            if (pos < k) put_index(a, row, pos, t0 + e);
+            ++pos;
+          }
+        base += total;
+      }
+      if (a.counts && tid == 0) a.counts[row] = k;
+      return;
+    }
+  }
+
+  // ---- 4. radix select over the band keys
   uint32_t prefix = 0, pmask = 0;
   {
     const int shifts[3] = {21, 10, 0};
