@@ -108,6 +108,33 @@ __device__ __forceinline__ int block_sum_i(int v, SH& sh) {
   return r;
 }
 
+// min, max and sum over the block in one exchange (one pair of barriers)
+template <typename SH>
+__device__ __forceinline__ void block_min_max_sum(float& lo, float& hi, int& n, SH& sh) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    lo = fminf(lo, __shfl_xor(lo, o));
+    hi = fmaxf(hi, __shfl_xor(hi, o));
+    n += __shfl_xor(n, o);
+  }
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  if (lane == 0) {
+    sh.redf[0][wid] = lo;
+    sh.redf[1][wid] = hi;
+    sh.redi[wid] = n;
+  }
+  __syncthreads();
+  lo = sh.redf[0][0];
+  hi = sh.redf[1][0];
+  n = sh.redi[0];
+  for (int w = 1; w < kSelWaves; ++w) {
+    lo = fminf(lo, sh.redf[0][w]);
+    hi = fmaxf(hi, sh.redf[1][w]);
+    n += sh.redi[w];
+  }
+  __syncthreads();
+}
+
 // Neighbouring binary32 values (finite inputs).
 __device__ __forceinline__ float next_up(float x) {
   const uint32_t u = __float_as_uint(x);
@@ -350,9 +377,7 @@ __device__ __forceinline__ void select_row_block(const SelectArgs& a, int row, S
         }
     }
   }
-  lo = block_min_f(lo, sh);
-  hi = block_max_f(hi, sh);
-  nfin = block_sum_i(nfin, sh);
+  block_min_max_sum(lo, hi, nfin, sh);
 
   // ---- 2. histogram and the bin of the k-th largest
   // value-linear bins; float arithmetic is monotone in x, which is all the
@@ -448,8 +473,15 @@ __device__ __forceinline__ void select_row_block(const SelectArgs& a, int row, S
       sh.cls[(sc * NI + i) * kSelThreads + tid] = (uint8_t)byte;
     }
   }
-  n_in = block_sum_i(n_in, sh);  // (has __syncthreads: classes visible)
-  n_band = block_sum_i(n_band, sh);
+  if constexpr (RESIDENT && NI * kTile < 65536) {
+    // both counts in one sum (each at most the row length, below 2^16)
+    const int packed = block_sum_i(n_in | (n_band << 16), sh);  // (has __syncthreads: classes visible)
+    n_in = packed & 0xFFFF;
+    n_band = packed >> 16;
+  } else {
+    n_in = block_sum_i(n_in, sh);  // (has __syncthreads: classes visible)
+    n_band = block_sum_i(n_band, sh);
+  }
 
   // ---- FAST: exact scores of the band tokens (each wave re-scores the band
   // tokens among its own 64 threads' positions)
@@ -526,29 +558,43 @@ __device__ __forceinline__ void select_row_block(const SelectArgs& a, int row, S
         sh.rkeep[j] = rank < remaining;
       }
       __syncthreads();
-      int base = 0;
+      uint32_t keepm[NI];
+      int kept[NI];
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const uint32_t byte = sh.cls[i * kSelThreads + tid];
-        const int t0 = tok(0, i);
-        uint32_t keepm = 0;
-        int kept = 0;
+        keepm[i] = 0;
+        kept[i] = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const uint32_t c = (byte >> (2 * e)) & 3u;
           const bool kp = c == kIn || (c == kBand && sh.rkeep[bidx[i][e]]);
-          keepm |= (uint32_t)kp << e;
-          kept += kp;
+          keepm[i] |= (uint32_t)kp << e;
+          kept[i] += kp;
         }
-        int total;
-        int pos = base + block_excl_scan<kSelThreads>(kept, sh.tmp, &total);
+      }
+      auto emit_tile = [&](int i, int pos) {
+        const int t0 = tok(0, i);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if ((keepm >> e) & 1u) {
+          if ((keepm[i] >> e) & 1u) {
             if (pos < k) put_index(a, row, pos, t0 + e);
             ++pos;
           }
-        base += total;
+      };
+      if constexpr (NI <= 2) {  // both tiles' counts (below 2^16 each) in one scan
+        int total;
+        const int packed = block_excl_scan<kSelThreads>(kept[0] | (NI > 1 ? kept[NI - 1] << 16 : 0), sh.tmp, &total);
+        emit_tile(0, packed & 0xFFFF);
+        if constexpr (NI > 1) emit_tile(1, (total & 0xFFFF) + (packed >> 16));
+      } else {
+        int base = 0;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          int total;
+          emit_tile(i, base + block_excl_scan<kSelThreads>(kept[i], sh.tmp, &total));
+          base += total;
+        }
       }
       if (a.counts && tid == 0) a.counts[row] = k;
       return;
