@@ -64,8 +64,8 @@ __device__ __forceinline__ int64_t sel_row(const AttnArgs& a, const int32_t* bt,
 
 // One block per (split, request*KV head); four waves.  A row of D elements is
 // spread over LPR lanes (16 bytes each), so a wave works on 64/LPR rows at
-// a time, each row slot with its own running (m, l, o); slots and waves are
-// merged at the end.
+// a time (RPW row slots), each slot with its own running (m, l, o); slots
+// and waves are merged at the end.
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void attn_vec_kernel(AttnArgs a) {
   constexpr int EPL = Vec<T>::kPer;

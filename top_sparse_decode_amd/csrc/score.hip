@@ -5,12 +5,14 @@
 // compression method", Key Design Decisions: direct paged-pool scoring with
 // no gather or reformat; Summary: per-head scores reduced to one per KV head).
 //
-// Two kernels:
-//  * score_exact_kernel: one lane per token; each lane evaluates the binary32
-//    dot products left to right over the head dimension (one rounding per
-//    product and per sum; for bf16 operands the product is exact, so a fused
-//    multiply-add per step gives the same bits), then reduces over the group's
-//    heads in head order.  Bit-identical to any other evaluation in that order.
+// Kernels:
+//  * score_exact_staged_kernel / score_exact_kernel: one lane per token; each
+//    lane evaluates the binary32 dot products left to right over the head
+//    dimension (one rounding per product and per sum; for bf16 operands the
+//    product is exact, so a fused multiply-add per step gives the same bits),
+//    then reduces over the group's heads in head order.  Bit-identical to any
+//    other evaluation in that order.  The staged kernel brings K rows and the
+//    query through LDS with whole-row loads; the other reads rows directly.
 //  * score_dsa_kernel: the DSA indexer score s_t = sum_h w_h relu(q_h.k_t)
 //    ("Overlap DSA heuristic prev_topk write-back on the aux stream",
 //    Description: the indexer scores every token before the top-k kernel) on
@@ -18,6 +20,9 @@
 //    contraction there (64 x tokens x 128).  It also produces a rigorous
 //    per-row bound on |fast score - exact score| so that selection can still
 //    be made exact (see topk.hip).
+//  * score_dsa_fp8_kernel: the same score over an FP8 E4M3 indexer cache with
+//    one binary32 scale per row (codes widened exactly to bf16 for the matrix
+//    cores, the bound on the fp8 matrix cores).
 #include "common.h"
 #include "kernels.h"
 
