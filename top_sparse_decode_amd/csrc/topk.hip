@@ -1050,14 +1050,17 @@ __global__ __launch_bounds__(kChunkThreads) void select_hist_kernel(SelectArgs a
 template <bool FAST>
 __global__ __launch_bounds__(kChunkThreads) void select_classify_kernel(SelectArgs a) {
   __shared__ ChunkShared sh;
-  __shared__ int s_band[kSelChunk];       // band positions of the chunk
-  __shared__ uint32_t s_bkey[kSelChunk];  // and their exact keys
+  __shared__ uint16_t s_bpos[kSelChunk];  // band tokens of the chunk (offsets in it)
   __shared__ int s_nband, s_base;
   __shared__ __attribute__((aligned(16))) float s_terms[kSelWaves][kWave];
   // K rows of band tokens being re-scored: bf16 rows as they are (256 bytes),
   // fp8 rows dequantized to binary32 (512 bytes)
   __shared__ __attribute__((aligned(16))) float s_krow[kStageRows][128];
-  __shared__ int s_bpage[FAST ? kSelChunk : 1];      // page of each band token
+  __shared__ int s_tpage[FAST ? kChunkThreads : 1];  // page of each thread's eight tokens
+  // query rows of the band re-score, one per head, 17 units apart (the
+  // per-lane reads of one unit then hit distinct banks)
+  constexpr int kQStride = 17;
+  __shared__ __attribute__((aligned(16))) uint4 s_q[FAST ? 64 * kQStride : 1];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int row = blockIdx.y, c = blockIdx.x;
   const int g = row % a.groups, b = row / a.groups;
@@ -1098,48 +1101,70 @@ __global__ __launch_bounds__(kChunkThreads) void select_classify_kernel(SelectAr
   uint32_t* keys = reinterpret_cast<uint32_t*>(a.keys) + (int64_t)row * a.row_stride;
   int32_t* st = a.stats + (int64_t)row * kStatStride;
   uint64_t* band = a.band + (int64_t)row * kBandCap;
+  const int cstart = c * kSelChunk;
+  // band tokens go to the chunk's list; this thread remembers their list
+  // slots (-1: not in the band)
+  int bslot[kPerThread];
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
     const uint32_t cl = classify(v, cut, x[e], FAST);
     n_in += cl == kIn;
     n_neg += (x[e] == -__builtin_inff());
+    bslot[e] = -1;
     if (cl == kBand) {
-      const int i = atomicAdd(&s_nband, 1);
-      s_band[i] = t0 + e;
-      s_bkey[i] = score_key(x[e]);  // fast scores: replaced by the exact key below
-      if constexpr (FAST) s_bpage[i] = tpage;
+      bslot[e] = atomicAdd(&s_nband, 1);
+      s_bpos[bslot[e]] = (uint16_t)(t0 + e - cstart);
     }
   }
+  if constexpr (FAST) s_tpage[tid] = tpage;
   n_in = chunk_sum_i(n_in, sh.redi);
-  n_neg = chunk_sum_i(n_neg, sh.redi);  // (barrier: s_band complete)
+  n_neg = chunk_sum_i(n_neg, sh.redi);  // (barrier: the band list complete)
   if (tid == 0) {
     int32_t* cc = a.chunk_counts + ((int64_t)row * a.nchunks + c) * 2;
     cc[0] = n_in;
     cc[1] = n_neg;
   }
   const int nb = s_nband;  // (visible: the barriers above)
-  if (FAST && cut.bstar >= 0 && nb > 0) {
-    // Exact re-score of the band: the K rows of up to kStageRows tokens at a
-    // time are staged in LDS (one round trip), each wave holds its lane's
-    // query row in registers, and a wave scores one token in the library's
-    // exact order (lane h: dot_h left to right; then the head terms in head
-    // order), bit-identical to the exact scorer.
-    const bool hact = lane < G;
-    uint4 qr[16];
-    float wh = 0.0f;
-    if (hact) {
+  if (nb == 0) return;
+  // the chunk's entries of the row's band list: one reservation per block
+  if (tid == 0) s_base = atomicAdd(&st[2], nb);
+  __syncthreads();
+  const int base = s_base;
+  // band entry of token t with key `key`, list slot i of the chunk
+  auto put_band = [&](int i, int t, uint32_t key) {
+    keys[t] = key;
+    if (base + i < kBandCap) band[base + i] = ((uint64_t)key << 32) | (uint32_t)~(uint32_t)t;
+  };
+  if (!FAST || cut.bstar < 0) {
+    // the scores are the keys: each thread writes its own band tokens
 #pragma unroll
-      for (int i = 0; i < 16; ++i) qr[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(sa.q) + ((int64_t)b * sa.q_heads + g * G + lane) * 128 + 8 * i);
-      wh = sa.head_weights[(int64_t)b * sa.q_heads + g * G + lane];
+    for (int e = 0; e < kPerThread; ++e)
+      if (bslot[e] >= 0) put_band(bslot[e], t0 + e, score_key(x[e]));
+    return;
+  }
+  {
+    // Exact re-score of the band: the group's query rows and the K rows of
+    // up to kStageRows tokens at a time are staged in LDS (one round trip),
+    // and a wave scores one token in the library's exact order (lane h:
+    // dot_h left to right; then the head terms in head order),
+    // bit-identical to the exact scorer.
+    const bool hact = lane < G;
+    const float wh = hact ? sa.head_weights[(int64_t)b * sa.q_heads + g * G + lane] : 0.0f;
+    for (int u = tid; u < G * 16; u += kChunkThreads) {
+      const int h = u >> 4, part = u & 15;
+      s_q[h * kQStride + part] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(sa.q) +
+                                                                ((int64_t)b * sa.q_heads + g * G + h) * 128 + 8 * part);
     }
+    const uint4* qrow = s_q + lane * kQStride;
     const bool fp8 = sa.dtype == 2;
     for (int p0 = 0; p0 < nb; p0 += kStageRows) {
       const int np = min(kStageRows, nb - p0);
       {
         const int i = tid >> 4, part = tid & 15;  // 16 threads per row
         if (i < np) {
-          const int t = s_band[p0 + i];
-          const int page = s_bpage[p0 + i];
+          const int off = s_bpos[p0 + i];
+          const int t = cstart + off;
+          const int page = s_tpage[off / kPerThread];
           const int slot = t % sa.page_size;
           const int64_t koff = (int64_t)page * sa.page_stride + (int64_t)g * sa.head_stride +
                                (int64_t)slot * sa.token_stride;
@@ -1170,11 +1195,16 @@ __global__ __launch_bounds__(kChunkThreads) void select_classify_kernel(SelectAr
               const float4 hi = *reinterpret_cast<const float4*>(&s_krow[i][8 * c8 + 4]);
               kd[0] = lo.x; kd[1] = lo.y; kd[2] = lo.z; kd[3] = lo.w;
               kd[4] = hi.x; kd[5] = hi.y; kd[6] = hi.z; kd[7] = hi.w;
-              acc = dot8_f32k(acc, qr[c8], kd);
+              acc = dot8_f32k(acc, qrow[c8], kd);
+              // K reads in groups of four units: fewer registers live at once
+              if ((c8 & 3) == 3) __builtin_amdgcn_sched_barrier(0);
             }
           } else {
 #pragma unroll
-            for (int c8 = 0; c8 < 16; ++c8) acc = dot8_bf16(acc, qr[c8], reinterpret_cast<const uint4*>(s_krow[i])[c8]);
+            for (int c8 = 0; c8 < 16; ++c8) {
+              acc = dot8_bf16(acc, qrow[c8], reinterpret_cast<const uint4*>(s_krow[i])[c8]);
+              if ((c8 & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+            }
           }
           term = __fmul_rn(wh, acc > 0.0f ? acc : 0.0f);
         }
@@ -1193,22 +1223,10 @@ __global__ __launch_bounds__(kChunkThreads) void select_classify_kernel(SelectAr
 #pragma unroll
           for (int j = 0; j < 16; ++j) total = __fadd_rn(total, tv[j]);
         }
-        if (lane == 0) s_bkey[p0 + i] = score_key(total);
+        if (lane == 0) put_band(p0 + i, cstart + s_bpos[p0 + i], score_key(total));
         __builtin_amdgcn_wave_barrier();
       }
-      __syncthreads();  // keys visible; the staging rows may be reused
-    }
-  }
-  // the chunk's band entries: one slot reservation per block
-  if (nb > 0) {
-    if (tid == 0) s_base = atomicAdd(&st[2], nb);
-    __syncthreads();
-    for (int i = tid; i < nb; i += kChunkThreads) {
-      const int t = s_band[i];
-      const uint32_t key = s_bkey[i];
-      keys[t] = key;
-      const int slot = s_base + i;
-      if (slot < kBandCap) band[slot] = ((uint64_t)key << 32) | (uint32_t)~(uint32_t)t;
+      __syncthreads();  // the staging rows may be reused
     }
   }
 }
