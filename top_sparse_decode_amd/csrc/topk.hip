@@ -257,36 +257,36 @@ __device__ float exact_dsa_score(const ScoreArgs& sa, int b, int g, int t, float
     float term = 0.0f;
     if (h < G) {
       const uint16_t* qh = qb + (int64_t)h * 128;
-      // all loads in flight at once, then the ordered dot product
-      uint4 kr[16], qr[16];
-      float ksc = 1.0f;
-      if (fp8) {
-        const uint8_t* krow = reinterpret_cast<const uint8_t*>(sa.k) + koff;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) kr[i] = *reinterpret_cast<const uint4*>(krow + 16 * i);
-        ksc = sa.k_scale[fp8_scale_index(page, g, slot, sa.num_kv_heads, sa.page_size)];
-      } else {
-        const uint16_t* krow = reinterpret_cast<const uint16_t*>(sa.k) + koff;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) kr[i] = *reinterpret_cast<const uint4*>(krow + 8 * i);
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) qr[i] = *reinterpret_cast<const uint4*>(qh + 8 * i);
+      const float ksc = fp8 ? sa.k_scale[fp8_scale_index(page, g, slot, sa.num_kv_heads, sa.page_size)] : 1.0f;
+      // two halves of the row (dims 0..63, 64..127), each with its loads in
+      // flight at once, then the ordered dot product
       float acc = 0.0f;
-      if (fp8) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          float kd[16];
-          fp8x4_dequant(kr[i].x, ksc, kd);
-          fp8x4_dequant(kr[i].y, ksc, kd + 4);
-          fp8x4_dequant(kr[i].z, ksc, kd + 8);
-          fp8x4_dequant(kr[i].w, ksc, kd + 12);
-          acc = dot8_f32k(acc, qr[2 * i], kd);
-          acc = dot8_f32k(acc, qr[2 * i + 1], kd + 8);
+      for (int half = 0; half < 2; ++half) {
+        uint4 kr[8], qr[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qr[i] = *reinterpret_cast<const uint4*>(qh + 64 * half + 8 * i);
+        if (fp8) {
+          const uint8_t* krow = reinterpret_cast<const uint8_t*>(sa.k) + koff + 64 * half;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) kr[i] = *reinterpret_cast<const uint4*>(krow + 16 * i);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float kd[16];
+            fp8x4_dequant(kr[i].x, ksc, kd);
+            fp8x4_dequant(kr[i].y, ksc, kd + 4);
+            fp8x4_dequant(kr[i].z, ksc, kd + 8);
+            fp8x4_dequant(kr[i].w, ksc, kd + 12);
+            acc = dot8_f32k(acc, qr[2 * i], kd);
+            acc = dot8_f32k(acc, qr[2 * i + 1], kd + 8);
+          }
+        } else {
+          const uint16_t* krow = reinterpret_cast<const uint16_t*>(sa.k) + koff + 64 * half;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) kr[i] = *reinterpret_cast<const uint4*>(krow + 8 * i);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc = dot8_bf16(acc, qr[i], kr[i]);
         }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc = dot8_bf16(acc, qr[i], kr[i]);
       }
       const float r = acc > 0.0f ? acc : 0.0f;
       term = __fmul_rn(wb[h], r);
@@ -331,6 +331,9 @@ __device__ __forceinline__ void select_row_block(const SelectArgs& a, int row, S
   const float* s = a.scores + (int64_t)row * a.row_stride;
   uint32_t* keys = reinterpret_cast<uint32_t*>(a.keys) + (int64_t)row * a.row_stride;
   constexpr int PER = kTile * NI;
+  // loops over the tiles: unrolled in full when the tiles are held in
+  // registers, by two when they are re-read (the rare overflow fallback)
+  constexpr int kU = RESIDENT ? NI : 2;
   const int nsc = RESIDENT ? 1 : (L + PER - 1) / PER;
   const bool vec = ((reinterpret_cast<uintptr_t>(s) & 15) == 0);
   const float kNan = __builtin_nanf("");
@@ -364,7 +367,7 @@ __device__ __forceinline__ void select_row_block(const SelectArgs& a, int row, S
   float lo = __builtin_inff(), hi = -__builtin_inff();
   int nfin = 0;
   for (int sc = 0; sc < nsc; ++sc) {
-#pragma unroll
+#pragma unroll kU
     for (int i = 0; i < NI; ++i) {
       const float4 x = get(sc, i);
       const float e4[4] = {x.x, x.y, x.z, x.w};
@@ -392,7 +395,7 @@ __device__ __forceinline__ void select_row_block(const SelectArgs& a, int row, S
     for (int i = tid; i < kBins; i += kSelThreads) sh.hist[i] = 0;
     __syncthreads();
     for (int sc = 0; sc < nsc; ++sc) {
-#pragma unroll
+#pragma unroll kU
       for (int i = 0; i < NI; ++i) {
         const float4 x = get(sc, i);
         const float e4[4] = {x.x, x.y, x.z, x.w};
@@ -417,7 +420,7 @@ __device__ __forceinline__ void select_row_block(const SelectArgs& a, int row, S
     if (bstar >= 0) {
       float mlo = __builtin_inff(), mhi = -__builtin_inff();
       for (int sc = 0; sc < nsc; ++sc) {
-#pragma unroll
+#pragma unroll kU
         for (int i = 0; i < NI; ++i) {
           const float4 x = get(sc, i);
           const float e4[4] = {x.x, x.y, x.z, x.w};
@@ -441,7 +444,7 @@ __device__ __forceinline__ void select_row_block(const SelectArgs& a, int row, S
   }
   int n_in = 0, n_band = 0;
   for (int sc = 0; sc < nsc; ++sc) {
-#pragma unroll
+#pragma unroll kU
     for (int i = 0; i < NI; ++i) {
       const float4 x = get(sc, i);
       const float e4[4] = {x.x, x.y, x.z, x.w};
@@ -534,7 +537,7 @@ __device__ __forceinline__ void select_row_block(const SelectArgs& a, int row, S
       if (tid == 0) sh.rcount = 0;
       __syncthreads();
       int bidx[NI][4];
-#pragma unroll
+#pragma unroll kU
       for (int i = 0; i < NI; ++i) {
         const uint32_t byte = sh.cls[i * kSelThreads + tid];
         const int t0 = tok(0, i);
@@ -560,7 +563,7 @@ __device__ __forceinline__ void select_row_block(const SelectArgs& a, int row, S
       __syncthreads();
       uint32_t keepm[NI];
       int kept[NI];
-#pragma unroll
+#pragma unroll kU
       for (int i = 0; i < NI; ++i) {
         const uint32_t byte = sh.cls[i * kSelThreads + tid];
         keepm[i] = 0;
@@ -589,7 +592,7 @@ __device__ __forceinline__ void select_row_block(const SelectArgs& a, int row, S
         if constexpr (NI > 1) emit_tile(1, (total & 0xFFFF) + (packed >> 16));
       } else {
         int base = 0;
-#pragma unroll
+#pragma unroll kU
         for (int i = 0; i < NI; ++i) {
           int total;
           emit_tile(i, base + block_excl_scan<kSelThreads>(kept[i], sh.tmp, &total));
