@@ -1065,7 +1065,7 @@ __global__ __launch_bounds__(kChunkThreads) void select_classify_kernel(SelectAr
   constexpr int kQStride = 17;
   __shared__ __attribute__((aligned(16))) uint4 s_q[FAST ? 64 * kQStride : 1];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int row = blockIdx.y, c = blockIdx.x;
+  const int row = blockIdx.x, c = blockIdx.y;  // chunk-major grid
   const int g = row % a.groups, b = row / a.groups;
   const ScoreArgs& sa = a.score;
   const int G = FAST ? sa.q_heads / sa.num_kv_heads : 0;  // <= 64 on the fast path
@@ -1249,7 +1249,7 @@ __global__ __launch_bounds__(kChunkThreads) void select_emit_kernel(SelectArgs a
   } u;
   __shared__ __attribute__((aligned(16))) float s_terms[kSelWaves][kWave];
   const int tid = threadIdx.x;
-  const int row = blockIdx.y, c = blockIdx.x;
+  const int row = blockIdx.x, c = blockIdx.y;  // chunk-major grid
   const int cstart = c * kSelChunk;
   // loads that do not depend on the row's statistics, in flight together
   float x[kPerThread];
@@ -1477,13 +1477,18 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t st) {
   if (rows == 0) return hipSuccess;
   if (a.row_stride > select_max_row()) return hipErrorInvalidValue;
   const dim3 grid(max(a.nchunks, 1), rows);
+  // classify and emit run chunk-major (block x = row, y = chunk): blocks
+  // handed out together belong to different rows, the row's blocks share an
+  // XCD when the row count is a multiple of 8, and the blocks of chunks past
+  // short rows' ends come last
+  const dim3 cgrid(rows, max(a.nchunks, 1));
   if (a.nchunks > 0) {
     select_hist_kernel<<<grid, kChunkThreads, 0, st>>>(a);
-    if (a.row_bound) select_classify_kernel<true><<<grid, kChunkThreads, 0, st>>>(a);
-    else select_classify_kernel<false><<<grid, kChunkThreads, 0, st>>>(a);
+    if (a.row_bound) select_classify_kernel<true><<<cgrid, kChunkThreads, 0, st>>>(a);
+    else select_classify_kernel<false><<<cgrid, kChunkThreads, 0, st>>>(a);
   }
   // emit also covers the output of rows whose tokens are all kept
-  const dim3 egrid(max(a.nchunks, (a.k + kSelChunk - 1) / kSelChunk), rows);
+  const dim3 egrid(rows, max(a.nchunks, (a.k + kSelChunk - 1) / kSelChunk));
   if (a.row_bound) select_emit_kernel<true><<<egrid, kChunkThreads, 0, st>>>(a);
   else select_emit_kernel<false><<<egrid, kChunkThreads, 0, st>>>(a);
   return hipGetLastError();
