@@ -1129,16 +1129,20 @@ __global__ __launch_bounds__(kChunkThreads) void select_classify_kernel(SelectAr
   }
   const int nb = s_nband;  // (visible: the barriers above)
   if (nb == 0) return;
-  // the chunk's entries of the row's band list: one reservation per block
-  if (tid == 0) s_base = atomicAdd(&st[2], nb);
-  __syncthreads();
-  const int base = s_base;
+  // The chunk's entries of the row's band list: one reservation per block.
+  // Re-scored bands publish the reservation with the staging barrier below,
+  // so that its round trip overlaps the staging loads.
+  int reserved = 0;
+  if (tid == 0) reserved = atomicAdd(&st[2], nb);
   // band entry of token t with key `key`, list slot i of the chunk
   auto put_band = [&](int i, int t, uint32_t key) {
+    const int slot = s_base + i;
     keys[t] = key;
-    if (base + i < kBandCap) band[base + i] = ((uint64_t)key << 32) | (uint32_t)~(uint32_t)t;
+    if (slot < kBandCap) band[slot] = ((uint64_t)key << 32) | (uint32_t)~(uint32_t)t;
   };
   if (!FAST || cut.bstar < 0) {
+    if (tid == 0) s_base = reserved;
+    __syncthreads();
     // the scores are the keys: each thread writes its own band tokens
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e)
@@ -1185,6 +1189,7 @@ __global__ __launch_bounds__(kChunkThreads) void select_classify_kernel(SelectAr
           }
         }
       }
+      if (p0 == 0 && tid == 0) s_base = reserved;
       __syncthreads();
       for (int i = wid; i < np; i += kSelWaves) {
         float term = 0.0f;
