@@ -37,6 +37,23 @@ struct Vec<uint16_t> {
   }
 };
 
+// Sum of x over each aligned group of N lanes (N = 8, 16 or 32), in every
+// lane of the group.  Groups of 16 use DPP rotations within a 16-lane row
+// (VALU operands, no LDS permutes); other sizes use lane shuffles.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N == 16) {
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x122, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x121, 0xF, 0xF, false));
+  } else {
+#pragma unroll
+    for (int off = N / 2; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  }
+  return x;
+}
+
 __device__ __forceinline__ void merge_ml(float& m, float& l, float mo, float lo, float& a_self, float& a_other) {
   const float M = fmaxf(m, mo);
   if (M == -__builtin_inff()) {
@@ -156,28 +173,48 @@ __global__ __launch_bounds__(256) void attn_vec_kernel(AttnArgs a) {
           kbuf[q] = *reinterpret_cast<const uint4*>(kb + (okb[q] ? k_o : 0) + sub * EPL);
           vbuf[q] = *reinterpret_cast<const uint4*>(vb + (okb[q] ? v_o : 0) + sub * EPL);
         }
+        // the group's logits first, then one rescale per head for the kPF
+        // rows (against their joint maximum) and their weighted V rows
+        float x[kPF][G];
 #pragma unroll
         for (int q = 0; q < kPF; ++q) {
-          const bool ok = okb[q];
-          float kv[EPL], vv[EPL];
+          float kv[EPL];
           Vec<T>::unpack(kbuf[q], kv);
+#pragma unroll
+          for (int j = 0; j < G; ++j) {
+            float d = 0.0f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) d = __builtin_fmaf(qf[j][e], kv[e], d);
+            x[q][j] = group_sum<LPR>(d);
+          }
+        }
+        float mn[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          mn[j] = m[j];
+#pragma unroll
+          for (int q = 0; q < kPF; ++q)
+            if (okb[q]) mn[j] = fmaxf(mn[j], x[q][j]);
+          // no usable row yet: nothing to rescale or add
+          if (mn[j] != -__builtin_inff()) {
+            const float al = exp2f(m[j] - mn[j]);  // 0 while m is -inf
+            l[j] *= al;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) o[j][e] *= al;
+            m[j] = mn[j];
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < kPF; ++q) {
+          if (!okb[q]) continue;
+          float vv[EPL];
           Vec<T>::unpack(vbuf[q], vv);
 #pragma unroll
           for (int j = 0; j < G; ++j) {
-            float x = 0.0f;
+            const float p = exp2f(x[q][j] - mn[j]);
+            l[j] += p;
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) x = __builtin_fmaf(qf[j][e], kv[e], x);
-#pragma unroll
-            for (int off = LPR / 2; off > 0; off >>= 1) x += __shfl_xor(x, off);
-            if (ok) {
-              const float mn = fmaxf(m[j], x);
-              const float al = exp2f(m[j] - mn);
-              const float p = exp2f(x - mn);
-              l[j] = l[j] * al + p;
-#pragma unroll
-              for (int e = 0; e < EPL; ++e) o[j][e] = o[j][e] * al + p * vv[e];
-              m[j] = mn;
-            }
+            for (int e = 0; e < EPL; ++e) o[j][e] = __builtin_fmaf(p, vv[e], o[j][e]);
           }
         }
       }
