@@ -608,26 +608,27 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_mla_kernel(AttnArgs a) {
   }
 }
 
-// Combine of the MLA partials: one 256-thread block per (request, wave w,
-// quarter of the value columns): thread (tile n, lane l) owns heads
-// 32w + 8(r/4) + 4(l/32) + r%4 (r < 16) at dv = 128*quarter + 32*(n%4) +
-// l%32.  Split weights 2^(m_s - M) / sum_s l_s 2^(m_s - M) are computed once
-// per head into LDS; each thread then has the partials of eight splits in
-// flight at a time; the result is transposed through LDS so output rows are
+// Combine of the MLA partials: one 512-thread block per (request, wave w,
+// quarter of the value columns): thread (tile n, half jh, lane l) owns heads
+// 32w + 8(r/4) + 4(l/32) + r%4 (8jh <= r < 8jh + 8) at dv = 128*quarter +
+// 32*(n%4) + l%32.  Split weights 2^(m_s - M) / sum_s l_s 2^(m_s - M) are
+// computed once per head into LDS; each thread then has the partials of 16
+// splits in flight at a time; the result is transposed through LDS so output rows are
 // written contiguously.
 constexpr int kMlaMaxSplits = 64;
 
-__global__ __launch_bounds__(256) void attn_mla_combine_kernel(AttnArgs a, int nw) {
+__global__ __launch_bounds__(512) void attn_mla_combine_kernel(AttnArgs a, int nw) {
   __shared__ float s_m[kMlaMaxSplits][32], s_l[kMlaMaxSplits][32];
   __shared__ float s_w[kMlaMaxSplits][32];   // weight of split s for head 32w + h
   __shared__ float s_out[32][128 + 4];       // [head][dv in the quarter], padded
   const int tid = threadIdx.x;
-  const int lane = tid & 63, n = tid >> 6;  // tile within the quarter: 0..3
+  const int lane = tid & 63, n = tid >> 7;  // tile within the quarter: 0..3
+  const int jh = (tid >> 6) & 1;            // which eight of the lane's 16 values
   const int quarter = blockIdx.x % 4, w = (blockIdx.x / 4) % nw, b = blockIdx.x / (4 * nw);
   const int col = lane & 31, hf = lane >> 5;
   const int S = a.splits;
   // ---- m and l of (split, head), all loads at once
-  for (int i = tid; i < S * 32; i += 256) {
+  for (int i = tid; i < S * 32; i += 512) {
     const int sp = i >> 5, h = i & 31;
     const float* ml = a.part_ml + (((int64_t)b * S + sp) * a.q_heads + 32 * w + h) * 2;
     s_m[sp][h] = ml[0];
@@ -649,41 +650,37 @@ __global__ __launch_bounds__(256) void attn_mla_combine_kernel(AttnArgs a, int n
   }
   __syncthreads();
   // ---- weighted sum over splits of this thread's 16 partial values
-  float o[16];
+  float o[8];  // values 8jh .. 8jh+7 of the lane's 16
 #pragma unroll
-  for (int r = 0; r < 16; ++r) o[r] = 0.0f;
+  for (int r = 0; r < 8; ++r) o[r] = 0.0f;
   const int tile = 4 * quarter + n;  // N tile of the partial layout (0..15)
   const uint16_t* pbase = reinterpret_cast<const uint16_t*>(a.part_o) + (((int64_t)w * 16 + tile) * 64 + lane) * 16;
   const int64_t sstride = (int64_t)nw * 16 * 64 * 16;  // one split's partial, in elements
-  for (int s0 = 0; s0 < S; s0 += 8) {
-    uint4 q[8][2];
+  for (int s0 = 0; s0 < S; s0 += 16) {
+    uint4 q[16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < 16; ++u)
+      if (s0 + u < S) q[u] = reinterpret_cast<const uint4*>(pbase + ((int64_t)b * S + s0 + u) * sstride)[jh];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
       if (s0 + u < S) {
-        const uint4* src = reinterpret_cast<const uint4*>(pbase + ((int64_t)b * S + s0 + u) * sstride);
-        q[u][0] = src[0];
-        q[u][1] = src[1];
-      }
+        const uint32_t wv[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (s0 + u < S) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const uint32_t wv[4] = {q[u][j].x, q[u][j].y, q[u][j].z, q[u][j].w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r0 = 8 * j + 2 * e;
-            o[r0] += bf16_lo(wv[e]) * s_w[s0 + u][8 * (r0 / 4) + 4 * hf + (r0 % 4)];
-            o[r0 + 1] += bf16_hi(wv[e]) * s_w[s0 + u][8 * ((r0 + 1) / 4) + 4 * hf + ((r0 + 1) % 4)];
-          }
+        for (int e = 0; e < 4; ++e) {
+          const int r0 = 8 * jh + 2 * e;
+          o[2 * e] += bf16_lo(wv[e]) * s_w[s0 + u][8 * (r0 / 4) + 4 * hf + (r0 % 4)];
+          o[2 * e + 1] += bf16_hi(wv[e]) * s_w[s0 + u][8 * ((r0 + 1) / 4) + 4 * hf + ((r0 + 1) % 4)];
         }
       }
   }
   // ---- transpose to [head][dv] and write rows
 #pragma unroll
-  for (int r = 0; r < 16; ++r) s_out[8 * (r / 4) + 4 * hf + (r % 4)][32 * n + col] = o[r];
+  for (int r = 0; r < 8; ++r) {
+    const int rr = 8 * jh + r;
+    s_out[8 * (rr / 4) + 4 * hf + (rr % 4)][32 * n + col] = o[r];
+  }
   __syncthreads();
-  for (int i = tid; i < 32 * 128; i += 256) {
+  for (int i = tid; i < 32 * 128; i += 512) {
     const int h = i / 128, d = i % 128;
     const int64_t oi = ((int64_t)b * a.q_heads + 32 * w + h) * kMlaDv + 128 * quarter + d;
     if (a.out_dtype == 0)
@@ -779,7 +776,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
       default: return hipErrorInvalidValue;
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    attn_mla_combine_kernel<<<a.batch * nw * 4, 256, 0, st>>>(a, nw);
+    attn_mla_combine_kernel<<<a.batch * nw * 4, 512, 0, st>>>(a, nw);
     return hipGetLastError();
   } else {
     dim3 grid(a.splits, a.batch * a.num_kv_heads);
