@@ -327,28 +327,25 @@ int orc_local_to_global(const int32_t* block_table, int32_t max_pages, int32_t b
 
 /* ------------------------------------------------------------------ TriAttention modes */
 
-/* Normalization of one member row (see oracle.h): strided binary64 partial
- * sums in token order, then the partials in order. */
+/* Normalization of one member row (see oracle.h): the population mean and
+ * standard deviation of the row's finite scores, each sum taken in plain
+ * token order with every binary64 operation rounded on its own. */
 static void tri_normalize_row(const float* row, int32_t L, int32_t row_len, float* z) {
-  double part[256];
   int64_t n = 0;
-  for (int c = 0; c < 256; ++c) part[c] = 0.0;
+  double s1 = 0.0;
   for (int32_t t = 0; t < L; ++t)
     if (isfinite(row[t])) {
-      part[t % 256] = part[t % 256] + (double)row[t];
+      s1 = s1 + (double)row[t];
       ++n;
     }
-  double s1 = 0.0;
-  for (int c = 0; c < 256; ++c) s1 = s1 + part[c];
   const double mu = n > 0 ? s1 / (double)n : 0.0;
-  for (int c = 0; c < 256; ++c) part[c] = 0.0;
+  double s2 = 0.0;
   for (int32_t t = 0; t < L; ++t)
     if (isfinite(row[t])) {
       const double d = (double)row[t] - mu;
-      part[t % 256] = part[t % 256] + d * d;
+      const double dd = d * d;
+      s2 = s2 + dd;
     }
-  double s2 = 0.0;
-  for (int c = 0; c < 256; ++c) s2 = s2 + part[c];
   const double sigma = n > 0 ? sqrt(s2 / (double)n) : 0.0;
   for (int32_t t = 0; t < row_len; ++t) {
     if (t >= L || !isfinite(row[t])) {
@@ -356,7 +353,8 @@ static void tri_normalize_row(const float* row, int32_t L, int32_t row_len, floa
     } else if (sigma == 0.0) {
       z[t] = 0.0f;
     } else {
-      z[t] = (float)(((double)row[t] - mu) / sigma);
+      const double d = (double)row[t] - mu;
+      z[t] = (float)(d / sigma);
     }
   }
 }

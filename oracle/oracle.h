@@ -110,11 +110,12 @@ int orc_local_to_global(const int32_t* block_table, int32_t max_pages, int32_t b
  * them, written out in full.
  *
  * scores is [layers][batch][groups][row_len].  Normalization, per member row
- * (layer, b, g), over its finite scores at t < kv_lens[b] (n of them):
- *   P_c = sum over those t with t % 256 == c, t ascending, of (double)s_t
- *         (each addition rounded in binary64), c = 0..255;
- *   mu  = (sum of P_0 .. P_255 in order, binary64) / n;
- *   Q_c, var likewise from d_t * d_t with d_t = (double)s_t - mu; var = sum / n;
+ * (layer, b, g), over its finite scores at t < kv_lens[b] (n of them), every
+ * binary64 operation rounded on its own:
+ *   mu  = (((0 + s_t0) + s_t1) + ...) / n, the finite s_t in token order,
+ *         each widened exactly to binary64;
+ *   var = (((0 + d_t0*d_t0) + d_t1*d_t1) + ...) / n, same order, with
+ *         d_t = (double)s_t - mu;
  *   sigma = sqrt(var);
  *   z_t = (float)(((double)s_t - mu) / sigma)  (0 when sigma == 0),
  *   z_t = -inf for a non-finite score and for t >= kv_lens[b].

@@ -534,6 +534,34 @@ def test_tri_normalize_bitwise_where_every_order_is_exact():
     assert np.array_equal(z4.view(np.uint32), z.view(np.uint32))
 
 
+def test_tri_normalize_sums_in_token_order():
+    # Rows built so that the binary64 sums round differently in every order.
+    # ulp(2^60) in binary64 is 256, so 2^60 + 1 rounds back to 2^60, while
+    # 2^60 + 255 rounds up to 2^60 + 256.  Closed forms of the sequential sums:
+    #   A = [2^60, 1 (x255), -2^60]: mu = 0 exactly (the ones vanish); a sum
+    #       over 256 strided partials (t % 256) would give 255/257, as would
+    #       the exact sum;
+    #   B = [1 (x255), 2^60, -2^60]: mu = 256/257 (the ones round up to 256
+    #       on meeting 2^60); the reverse order, the strided order and the
+    #       exact sum give 255/257.
+    # In both rows the squared deviations sum to exactly 2^121 (the terms
+    # near 1 vanish next to 2^120), so sigma = sqrt(2^121 / 257).
+    import math
+    big = F32(2.0 ** 60)
+    a = np.concatenate([[big], np.ones(255, F32), [-big]]).astype(F32)
+    b = np.concatenate([np.ones(255, F32), [big], [-big]]).astype(F32)
+    s = np.stack([a, b]).reshape(1, 1, 2, 257)
+    z = oracle.tri_select(s, np.array([257], np.int32), "per_layer_perhead", 4)["z"][0, 0]
+    sigma = math.sqrt(2.0 ** 121 / 257)
+    for g, mu in ((0, 0.0), (1, 256.0 / 257.0)):
+        row = s[0, 0, g].astype(np.float64)
+        want = np.array([(x - mu) / sigma for x in row]).astype(F32)
+        assert np.array_equal(z[g].view(np.uint32), want.view(np.uint32)), f"row {g}"
+    # the strided reading's mean would move every z of a one by a visible amount
+    strided_mu = 255.0 / 257.0
+    assert F32((1.0 - strided_mu) / sigma) != z[0, 1]
+
+
 def test_tri_constant_row_and_empty_row():
     s = np.full((1, 2, 1, 300), 3.25, F32)
     kv = np.array([300, 0], np.int32)
