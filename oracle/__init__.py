@@ -40,7 +40,7 @@ GROUP_SUM, GROUP_MEAN, RELU_WEIGHTED = 0, 1, 2
 _MODES = {"group_sum": GROUP_SUM, "group_mean": GROUP_MEAN, "relu_weighted": RELU_WEIGHTED}
 _ERRORS = {1: "bad argument", 2: "page id out of range", 3: "NaN score", 4: "index out of range"}
 
-CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-std=c11"]
+CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-std=c11", "-fopenmp"]
 
 
 def build(force: bool = True) -> str:
@@ -83,10 +83,18 @@ def _load():
         lib.orc_attention.argtypes = [P, I32, P, I32, P, I32, I32, PP, PP, I32, P, I32, F, P]
         lib.orc_local_to_global.argtypes = [P, I32, I32, I32, I32, P, I32, I32, P]
         lib.orc_tri_select.argtypes = [P, I32, I32, I32, I32, P, I32, I32, P, P, P, P]
+        lib.orc_set_threads.argtypes = [I32]
+        lib.orc_set_threads.restype = ctypes.c_int
         for f in (lib.orc_score, lib.orc_topk, lib.orc_attention, lib.orc_local_to_global, lib.orc_tri_select):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
+
+
+def set_threads(n: int = 0) -> int:
+    """Threads the oracle's row loops use (n > 0 sets them); returns the count
+    in effect.  Results are bit-identical for every count."""
+    return int(_load().orc_set_threads(int(n)))
 
 
 def _check(rc: int, what: str) -> None:

@@ -15,6 +15,22 @@
 #include <stdlib.h>
 #include <string.h>
 
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------ threads */
+
+int orc_set_threads(int32_t n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+  return omp_get_max_threads();
+#else
+  (void)n;
+  return 1;
+#endif
+}
+
 /* ------------------------------------------------------------------ helpers */
 
 /* bfloat16 is the upper 16 bits of a binary32: widening is exact. */
@@ -106,18 +122,26 @@ int orc_score(const int32_t* block_table, int32_t max_pages, const int32_t* kv_l
   const int32_t G = q_heads / Hkv;
   const float inv_g = (float)(1.0 / (double)G);
 
-  float* qf = (float*)malloc(sizeof(float) * (size_t)q_heads * (size_t)D);
-  float* kf = (float*)malloc(sizeof(float) * (size_t)D);
-  if (!qf || !kf) { free(qf); free(kf); return ORC_EARG; }
-
-  int rc = ORC_OK;
-  for (int32_t b = 0; b < batch && rc == ORC_OK; ++b) {
-    int32_t L = kv_lens[b];
-    if (L < 0 || L > row_len || L > max_pages * k->page_size) { rc = ORC_EARG; break; }
-    for (int32_t i = 0; i < q_heads * D; ++i)
-      qf[i] = load_elem(q, q_dtype, (int64_t)b * q_heads * D + i);
-    for (int32_t g = 0; g < Hkv && rc == ORC_OK; ++g) {
-      float* row = scores + ((int64_t)b * Hkv + g) * row_len;
+  /* rows (b, g) are independent: with OpenMP they run on several threads,
+   * each row's arithmetic unchanged (the result does not depend on the
+   * thread count); the first failing row in row order decides the status */
+  const int64_t nrows = (int64_t)batch * Hkv;
+  int* row_rc = (int*)calloc((size_t)(nrows > 0 ? nrows : 1), sizeof(int));
+  if (!row_rc) return ORC_EARG;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < nrows; ++r) {
+    const int32_t b = (int32_t)(r / Hkv), g = (int32_t)(r % Hkv);
+    float* qf = (float*)malloc(sizeof(float) * (size_t)G * (size_t)D);
+    float* kf = (float*)malloc(sizeof(float) * (size_t)D);
+    int rc = ORC_OK;
+    const int32_t L = kv_lens[b];
+    float* row = scores + r * row_len;
+    if (!qf || !kf) rc = ORC_EARG;
+    else if (L < 0 || L > row_len || L > max_pages * k->page_size) rc = ORC_EARG;
+    if (rc == ORC_OK) {
+      for (int32_t j = 0; j < G; ++j)
+        for (int32_t d = 0; d < D; ++d)
+          qf[(int64_t)j * D + d] = load_elem(q, q_dtype, ((int64_t)b * q_heads + g * G + j) * D + d);
       for (int32_t t = 0; t < row_len; ++t) row[t] = -INFINITY;
       for (int32_t t = 0; t < L; ++t) {
         int64_t off = row_offset(k, block_table, max_pages, b, g, t);
@@ -132,15 +156,15 @@ int orc_score(const int32_t* block_table, int32_t max_pages, const int32_t* kv_l
         float s = 0.0f;
         for (int32_t j = 0; j < G; ++j) {
           int32_t h = g * G + j;
-          float dh = dot_f32_sequential(qf + (int64_t)h * D, kf, D);
+          float dh = dot_f32_sequential(qf + (int64_t)j * D, kf, D);
           if (mode == ORC_GROUP_SUM) {
             float term = dh * head_scale;
             s = s + term;
           } else if (mode == ORC_GROUP_MEAN) {
             s = s + dh;
           } else {
-            float r = dh > 0.0f ? dh : 0.0f;
-            float term = weights[(int64_t)b * q_heads + h] * r;
+            float rl = dh > 0.0f ? dh : 0.0f;
+            float term = weights[(int64_t)b * q_heads + h] * rl;
             s = s + term;
           }
         }
@@ -148,9 +172,13 @@ int orc_score(const int32_t* block_table, int32_t max_pages, const int32_t* kv_l
         row[t] = s;
       }
     }
+    row_rc[r] = rc;
+    free(qf);
+    free(kf);
   }
-  free(qf);
-  free(kf);
+  int rc = ORC_OK;
+  for (int64_t r = 0; r < nrows && rc == ORC_OK; ++r) rc = row_rc[r];
+  free(row_rc);
   return rc;
 }
 
@@ -188,32 +216,41 @@ int orc_topk(const float* scores, int32_t batch, int32_t groups, int32_t row_len
              const int32_t* kv_lens, int32_t k, int32_t* indices, int32_t* counts) {
   if (!scores || !kv_lens || !indices || batch < 0 || groups <= 0 || row_len < 0 || k <= 0)
     return ORC_EARG;
-  scored_tok* buf = (scored_tok*)malloc(sizeof(scored_tok) * (size_t)(row_len > 0 ? row_len : 1));
-  int32_t* keep = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
-  if (!buf || !keep) { free(buf); free(keep); return ORC_EARG; }
-  int rc = ORC_OK;
-  for (int32_t b = 0; b < batch && rc == ORC_OK; ++b) {
-    int32_t L = kv_lens[b];
-    if (L < 0 || L > row_len) { rc = ORC_EARG; break; }
-    for (int32_t g = 0; g < groups; ++g) {
-      const float* row = scores + ((int64_t)b * groups + g) * row_len;
+  const int64_t nrows = (int64_t)batch * groups;
+  int* row_rc = (int*)calloc((size_t)(nrows > 0 ? nrows : 1), sizeof(int));
+  if (!row_rc) return ORC_EARG;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < nrows; ++r) {
+    const int32_t b = (int32_t)(r / groups);
+    scored_tok* buf = (scored_tok*)malloc(sizeof(scored_tok) * (size_t)(row_len > 0 ? row_len : 1));
+    int32_t* keep = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+    int rc = ORC_OK;
+    const int32_t L = kv_lens[b];
+    if (!buf || !keep || L < 0 || L > row_len) rc = ORC_EARG;
+    if (rc == ORC_OK) {
+      const float* row = scores + r * row_len;
       for (int32_t t = 0; t < L; ++t) {
         if (isnan(row[t])) { rc = ORC_ENAN; break; }
         buf[t].s = row[t];
         buf[t].t = t;
       }
-      if (rc != ORC_OK) break;
+    }
+    if (rc == ORC_OK) {
       qsort(buf, (size_t)L, sizeof(scored_tok), cmp_rank);
       int32_t n = L < k ? L : k;
       for (int32_t i = 0; i < n; ++i) keep[i] = buf[i].t;
       qsort(keep, (size_t)n, sizeof(int32_t), cmp_int);
-      int32_t* out = indices + ((int64_t)b * groups + g) * k;
+      int32_t* out = indices + r * k;
       for (int32_t i = 0; i < k; ++i) out[i] = i < n ? keep[i] : -1;
-      if (counts) counts[(int64_t)b * groups + g] = n;
+      if (counts) counts[r] = n;
     }
+    row_rc[r] = rc;
+    free(buf);
+    free(keep);
   }
-  free(buf);
-  free(keep);
+  int rc = ORC_OK;
+  for (int64_t r = 0; r < nrows && rc == ORC_OK; ++r) rc = row_rc[r];
+  free(row_rc);
   return rc;
 }
 
@@ -239,63 +276,67 @@ int orc_attention(const int32_t* block_table, int32_t max_pages, const int32_t* 
   if (k->dtype == ORC_FP8 || v->dtype == ORC_FP8) return ORC_EARG;  /* indexer pools only */
   const int32_t G = q_heads / Hkv;
 
-  double* x = (double*)malloc(sizeof(double) * (size_t)k_sel);
-  int64_t* koff = (int64_t*)malloc(sizeof(int64_t) * (size_t)k_sel);
-  int64_t* voff = (int64_t*)malloc(sizeof(int64_t) * (size_t)k_sel);
-  double* acc = (double*)malloc(sizeof(double) * (size_t)v_dim);
-  if (!x || !koff || !voff || !acc) { free(x); free(koff); free(voff); free(acc); return ORC_EARG; }
-
-  int rc = ORC_OK;
-  for (int32_t b = 0; b < batch && rc == ORC_OK; ++b) {
-    int32_t L = kv_lens[b];
-    for (int32_t g = 0; g < Hkv && rc == ORC_OK; ++g) {
-      const int32_t* sel = indices + ((int64_t)b * Hkv + g) * k_sel;
-      int32_t n = 0;
-      for (int32_t i = 0; i < k_sel; ++i) {
-        int32_t t = sel[i];
-        if (t < 0) continue;
-        if (t >= L) { rc = ORC_EINDEX; break; }
-        int64_t ko = row_offset(k, block_table, max_pages, b, g, t);
-        int64_t vo = row_offset(v, block_table, max_pages, b, g, t);
-        if (ko < 0 || vo < 0) { rc = ORC_EPAGE; break; }
-        koff[n] = ko;
-        voff[n] = vo;
-        ++n;
-      }
-      if (rc != ORC_OK) break;
-      for (int32_t j = 0; j < G; ++j) {
-        int32_t h = g * G + j;
-        double* o = out + ((int64_t)b * q_heads + h) * v_dim;
-        if (n == 0) {
-          for (int32_t d = 0; d < v_dim; ++d) o[d] = 0.0;
-          continue;
-        }
-        int64_t qo = ((int64_t)b * q_heads + h) * D;
-        double m = -INFINITY;
-        for (int32_t i = 0; i < n; ++i) {
-          double s = 0.0;
-          for (int32_t d = 0; d < D; ++d)
-            s += (double)load_elem(q, q_dtype, qo + d) *
-                 (double)load_elem(k->data, k->dtype, koff[i] + d);
-          x[i] = (double)scale * s;
-          if (x[i] > m) m = x[i];
-        }
-        double l = 0.0;
-        for (int32_t d = 0; d < v_dim; ++d) acc[d] = 0.0;
-        for (int32_t i = 0; i < n; ++i) {
-          double p = exp(x[i] - m);
-          l += p;
-          for (int32_t d = 0; d < v_dim; ++d)
-            acc[d] += p * (double)load_elem(v->data, v->dtype, voff[i] + d);
-        }
-        for (int32_t d = 0; d < v_dim; ++d) o[d] = acc[d] / l;
-      }
+  const int64_t nrows = (int64_t)batch * Hkv;
+  int* row_rc = (int*)calloc((size_t)(nrows > 0 ? nrows : 1), sizeof(int));
+  if (!row_rc) return ORC_EARG;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < nrows; ++r) {
+    const int32_t b = (int32_t)(r / Hkv), g = (int32_t)(r % Hkv);
+    double* x = (double*)malloc(sizeof(double) * (size_t)k_sel);
+    int64_t* koff = (int64_t*)malloc(sizeof(int64_t) * (size_t)k_sel);
+    int64_t* voff = (int64_t*)malloc(sizeof(int64_t) * (size_t)k_sel);
+    double* acc = (double*)malloc(sizeof(double) * (size_t)v_dim);
+    int rc = (!x || !koff || !voff || !acc) ? ORC_EARG : ORC_OK;
+    const int32_t L = kv_lens[b];
+    const int32_t* sel = indices + r * k_sel;
+    int32_t n = 0;
+    for (int32_t i = 0; i < k_sel && rc == ORC_OK; ++i) {
+      int32_t t = sel[i];
+      if (t < 0) continue;
+      if (t >= L) { rc = ORC_EINDEX; break; }
+      int64_t ko = row_offset(k, block_table, max_pages, b, g, t);
+      int64_t vo = row_offset(v, block_table, max_pages, b, g, t);
+      if (ko < 0 || vo < 0) { rc = ORC_EPAGE; break; }
+      koff[n] = ko;
+      voff[n] = vo;
+      ++n;
     }
+    for (int32_t j = 0; j < G && rc == ORC_OK; ++j) {
+      int32_t h = g * G + j;
+      double* o = out + ((int64_t)b * q_heads + h) * v_dim;
+      if (n == 0) {
+        for (int32_t d = 0; d < v_dim; ++d) o[d] = 0.0;
+        continue;
+      }
+      int64_t qo = ((int64_t)b * q_heads + h) * D;
+      double m = -INFINITY;
+      for (int32_t i = 0; i < n; ++i) {
+        double sd = 0.0;
+        for (int32_t d = 0; d < D; ++d)
+          sd += (double)load_elem(q, q_dtype, qo + d) *
+                (double)load_elem(k->data, k->dtype, koff[i] + d);
+        x[i] = (double)scale * sd;
+        if (x[i] > m) m = x[i];
+      }
+      double l = 0.0;
+      for (int32_t d = 0; d < v_dim; ++d) acc[d] = 0.0;
+      for (int32_t i = 0; i < n; ++i) {
+        double p = exp(x[i] - m);
+        l += p;
+        for (int32_t d = 0; d < v_dim; ++d)
+          acc[d] += p * (double)load_elem(v->data, v->dtype, voff[i] + d);
+      }
+      for (int32_t d = 0; d < v_dim; ++d) o[d] = acc[d] / l;
+    }
+    row_rc[r] = rc;
+    free(x);
+    free(koff);
+    free(voff);
+    free(acc);
   }
-  free(x);
-  free(koff);
-  free(voff);
-  free(acc);
+  int rc = ORC_OK;
+  for (int64_t r = 0; r < nrows && rc == ORC_OK; ++r) rc = row_rc[r];
+  free(row_rc);
   return rc;
 }
 
@@ -375,6 +416,7 @@ int orc_tri_select(const float* scores, int32_t layers, int32_t batch, int32_t g
   }
   float* zz = (float*)malloc(sizeof(float) * (size_t)(members * row_len > 0 ? members * row_len : 1));
   if (!zz) return ORC_EARG;
+#pragma omp parallel for schedule(dynamic, 1)
   for (int64_t m = 0; m < members; ++m) {
     const int32_t b = (int32_t)((m / groups) % batch);
     tri_normalize_row(scores + m * row_len, kv_lens[b], row_len, zz + m * row_len);

@@ -127,6 +127,11 @@ int orc_local_to_global(const int32_t* block_table, int32_t max_pages, int32_t b
  * z (optional) receives every member's z, shape of scores; reduced
  * (optional) the reduced rows [out_rows][row_len]; indices [out_rows][k],
  * counts [out_rows] (may be NULL). */
+/* Threads used by the row loops above (OpenMP over independent (request,
+ * head group) rows; every result is bit-identical for any thread count).
+ * n > 0 sets the count; returns the count now in effect. */
+int orc_set_threads(int32_t n);
+
 #define ORC_PER_LAYER_PERHEAD 0
 #define ORC_PER_HEAD 1
 #define ORC_UNION 2

@@ -158,17 +158,14 @@ def test_fp8_band_overflow_falls_back_exactly():
     assert_outputs_close(out_to_numpy(step.out), ref["out"], w.out_dtype, "fp8 band overflow")
 
 
-def test_fp8_full_dsa_sampled():
+def test_fp8_full_dsa_all_requests():
     w = synth.make_workload(4, index_dtype="fp8")
-    say("[fp8 config 4 sampled]")
+    say("[fp8 config 4, all requests]")
     step = api.prepare(w, precision=api.FAST)
     step.run()
     torch.cuda.synchronize()
-    reqs = [0, w.batch - 1]
-    ref = oracle_run(w, reqs)
-    assert np.array_equal(step.indices.cpu().numpy()[reqs], ref["indices"])
-    worst = assert_outputs_close(out_to_numpy(step.out)[reqs], ref["out"], w.out_dtype, "fp8 config 4")
+    ref = oracle_run(w)
+    assert np.array_equal(step.indices.cpu().numpy(), ref["indices"])
+    assert np.array_equal(step.counts.cpu().numpy(), ref["counts"])
+    worst = assert_outputs_close(out_to_numpy(step.out), ref["out"], w.out_dtype, "fp8 config 4")
     say(f"fp8 config 4: worst row rel-L2 {worst:.3e}")
-    idx = step.indices.cpu().numpy()
-    assert np.all(np.diff(idx, axis=-1) > 0)
-    assert torch.isfinite(step.out.float()).all()

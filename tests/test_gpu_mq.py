@@ -58,8 +58,8 @@ def test_mq_with_hint_writeback():
         assert torch.equal(step.hint, step.indices)
 
 
-def test_mq_full_dsa_sampled():
+def test_mq_full_dsa_all_requests():
     w = synth.make_workload(4, next_n=2)
-    worst, step = check(w, api.FAST, reqs=[0, 15], what="config 4 next_n 2 (sampled)")
+    worst, step = check(w, api.FAST, what="config 4 next_n 2 (all requests)")
     say(f"config 4 next_n 2: worst row rel-L2 {worst:.3e}")
     assert torch.isfinite(step.out.float()).all()

@@ -4,6 +4,7 @@ definitions, a library SDPA, and invariants the method implies), chosen so
 that a plausible slip -- a dropped term, a wrong index or sign, a transposed
 operand, a different summation order, FMA contraction, the wrong tie rule --
 fails at least one of them.  CPU only."""
+import os
 from fractions import Fraction
 
 import numpy as np
@@ -678,3 +679,24 @@ def test_block_attention_of_one_covering_block_is_dense_attention():
     blk = oracle.expand_blocks(np.zeros((2, G, 1), np.int32), w.kv_lens, 128)   # one block of 128
     got = oracle.attention(w.block_table, w.kv_lens, w.q, w.k, w.v, w.v_dim, blk, w.softmax_scale)
     assert np.array_equal(got, dense)
+
+
+# ---------------------------------------------------------------- threads
+
+def test_oracle_results_do_not_depend_on_thread_count():
+    # the row loops run on several threads; each row's arithmetic is the
+    # same, so every output is bit-identical to the one-thread run
+    w = synth.make_workload(5, batch=6, min_len=300, max_len=5000, topk=256, idx_heads=16, heads=32)
+    s = np.random.default_rng(36).standard_normal((2, 3, 2, 3000)).astype(F32)
+    kv = np.array([3000, 1700, 5], np.int32)
+    runs = []
+    for n in (1, 4):
+        oracle.set_threads(n)
+        runs.append((oracle.sparse_decode(w), oracle.tri_select(s, kv, "union", 64)))
+    oracle.set_threads(os.cpu_count() or 1)
+    (a, ta), (b, tb) = runs
+    for key in ("scores", "indices", "counts"):
+        assert np.array_equal(np.asarray(a[key]).view(np.uint8), np.asarray(b[key]).view(np.uint8)), key
+    assert np.array_equal(a["out"].view(np.uint64), b["out"].view(np.uint64))
+    for key in ("z", "reduced", "indices", "counts"):
+        assert np.array_equal(np.asarray(ta[key]).view(np.uint8), np.asarray(tb[key]).view(np.uint8)), key

@@ -5,24 +5,24 @@
 // normalize/reduce step between paged-K scoring and TopK / tie settlement and
 // names three eviction modes (union, per_head, per_layer_perhead); its Main
 // Files name score normalization and union reduction.  The pages give no
-// formula, so the library fixes one evaluation and keeps to it bit for bit:
+// formula; the library computes the plain population z-score, with its sums
+// taken in token order like every other reduction of the library:
 //
 //   per member row m = (layer, request b, KV head g), over its finite scores
-//   at t < kv_len[b] (n of them):
-//     P_c  = sum_{t % 256 == c} (double)s_t, t ascending, binary64 adds;
-//     mu   = (P_0 + P_1 + ... + P_255, in order) / n;
-//     var  = (the same sums of d_t * d_t, d_t = (double)s_t - mu) / n;
+//   at t < kv_len[b] (n of them), every binary64 operation rounded on its own:
+//     mu   = (((0 + s_t0) + s_t1) + ...) / n, t ascending;
+//     var  = (((0 + d_t0*d_t0) + d_t1*d_t1) + ...) / n, d_t = (double)s_t - mu;
 //     z_t  = (float)(((double)s_t - mu) / sqrt(var)), 0 when var == 0,
 //            -inf for a non-finite score or t >= kv_len[b];
 //   reduced row: r_t = max over the mode's members of z_t, members visited
 //   layer by layer and head by head, a later member replacing the running
 //   value only when strictly larger.
 //
-// Kernels: tri_stats_kernel (one 256-thread block per member row: thread c
-// owns the tokens t = c + 256 i, so its partial is exactly P_c and the loads
-// are coalesced; rows up to 4096 tokens stay in registers between the two
-// passes) and tri_reduce_kernel (a token per lane, the members split into
-// four ordered quarters).  Selection then runs on the reduced rows.
+// Kernels: tri_stats_kernel (one lane per member row walks its row in token
+// order; the wave brings tiles of its rows in with coalesced loads and hands
+// each row to its lane through LDS) and tri_reduce_kernel /
+// tri_reduce4_kernel (a token per lane, the members split into four ordered
+// quarters).  Selection then runs on the reduced rows.
 #include "common.h"
 #include "kernels.h"
 
@@ -31,83 +31,99 @@
 namespace sd {
 
 constexpr int kTriThreads = 256;
-constexpr int kTriRegs = 16;  // tokens per thread kept in registers (rows up to 4096)
 constexpr int kTriSpan = 4096;  // tokens per block of the one-slice reduce
 
+// Statistics: the sums are chains of dependent binary64 additions, one chain
+// per member row, so the work is spread as one lane per row.  A wave owns
+// kTriRows rows (lanes 0 .. kTriRows-1 run the chains).  Tiles of kTriTile
+// tokens of those rows come in with one coalesced load per row and 64-token
+// piece (lane l: token 64 i + l), sit in registers while the previous tile's
+// chains run, and reach the owning lanes through LDS (row stride padded by
+// one float).  Both passes read the row from memory; the second pass finds
+// most of it in the last-level cache.
+constexpr int kTriRows = 16;
+constexpr int kTriTile = 256;
+constexpr int kTriPieces = kTriTile / 64;
+constexpr int kTriWaves = kTriThreads / 64;
+
 __global__ __launch_bounds__(kTriThreads) void tri_stats_kernel(TriArgs a) {
-  __shared__ double s_part[kTriThreads];
-  __shared__ double s_mu;
-  const int m = blockIdx.x;  // member row (layer, b, g)
-  const int tid = threadIdx.x;
-  const int b = (m / a.groups) % a.batch;
-  const int L = clamp_len(a.kv_lens[b], a.row_stride);
-  const float* row = a.scores + (int64_t)m * a.row_stride;
-  if (a.lens && (m % a.groups) == 0 && tid == 0) a.lens[m / a.groups] = a.kv_lens[b];
-  const bool resident = L <= kTriThreads * kTriRegs;
-  float x[kTriRegs];
-  double part = 0.0;
+  __shared__ float s_tile[kTriWaves][kTriRows][kTriTile + 1];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int members = a.layers * a.batch * a.groups;
+  const int m0 = (blockIdx.x * kTriWaves + wid) * kTriRows;  // first row of this wave
+  if (m0 >= members) return;
+  const int nrows = min(kTriRows, members - m0);
+  // lane r < nrows owns row m0 + r; Lr is its kv_len, Lmax the wave's longest
+  int Lr = 0;
+  if (lane < nrows) {
+    const int m = m0 + lane;
+    const int b = (m / a.groups) % a.batch;
+    Lr = clamp_len(a.kv_lens[b], a.row_stride);
+    if (a.lens && (m % a.groups) == 0) a.lens[m / a.groups] = a.kv_lens[b];
+  }
+  const int Lmax = wave_max(Lr);
+  const float* base = a.scores + (int64_t)m0 * a.row_stride;
+  float (*tile)[kTriTile + 1] = s_tile[wid];
+  // tile loads: row r, tokens t0 + 64 i + lane (in bounds of the row; tokens
+  // past the row's kv_len are loaded only if the row is that long, else -inf)
+  auto load_tile = [&](int t0, float (&v)[kTriRows][kTriPieces]) {
+#pragma unroll
+    for (int r = 0; r < kTriRows; ++r) {
+      const int Lrow = __shfl(Lr, r);
+#pragma unroll
+      for (int i = 0; i < kTriPieces; ++i) {
+        const int t = t0 + 64 * i + lane;
+        v[r][i] = (r < nrows && t < Lrow) ? base[(int64_t)r * a.row_stride + t] : -__builtin_inff();
+      }
+    }
+  };
+  auto store_tile = [&](const float (&v)[kTriRows][kTriPieces]) {
+#pragma unroll
+    for (int r = 0; r < kTriRows; ++r)
+#pragma unroll
+      for (int i = 0; i < kTriPieces; ++i) tile[r][64 * i + lane] = v[r][i];
+  };
+  // one pass: the chain over the row in token order; `second` selects the
+  // squared deviations from mu
+  auto pass = [&](bool second, double mu, int& n) -> double {
+    double acc = 0.0;
+    n = 0;
+    float v[kTriRows][kTriPieces];
+    load_tile(0, v);
+    for (int t0 = 0; t0 < Lmax; t0 += kTriTile) {
+      store_tile(v);
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      // the next tile's loads go out before this tile's chains run
+      if (t0 + kTriTile < Lmax) load_tile(t0 + kTriTile, v);
+      if (lane < nrows) {
+        const int tend = min(kTriTile, Lr - t0);
+        for (int j = 0; j < tend; ++j) {
+          const float x = tile[lane][j];
+          if (__builtin_isfinite(x)) {
+            if (second) {
+              const double d = __dsub_rn((double)x, mu);
+              acc = __dadd_rn(acc, __dmul_rn(d, d));
+            } else {
+              acc = __dadd_rn(acc, (double)x);
+            }
+            ++n;
+          }
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+    }
+    return acc;
+  };
   int n = 0;
-  if (resident) {
-#pragma unroll
-    for (int i = 0; i < kTriRegs; ++i) {
-      const int t = tid + kTriThreads * i;
-      x[i] = t < L ? row[t] : -__builtin_inff();
-    }
-#pragma unroll
-    for (int i = 0; i < kTriRegs; ++i)
-      if (__builtin_isfinite(x[i])) {
-        part = __dadd_rn(part, (double)x[i]);
-        ++n;
-      }
-  } else {
-    for (int t = tid; t < L; t += kTriThreads) {
-      const float v = row[t];
-      if (__builtin_isfinite(v)) {
-        part = __dadd_rn(part, (double)v);
-        ++n;
-      }
-    }
-  }
-  s_part[tid] = part;
-  // n over the block (exact integer sum)
-  int nn = wave_sum(n);
-  __shared__ int s_n[kTriThreads / 64];
-  if ((tid & 63) == 0) s_n[tid >> 6] = nn;
-  __syncthreads();
-  const int total = s_n[0] + s_n[1] + s_n[2] + s_n[3];
-  if (tid == 0) {
-    double s1 = 0.0;
-    for (int c = 0; c < kTriThreads; ++c) s1 = __dadd_rn(s1, s_part[c]);
-    s_mu = total > 0 ? __ddiv_rn(s1, (double)total) : 0.0;
-  }
-  __syncthreads();
-  const double mu = s_mu;
-  part = 0.0;
-  if (resident) {
-#pragma unroll
-    for (int i = 0; i < kTriRegs; ++i)
-      if (__builtin_isfinite(x[i])) {
-        const double d = __dsub_rn((double)x[i], mu);
-        part = __dadd_rn(part, __dmul_rn(d, d));
-      }
-  } else {
-    for (int t = tid; t < L; t += kTriThreads) {
-      const float v = row[t];
-      if (__builtin_isfinite(v)) {
-        const double d = __dsub_rn((double)v, mu);
-        part = __dadd_rn(part, __dmul_rn(d, d));
-      }
-    }
-  }
-  __syncthreads();  // every thread has read s_mu
-  s_part[tid] = part;
-  __syncthreads();
-  if (tid == 0) {
-    double s2 = 0.0;
-    for (int c = 0; c < kTriThreads; ++c) s2 = __dadd_rn(s2, s_part[c]);
-    const double sigma = total > 0 ? __dsqrt_rn(__ddiv_rn(s2, (double)total)) : 0.0;
-    a.stats[2 * (int64_t)m] = mu;
-    a.stats[2 * (int64_t)m + 1] = sigma;
+  const double s1 = pass(false, 0.0, n);
+  const double mu = n > 0 ? __ddiv_rn(s1, (double)n) : 0.0;
+  const double s2 = pass(true, mu, n);
+  if (lane < nrows) {
+    const double sigma = n > 0 ? __dsqrt_rn(__ddiv_rn(s2, (double)n)) : 0.0;
+    a.stats[2 * (int64_t)(m0 + lane)] = mu;
+    a.stats[2 * (int64_t)(m0 + lane) + 1] = sigma;
   }
 }
 
@@ -308,7 +324,8 @@ hipError_t launch_tri(const TriArgs& a, hipStream_t st) {
   const int members = a.layers * a.batch * a.groups;
   const int out_rows = tri_out_rows(a.layers, a.batch, a.groups, a.mode);
   if (members == 0 || a.row_stride == 0) return hipSuccess;
-  tri_stats_kernel<<<members, kTriThreads, 0, st>>>(a);
+  const int stat_blocks = (members + kTriWaves * kTriRows - 1) / (kTriWaves * kTriRows);
+  tri_stats_kernel<<<stat_blocks, kTriThreads, 0, st>>>(a);
   const int nm = a.mode == 0 ? 1 : (a.mode == 1 ? a.layers : a.layers * a.groups);
   const bool vec = (a.row_stride % 4) == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(a.reduced) & 15) == 0;
