@@ -346,6 +346,23 @@ sd_status sd_sparse_decode_workspace_size(const sd_sparse_decode_args* args, siz
 sd_status sd_sparse_decode(const sd_sparse_decode_args* args, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
 
+/* The fused step without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, kernels and results as
+ * sd_sparse_decode; its scratch is a fixed array inside the library, one per
+ * device (sd_sparse_decode_noalloc_max_bytes() bytes = 64 MiB, held by each
+ * GPU the library runs on until the process ends).  The call allocates and
+ * frees nothing.  A call whose workspace (sd_sparse_decode_workspace_size)
+ * would exceed the scratch returns SD_ERR_WORKSPACE_TOO_SMALL and launches
+ * nothing.  stream must belong to the current device (else
+ * SD_ERR_INVALID_ARGUMENT).  The first call on a device looks up the
+ * scratch's device address there (no allocation).  Every call on one device
+ * shares that device's scratch: calls that overlap on one GPU (other streams,
+ * other threads) race and must be serialized by the caller; the scratch keeps
+ * the last call's contents, and nothing in the step depends on them. */
+size_t sd_sparse_decode_noalloc_max_bytes(void);
+sd_status sd_sparse_decode_noalloc(const sd_sparse_decode_args* args, hipStream_t stream);
+
 /* ------------------------------------------------------------------ indices */
 
 /* Request-local position -> flat pool slot page*page_size + t%page_size, -1

@@ -22,7 +22,7 @@ def _lib():
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:sd_status|const char\*|int32_t)\s+(sd_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:sd_status|const char\*|int32_t|size_t)\s+(sd_\w+)\s*\(", text, re.M)))
 
 
 def test_header_declares_the_entry_points():
@@ -221,6 +221,31 @@ def test_fused_workspace_and_validation():
     a.k.page_size = 32
     a.v = a.k
     assert lib.sd_sparse_decode_workspace_size(ctypes.byref(a), ctypes.byref(n)) == api.ERR_INVALID_ARGUMENT
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch():
+    # host-side checks only: nothing reaches a device.  Config-5 sizes (64
+    # requests up to 131072 tokens) need more scratch than the library holds.
+    lib = _lib()
+    cap = lib.sd_sparse_decode_noalloc_max_bytes()
+    assert cap == 64 << 20
+    a = api.sd_sparse_decode_args()
+    a.pages = api.sd_pages(8192, 12288, 64, 2048, 131072)
+    a.score_k = api.sd_pool(4096, api.BF16, 140000, 64, 1, 128, 64 * 128, 64 * 128, 128, None)
+    a.score_q, a.score_q_dtype, a.score_heads, a.head_weights = 16384, api.BF16, 64, 20480
+    a.mode, a.head_scale, a.precision, a.topk = api.RELU_WEIGHTED, 1.0, api.FAST, 2048
+    a.q, a.q_dtype, a.q_heads = 24576, api.BF16, 128
+    a.k = api.sd_pool(8192, api.BF16, 140000, 64, 1, 576, 64 * 576, 64 * 576, 576, None)
+    a.v = a.k
+    a.v_dim, a.softmax_scale, a.out, a.out_dtype = 512, 0.0721, 32768, api.BF16
+    n = ctypes.c_size_t(0)
+    assert lib.sd_sparse_decode_workspace_size(ctypes.byref(a), ctypes.byref(n)) == api.OK
+    assert n.value > cap
+    assert lib.sd_sparse_decode_noalloc(ctypes.byref(a), None) == api.ERR_WORKSPACE_TOO_SMALL
+    assert b"64 MiB" in lib.sd_last_error() or str(cap).encode() in lib.sd_last_error()
+    # argument errors are reported before any size or device question
+    a.topk = 0
+    assert lib.sd_sparse_decode_noalloc(ctypes.byref(a), None) == api.ERR_INVALID_ARGUMENT
 
 
 def test_local_to_global_validation():

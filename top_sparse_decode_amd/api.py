@@ -68,6 +68,7 @@ EXPORTS = ["sd_sparse_score_paged", "sd_topk_workspace_size", "sd_topk_select", 
            "sd_sparse_decode_workspace_size", "sd_sparse_decode", "sd_local_to_global",
            "sd_triattention_select_workspace_size", "sd_triattention_select",
            "sd_sparse_decode_attn_blocks_workspace_size", "sd_sparse_decode_attn_blocks",
+           "sd_sparse_decode_noalloc_max_bytes", "sd_sparse_decode_noalloc",
            "sd_status_string", "sd_last_error", "sd_version"]
 
 _lib = None
@@ -96,6 +97,7 @@ def load(path: str = LIB_PATH):
         "sd_sparse_decode_attn": [PP, P, E, I32, PL, PL, I32, P, I32, F, P, E, P, SZ, P],
         "sd_sparse_decode_workspace_size": [PA, ctypes.POINTER(SZ)],
         "sd_sparse_decode": [PA, P, SZ, P],
+        "sd_sparse_decode_noalloc": [PA, P],
         "sd_local_to_global": [PP, I32, I32, P, I32, I32, P, P],
         "sd_triattention_select_workspace_size": [I32, I32, I32, I32, E, I32, ctypes.POINTER(SZ)],
         "sd_sparse_decode_attn_blocks_workspace_size": [PP, I32, PL, I32, I32, I32, ctypes.POINTER(SZ)],
@@ -112,6 +114,8 @@ def load(path: str = LIB_PATH):
     lib.sd_last_error.restype = ctypes.c_char_p
     lib.sd_version.argtypes = []
     lib.sd_version.restype = ctypes.c_int32
+    lib.sd_sparse_decode_noalloc_max_bytes.argtypes = []
+    lib.sd_sparse_decode_noalloc_max_bytes.restype = ctypes.c_size_t
     _lib = lib
     return lib
 
@@ -267,6 +271,17 @@ def sparse_decode(args: sd_sparse_decode_args, workspace, workspace_bytes: Optio
     wb = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
     rc = load().sd_sparse_decode(ctypes.byref(args), _ptr(workspace), wb, _stream(stream))
     _check(rc, "sd_sparse_decode")
+
+
+def sparse_decode_noalloc_max_bytes() -> int:
+    return int(load().sd_sparse_decode_noalloc_max_bytes())
+
+
+def sparse_decode_noalloc(args: sd_sparse_decode_args, stream=None):
+    """sd_sparse_decode on the library's own per-device scratch (no caller
+    workspace, no allocation)."""
+    rc = load().sd_sparse_decode_noalloc(ctypes.byref(args), _stream(stream))
+    _check(rc, "sd_sparse_decode_noalloc")
 
 
 def local_to_global(pg: sd_pages, page_size: int, num_pages: int, local, out, stream=None):

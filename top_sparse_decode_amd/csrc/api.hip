@@ -10,11 +10,15 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "common.h"
 #include "kernels.h"
 #include "sparse_decode.h"
+
+// Device scratch of sd_sparse_decode_noalloc (64 MiB per device, see below).
+static __device__ __align__(256) unsigned char sd_noalloc_scratch[size_t(64) << 20];
 
 namespace {
 
@@ -607,19 +611,16 @@ sd_status sd_sparse_decode_workspace_size(const sd_sparse_decode_args* args, siz
   return SD_OK;
 }
 
-sd_status sd_sparse_decode(const sd_sparse_decode_args* args, void* workspace, size_t workspace_bytes,
-                           hipStream_t stream) {
-  g_err.clear();
-  sd_sparse_decode_args y;
-  FusedPlan f;
-  size_t mq = 0;
-  sd_status st = plan_multi_query(args, true, nullptr, &y, &f, &mq);
-  if (st != SD_OK) return st;
-  if (workspace_bytes < f.total + mq || (f.total + mq && !workspace))
-    return fail(SD_ERR_WORKSPACE_TOO_SMALL, "sparse_decode needs %zu workspace bytes", f.total + mq);
-  if (!aligned16(workspace)) return fail(SD_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+}  // extern "C"
+
+namespace {
+
+// The fused step on a validated plan (plan_multi_query with pointers) and a
+// workspace of at least f.total + mq bytes.
+sd_status run_sparse_decode(const sd_sparse_decode_args* args, sd_sparse_decode_args y, FusedPlan f,
+                            size_t mq, char* ws, hipStream_t stream) {
+  sd_status st = SD_OK;
   if (args->pages.batch == 0) return SD_OK;
-  char* ws = static_cast<char*>(workspace);
   if (mq) {
     // one decode row per (request, query token): the page tables repeated
     // and the causal lengths, at the end of the workspace; then plan again
@@ -681,6 +682,79 @@ sd_status sd_sparse_decode(const sd_sparse_decode_args* args, void* workspace, s
   f.attn.a.indices = idx;
   bind_attn_ws(&f.attn, ws + f.off_attn);
   return hip_status(sd::launch_attn(f.attn.a, stream), "attention");
+}
+
+// Scratch of the allocation-free fused step: one array per device (each GPU
+// the library runs on holds its own copy until the process ends), shared by
+// every call on that device.  In host code `sd_noalloc_scratch` names a
+// host-side stand-in, not device memory: the kernels get the device address
+// that hipGetSymbolAddress returns for the current device, looked up once
+// per device and kept.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+sd_status noalloc_scratch(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (stream) {
+    hipDevice_t sdev = -1;
+    if ((e = hipStreamGetDevice(stream, &sdev)) != hipSuccess) return hip_status(e, "hipStreamGetDevice");
+    if (sdev != dev)
+      return fail(SD_ERR_INVALID_ARGUMENT, "stream belongs to device %d but device %d is current", (int)sdev, dev);
+  }
+  if (dev < 0 || dev >= kMaxDevices) return fail(SD_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(sd_noalloc_scratch))) != hipSuccess)
+      return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(SD_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sd_status sd_sparse_decode(const sd_sparse_decode_args* args, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  g_err.clear();
+  sd_sparse_decode_args y;
+  FusedPlan f;
+  size_t mq = 0;
+  sd_status st = plan_multi_query(args, true, nullptr, &y, &f, &mq);
+  if (st != SD_OK) return st;
+  if (workspace_bytes < f.total + mq || (f.total + mq && !workspace))
+    return fail(SD_ERR_WORKSPACE_TOO_SMALL, "sparse_decode needs %zu workspace bytes", f.total + mq);
+  if (!aligned16(workspace)) return fail(SD_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  return run_sparse_decode(args, y, f, mq, static_cast<char*>(workspace), stream);
+}
+
+size_t sd_sparse_decode_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+sd_status sd_sparse_decode_noalloc(const sd_sparse_decode_args* args, hipStream_t stream) {
+  g_err.clear();
+  sd_sparse_decode_args y;
+  FusedPlan f;
+  size_t mq = 0;
+  sd_status st = plan_multi_query(args, true, nullptr, &y, &f, &mq);
+  if (st != SD_OK) return st;
+  if (f.total + mq > kNoAllocScratchBytes)
+    return fail(SD_ERR_WORKSPACE_TOO_SMALL,
+                "sparse_decode_noalloc: this call needs %zu bytes of scratch, more than the %zu the library holds "
+                "per device; use sd_sparse_decode with a caller workspace",
+                f.total + mq, kNoAllocScratchBytes);
+  if (args->pages.batch == 0) return SD_OK;
+  void* scratch = nullptr;
+  if ((st = noalloc_scratch(stream, &scratch)) != SD_OK) return st;
+  return run_sparse_decode(args, y, f, mq, static_cast<char*>(scratch), stream);
 }
 
 sd_status sd_local_to_global(const sd_pages* pages, int32_t page_size, int32_t num_pages,
