@@ -34,8 +34,10 @@ struct ScoreArgs {
 
 // Per-row selection statistics: [kmin key, kmax key, band count, cut (4
 // slots), score floor certified by the hint (float bits, -inf = none),
-// 2048-bin histogram].
-constexpr int kStatStride = 8 + 2048;
+// 2048-bin histogram, arrival counters of the one-launch selection's two row
+// barriers, 6 unused].  Cleared by the fast scorer or select_init.
+constexpr int kStatStride = 8 + 2048 + 8;
+constexpr int kStatBarrier = 8 + 2048;
 constexpr int kSelChunk = 4096;   // tokens per block in the multi-block selection
 constexpr int kBandCap = 4096;    // band entries kept per row before falling back
 
@@ -65,6 +67,9 @@ struct SelectArgs {
   // histogram pass reduces them into stats[0..1] and row_bound
   const int32_t* span_slots;  // [rows][nspans][4] or null
   int32_t nspans;
+  // one-launch selection: how long a block waits at a row barrier before it
+  // finishes its row alone (wall-clock ticks, 100 MHz; 0 = the default)
+  int64_t spin_ticks;
 };
 
 struct AttnArgs {

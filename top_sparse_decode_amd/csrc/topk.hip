@@ -34,6 +34,8 @@
 // (one wave per token: lane h evaluates head h's dot product left to right,
 // then the head terms are added in head order) and selected on exact keys.
 // The result is exactly the top-k of the exact scores.
+#include <stdlib.h>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -46,6 +48,27 @@ constexpr int kTile = 4 * kSelThreads;  // tokens per tile (one float4 per threa
 constexpr int kMaxNI = 32;              // tiles held in registers: rows up to 65536
 constexpr int kMaxChunks = 4;           // longer rows: up to 4 super-chunks, re-read per pass
 enum : uint32_t { kOut = 0, kIn = 1, kBand = 2, kPad = 3 };
+
+// Data that blocks of one launch hand to each other (the selection's band
+// list and chunk counts, read after a row barrier): device-coherent stores
+// and loads (agent-scope atomics, which bypass the per-XCD L2 state), no
+// cache-wide fences.
+__device__ __forceinline__ void st_coherent(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coherent(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t ld_coherent(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_coherent(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int2 ld_coherent2(const int32_t* p) {
+  const uint64_t v = ld_coherent(reinterpret_cast<const uint64_t*>(p));
+  return int2{(int)(uint32_t)v, (int)(uint32_t)(v >> 32)};
+}
 
 // Slot i of a row's output, and of its copy for the next step's hint when
 // the caller asked for one (the write-back rides along with the output
@@ -1050,55 +1073,53 @@ __global__ __launch_bounds__(kChunkThreads) void select_hist_kernel(SelectArgs a
     if (hist[i]) atomicAdd(&gh[i], hist[i]);
 }
 
+// Shared memory of the classify pass (the re-score buffers only with fast scores).
 template <bool FAST>
-__global__ __launch_bounds__(kChunkThreads) void select_classify_kernel(SelectArgs a) {
-  __shared__ ChunkShared sh;
-  __shared__ uint16_t s_bpos[kSelChunk];  // band tokens of the chunk (offsets in it)
-  __shared__ int s_nband, s_base;
-  __shared__ __attribute__((aligned(16))) float s_terms[kSelWaves][kWave];
+struct ClassifySmem {
+  ChunkShared sh;
+  uint16_t s_bpos[kSelChunk];  // band tokens of the chunk (offsets in it)
+  int s_nband, s_base;
   // K rows of band tokens being re-scored: bf16 rows as they are (256 bytes),
   // fp8 rows dequantized to binary32 (512 bytes)
-  __shared__ __attribute__((aligned(16))) float s_krow[kStageRows][128];
-  __shared__ int s_tpage[FAST ? kChunkThreads : 1];  // page of each thread's eight tokens
+  __attribute__((aligned(16))) float s_krow[kStageRows][128];
+  int s_tpage[FAST ? kChunkThreads : 1];  // page of each thread's eight tokens (fast scores)
   // query rows of the band re-score, one per head, 17 units apart (the
   // per-lane reads of one unit then hit distinct banks)
+  __attribute__((aligned(16))) uint4 s_q[FAST ? 64 * 17 : 1];
+};
+
+// This thread's page of its eight tokens (fast scores; one page: the fast
+// path's page size is a multiple of 16), or -1.
+__device__ __forceinline__ int thread_page(const SelectArgs& a, int b, int t0) {
+  const ScoreArgs& sa = a.score;
+  const int pi = t0 / sa.page_size;
+  return (t0 < a.row_stride && pi < sa.max_pages) ? sa.block_table[(int64_t)b * sa.max_pages + pi] : -1;
+}
+
+// Classify pass of chunk c of a row of more than k tokens, on the row's view
+// v, this thread's eight scores x (NaN past kv_len) and its bins hb of the
+// row's histogram: the cut, the chunk's (kept-for-sure, -inf) counts, and
+// its band entries (exact keys; re-scored with fast scores).  Returns the cut.
+template <bool FAST>
+__device__ RowCut classify_chunk(const SelectArgs& a, int row, int c, const RowView& v, const float (&x)[kPerThread],
+                                 const int (&hb)[kBinsPerThread], int tpage, ClassifySmem<FAST>& S,
+                                 float (*s_terms)[kWave]) {
   constexpr int kQStride = 17;
-  __shared__ __attribute__((aligned(16))) uint4 s_q[FAST ? 64 * kQStride : 1];
+  ChunkShared& sh = S.sh;
+  uint16_t* s_bpos = S.s_bpos;
+  int& s_nband = S.s_nband;
+  int& s_base = S.s_base;
+  float (*s_krow)[128] = S.s_krow;
+  int* s_tpage = S.s_tpage;
+  uint4* s_q = S.s_q;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int row = blockIdx.x, c = blockIdx.y;  // chunk-major grid
   const int g = row % a.groups, b = row / a.groups;
   const ScoreArgs& sa = a.score;
   const int G = FAST ? sa.q_heads / sa.num_kv_heads : 0;  // <= 64 on the fast path
-  // loads that do not depend on the cut, all in flight together
-  float x[kPerThread];
   const int t0 = c * kSelChunk + kPerThread * tid;
-  load8_raw(a.scores + (int64_t)row * a.row_stride, t0, a.row_stride, x);
-  int hb[kBinsPerThread];
-  {
-    const int32_t* gh = a.stats + (int64_t)row * kStatStride + 8;
-#pragma unroll
-    for (int j = 0; j < kBinsPerThread; ++j) hb[j] = gh[tid + j * kChunkThreads];
-  }
-  // fast scores: the page of this thread's eight tokens (one page: the fast
-  // path's page size is a multiple of 16)
-  int tpage = -1;
-  if constexpr (FAST) {
-    const int pi = t0 / sa.page_size;
-    if (t0 < a.row_stride && pi < sa.max_pages) tpage = sa.block_table[(int64_t)b * sa.max_pages + pi];
-  }
-  const RowView v = row_view(a, row);
-  if (v.L <= a.k || c * kSelChunk >= v.L) return;
-  mask8(t0, v.L, x);
   const RowCut cut = row_cut(a, row, v, sh, FAST, hb);
 
   if (tid == 0) s_nband = 0;
-  if (c == 0 && tid == 0) {  // for the emit kernel (identical in every block)
-    int32_t* stc = a.stats + (int64_t)row * kStatStride;
-    stc[3] = cut.bstar;
-    stc[4] = cut.nfin;
-    stc[5] = __float_as_int(cut.band_lo);
-    stc[6] = __float_as_int(cut.band_hi);
-  }
   __syncthreads();
   int n_in = 0, n_neg = 0;
   uint32_t* keys = reinterpret_cast<uint32_t*>(a.keys) + (int64_t)row * a.row_stride;
@@ -1124,11 +1145,10 @@ __global__ __launch_bounds__(kChunkThreads) void select_classify_kernel(SelectAr
   n_neg = chunk_sum_i(n_neg, sh.redi);  // (barrier: the band list complete)
   if (tid == 0) {
     int32_t* cc = a.chunk_counts + ((int64_t)row * a.nchunks + c) * 2;
-    cc[0] = n_in;
-    cc[1] = n_neg;
+    st_coherent(reinterpret_cast<uint64_t*>(cc), (uint64_t)(uint32_t)n_in | ((uint64_t)(uint32_t)n_neg << 32));
   }
   const int nb = s_nband;  // (visible: the barriers above)
-  if (nb == 0) return;
+  if (nb == 0) return cut;
   // The chunk's entries of the row's band list: one reservation per block.
   // Re-scored bands publish the reservation with the staging barrier below,
   // so that its round trip overlaps the staging loads.
@@ -1138,7 +1158,7 @@ __global__ __launch_bounds__(kChunkThreads) void select_classify_kernel(SelectAr
   auto put_band = [&](int i, int t, uint32_t key) {
     const int slot = s_base + i;
     keys[t] = key;
-    if (slot < kBandCap) band[slot] = ((uint64_t)key << 32) | (uint32_t)~(uint32_t)t;
+    if (slot < kBandCap) st_coherent(band + slot, ((uint64_t)key << 32) | (uint32_t)~(uint32_t)t);
   };
   if (!FAST || cut.bstar < 0) {
     if (tid == 0) s_base = reserved;
@@ -1147,7 +1167,7 @@ __global__ __launch_bounds__(kChunkThreads) void select_classify_kernel(SelectAr
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e)
       if (bslot[e] >= 0) put_band(bslot[e], t0 + e, score_key(x[e]));
-    return;
+    return cut;
   }
   {
     // Exact re-score of the band: the group's query rows and the K rows of
@@ -1237,6 +1257,38 @@ __global__ __launch_bounds__(kChunkThreads) void select_classify_kernel(SelectAr
       __syncthreads();  // the staging rows may be reused
     }
   }
+  return cut;
+}
+
+template <bool FAST>
+__global__ __launch_bounds__(kChunkThreads) void select_classify_kernel(SelectArgs a) {
+  __shared__ ClassifySmem<FAST> S;
+  __shared__ __attribute__((aligned(16))) float s_terms[kSelWaves][kWave];
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x, c = blockIdx.y;  // chunk-major grid
+  const int b = row / a.groups;
+  // loads that do not depend on the cut, all in flight together
+  float x[kPerThread];
+  const int t0 = c * kSelChunk + kPerThread * tid;
+  load8_raw(a.scores + (int64_t)row * a.row_stride, t0, a.row_stride, x);
+  int hb[kBinsPerThread];
+  {
+    const int32_t* gh = a.stats + (int64_t)row * kStatStride + 8;
+#pragma unroll
+    for (int j = 0; j < kBinsPerThread; ++j) hb[j] = gh[tid + j * kChunkThreads];
+  }
+  const int tpage = FAST ? thread_page(a, b, t0) : -1;
+  const RowView v = row_view(a, row);
+  if (v.L <= a.k || c * kSelChunk >= v.L) return;
+  mask8(t0, v.L, x);
+  const RowCut cut = classify_chunk<FAST>(a, row, c, v, x, hb, tpage, S, s_terms);
+  if (c == 0 && tid == 0) {  // for the emit kernel (identical in every block)
+    int32_t* stc = a.stats + (int64_t)row * kStatStride;
+    stc[3] = cut.bstar;
+    stc[4] = cut.nfin;
+    stc[5] = __float_as_int(cut.band_lo);
+    stc[6] = __float_as_int(cut.band_hi);
+  }
 }
 
 struct EmitShared {
@@ -1246,45 +1298,24 @@ struct EmitShared {
   int red2[4];
 };
 
+union EmitSmem {
+  EmitShared e;
+  SelShared one;  // fallback: one block finishes the row
+};
+
+// Emit pass of chunk c of a row of more than k tokens: the kept band entries
+// (the first k - |IN| in (key desc, position asc) order), then this chunk's
+// kept positions written at the offset the per-chunk counts give.  x holds
+// this thread's eight scores as loaded (masked here), ccv wave 0's chunk
+// counts (chunks tid and tid + 64).
 template <bool FAST>
-__global__ __launch_bounds__(kChunkThreads) void select_emit_kernel(SelectArgs a) {
-  __shared__ union {
-    EmitShared e;
-    SelShared one;  // fallback: one block finishes the row
-  } u;
-  __shared__ __attribute__((aligned(16))) float s_terms[kSelWaves][kWave];
+__device__ void emit_chunk(const SelectArgs& a, int row, int c, const RowView& v, const RowCut& cut, int nband,
+                           float (&x)[kPerThread], const int2 (&ccv)[2], EmitShared& ue) {
   const int tid = threadIdx.x;
-  const int row = blockIdx.x, c = blockIdx.y;  // chunk-major grid
   const int cstart = c * kSelChunk;
-  // loads that do not depend on the row's statistics, in flight together
-  float x[kPerThread];
   const int t0 = cstart + kPerThread * tid;
-  load8_raw(a.scores + (int64_t)row * a.row_stride, t0, a.row_stride, x);
-  const int32_t* cc = a.chunk_counts + (int64_t)row * a.nchunks * 2;
-  int2 ccv[2] = {};  // chunk tid and tid + 64 (wave 0)
-  if (tid < kWave) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      if (tid + kWave * j < a.nchunks) ccv[j] = *reinterpret_cast<const int2*>(cc + 2 * (tid + kWave * j));
-  }
-  const RowView v = row_view(a, row);
   const int k = a.k;
-  if (v.L <= k) {  // every token kept (dense-equivalent)
-    for (int t = cstart + tid; t < min(v.L, cstart + kSelChunk); t += kChunkThreads) put_index(a, row, t, t);
-    if (c == 0) {
-      for (int i = v.L + tid; i < k; i += kChunkThreads) put_index(a, row, i, -1);
-      if (a.counts && tid == 0) a.counts[row] = v.L;
-    }
-    return;
-  }
-  if (cstart >= v.L) return;
-  const int32_t* st = a.stats + (int64_t)row * kStatStride;
-  const int nband = st[2];
-  if (nband > kBandCap) {
-    if (c == 0) select_row_block<kMaxNI, false, FAST>(a, row, u.one, s_terms);
-    return;
-  }
-  const RowCut cut = stored_cut(a, row);
+  const int32_t* cc = a.chunk_counts + (int64_t)row * a.nchunks * 2;
   // per-chunk counts (kept-for-sure, -inf) before this chunk and in total:
   // wave 0 reduces them, LDS hands them to the block
   const int nch = (v.L + kSelChunk - 1) / kSelChunk;
@@ -1300,20 +1331,20 @@ __global__ __launch_bounds__(kChunkThreads) void select_emit_kernel(SelectArgs a
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       if (tid + kWave * j < nch) add(tid + kWave * j, ccv[j]);
-    for (int i = tid + 2 * kWave; i < nch; i += kWave) add(i, *reinterpret_cast<const int2*>(cc + 2 * i));
+    for (int i = tid + 2 * kWave; i < nch; i += kWave) add(i, ld_coherent2(cc + 2 * i));
     in_total = wave_sum(in_total);
     in_before = wave_sum(in_before);
     neg_before = wave_sum(neg_before);
     if (tid == 0) {
-      u.e.red2[0] = in_total;
-      u.e.red2[1] = in_before;
-      u.e.red2[2] = neg_before;
+      ue.red2[0] = in_total;
+      ue.red2[1] = in_before;
+      ue.red2[2] = neg_before;
     }
   }
-  for (int i = tid; i < nband; i += kChunkThreads) u.e.band[i] = a.band[(int64_t)row * kBandCap + i];
-  for (int i = tid; i < kSelChunk / 32; i += kChunkThreads) u.e.chosen[i] = 0u;
+  for (int i = tid; i < nband; i += kChunkThreads) ue.band[i] = ld_coherent(a.band + (int64_t)row * kBandCap + i);
+  for (int i = tid; i < kSelChunk / 32; i += kChunkThreads) ue.chosen[i] = 0u;
   __syncthreads();
-  const int in_total = u.e.red2[0], in_before = u.e.red2[1], neg_before = u.e.red2[2];
+  const int in_total = ue.red2[0], in_before = ue.red2[1], neg_before = ue.red2[2];
   const int need = k - in_total;  // BAND tokens to keep (>= 1)
 
   // Band entry i is kept iff fewer than `need` entries come before it in
@@ -1325,20 +1356,20 @@ __global__ __launch_bounds__(kChunkThreads) void select_emit_kernel(SelectArgs a
   if (cut.bstar >= 0) {
     if (nband <= 2 * kChunkThreads) {
       for (int i = tid; i < nband; i += kChunkThreads) {
-        const uint64_t x = u.e.band[i];
+        const uint64_t x = ue.band[i];
         int rank = 0;
-        for (int j = 0; j < nband; ++j) rank += u.e.band[j] > x;
+        for (int j = 0; j < nband; ++j) rank += ue.band[j] > x;
         if (rank < need) {
           const int t = (int)~(uint32_t)(x & 0xFFFFFFFFull);
           if (t < cstart) ++chosen_before;
-          else if (t < cstart + kSelChunk) atomicOr(&u.e.chosen[(t - cstart) >> 5], 1u << ((t - cstart) & 31));
+          else if (t < cstart + kSelChunk) atomicOr(&ue.chosen[(t - cstart) >> 5], 1u << ((t - cstart) & 31));
         }
       }
     } else {
       // sort (key desc, position asc) = descending 64-bit composite
       int nb_pow = 1;
       while (nb_pow < nband) nb_pow <<= 1;
-      for (int i = nband + tid; i < nb_pow; i += kChunkThreads) u.e.band[i] = 0ull;
+      for (int i = nband + tid; i < nb_pow; i += kChunkThreads) ue.band[i] = 0ull;
       __syncthreads();
       for (int size = 2; size <= nb_pow; size <<= 1)
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
@@ -1346,22 +1377,22 @@ __global__ __launch_bounds__(kChunkThreads) void select_emit_kernel(SelectArgs a
             const int lo = 2 * i - (i & (stride - 1));
             const int hi = lo + stride;
             const bool desc = (lo & size) == 0;
-            const uint64_t x0 = u.e.band[lo], x1 = u.e.band[hi];
+            const uint64_t x0 = ue.band[lo], x1 = ue.band[hi];
             if ((x0 < x1) == desc) {
-              u.e.band[lo] = x1;
-              u.e.band[hi] = x0;
+              ue.band[lo] = x1;
+              ue.band[hi] = x0;
             }
           }
           __syncthreads();
         }
       for (int i = tid; i < need && i < nband; i += kChunkThreads) {
-        const int t = (int)~(uint32_t)(u.e.band[i] & 0xFFFFFFFFull);
+        const int t = (int)~(uint32_t)(ue.band[i] & 0xFFFFFFFFull);
         if (t < cstart) ++chosen_before;
-        else if (t < cstart + kSelChunk) atomicOr(&u.e.chosen[(t - cstart) >> 5], 1u << ((t - cstart) & 31));
+        else if (t < cstart + kSelChunk) atomicOr(&ue.chosen[(t - cstart) >> 5], 1u << ((t - cstart) & 31));
       }
     }
   }
-  chosen_before = chunk_sum_i(chosen_before, u.e.cs.redi);  // (barrier: bitmap complete)
+  chosen_before = chunk_sum_i(chosen_before, ue.cs.redi);  // (barrier: bitmap complete)
 
   mask8(t0, v.L, x);
   uint32_t keep = 0;
@@ -1373,7 +1404,7 @@ __global__ __launch_bounds__(kChunkThreads) void select_emit_kernel(SelectArgs a
     if (cl == kBand) {
       if (cut.bstar >= 0) {
         const int r = t0 + e - cstart;
-        kp = (u.e.chosen[r >> 5] >> (r & 31)) & 1u;
+        kp = (ue.chosen[r >> 5] >> (r & 31)) & 1u;
       } else {
         ++nneg;  // -inf filler: decided by rank below
       }
@@ -1384,16 +1415,16 @@ __global__ __launch_bounds__(kChunkThreads) void select_emit_kernel(SelectArgs a
   int total;
   int offset;
   if (cut.bstar >= 0) {
-    offset = in_before + chosen_before + block_excl_scan<kChunkThreads>(nkeep, u.e.cs.tmp, &total);
+    offset = in_before + chosen_before + block_excl_scan<kChunkThreads>(nkeep, ue.cs.tmp, &total);
   } else {
     // fewer finite scores than k: all finite kept, then -inf ones by position
     const int need_neg = k - in_total;
-    const int neg_rank = neg_before + block_excl_scan<kChunkThreads>(nneg, u.e.cs.tmp, &total);
+    const int neg_rank = neg_before + block_excl_scan<kChunkThreads>(nneg, ue.cs.tmp, &total);
     int taken_before = min(max(need_neg, 0), neg_before);
     // kept so far in earlier chunks: their finite ones plus their taken -inf
     offset = in_before + taken_before;
     // this thread: finite kept before it in the chunk + -inf taken before it
-    int fin_prefix = block_excl_scan<kChunkThreads>(nkeep, u.e.cs.tmp, &total);
+    int fin_prefix = block_excl_scan<kChunkThreads>(nkeep, ue.cs.tmp, &total);
     const int take_before_me = min(max(need_neg, 0), neg_rank) - taken_before;
     offset += fin_prefix + take_before_me;
     int r = neg_rank;
@@ -1412,6 +1443,187 @@ __global__ __launch_bounds__(kChunkThreads) void select_emit_kernel(SelectArgs a
       ++offset;
     }
   if (a.counts && c == 0 && tid == 0) a.counts[row] = k;
+}
+
+// Rows of at most k tokens: every token kept, in order (chunk c's share),
+// then the -1 padding and the count (chunk 0).
+__device__ __forceinline__ void emit_all(const SelectArgs& a, int row, int c, int L) {
+  const int tid = threadIdx.x, cstart = c * kSelChunk, k = a.k;
+  for (int t = cstart + tid; t < min(L, cstart + kSelChunk); t += kChunkThreads) put_index(a, row, t, t);
+  if (c == 0) {
+    for (int i = L + tid; i < k; i += kChunkThreads) put_index(a, row, i, -1);
+    if (a.counts && tid == 0) a.counts[row] = L;
+  }
+}
+
+// Wave 0's per-chunk counts of a row (chunks tid and tid + 64).
+__device__ __forceinline__ void load_chunk_counts(const SelectArgs& a, int row, int2 (&ccv)[2]) {
+  const int tid = threadIdx.x;
+  const int32_t* cc = a.chunk_counts + (int64_t)row * a.nchunks * 2;
+  ccv[0] = ccv[1] = int2{0, 0};
+  if (tid < kWave) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      if (tid + kWave * j < a.nchunks) ccv[j] = ld_coherent2(cc + 2 * (tid + kWave * j));
+  }
+}
+
+template <bool FAST>
+__global__ __launch_bounds__(kChunkThreads) void select_emit_kernel(SelectArgs a) {
+  __shared__ EmitSmem u;
+  __shared__ __attribute__((aligned(16))) float s_terms[kSelWaves][kWave];
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x, c = blockIdx.y;  // chunk-major grid
+  const int cstart = c * kSelChunk;
+  // loads that do not depend on the row's statistics, in flight together
+  float x[kPerThread];
+  const int t0 = cstart + kPerThread * tid;
+  load8_raw(a.scores + (int64_t)row * a.row_stride, t0, a.row_stride, x);
+  int2 ccv[2];
+  load_chunk_counts(a, row, ccv);
+  const RowView v = row_view(a, row);
+  if (v.L <= a.k) {  // every token kept (dense-equivalent)
+    emit_all(a, row, c, v.L);
+    return;
+  }
+  if (cstart >= v.L) return;
+  const int32_t* st = a.stats + (int64_t)row * kStatStride;
+  const int nband = st[2];
+  if (nband > kBandCap) {
+    if (c == 0) select_row_block<kMaxNI, false, FAST>(a, row, u.one, s_terms);
+    return;
+  }
+  emit_chunk<FAST>(a, row, c, v, stored_cut(a, row), nband, x, ccv, u.e);
+}
+
+// ------------------------------------------------------------------ one launch
+
+// The three passes above in one launch, for grids whose blocks are all
+// resident at once: the blocks of a row meet at two row barriers (after the
+// histogram, after the classification) instead of kernel boundaries, and
+// keep their scores, view and cut in registers across them.
+//
+// A row barrier is an arrival counter in the row's statistics (cleared by
+// the fast scorer or select_init): each block publishes its writes, adds
+// one, and waits until every participating block has arrived.  The wait is
+// bounded: a block that has waited spin_ticks (it can only happen when other
+// work holds the CUs its partners need) finishes the whole row by itself
+// with select_row_block, which is exact on its own, and the row's other
+// blocks, which then never see it at the next barrier, do the same; every
+// block that writes the row's outputs writes the same values.
+constexpr int64_t kDefaultSpinTicks = 200000;  // 2 ms at the 100 MHz wall clock
+
+__device__ __forceinline__ bool row_barrier(int32_t* counter, int target, int64_t ticks, int* s_flag) {
+  // this thread's stores (coherent ones, atomics) have completed
+  asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int ok = 1;
+    const uint64_t t_start = wall_clock64();
+    while (ld_coherent(counter) < target) {
+      if ((int64_t)(wall_clock64() - t_start) > ticks) {
+        ok = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    *s_flag = ok;
+  }
+  __syncthreads();
+  const bool ok = *s_flag != 0;
+  __syncthreads();  // s_flag may be reused
+  return ok;
+}
+
+template <bool FAST>
+__global__ __launch_bounds__(kChunkThreads) void select_fused_kernel(SelectArgs a) {
+  __shared__ union {
+    struct {
+      int hist[kBins];
+      int red[kSelWaves];
+      uint32_t red3[3][kSelWaves];
+    } h;
+    ClassifySmem<FAST> cl;
+    EmitSmem em;
+  } u;
+  __shared__ __attribute__((aligned(16))) float s_terms[kSelWaves][kWave];
+  __shared__ int s_flag;
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x, c = blockIdx.y;  // chunk-major grid
+  const int b = row / a.groups;
+  int32_t* st = a.stats + (int64_t)row * kStatStride;
+  const int64_t ticks = a.spin_ticks > 0 ? a.spin_ticks : kDefaultSpinTicks;
+  // loads that do not depend on the row's statistics
+  float x[kPerThread];
+  const int t0 = c * kSelChunk + kPerThread * tid;
+  load8_raw(a.scores + (int64_t)row * a.row_stride, t0, a.row_stride, x);
+  const int tpage = FAST ? thread_page(a, b, t0) : -1;
+  RowKeys r;
+  if (a.span_slots) {
+    r = reduce_span_slots(a, row, u.h.red3);
+    // every block publishes the (identical) row keys and bound: a block that
+    // finishes the row alone reads them back
+    if (tid == 0) {
+      st[0] = (int32_t)r.kmin;
+      st[1] = (int32_t)r.kmax;
+      a.row_bound[row] = r.bound;
+    }
+  } else {
+    r = RowKeys{(uint32_t)st[0], (uint32_t)st[1], a.row_bound ? a.row_bound[row] : 0.0f};
+  }
+  RowView v = view_of_keys(a, row, r.kmin, r.kmax, -__builtin_inff());
+  if (v.L <= a.k) {  // every token kept (dense-equivalent): no barriers
+    emit_all(a, row, c, v.L);
+    return;
+  }
+  const int nch = (v.L + kSelChunk - 1) / kSelChunk;  // the row's participating blocks
+  if (c >= nch) return;
+  if (a.hint && v.any_finite) {
+    const float floor = hint_floor(a, row, v.L, r.bound, u.h.red);
+    v = view_of_keys(a, row, r.kmin, r.kmax, floor);
+    if (tid == 0) st[7] = __float_as_int(floor);
+  }
+  __syncthreads();  // stats written above, before a fallback reads them back
+
+  // ---- histogram (select_hist_kernel's pass)
+  mask8(t0, v.L, x);
+  if (v.any_finite) {
+    for (int i = tid; i < kBins; i += kChunkThreads) u.h.hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      const bool fin = __builtin_isfinite(x[e]) && x[e] >= v.lo;
+      hist_add(u.h.hist, fin ? bin_of_v(v, x[e]) : 0, fin);
+    }
+    __syncthreads();
+    int32_t* gh = st + 8;
+    for (int i = tid; i < kBins; i += kChunkThreads)
+      if (u.h.hist[i]) atomicAdd(&gh[i], u.h.hist[i]);
+  }
+  // the block finishes the row alone after a barrier it waited too long
+  // at, and block 0 does when the band overflows its list (one call site)
+  bool solo = !row_barrier(st + kStatBarrier, nch, ticks, &s_flag);
+  if (!solo) {
+    // ---- classification (select_classify_kernel's pass)
+    int hb[kBinsPerThread];
+#pragma unroll
+    for (int j = 0; j < kBinsPerThread; ++j) hb[j] = ld_coherent(st + 8 + tid + j * kChunkThreads);
+    const RowCut cut = classify_chunk<FAST>(a, row, c, v, x, hb, tpage, u.cl, s_terms);
+    solo = !row_barrier(st + kStatBarrier + 1, nch, ticks, &s_flag);
+    if (!solo) {
+      // ---- emission (select_emit_kernel's pass)
+      const int nband = ld_coherent(st + 2);
+      if (nband <= kBandCap) {
+        int2 ccv[2];
+        load_chunk_counts(a, row, ccv);
+        emit_chunk<FAST>(a, row, c, v, cut, nband, x, ccv, u.em.e);  // (masking x again changes nothing)
+        return;
+      }
+      if (c != 0) return;
+    }
+  }
+  select_row_block<kMaxNI, false, FAST>(a, row, u.em.one, s_terms);
 }
 
 // ------------------------------------------------------------------ launch
@@ -1477,10 +1689,52 @@ hipError_t launch_select_stats(const SelectArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Blocks of the one-launch selection that may be resident at once on this
+// device (occupancy times compute units), looked up once per device.
+static int fused_capacity(bool fast) {
+  static int cap[2][64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int& c = cap[fast][dev];
+  if (c == 0) {
+    int per_cu = 0, cus = 0;
+    const hipError_t e = fast ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, select_fused_kernel<true>, kChunkThreads, 0)
+                              : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, select_fused_kernel<false>, kChunkThreads, 0);
+    if (e != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      c = -1;
+    else
+      c = per_cu * cus;
+  }
+  return c;
+}
+
 hipError_t launch_select(const SelectArgs& a, hipStream_t st) {
   const int rows = a.batch * a.groups;
   if (rows == 0) return hipSuccess;
   if (a.row_stride > select_max_row()) return hipErrorInvalidValue;
+  {
+    // one launch when the whole grid fits in half of what the device holds
+    // at once (so that a second call on another stream fits beside it)
+    const int ny = max(max(a.nchunks, 1), (a.k + kSelChunk - 1) / kSelChunk);
+    const int64_t blocks = (int64_t)rows * ny;
+    const int cap = fused_capacity(a.row_bound != nullptr);
+    // SD_SELECT_ONE_LAUNCH=0 (tests): always the three launches
+    const char* one = getenv("SD_SELECT_ONE_LAUNCH");
+    const bool allowed = !(one && one[0] == '0');
+    if (allowed && cap > 0 && 2 * blocks <= cap) {
+      const dim3 fgrid(rows, ny);
+      SelectArgs f = a;
+      // SD_SELECT_SPIN_TICKS (tests): a shorter wait at the row barriers, to
+      // exercise the path where blocks finish their rows alone
+      if (f.spin_ticks <= 0) {
+        const char* env = getenv("SD_SELECT_SPIN_TICKS");
+        if (env && *env) f.spin_ticks = strtoll(env, nullptr, 10);
+      }
+      if (a.row_bound) select_fused_kernel<true><<<fgrid, kChunkThreads, 0, st>>>(f);
+      else select_fused_kernel<false><<<fgrid, kChunkThreads, 0, st>>>(f);
+      return hipGetLastError();
+    }
+  }
   const dim3 grid(max(a.nchunks, 1), rows);
   // classify and emit run chunk-major (block x = row, y = chunk): blocks
   // handed out together belong to different rows, the row's blocks share an
