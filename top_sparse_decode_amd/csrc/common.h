@@ -143,6 +143,30 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
   return wexcl + inc - v;
 }
 
+// Data that blocks of one launch hand to each other (read after the writer
+// has announced it through an atomic counter): device-coherent stores and
+// loads (agent-scope atomic accesses, coherent across the XCDs' L2 caches),
+// no cache-wide fences.
+__device__ __forceinline__ void st_coherent(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coherent(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t ld_coherent(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_coherent(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int2 ld_coherent2(const int32_t* p) {
+  const uint64_t v = ld_coherent(reinterpret_cast<const uint64_t*>(p));
+  return int2{(int)(uint32_t)v, (int)(uint32_t)(v >> 32)};
+}
+
+// Wait until this thread's stores and atomics have completed.
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" : : : "memory"); }
+
 __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
 
 }  // namespace sd

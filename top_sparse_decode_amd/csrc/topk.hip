@@ -49,27 +49,6 @@ constexpr int kMaxNI = 32;              // tiles held in registers: rows up to 6
 constexpr int kMaxChunks = 4;           // longer rows: up to 4 super-chunks, re-read per pass
 enum : uint32_t { kOut = 0, kIn = 1, kBand = 2, kPad = 3 };
 
-// Data that blocks of one launch hand to each other (the selection's band
-// list and chunk counts, read after a row barrier): device-coherent stores
-// and loads (agent-scope atomics, which bypass the per-XCD L2 state), no
-// cache-wide fences.
-__device__ __forceinline__ void st_coherent(int32_t* p, int32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_coherent(uint64_t* p, uint64_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int32_t ld_coherent(const int32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t ld_coherent(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int2 ld_coherent2(const int32_t* p) {
-  const uint64_t v = ld_coherent(reinterpret_cast<const uint64_t*>(p));
-  return int2{(int)(uint32_t)v, (int)(uint32_t)(v >> 32)};
-}
-
 // Slot i of a row's output, and of its copy for the next step's hint when
 // the caller asked for one (the write-back rides along with the output
 // stores instead of a copy kernel after them).
@@ -1514,8 +1493,7 @@ __global__ __launch_bounds__(kChunkThreads) void select_emit_kernel(SelectArgs a
 constexpr int64_t kDefaultSpinTicks = 200000;  // 2 ms at the 100 MHz wall clock
 
 __device__ __forceinline__ bool row_barrier(int32_t* counter, int target, int64_t ticks, int* s_flag) {
-  // this thread's stores (coherent ones, atomics) have completed
-  asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+  wait_stores();  // this thread's coherent stores and atomics have completed
   __syncthreads();
   if (threadIdx.x == 0) {
     __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
