@@ -275,11 +275,14 @@ __global__ __launch_bounds__(256) void attn_vec_kernel(AttnArgs a) {
 // (global_load_lds) in four 32-row chunks and stay resident (147 KB):
 //   S^T[token][head] = K_chunk (A operand, 32 tokens x 16 dims per step) *
 //     Q^T (B operand, the wave's 32 heads over all 36 steps of the 576 dims,
-//     held in registers), chunk by chunk as each chunk lands, the chunk
-//     after next issued as soon as a chunk's S is done; P = 2^(x - m) is
-//     formed per chunk (bf16, in registers) against a running reference m,
-//     the running max rounded up to an integer, and earlier chunks' P are
-//     rescaled by the exact power of two 2^(m_old - m_new) when m rises;
+//     loaded from global memory straight into registers), chunk by chunk as
+//     each chunk lands (all four are requested at once); P = 2^(x - m) is
+//     formed per chunk (bf16, in registers) against a reference m per head,
+//     an integer, with x <= m + 8: it becomes ceil(max) at the first usable
+//     token and again only when a chunk's max passes m + 8, and then the
+//     earlier chunks' P are rescaled by the exact power of two
+//     2^(m_old - m_new) (any reference gives the same softmax; the bound
+//     keeps P in range and makes rescaling rare);
 //   O[:, 0:256] += P * V[:, 0:256], then O[:, 256:512] += P * V[:, 256:512],
 //     the V operand fetched with the transposing LDS read (ds_read_b64_tr_b16)
 //     that hands each lane one value column of four rows.
@@ -316,6 +319,7 @@ constexpr int kMlaStride = kMlaUnits + 4;                  // LDS row stride in 
 constexpr int kMlaRowBytes = kMlaStride * 16;              // 1216
 constexpr int kMlaChunkUnits = kMlaChunkRows * kMlaStride;  // 2432
 constexpr int kMlaChunkInsts = (kMlaChunkUnits + 63) / 64;  // 38 DMA instructions per chunk
+constexpr float kMlaHeadroom = 8.0f;                         // P <= 2^8 between reference moves
 
 // swizzle of row r's units (see above)
 __host__ __device__ constexpr int mla_swz(int r) { return (r >> 2) & 7; }
@@ -391,85 +395,64 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_mla_kernel(AttnArgs a) {
   const int head0 = wid * 32;
 
   const uint32_t kv0 = (uint32_t)(uintptr_t)(lds_ptr_t)s_kv;
-  // One DMA instruction: LDS units ub .. ub+63 (u = row * 73 + slot) of
-  // the rows whose byte offsets rowoff(row) returns (negative: the row is
-  // filled from the first query row instead).  Pad units read a harmless
-  // 16 bytes of that row.  Every lane is in bounds; lanes past `units` do
-  // nothing, and there is always an active lane.
-  auto dma64 = [&](int ub, int units, const char* base, auto&& rowoff, bool stream) {
-    const int rowA = ub / kMlaStride;            // the at most two rows it touches
-    const int64_t oA = rowoff(rowA), oB = rowoff(rowA + 1);
-    const int u = ub + lane;
-    const int row = u / kMlaStride, slot = u - row * kMlaStride;
-    const int64_t ro = row == rowA ? oA : oB;
-    const int sl = slot < kMlaUnits ? slot ^ mla_swz(row) : 0;  // data unit held at position `slot`
-    const char* src = ro >= 0 ? base + ro + sl * 16 : qrow0 + sl * 16;
-    if (u < units) {
-      if (stream)
-        __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(uintptr_t)(kv0 + 16u * ub), 16, 0, kLoadStream);
-      else
-        __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(uintptr_t)(kv0 + 16u * ub), 16, 0, kLoadReuse);
-    }
-  };
-
-  // ---- the block's query rows (heads 0 .. 32*NW-1) into LDS, same layout
-  // as the latent rows, while the row offsets are looked up
-  {
-    constexpr int qunits = 32 * NW * kMlaStride;
-    auto qoff = [&](int h) -> int64_t { return h < 32 * NW ? (int64_t)h * kMlaD * 2 : -1; };
-    for (int i = wid; i < (qunits + 63) / 64; i += NW)
-      dma64(64 * i, qunits, qrow0, qoff, false);
-  }
-  // byte offsets of rows lane and lane + 64 of the split (-1: not usable)
+  // ---- byte offsets of rows lane and lane + 64 of the split (-1: not
+  // usable); the query fragments are requested between the index and the
+  // page-table lookups (B operand: lane l holds head head0 + l%32, dims
+  // 16 s + 8 (l/32) .. +8)
+  bf16x8 qf[KSTEPS];
   int64_t off_lo, off_hi;
   {
     const int i0 = r0 + lane, i1 = r0 + 64 + lane;
     const int t0 = i0 < r1 ? sel[i0] : -1;
     const int t1 = i1 < r1 ? sel[i1] : -1;
+    const uint4* qp = reinterpret_cast<const uint4*>(qrow0 + (int64_t)(head0 + col) * kMlaD * 2) + hf;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) qf[s] = __builtin_bit_cast(bf16x8, qp[2 * s]);
     const int64_t e0 = sel_row(a, bt, L, t0, 0, a.k_page_stride, a.k_head_stride, a.k_token_stride, a.k_num_pages);
     const int64_t e1 = sel_row(a, bt, L, t1, 0, a.k_page_stride, a.k_head_stride, a.k_token_stride, a.k_num_pages);
     off_lo = e0 < 0 ? -1 : e0 * 2;
     off_hi = e1 < 0 ? -1 : e1 * 2;
   }
-  asm volatile("" : : "v"(off_lo), "v"(off_hi));
-  mla_wait_vmcnt_barrier<0>();
-  // Q^T fragments from LDS: lane holds head (head0+col), dims 16s + 8hf .. +8
-  bf16x8 qf[KSTEPS];
-  {
-    const uint4* qs = s_kv + (head0 + col) * kMlaStride;
-    const int sw = mla_swz(head0 + col);
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) qf[s] = __builtin_bit_cast(bf16x8, qs[(2 * s + hf) ^ sw]);
-  }
-  // the latent rows overwrite the query rows: every wave has its fragments
-  __syncthreads();
+  // the query fragments and offsets have landed (a wait the compiler sees,
+  // so that it waits for no DMA when the fragments are used)
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   // usable-row masks, rows 0..63 and 64..127
   const uint64_t ok_lo = __ballot(off_lo >= 0), ok_hi = __ballot(off_hi >= 0);
 
   // ---- DMA of the latent rows, 32-row chunks; wave w issues instructions
-  // w, w + NW, ... of each chunk: (38 - w + NW - 1) / NW of them
-  auto row_off = [&](int row) -> int64_t {  // wave-uniform row
-    if (row >= kMlaSplitRows) return -1;
-    const int64_t v = row < 64 ? off_lo : off_hi;
-    const int ln = row & 63;
-    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)(uint64_t)v, ln);
-    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)v >> 32), ln);
-    return (int64_t)(((uint64_t)hi << 32) | lo);
-  };
+  // w, w + NW, ... of each chunk: (38 - w + NW - 1) / NW of them.
+  // Instruction i moves LDS units 64 i .. +63 of the chunk; this lane's unit
+  // u = 64 i + l is chunk row r = u / 76, position u % 76, which holds data
+  // unit position ^ swizzle (pad positions re-read unit 0).  The row's
+  // offset (16-byte units, int32) comes from the lane that resolved it; a
+  // row that is not usable is filled from the request's first query row:
+  // any finite data will do, its probability is exactly zero.
+  const int32_t u_lo = off_lo < 0 ? -1 : (int32_t)(off_lo >> 4);
+  const int32_t u_hi = off_hi < 0 ? -1 : (int32_t)(off_hi >> 4);
   auto issue_chunk = [&](int j) {
-    for (int i = wid; i < kMlaChunkInsts; i += NW)
-      dma64(j * kMlaChunkUnits + 64 * i, kMlaSplitRows * kMlaStride, kb, row_off, true);
+    const int32_t held = j < 2 ? u_lo : u_hi;  // chunk j's rows 32 j .. +31 sit in one half
+    const uint32_t cbase = kv0 + 16u * (uint32_t)(j * kMlaChunkUnits);
+#pragma unroll
+    for (int k = 0; k < (kMlaChunkInsts + NW - 1) / NW; ++k) {
+      const int i = wid + NW * k;
+      if (i < kMlaChunkInsts) {
+        const int u = 64 * i + lane;
+        const int r = u / kMlaStride, pos = u - r * kMlaStride;
+        const int32_t o = __builtin_amdgcn_ds_bpermute(4 * ((32 * j + r) & 63), held);
+        const int du = pos < kMlaUnits ? pos ^ mla_swz(r) : 0;
+        const char* src = (o >= 0 ? kb + 16 * (int64_t)o : qrow0) + 16 * du;
+        __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(uintptr_t)(cbase + 1024u * i), 16, 0, kLoadStream);
+      }
+    }
   };
-  issue_chunk(0);
-  issue_chunk(1);
+#pragma unroll
+  for (int j = 0; j < kMlaChunks; ++j) issue_chunk(j);
 
-  // ---- S^T chunk by chunk as the chunks land; chunk j + 2 is issued once
-  // S of chunk j is done.  This lane: head `col`, tokens 32j + 8*(r/4) +
-  // 4*hf + (r%4).  Probabilities are formed chunk by chunk against a
-  // running reference m (the running max rounded up to an integer, -inf
-  // while no token is usable): when a chunk raises it, the probabilities
-  // already formed are scaled by 2^(m_old - m_new), an exact power of two,
-  // so the result equals forming them all against the final m.
+  // ---- S^T chunk by chunk as the chunks land.  This lane: head `col`,
+  // tokens 32j + 8*(r/4) + 4*hf + (r%4).  Probabilities are formed chunk by
+  // chunk against the reference m (-inf while no token is usable); when it
+  // moves, the probabilities already formed are scaled by 2^(m_old - m_new),
+  // an exact power of two.
   uint32_t pw[kMlaChunks][8];  // bf16 P of each chunk, A-operand layout
   float m_run = -__builtin_inff(), psum = 0.0f;
   // K fragment bases: row col of the chunk, data unit 2t + hf (t = s & 3)
@@ -478,9 +461,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_mla_kernel(AttnArgs a) {
   for (int t = 0; t < 4; ++t) kaddr[t] = kv0 + (uint32_t)(col * kMlaRowBytes + 16 * ((2 * t + hf) ^ mla_swz(col)));
   mla_static_for<0, kMlaChunks>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
-    // chunk j + 1 (if any) may still be in flight: wait for the rest, then
-    // for everyone's
-    constexpr int later = j + 1 < kMlaChunks ? 1 : 0;
+    // the later chunks may still be in flight: wait for the rest, then for
+    // everyone's
+    constexpr int later = kMlaChunks - 1 - j;
     mla_static_for<0, NW>([&](auto wc) {
       constexpr int w = decltype(wc)::value;
       if (wid == w) mla_wait_vmcnt_barrier<later * ((kMlaChunkInsts - w + NW - 1) / NW)>();
@@ -497,7 +480,6 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_mla_kernel(AttnArgs a) {
       for (int e = 0; e < 6; ++e)
         st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[e]), qf[6 * g + e], st, 0, 0, 0);
     });
-    if constexpr (j + 2 < kMlaChunks) issue_chunk(j + 2);
     float cmax = -__builtin_inff();
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -507,18 +489,22 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_mla_kernel(AttnArgs a) {
       cmax = fmaxf(cmax, st[r]);
     }
     cmax = fmaxf(cmax, __shfl_xor(cmax, 32));  // both token halves of head `col`
-    const float m_new = fmaxf(m_run, ceilf(cmax));
+    const bool mv = cmax > m_run + kMlaHeadroom || (m_run == -__builtin_inff() && cmax != -__builtin_inff());
+    const float m_new = mv ? ceilf(cmax) : m_run;
     if constexpr (j > 0) {
-      // 2^(m_run - m_new): 1 while nothing changes, 0 before any usable token
-      const float f = m_new == -__builtin_inff() ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-      psum *= f;
+      // 2^(m_run - m_new) where m moves from a finite value (before the
+      // first usable token every P so far is zero)
+      if (__ballot(mv && m_run != -__builtin_inff())) {
+        const float f = mv && m_run != -__builtin_inff() ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+        psum *= f;
 #pragma unroll
-      for (int jj = 0; jj < j; ++jj)
+        for (int jj = 0; jj < j; ++jj)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float lo = bf16_lo(pw[jj][e]) * f, hi = bf16_hi(pw[jj][e]) * f;
-          pw[jj][e] = __builtin_bit_cast(uint32_t, __builtin_convertvector((float2v){lo, hi}, bf16x2));
-        }
+          for (int e = 0; e < 8; ++e) {
+            const float lo = bf16_lo(pw[jj][e]) * f, hi = bf16_hi(pw[jj][e]) * f;
+            pw[jj][e] = __builtin_bit_cast(uint32_t, __builtin_convertvector((float2v){lo, hi}, bf16x2));
+          }
+      }
     }
     m_run = m_new;
     // masked tokens: exp2(-inf - mref) = 0 (mref finite even with no token)
@@ -612,9 +598,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_mla_kernel(AttnArgs a) {
 // quarter of the value columns): thread (tile n, half jh, lane l) owns heads
 // 32w + 8(r/4) + 4(l/32) + r%4 (8jh <= r < 8jh + 8) at dv = 128*quarter +
 // 32*(n%4) + l%32.  Split weights 2^(m_s - M) / sum_s l_s 2^(m_s - M) are
-// computed once per head into LDS; each thread then has the partials of 16
-// splits in flight at a time; the result is transposed through LDS so output rows are
-// written contiguously.
+// computed once per head into LDS while each thread's partials of the first
+// 16 splits are already in flight (the two reads do not depend on each
+// other); the result is transposed through LDS so output rows are written
+// contiguously.
 constexpr int kMlaMaxSplits = 64;
 
 __global__ __launch_bounds__(512) void attn_mla_combine_kernel(AttnArgs a, int nw) {
@@ -627,6 +614,14 @@ __global__ __launch_bounds__(512) void attn_mla_combine_kernel(AttnArgs a, int n
   const int quarter = blockIdx.x % 4, w = (blockIdx.x / 4) % nw, b = blockIdx.x / (4 * nw);
   const int col = lane & 31, hf = lane >> 5;
   const int S = a.splits;
+  const int tile = 4 * quarter + n;  // N tile of the partial layout (0..15)
+  const uint16_t* pbase = reinterpret_cast<const uint16_t*>(a.part_o) + (((int64_t)w * 16 + tile) * 64 + lane) * 16;
+  const int64_t sstride = (int64_t)nw * 16 * 64 * 16;  // one split's partial, in elements
+  // ---- this thread's partials of the first 16 splits, requested first
+  uint4 q[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u)
+    if (u < S) q[u] = reinterpret_cast<const uint4*>(pbase + ((int64_t)b * S + u) * sstride)[jh];
   // ---- m and l of (split, head), all loads at once
   for (int i = tid; i < S * 32; i += 512) {
     const int sp = i >> 5, h = i & 31;
@@ -653,14 +648,12 @@ __global__ __launch_bounds__(512) void attn_mla_combine_kernel(AttnArgs a, int n
   float o[8];  // values 8jh .. 8jh+7 of the lane's 16
 #pragma unroll
   for (int r = 0; r < 8; ++r) o[r] = 0.0f;
-  const int tile = 4 * quarter + n;  // N tile of the partial layout (0..15)
-  const uint16_t* pbase = reinterpret_cast<const uint16_t*>(a.part_o) + (((int64_t)w * 16 + tile) * 64 + lane) * 16;
-  const int64_t sstride = (int64_t)nw * 16 * 64 * 16;  // one split's partial, in elements
   for (int s0 = 0; s0 < S; s0 += 16) {
-    uint4 q[16];
+    if (s0 > 0) {
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
-      if (s0 + u < S) q[u] = reinterpret_cast<const uint4*>(pbase + ((int64_t)b * S + s0 + u) * sstride)[jh];
+      for (int u = 0; u < 16; ++u)
+        if (s0 + u < S) q[u] = reinterpret_cast<const uint4*>(pbase + ((int64_t)b * S + s0 + u) * sstride)[jh];
+    }
 #pragma unroll
     for (int u = 0; u < 16; ++u)
       if (s0 + u < S) {
@@ -727,6 +720,7 @@ bool attn_mla_supported(const AttnArgs& a) {
          (a.q_heads == 32 || a.q_heads == 64 || a.q_heads == 128) && a.k == a.v &&
          a.k_page_stride == a.v_page_stride && a.k_token_stride == a.v_token_stride &&
          a.k_num_pages == a.v_num_pages && (a.k_token_stride % 8) == 0 && (a.k_page_stride % 8) == 0 &&
+         (int64_t)a.k_num_pages * a.k_page_stride < ((int64_t)1 << 34) &&  // row offsets: int32 16-byte units
          a.k_sel <= kMlaMaxSplits * kMlaSplitRows;
 }
 
