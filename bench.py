@@ -11,7 +11,12 @@ indexer keys (268 MB per replica) do not sit in the 256 MB last-level cache.
 
 Prints one JSON line.  Algorithmic bytes per step = indexer K bytes scored
 + selected latent rows gathered.  The roofline entry is for the dominant
-kernel (the MFMA indexer scorer), timed with HIP events on its own stream.
+kernel (the MFMA indexer scorer), timed with HIP events on its own stream;
+a second entry covers the gather phase (attention + combine over the
+selected rows), and both are also put against a plain device copy's
+bandwidth measured in the same run.  Per-step times come from an event
+between every two steps.  The CPU baseline is the oracle on a sample of
+the same workload, on every host core this process may use and on one.
 """
 from __future__ import annotations
 
@@ -43,7 +48,9 @@ def parse():
     p.add_argument("--replicas", type=int, default=3, help="input replicas rotated per step")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-requests", type=int, default=16, help="requests in the oracle sample")
-    p.add_argument("--cpu-repeats", type=int, default=2, help="passes of the oracle over the sample")
+    p.add_argument("--cpu-repeats", type=int, default=20, help="passes of the oracle over the sample")
+    p.add_argument("--cpu-single-requests", type=int, default=16,
+                   help="requests in the single-threaded oracle sample")
     p.add_argument("--workload", choices=["dsa_mla", "triattention", "blocks", "gqa", "dsa_mixed"],
                    default="dsa_mla",
                    help="dsa_mla: the fused decode step (default); triattention: one eviction-time "
@@ -65,6 +72,17 @@ def parse():
                    help="also run a plain device copy of this many bytes (3 launches) before the "
                         "steps: the reference kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE")
     return p.parse_args()
+
+
+def per_step_stats(ms):
+    """Median, 10% trimmed mean, min and max of per-step times (ms in, us out)."""
+    v = sorted(ms)
+    n = len(v)
+    cut = n // 10
+    core = v[cut:n - cut] if n - 2 * cut > 0 else v
+    med = v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+    return {"median_us": round(med * 1e3, 2), "trimmed_mean_10_us": round(sum(core) / len(core) * 1e3, 2),
+            "min_us": round(v[0] * 1e3, 2), "max_us": round(v[-1] * 1e3, 2), "n": n}
 
 
 def scorer_traffic(kernel_hash: str, fp8: bool):
@@ -351,18 +369,56 @@ def main():
         steps[i % len(steps)].run(stream)
     torch.cuda.synchronize()
 
-    # ---- timed region: K whole steps
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # ---- timed region: K whole steps, an event between every two
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    e0.record(stream)
+    ev[0].record(stream)
     for i in range(args.steps):
         steps[i % len(steps)].run(stream)
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    ms_total = e0.elapsed_time(e1)
+    ms_total = ev[0].elapsed_time(ev[-1])
     ms_step = ms_total / args.steps
     steps_per_s = 1000.0 / ms_step
-    say(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step")
+    per_step = per_step_stats([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
+    say(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step (median {per_step['median_us']} us)")
+
+    # ---- warm figure: the same step on one replica, its pools partly in the
+    # last-level cache between steps
+    def timed_region(fn, n):
+        for i in range(min(args.warmup, 5)):
+            fn(i)
+        torch.cuda.synchronize()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for i in range(n):
+            fn(i)
+        a1.record(stream)
+        torch.cuda.synchronize()
+        return a0.elapsed_time(a1) / n
+    warm_ms = timed_region(lambda i: steps[0].run(stream), args.steps)
+
+    # ---- gather phase alone: attention + combine over each replica's
+    # selection (rotated like the steps)
+    Hq = w.q.shape[1]
+    attn_ws = torch.empty(api.sparse_decode_attn_workspace_size(steps[0].args.pages, Hq, steps[0].args.k,
+                                                                w.v_dim, w.topk * args.next_n),
+                          dtype=torch.uint8, device=dev)
+    attn_out = torch.empty_like(steps[0].out)
+
+    def attend(i):
+        s = steps[i % len(steps)]
+        api.sparse_decode_attn(s.args.pages, s.q, Hq, s.args.k, s.args.v, w.v_dim, s.indices,
+                               w.topk * args.next_n, w.softmax_scale, attn_out, attn_ws, stream=stream)
+    attn_ms = timed_region(attend, args.steps) if args.next_n == 1 else None
+
+    # ---- plain device copy (read + write) of 1 GiB: the bandwidth a simple
+    # streaming kernel reaches on this device, measured here
+    cp_src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    cp_dst = torch.empty_like(cp_src)
+    copy_ms = timed_region(lambda i: cp_dst.copy_(cp_src), 10)
+    copy_gbps = 2 * cp_src.numel() * 4 / (copy_ms * 1e-3) / 1e9
+    del cp_src, cp_dst
 
     # ---- dominant kernel: the MFMA indexer scorer alone (the call launches
     # that one kernel: its bound output is max-accumulated into a buffer
@@ -388,6 +444,7 @@ def main():
     score_ms = s0.elapsed_time(s1) / args.steps
     score_gbps = k_scored / (score_ms * 1e-3) / 1e9
     src_hash = hashlib.sha256(open(SCORER_SOURCE, "rb").read()).hexdigest()
+    gather_gbps = k_gathered / (attn_ms * 1e-3) / 1e9 if attn_ms else None
 
     result = {
         "metric": METRIC,
@@ -418,6 +475,21 @@ def main():
         "algorithmic_bytes_per_step": alg_bytes,
         "step_gbps": round(alg_bytes / (ms_step * 1e-3) / 1e9, 1),
         "step_frac_of_hbm_peak": round(alg_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "per_step": per_step,
+        "warm": {"what": "the same step on one replica (pools partly in the 256 MB last-level cache)",
+                 "steps_per_s": round(1000.0 / warm_ms, 2), "ms_per_step": round(warm_ms, 5)},
+        "stream_copy_gbps": round(copy_gbps, 1),
+        "roofline_gather": None if attn_ms is None else {
+            "kernel": "attn_mla_kernel + attn_mla_combine_kernel (selected latent rows)",
+            "bound": "hbm",
+            "achieved": round(gather_gbps, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(gather_gbps / PEAK_HBM_GBPS, 4),
+            "frac_of_stream_copy": round(gather_gbps / copy_gbps, 4),
+            "avg_call_us": round(attn_ms * 1e3, 2),
+            "bytes_per_launch": k_gathered,
+        },
         "roofline": {
             "kernel": "score_dsa_fp8_kernel<4, 8, 3, 16>" if fp8 else "score_dsa_kernel<4, 4, 4, 32>",
             "bound": "hbm",
@@ -425,6 +497,7 @@ def main():
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(score_gbps / PEAK_HBM_GBPS, 4),
+            "frac_of_stream_copy": round(score_gbps / copy_gbps, 4),
             "traffic": scorer_traffic(src_hash, fp8),
             "avg_launch_us": round(score_ms * 1e3, 2),
             "bytes_per_launch": k_scored,
@@ -444,20 +517,35 @@ def main():
                                  score_q=w.score_q[rows], head_weights=w.head_weights[rows],
                                  q=w.q[rows])
         reps = max(1, args.cpu_repeats)
-        say(f"[bench] oracle on {n} request(s) x {reps} ...")
+        cores = len(os.sched_getaffinity(0))
+        used = oracle.set_threads(cores)
+        say(f"[bench] oracle on {n} request(s) x {reps}, {used} threads ...")
         t0 = time.perf_counter()
         for _ in range(reps):
             ref = oracle.sparse_decode(ws)
         cpu_s = time.perf_counter() - t0
-        per_step = cpu_s / (n * reps) * B
+        per_step_s = cpu_s / (n * reps) * B
+        # the same oracle on one thread, over fewer requests
+        n1 = max(1, min(args.cpu_single_requests, n))
+        ws1 = dataclasses.replace(ws, block_table=ws.block_table[:n1], kv_lens=ws.kv_lens[:n1],
+                                  score_q=ws.score_q[:n1 * nq], head_weights=ws.head_weights[:n1 * nq],
+                                  q=ws.q[:n1 * nq])
+        oracle.set_threads(1)
+        say(f"[bench] oracle on {n1} request(s), 1 thread ...")
+        t1 = time.perf_counter()
+        oracle.sparse_decode(ws1)
+        cpu1_s = time.perf_counter() - t1
+        oracle.set_threads(used)
         result["cpu_baseline"] = {
-            "value": round(1.0 / per_step, 5),
+            "value": round(1.0 / per_step_s, 5),
             "unit": "steps/s",
-            "cores": 1,
+            "cores": used,
             "kind": "oracle",
-            "sample": f"{reps} pass(es) over {n} of {B} requests of the same workload (score "
-                      f"all 65536 tokens, full sort, float64 attention), {cpu_s:.1f}s "
-                      f"single-threaded, scaled to one step",
+            "sample": f"{reps} pass(es) over {n} of {B} requests of the same workload (score all "
+                      f"65536 tokens, full sort, float64 attention), {cpu_s:.1f}s on {used} threads "
+                      f"(OpenMP over rows; every host core this process may use), scaled to one step",
+            "single_thread": {"value": round(1.0 / (cpu1_s / n1 * B), 5), "unit": "steps/s", "cores": 1,
+                              "sample": f"{n1} of {B} requests, {cpu1_s:.1f}s, scaled to one step"},
         }
         s0 = steps[(args.steps - 1) % len(steps)]
         idx = s0.indices.cpu().numpy()[rows]
