@@ -1557,11 +1557,10 @@ __global__ __launch_bounds__(kChunkThreads) void select_fused_kernel(SelectArgs 
   }
   const int nch = (v.L + kSelChunk - 1) / kSelChunk;  // the row's participating blocks
   if (c >= nch) return;
-  if (a.hint && v.any_finite) {
-    const float floor = hint_floor(a, row, v.L, r.bound, u.h.red);
-    v = view_of_keys(a, row, r.kmin, r.kmax, floor);
-    if (tid == 0) st[7] = __float_as_int(floor);
-  }
+  // A top-k hint is not used here: its floor costs every block a scan of the
+  // hint and of the scores it names, and can only narrow the histogram's
+  // range, while this pass's band is already a few dozen tokens per row
+  // (the hint never changes the result; its write-back is the emission's).
   __syncthreads();  // stats written above, before a fallback reads them back
 
   // ---- histogram (select_hist_kernel's pass)
