@@ -18,9 +18,10 @@
 //   layer by layer and head by head, a later member replacing the running
 //   value only when strictly larger.
 //
-// Kernels: tri_stats_kernel (one lane per member row walks its row in token
-// order; the wave brings tiles of its rows in with coalesced loads and hands
-// each row to its lane through LDS) and tri_reduce_kernel /
+// Kernels: tri_stats_stream_kernel (one lane per member row walks its row in
+// token order, 64 rows per wave, the rows streaming through an LDS ring by
+// DMA; tri_stats_kernel is the same walk for rows that are not whole 16-byte
+// units) and tri_reduce_kernel /
 // tri_reduce4_kernel (a token per lane, the members split into four ordered
 // quarters).  Selection then runs on the reduced rows.
 #include "common.h"
@@ -320,12 +321,157 @@ int tri_out_rows(int layers, int batch, int groups, int mode) {
   return mode == 0 ? layers * batch * groups : (mode == 1 ? batch * groups : batch);
 }
 
+// Statistics, streamed: wave w (a block of its own) owns member rows
+// 64 w .. 64 w + 63, lane r the chain of row 64 w + r.  The rows come in as
+// 64-token tiles (64 rows x 256 bytes, 16 KB) through a five-stage LDS ring
+// by DMA (global_load_lds), the two passes back to back as one sequence of
+// tiles (the second pass's loads do not depend on mu).  DMA instruction i of
+// a tile moves rows 4i .. 4i+3: lane l takes 16 bytes (4 tokens) of row
+// 4i + l/16 into LDS position l%16 of that row, holding data chunk
+// (l%16) ^ (row%16); lane r then reads its own row four tokens at a time
+// (ds_read_b128 at chunk position (j/4) ^ (r%16)): the 16 lanes of each
+// 256-byte phase hit 16 different 4-bank groups.  A token past the row's
+// kv_len, or not finite, adds +0.0 to the chain, which leaves every partial
+// sum unchanged (a sum of binary64 values starting at +0.0 is never -0.0),
+// so the chain rounds exactly as the token-order definition above.
+// Requires 16-byte aligned rows (row_stride % 4 == 0, aligned pointer).
+constexpr int kTsStages = 5;
+constexpr int kTsTok = 64;                          // tokens per tile
+constexpr int kTsTileBytes = 64 * kTsTok * 4;       // 16 KB
+constexpr int kTsInsts = kTsTileBytes / 1024;       // 16 DMA instructions per tile
+static_assert(kTsInsts * (kTsStages - 2) <= 63, "the DMA counter holds the tiles in flight");
+
+// The 16 b128 reads of this lane's row in one tile (64 tokens), one wait.
+__device__ __forceinline__ void ts_read_row(float4 (&v)[16], const uint32_t (&addr)[16]) {
+  asm volatile(
+      "ds_read_b128 %0, %16\n\tds_read_b128 %1, %17\n\tds_read_b128 %2, %18\n\tds_read_b128 %3, %19\n\t"
+      "ds_read_b128 %4, %20\n\tds_read_b128 %5, %21\n\tds_read_b128 %6, %22\n\tds_read_b128 %7, %23\n\t"
+      "ds_read_b128 %8, %24\n\tds_read_b128 %9, %25\n\tds_read_b128 %10, %26\n\tds_read_b128 %11, %27\n\t"
+      "ds_read_b128 %12, %28\n\tds_read_b128 %13, %29\n\tds_read_b128 %14, %30\n\tds_read_b128 %15, %31\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]),
+        "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]), "=&v"(v[13]), "=&v"(v[14]), "=&v"(v[15])
+      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "v"(addr[4]), "v"(addr[5]), "v"(addr[6]),
+        "v"(addr[7]), "v"(addr[8]), "v"(addr[9]), "v"(addr[10]), "v"(addr[11]), "v"(addr[12]), "v"(addr[13]),
+        "v"(addr[14]), "v"(addr[15])
+      : "memory");
+}
+
+__global__ __launch_bounds__(64) void tri_stats_stream_kernel(TriArgs a) {
+  __shared__ __attribute__((aligned(1024))) float s_ring[kTsStages][64 * kTsTok];
+  const int lane = threadIdx.x;
+  const int members = a.layers * a.batch * a.groups;
+  const int m0 = blockIdx.x * 64;
+  const int nrows = min(64, members - m0);
+  int Lr = 0;
+  if (lane < nrows) {
+    const int m = m0 + lane;
+    const int b = (m / a.groups) % a.batch;
+    Lr = clamp_len(a.kv_lens[b], a.row_stride);
+    if (a.lens && (m % a.groups) == 0) a.lens[m / a.groups] = a.kv_lens[b];
+  }
+  const int Lmax = wave_max(Lr);
+  const int ntiles = (Lmax + kTsTok - 1) / kTsTok;
+  const int nseq = 2 * ntiles;  // both passes
+  // DMA slots of this lane: instruction i, row 4i + l/16 (rows past the
+  // wave's last read row 0), data chunk (l%16) ^ (row%16)
+  const int prow = lane >> 4, ppos = lane & 15;
+  const float* rbase = a.scores + (int64_t)m0 * a.row_stride;
+  const uint32_t ring0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)s_ring;
+  auto issue = [&](int k) __attribute__((always_inline)) {  // tile k of the sequence into stage k % S
+    const int T = k < ntiles ? k : k - ntiles;
+    const uint32_t dst = ring0 + (uint32_t)((k % kTsStages) * kTsTileBytes);
+#pragma unroll
+    for (int i = 0; i < kTsInsts; ++i) {
+      const int r = 4 * i + prow;
+      const int rr = r < nrows ? r : 0;
+      const int c = ppos ^ (r & 15);
+      // 16 bytes inside the row: tiles stop at the wave's longest kv_len <= row_stride,
+      // and row_stride is a whole number of 4-token chunks
+      const int t = min(kTsTok * T + 4 * c, a.row_stride - 4);
+      __builtin_amdgcn_global_load_lds(rbase + (int64_t)rr * a.row_stride + t,
+                                       (__attribute__((address_space(3))) void*)(uintptr_t)(dst + 1024u * i), 16, 0,
+                                       kLoadStream);
+    }
+  };
+  uint32_t raddr[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) raddr[q] = ring0 + (uint32_t)(lane * 256 + 16 * (q ^ (lane & 15)));
+
+  for (int k = 0; k < min(nseq, kTsStages - 1); ++k) issue(k);
+  double acc = 0.0, mu = 0.0;
+  int n = 0;
+  for (int k = 0; k < nseq; ++k) {
+    const int ahead = min(nseq - 1 - k, kTsStages - 2);  // later tiles in flight
+    if (ahead >= 3) asm volatile("s_waitcnt vmcnt(48)" ::: "memory");
+    else if (ahead == 2) asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+    else if (ahead == 1) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    float4 v[16];
+    uint32_t ra[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) ra[q] = raddr[q] + (uint32_t)((k % kTsStages) * kTsTileBytes);
+    ts_read_row(v, ra);
+    // the stage just read is free: the tile S - 1 ahead goes there
+    if (k + kTsStages - 1 < nseq) issue(k + kTsStages - 1);
+    const bool second = k >= ntiles;  // (wave-uniform)
+    const int t0 = kTsTok * (second ? k - ntiles : k);
+    if (k == ntiles) {  // first pass done
+      mu = n > 0 ? __ddiv_rn(acc, (double)n) : 0.0;
+      acc = 0.0;
+    }
+    // this lane's 64 values; a token past kv_len reads as NaN (only in the
+    // tile that crosses it), so that "finite" alone decides what counts
+    float xv[64];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      xv[4 * q] = v[q].x;
+      xv[4 * q + 1] = v[q].y;
+      xv[4 * q + 2] = v[q].z;
+      xv[4 * q + 3] = v[q].w;
+    }
+    if (__builtin_amdgcn_ballot_w64(t0 + kTsTok > Lr) != 0) {
+#pragma unroll
+      for (int j = 0; j < 64; ++j) xv[j] = t0 + j < Lr ? xv[j] : __builtin_nanf("");
+    }
+    // groups of 16 values, kept apart so that their masks do not all live at once
+    if (!second) {
+#pragma unroll
+      for (int j = 0; j < 64; ++j) {
+        const bool ok = __builtin_isfinite(xv[j]);
+        acc = __dadd_rn(acc, (double)(ok ? xv[j] : 0.0f));
+        n += ok;
+        if ((j & 15) == 15) __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 64; ++j) {
+        const double d = __dsub_rn((double)xv[j], mu);
+        const double dd = __dmul_rn(d, d);
+        acc = __dadd_rn(acc, __builtin_isfinite(xv[j]) ? dd : 0.0);
+        if ((j & 15) == 15) __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  if (ntiles == 0) mu = 0.0;
+  if (lane < nrows) {
+    const double sigma = n > 0 ? __dsqrt_rn(__ddiv_rn(acc, (double)n)) : 0.0;
+    a.stats[2 * (int64_t)(m0 + lane)] = mu;
+    a.stats[2 * (int64_t)(m0 + lane) + 1] = sigma;
+  }
+}
+
 hipError_t launch_tri(const TriArgs& a, hipStream_t st) {
   const int members = a.layers * a.batch * a.groups;
   const int out_rows = tri_out_rows(a.layers, a.batch, a.groups, a.mode);
   if (members == 0 || a.row_stride == 0) return hipSuccess;
-  const int stat_blocks = (members + kTriWaves * kTriRows - 1) / (kTriWaves * kTriRows);
-  tri_stats_kernel<<<stat_blocks, kTriThreads, 0, st>>>(a);
+  const bool rows16 = (a.row_stride % 4) == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0;
+  if (rows16) {
+    tri_stats_stream_kernel<<<(members + 63) / 64, 64, 0, st>>>(a);
+  } else {
+    const int stat_blocks = (members + kTriWaves * kTriRows - 1) / (kTriWaves * kTriRows);
+    tri_stats_kernel<<<stat_blocks, kTriThreads, 0, st>>>(a);
+  }
   const int nm = a.mode == 0 ? 1 : (a.mode == 1 ? a.layers : a.layers * a.groups);
   const bool vec = (a.row_stride % 4) == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(a.reduced) & 15) == 0;
