@@ -83,9 +83,11 @@ def _load():
         lib.orc_attention.argtypes = [P, I32, P, I32, P, I32, I32, PP, PP, I32, P, I32, F, P]
         lib.orc_local_to_global.argtypes = [P, I32, I32, I32, I32, P, I32, I32, P]
         lib.orc_tri_select.argtypes = [P, I32, I32, I32, I32, P, I32, I32, P, P, P, P]
+        lib.orc_exact_sum.argtypes = [P, I64, P]
         lib.orc_set_threads.argtypes = [I32]
         lib.orc_set_threads.restype = ctypes.c_int
-        for f in (lib.orc_score, lib.orc_topk, lib.orc_attention, lib.orc_local_to_global, lib.orc_tri_select):
+        for f in (lib.orc_score, lib.orc_topk, lib.orc_attention, lib.orc_local_to_global, lib.orc_tri_select,
+                  lib.orc_exact_sum):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -95,6 +97,16 @@ def set_threads(n: int = 0) -> int:
     """Threads the oracle's row loops use (n > 0 sets them); returns the count
     in effect.  Results are bit-identical for every count."""
     return int(_load().orc_set_threads(int(n)))
+
+
+def exact_sum(values) -> float:
+    """The exactly rounded sum of finite binary64 values: their exact real sum
+    rounded once to the nearest binary64, ties to even (the sums of the
+    TriAttention normalization)."""
+    v = np.ascontiguousarray(np.asarray(values, dtype=np.float64))
+    out = np.zeros(1, dtype=np.float64)
+    _check(_load().orc_exact_sum(v.ctypes.data, v.size, out.ctypes.data), "exact_sum")
+    return float(out[0])
 
 
 def _check(rc: int, what: str) -> None:

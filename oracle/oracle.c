@@ -368,25 +368,128 @@ int orc_local_to_global(const int32_t* block_table, int32_t max_pages, int32_t b
 
 /* ------------------------------------------------------------------ TriAttention modes */
 
+/* Exactly rounded sums.  A long accumulator holds a non-negative multiple of
+ * 2^-1074 (the smallest binary64 step) in 64-bit words, word 0 lowest; 35
+ * words (2240 bits) take any finite binary64 magnitude (below 2^1024, so
+ * bit 2098 is the highest) 2^31 times over.  Positive and negative terms go to
+ * two accumulators; the sum is their difference, rounded once to the nearest
+ * binary64, ties to even. */
+#define ORC_ACC_WORDS 35
+typedef struct {
+  uint64_t w[ORC_ACC_WORDS];
+} orc_acc;
+
+/* acc += |v| for a finite v */
+static void acc_add_magnitude(orc_acc* a, double v) {
+  uint64_t bits;
+  memcpy(&bits, &v, sizeof bits);
+  const int ef = (int)((bits >> 52) & 0x7FF);
+  uint64_t m = bits & ((1ull << 52) - 1);
+  int pos; /* the bit of 2^-1074 multiples that m's lowest bit stands for */
+  if (ef == 0) {
+    pos = 0; /* subnormal: frac * 2^-1074 */
+  } else {
+    m |= 1ull << 52;
+    pos = ef - 1; /* (2^52 + frac) * 2^(ef - 1075) */
+  }
+  if (m == 0) return;
+  const int wi = pos / 64, sh = pos % 64;
+  /* m << sh spans words wi and wi + 1 */
+  const uint64_t lo = m << sh;
+  const uint64_t hi = sh == 0 ? 0 : m >> (64 - sh);
+  uint64_t old = a->w[wi];
+  a->w[wi] = old + lo;
+  uint64_t carry = a->w[wi] < old ? 1u : 0u;
+  uint64_t add = hi + carry; /* hi < 2^53: no overflow */
+  for (int j = wi + 1; add != 0 && j < ORC_ACC_WORDS; ++j) {
+    old = a->w[j];
+    a->w[j] = old + add;
+    add = a->w[j] < old ? 1u : 0u;
+  }
+}
+
+/* bit i of the accumulator */
+static int acc_bit(const orc_acc* a, int i) { return (int)((a->w[i / 64] >> (i % 64)) & 1u); }
+
+/* the nearest binary64 to p - n (ties to even) */
+static double acc_round(const orc_acc* p, const orc_acc* n) {
+  int cmp = 0;
+  for (int j = ORC_ACC_WORDS - 1; j >= 0 && cmp == 0; --j)
+    if (p->w[j] != n->w[j]) cmp = p->w[j] > n->w[j] ? 1 : -1;
+  if (cmp == 0) return 0.0;
+  const orc_acc* big = cmp > 0 ? p : n;
+  const orc_acc* small = cmp > 0 ? n : p;
+  orc_acc d; /* big - small */
+  uint64_t borrow = 0;
+  for (int j = 0; j < ORC_ACC_WORDS; ++j) {
+    const uint64_t x = big->w[j], y = small->w[j];
+    d.w[j] = x - y - borrow;
+    borrow = (x < y || (x == y && borrow)) ? 1u : 0u;
+  }
+  int top = ORC_ACC_WORDS * 64 - 1;
+  while (!acc_bit(&d, top)) --top;
+  double mag;
+  if (top <= 52) {
+    mag = ldexp((double)d.w[0], -1074); /* fits in 53 bits: exact */
+  } else {
+    const int lowbit = top - 52; /* the 53 kept bits are top .. lowbit */
+    uint64_t mant = 0;
+    for (int i = top; i >= lowbit; --i) mant = (mant << 1) | (uint64_t)acc_bit(&d, i);
+    const int round = acc_bit(&d, lowbit - 1);
+    int sticky = 0;
+    for (int i = lowbit - 2; i >= 0 && !sticky; --i) sticky = acc_bit(&d, i);
+    int e = lowbit;
+    if (round && (sticky || (mant & 1u))) {
+      ++mant;
+      if (mant == (1ull << 53)) {
+        mant >>= 1;
+        ++e;
+      }
+    }
+    mag = ldexp((double)mant, e - 1074);
+  }
+  return cmp > 0 ? mag : -mag;
+}
+
+int orc_exact_sum(const double* v, int64_t n, double* out) {
+  if ((!v && n > 0) || n < 0 || n > 2147483647 || !out) return ORC_EARG;
+  orc_acc p, m;
+  memset(&p, 0, sizeof p);
+  memset(&m, 0, sizeof m);
+  for (int64_t i = 0; i < n; ++i) {
+    if (!isfinite(v[i])) return ORC_EARG;
+    if (v[i] > 0.0) acc_add_magnitude(&p, v[i]);
+    else if (v[i] < 0.0) acc_add_magnitude(&m, v[i]);
+  }
+  *out = acc_round(&p, &m);
+  return ORC_OK;
+}
+
 /* Normalization of one member row (see oracle.h): the population mean and
- * standard deviation of the row's finite scores, each sum taken in plain
- * token order with every binary64 operation rounded on its own. */
+ * standard deviation of the row's finite scores, each sum exactly rounded. */
 static void tri_normalize_row(const float* row, int32_t L, int32_t row_len, float* z) {
   int64_t n = 0;
-  double s1 = 0.0;
+  orc_acc pos, neg;
+  memset(&pos, 0, sizeof pos);
+  memset(&neg, 0, sizeof neg);
   for (int32_t t = 0; t < L; ++t)
     if (isfinite(row[t])) {
-      s1 = s1 + (double)row[t];
+      const double x = (double)row[t];
+      if (x > 0.0) acc_add_magnitude(&pos, x);
+      else if (x < 0.0) acc_add_magnitude(&neg, x);
       ++n;
     }
+  const double s1 = acc_round(&pos, &neg);
   const double mu = n > 0 ? s1 / (double)n : 0.0;
-  double s2 = 0.0;
+  memset(&pos, 0, sizeof pos);
+  memset(&neg, 0, sizeof neg);
   for (int32_t t = 0; t < L; ++t)
     if (isfinite(row[t])) {
       const double d = (double)row[t] - mu;
       const double dd = d * d;
-      s2 = s2 + dd;
+      acc_add_magnitude(&pos, dd);
     }
+  const double s2 = acc_round(&pos, &neg);
   const double sigma = n > 0 ? sqrt(s2 / (double)n) : 0.0;
   for (int32_t t = 0; t < row_len; ++t) {
     if (t >= L || !isfinite(row[t])) {

@@ -111,11 +111,13 @@ int orc_local_to_global(const int32_t* block_table, int32_t max_pages, int32_t b
  *
  * scores is [layers][batch][groups][row_len].  Normalization, per member row
  * (layer, b, g), over its finite scores at t < kv_lens[b] (n of them), every
- * binary64 operation rounded on its own:
- *   mu  = (((0 + s_t0) + s_t1) + ...) / n, the finite s_t in token order,
- *         each widened exactly to binary64;
- *   var = (((0 + d_t0*d_t0) + d_t1*d_t1) + ...) / n, same order, with
- *         d_t = (double)s_t - mu;
+ * binary64 operation rounded on its own and each sum exactly rounded (the
+ * exact real sum of its terms, rounded once to the nearest binary64, ties to
+ * even; no order of summation enters):
+ *   mu  = S1 / n, S1 = the exactly rounded sum of the finite s_t, each
+ *         widened exactly to binary64;
+ *   var = S2 / n, S2 = the exactly rounded sum of the d_t * d_t (each product
+ *         rounded), d_t = (double)s_t - mu;
  *   sigma = sqrt(var);
  *   z_t = (float)(((double)s_t - mu) / sigma)  (0 when sigma == 0),
  *   z_t = -inf for a non-finite score and for t >= kv_lens[b].
@@ -135,6 +137,11 @@ int orc_set_threads(int32_t n);
 #define ORC_PER_LAYER_PERHEAD 0
 #define ORC_PER_HEAD 1
 #define ORC_UNION 2
+/* The exactly rounded sum of n finite binary64 values (the sums of the
+ * normalization above): *out = the nearest binary64 to their exact real sum,
+ * ties to even.  ORC_EARG for a non-finite value. */
+int orc_exact_sum(const double* v, int64_t n, double* out);
+
 int orc_tri_select(const float* scores, int32_t layers, int32_t batch, int32_t groups, int32_t row_len,
                    const int32_t* kv_lens, int32_t mode, int32_t k, float* z, float* reduced,
                    int32_t* indices, int32_t* counts);

@@ -106,3 +106,46 @@ def test_tri_many_members_both_reduce_paths(mode, S):
     s = random_scores(44, 5, 2, 4, S)
     kv = np.array([S, 1234], np.int32)
     check(s, kv, mode, 256, f"members S={S}")
+
+
+def wide_range_rows(seed, layers, B, G, S):
+    # binary32 scores whose magnitudes span 2^-120 .. 2^60 within a row, exact
+    # cancellations of large values, and rows where a few scores sit far from
+    # the rest: sums the grid extraction cannot take whole, so the long
+    # accumulation decides them
+    rs = np.random.default_rng(seed)
+    mant = rs.uniform(1, 2, size=(layers, B, G, S)) * rs.choice([-1.0, 1.0], size=(layers, B, G, S))
+    s = np.ldexp(mant, rs.integers(-120, 61, size=(layers, B, G, S))).astype(np.float32)
+    big = np.float32(2.0 ** 60)
+    s[0, 0, 0, :4] = [big, 1.0, -big, 3.0]                      # exact mean of the four: 1
+    s[0, 0, 0, 4:] = 0.0
+    s[-1, -1, -1, :] = np.float32(7.0)
+    s[-1, -1, -1, ::97] = np.float32(7.0 + 2.0 ** -21)          # deviations 2^-21 and tiny means
+    return s
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_tri_exact_sums_on_wide_range_rows(mode):
+    s = wide_range_rows(45, 2, 2, 3, 4096)
+    kv = np.array([4096, 2999], np.int32)
+    check(s, kv, mode, 300, "wide range")
+
+
+@pytest.mark.parametrize("S", [1000, 2048, 4096, 4100, 4099])
+def test_tri_every_row_layout(S):
+    # rows held in one, two or four 16-byte units per thread, and rows read
+    # again in every pass (longer, or a stride that is not a multiple of four)
+    s = random_scores(46, 2, 3, 2, S)
+    kv = np.array([S, S - 1, 1], np.int32)
+    check(s, kv, "per_layer_perhead", 64, f"layout S={S}")
+
+
+@pytest.mark.parametrize("S", [1000, 4096, 6000, 4099])
+def test_tri_long_accumulation_forced(S, monkeypatch):
+    # SD_TRI_EXACT_SLOW=1: every sum through the long accumulator
+    monkeypatch.setenv("SD_TRI_EXACT_SLOW", "1")
+    s = random_scores(47, 2, 2, 2, S)
+    s[1, 1, 1, :] = wide_range_rows(48, 3, 1, 1, S)[1, 0, 0]   # a random wide-range row
+    kv = np.array([S, S - 3], np.int32)
+    check(s, kv, "per_layer_perhead", 64, f"forced long S={S}")
+    check(s, kv, "union", 64, f"forced long S={S}")

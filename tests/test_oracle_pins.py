@@ -535,32 +535,90 @@ def test_tri_normalize_bitwise_where_every_order_is_exact():
     assert np.array_equal(z4.view(np.uint32), z.view(np.uint32))
 
 
-def test_tri_normalize_sums_in_token_order():
-    # Rows built so that the binary64 sums round differently in every order.
-    # ulp(2^60) in binary64 is 256, so 2^60 + 1 rounds back to 2^60, while
-    # 2^60 + 255 rounds up to 2^60 + 256.  Closed forms of the sequential sums:
-    #   A = [2^60, 1 (x255), -2^60]: mu = 0 exactly (the ones vanish); a sum
-    #       over 256 strided partials (t % 256) would give 255/257, as would
-    #       the exact sum;
-    #   B = [1 (x255), 2^60, -2^60]: mu = 256/257 (the ones round up to 256
-    #       on meeting 2^60); the reverse order, the strided order and the
-    #       exact sum give 255/257.
-    # In both rows the squared deviations sum to exactly 2^121 (the terms
-    # near 1 vanish next to 2^120), so sigma = sqrt(2^121 / 257).
+def test_exact_sum_is_the_correctly_rounded_real_sum():
+    # fractions.Fraction holds the exact real sum; float() of a Fraction is the
+    # nearest binary64 (CPython divides the integers with correct rounding)
+    from fractions import Fraction
+    import math
+    rs = np.random.default_rng(34)
+    for trial in range(40):
+        n = int(rs.integers(1, 400))
+        mant = rs.standard_normal(n)
+        expo = rs.integers(-60, 61, size=n) if trial % 2 else rs.integers(-1074, 1000, size=n)
+        v = np.ldexp(mant, expo)
+        v = v[np.isfinite(v)]
+        want = float(sum((Fraction(float(x)) for x in v), Fraction(0)))
+        got = oracle.exact_sum(v)
+        assert got == want, trial
+        assert got == math.fsum(v), trial
+    # ties go to the even neighbour: 2^53 + 1 and 2^53 + 3 lie halfway
+    t = 2.0 ** 53
+    assert oracle.exact_sum([t, 1.0]) == t
+    assert oracle.exact_sum([t + 2, 1.0]) == t + 4
+    assert oracle.exact_sum([t, 1.0, 2.0 ** -1074]) == t + 2      # a sticky bit breaks the tie upward
+    # cancellation and intermediate overflow do not enter
+    assert oracle.exact_sum([2.0 ** 60, 1.0, -(2.0 ** 60), 3.0]) == 4.0
+    assert oracle.exact_sum([1e308, 1e308, -1e308]) == 1e308
+    m = np.finfo(np.float64).max
+    assert oracle.exact_sum([m, m, -m, -m, 5.0]) == 5.0
+    # subnormal steps are kept exactly
+    assert oracle.exact_sum([2.0 ** -1074] * 3) == 3 * 2.0 ** -1074
+    assert oracle.exact_sum([2.0 ** -1022, -(2.0 ** -1074)]) == 2.0 ** -1022 - 2.0 ** -1074
+    assert oracle.exact_sum([]) == 0.0 and oracle.exact_sum([5.0, -5.0]) == 0.0
+    with pytest.raises(ValueError):
+        oracle.exact_sum([1.0, np.inf])
+
+
+def test_tri_normalize_follows_exact_sums_not_token_order():
+    # The rows' sums depend on the order in which a sequence of binary64 adds
+    # would take them; the exactly rounded sum does not.  ulp(2^60) is 256, so
+    # in token order 2^60 + 1 rounds back to 2^60:
+    #   A = [2^60, 1 (x255), -2^60]: a left-to-right sum gives 0;
+    #   B = [1 (x255), 2^60, -2^60]: a left-to-right sum gives 256;
+    # the exact sum is 255 for both, so mu = RN(255 / 257) in both rows.  The
+    # squared deviations sum to 2^121 exactly rounded (the terms near 1 are far
+    # below ulp(2^121)), so sigma = sqrt(2^121 / 257).  Each z is compared
+    # with Python's binary64 arithmetic, rounded to binary32.
     import math
     big = F32(2.0 ** 60)
     a = np.concatenate([[big], np.ones(255, F32), [-big]]).astype(F32)
     b = np.concatenate([np.ones(255, F32), [big], [-big]]).astype(F32)
     s = np.stack([a, b]).reshape(1, 1, 2, 257)
     z = oracle.tri_select(s, np.array([257], np.int32), "per_layer_perhead", 4)["z"][0, 0]
+    mu = 255.0 / 257.0
     sigma = math.sqrt(2.0 ** 121 / 257)
-    for g, mu in ((0, 0.0), (1, 256.0 / 257.0)):
+    for g in (0, 1):
         row = s[0, 0, g].astype(np.float64)
         want = np.array([(x - mu) / sigma for x in row]).astype(F32)
         assert np.array_equal(z[g].view(np.uint32), want.view(np.uint32)), f"row {g}"
-    # the strided reading's mean would move every z of a one by a visible amount
-    strided_mu = 255.0 / 257.0
-    assert F32((1.0 - strided_mu) / sigma) != z[0, 1]
+    # a token-order mean (0 for row A, 256/257 for row B) moves the z of a one
+    for seq_mu in (0.0, 256.0 / 257.0):
+        assert F32((1.0 - seq_mu) / sigma) != z[0, 1]
+
+
+def test_tri_normalize_bitwise_against_rational_statistics():
+    # Random rows over a wide dynamic range, every step written out in
+    # Python's binary64 arithmetic with Fraction for the exact sums: the
+    # oracle's z must agree bit for bit.
+    from fractions import Fraction
+    import math
+    rs = np.random.default_rng(35)
+    L = 700
+    x = (rs.standard_normal((1, 1, 3, L)) * np.exp2(rs.integers(-20, 21, size=(1, 1, 3, L)))).astype(F32)
+    x[0, 0, 1, ::7] = -np.inf
+    kv = np.array([L - 33], np.int32)
+    z = oracle.tri_select(x, kv, "per_layer_perhead", 8)["z"][0, 0]
+    Lr = int(kv[0])
+    for g in range(3):
+        row = [float(v) for v in x[0, 0, g, :Lr]]
+        fin = [v for v in row if math.isfinite(v)]
+        n = len(fin)
+        mu = float(sum(map(Fraction, fin), Fraction(0))) / n
+        sq = [(v - mu) * (v - mu) for v in fin]
+        sigma = math.sqrt(float(sum(map(Fraction, sq), Fraction(0))) / n)
+        want = np.array([(v - mu) / sigma if math.isfinite(v) else -np.inf for v in row]).astype(F32)
+        assert np.array_equal(z[g, :Lr].view(np.uint32), want.view(np.uint32)), g
+        assert np.all(z[g, Lr:] == -np.inf)
 
 
 def test_tri_constant_row_and_empty_row():

@@ -5,126 +5,378 @@
 // normalize/reduce step between paged-K scoring and TopK / tie settlement and
 // names three eviction modes (union, per_head, per_layer_perhead); its Main
 // Files name score normalization and union reduction.  The pages give no
-// formula; the library computes the plain population z-score, with its sums
-// taken in token order like every other reduction of the library:
+// formula; the library computes the plain population z-score with exactly
+// rounded sums (no order of summation enters the result):
 //
 //   per member row m = (layer, request b, KV head g), over its finite scores
 //   at t < kv_len[b] (n of them), every binary64 operation rounded on its own:
-//     mu   = (((0 + s_t0) + s_t1) + ...) / n, t ascending;
-//     var  = (((0 + d_t0*d_t0) + d_t1*d_t1) + ...) / n, d_t = (double)s_t - mu;
+//     mu   = S1 / n, S1 = the exact sum of the scores rounded once to binary64;
+//     var  = S2 / n, S2 = the same for the d_t * d_t, d_t = (double)s_t - mu;
 //     z_t  = (float)(((double)s_t - mu) / sqrt(var)), 0 when var == 0,
 //            -inf for a non-finite score or t >= kv_len[b];
 //   reduced row: r_t = max over the mode's members of z_t, members visited
 //   layer by layer and head by head, a later member replacing the running
 //   value only when strictly larger.
 //
-// Kernels: tri_stats_stream_kernel (one lane per member row walks its row in
-// token order, 64 rows per wave, the rows streaming through an LDS ring by
-// DMA; tri_stats_kernel is the same walk for rows that are not whole 16-byte
-// units) and tri_reduce_kernel /
-// tri_reduce4_kernel (a token per lane, the members split into four ordered
-// quarters).  Selection then runs on the reduced rows.
+// Kernels: tri_stats_kernel (one block per member row, the sums split over
+// exact grids so that the tokens are summed in parallel) and
+// tri_reduce_kernel / tri_reduce4_kernel (a token per lane, the members split
+// into four ordered quarters).  Selection then runs on the reduced rows.
 #include "common.h"
 #include "kernels.h"
 
 #include <math.h>
+#include <stdlib.h>
 
 namespace sd {
 
 constexpr int kTriThreads = 256;
 constexpr int kTriSpan = 4096;  // tokens per block of the one-slice reduce
 
-// Statistics: the sums are chains of dependent binary64 additions, one chain
-// per member row, so the work is spread as one lane per row.  A wave owns
-// kTriRows rows (lanes 0 .. kTriRows-1 run the chains).  Tiles of kTriTile
-// tokens of those rows come in with one coalesced load per row and 64-token
-// piece (lane l: token 64 i + l), sit in registers while the previous tile's
-// chains run, and reach the owning lanes through LDS (row stride padded by
-// one float).  Both passes read the row from memory; the second pass finds
-// most of it in the last-level cache.
-constexpr int kTriRows = 16;
-constexpr int kTriTile = 256;
-constexpr int kTriPieces = kTriTile / 64;
-constexpr int kTriWaves = kTriThreads / 64;
+// Statistics.  Both sums are exactly rounded, so their terms may be added in
+// any order: a member row is spread over one block (thread c holds tokens
+// 4 (c + 256 i) .. +3 when the row is held in registers), and the
+// partial sums meet in any order.  Each sum is taken exactly by splitting
+// every term over a few fixed grids (the error-free extraction of Rump, Ogita
+// and Oishi): with sigma = 1.5 * 2^k and |v| < 2^(k-1), h = (v + sigma) -
+// sigma is v rounded to a multiple of G = 2^(k-52), and v - h is exact, so
+// v = h + (v - h) with no error and the next grid takes v - h.  k comes from
+// a bound M on |v| (from the row's extremes) and the term count n:
+// k = log2 M + 1 + ceil(log2 n), so that every partial sum of the h of one
+// grid is a multiple of G below 2^53 G, hence exact in any order, across
+// lanes and waves too.  Each grid is 2^(51 - ceil(log2 n)) finer than the one
+// before.  A term is taken whole once the last grid divides it (two grids for
+// the scores: binary32 values down to about 2^-54 of the largest at 4096
+// tokens; three for the squared deviations: down to about 2^-64 of the
+// largest).  A row where some term is not, or every row when asked, is summed
+// instead in a long accumulator of 64-bit words spanning all of binary64
+// (word w in lane w), exact for any input.  The exact total is then rounded
+// once: a single binary64 addition for two grids, an integer form for three.
+constexpr int kTsThreads = 256;
+constexpr int kTsWaves = kTsThreads / 64;
+constexpr int kLongWords = 35;  // bit 0 = 2^-1074; 2240 bits hold 2^31 terms of any binary64 magnitude
 
-__global__ __launch_bounds__(kTriThreads) void tri_stats_kernel(TriArgs a) {
-  __shared__ float s_tile[kTriWaves][kTriRows][kTriTile + 1];
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int members = a.layers * a.batch * a.groups;
-  const int m0 = (blockIdx.x * kTriWaves + wid) * kTriRows;  // first row of this wave
-  if (m0 >= members) return;
-  const int nrows = min(kTriRows, members - m0);
-  // lane r < nrows owns row m0 + r; Lr is its kv_len, Lmax the wave's longest
-  int Lr = 0;
-  if (lane < nrows) {
-    const int m = m0 + lane;
-    const int b = (m / a.groups) % a.batch;
-    Lr = clamp_len(a.kv_lens[b], a.row_stride);
-    if (a.lens && (m % a.groups) == 0) a.lens[m / a.groups] = a.kv_lens[b];
+struct TsShared {
+  int n[kTsWaves];
+  float vmax[kTsWaves], vmin[kTsWaves];
+  double part1[kTsWaves][2], part2[kTsWaves][3];
+  int rest1[kTsWaves], rest2[kTsWaves];
+  uint64_t words[kTsWaves][4][kLongWords];  // per wave: positive words, their carries, negative words, carries
+  uint64_t tot[2][kLongWords];
+  double sum;
+};
+
+__device__ __forceinline__ int ceil_log2(int n) { return n <= 1 ? 0 : 32 - __clz(n - 1); }
+
+// e with v < 2^(e+1) for a finite v > 0 (floor(log2 v) for a normal v)
+__device__ __forceinline__ int exponent_bound(double v) {
+  return (int)(((uint64_t)__double_as_longlong(v) >> 52) & 0x7FF) - 1023;
+}
+
+// one grid of the extraction: v rounded to a multiple of the grid of sigma
+__device__ __forceinline__ double grid_part(double v, double sigma) { return __dsub_rn(__dadd_rn(v, sigma), sigma); }
+
+// The nearest binary64 to (mag + f) * 2^e, ties to even, where f = 0 when
+// !sticky and 0 < f < 1 otherwise (then mag >= 2^53).  The callers' values
+// lie in binary64's normal range.
+__device__ double round_mag(unsigned __int128 mag, bool sticky, int e) {
+  if (mag == 0) return 0.0;
+  const uint64_t hi = (uint64_t)(mag >> 64), lo = (uint64_t)mag;
+  const int p = hi ? 127 - __clzll((long long)hi) : 63 - __clzll((long long)lo);  // top bit
+  if (p <= 52) return ldexp((double)lo, e);
+  const int sh = p - 52;
+  uint64_t mant = (uint64_t)(mag >> sh);
+  const unsigned __int128 rem = mag & (((unsigned __int128)1 << sh) - 1);
+  const unsigned __int128 half = (unsigned __int128)1 << (sh - 1);
+  if (rem > half || (rem == half && (sticky || (mant & 1)))) ++mant;  // 2^53 is still exact
+  return ldexp((double)mant, e + sh);
+}
+
+__device__ double round_int(__int128 v, int e) {
+  if (v < 0) return -round_mag((unsigned __int128)(-v), false, e);
+  return round_mag((unsigned __int128)v, false, e);
+}
+
+// The nearest binary64 to A1 + A2 + A3, where A_j is a multiple of G_j with
+// |A_j| < 2^53 G_j, G3 = 2^g3, G2 = G3 2^s, G1 = G2 2^s (20 <= s <= 51).
+__device__ double round_three(double A1, double A2, double A3, int g3, int s) {
+  const int64_t a1 = (int64_t)ldexp(A1, -(g3 + 2 * s));  // integers of at most 53 bits: exact
+  const int64_t a2 = (int64_t)ldexp(A2, -(g3 + s));
+  const int64_t a3 = (int64_t)ldexp(A3, -g3);
+  const int64_t q = a3 >> s;          // floor(a3 / 2^s)
+  const int64_t r = a3 - (q << s);    // 0 <= r < 2^s
+  const __int128 N = ((__int128)a1 << s) + a2 + q;  // the total is (N + r / 2^s) G2
+  const __int128 lim = (__int128)1 << 54;
+  if (N >= -lim && N <= lim) return round_int((N << s) + r, g3);  // below 2^106 G3: whole
+  // |N| > 2^54: r / 2^s only decides ties
+  if (N > 0) return round_mag((unsigned __int128)N, r != 0, g3 + s);
+  return -round_mag((unsigned __int128)(-N) - (r != 0 ? 1 : 0), r != 0, g3 + s);
+}
+
+// Long accumulation: lane w holds word w of the positive terms' magnitudes
+// and of the negative terms', and the carries out of them.
+struct TsLong {
+  uint64_t p, n;
+  uint64_t cp, cn;
+};
+
+// adds the binary64 term with the given bits (the same in every lane)
+__device__ __forceinline__ void long_add(TsLong& acc, uint64_t bits, int lane) {
+  const int ef = (int)((bits >> 52) & 0x7FF);
+  const uint64_t m = (bits & ((1ull << 52) - 1)) | (ef ? (1ull << 52) : 0);
+  const int pos = (ef ? ef : 1) - 1;  // m's lowest bit stands for 2^(pos - 1074)
+  const int wi = pos >> 6, sh = pos & 63;
+  const uint64_t lo = m << sh, hi = (m >> 1) >> (63 - sh);
+  const uint64_t add = lane == wi ? lo : (lane == wi + 1 ? hi : 0);
+  const bool neg = (bits >> 63) != 0;
+  const uint64_t op = acc.p, on = acc.n;
+  acc.p = op + (neg ? 0 : add);
+  acc.n = on + (neg ? add : 0);
+  acc.cp += acc.p < op ? 1 : 0;
+  acc.cn += acc.n < on ? 1 : 0;
+}
+
+// Thread 0: the waves' words summed with their carries, the difference of
+// the positive and negative totals rounded to the nearest binary64.
+__device__ double long_round(TsShared& sh) {
+  for (int sgn = 0; sgn < 2; ++sgn) {
+    unsigned __int128 carry = 0;
+    for (int w = 0; w < kLongWords; ++w) {
+      unsigned __int128 t = carry;
+      for (int v = 0; v < kTsWaves; ++v) {
+        t += sh.words[v][2 * sgn][w];
+        if (w > 0) t += sh.words[v][2 * sgn + 1][w - 1];
+      }
+      sh.tot[sgn][w] = (uint64_t)t;
+      carry = t >> 64;
+    }
   }
-  const int Lmax = wave_max(Lr);
-  const float* base = a.scores + (int64_t)m0 * a.row_stride;
-  float (*tile)[kTriTile + 1] = s_tile[wid];
-  // tile loads: row r, tokens t0 + 64 i + lane (in bounds of the row; tokens
-  // past the row's kv_len are loaded only if the row is that long, else -inf)
-  auto load_tile = [&](int t0, float (&v)[kTriRows][kTriPieces]) {
+  int cmp = 0;
+  for (int w = kLongWords - 1; w >= 0 && cmp == 0; --w)
+    if (sh.tot[0][w] != sh.tot[1][w]) cmp = sh.tot[0][w] > sh.tot[1][w] ? 1 : -1;
+  if (cmp == 0) return 0.0;
+  uint64_t* big = sh.tot[cmp > 0 ? 0 : 1];
+  const uint64_t* small = sh.tot[cmp > 0 ? 1 : 0];
+  uint64_t borrow = 0;
+  for (int w = 0; w < kLongWords; ++w) {
+    const uint64_t x = big[w], y = small[w];
+    big[w] = x - y - borrow;
+    borrow = (x < y || (x == y && borrow)) ? 1 : 0;
+  }
+  int top = -1;
+  for (int w = kLongWords - 1; w >= 0 && top < 0; --w)
+    if (big[w]) top = 64 * w + 63 - __clzll((long long)big[w]);
+  double mag;
+  if (top <= 52) {
+    mag = ldexp((double)big[0], -1074);
+  } else {
+    const int q = top - 52;  // lowest kept bit
+    const int wq = q >> 6, bq = q & 63;
+    uint64_t mant = big[wq] >> bq;
+    if (bq) mant |= big[wq + 1] << (64 - bq);
+    mant &= (1ull << 53) - 1;
+    const int rb = q - 1;
+    const bool round = (big[rb >> 6] >> (rb & 63)) & 1;
+    bool sticky = (big[rb >> 6] & ((1ull << (rb & 63)) - 1)) != 0;
+    for (int w = 0; w < (rb >> 6) && !sticky; ++w) sticky = big[w] != 0;
+    if (round && (sticky || (mant & 1))) ++mant;
+    mag = ldexp((double)mant, q - 1074);
+  }
+  return cmp > 0 ? mag : -mag;
+}
+
+// NV > 0: the row is held in registers, NV 16-byte units per thread (rows of
+// at most 1024 NV tokens, 16-byte aligned, row_stride % 4 == 0); NV == 0:
+// every pass reads the row again.  One block per member row.
+template <int NV>
+__global__ __launch_bounds__(kTsThreads) void tri_stats_kernel(TriArgs a) {
+  __shared__ TsShared sh;
+  const int m = blockIdx.x;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int b = (m / a.groups) % a.batch;
+  const int Lr = clamp_len(a.kv_lens[b], a.row_stride);
+  if (threadIdx.x == 0 && a.lens && (m % a.groups) == 0) a.lens[m / a.groups] = a.kv_lens[b];
+  const float* row = a.scores + (int64_t)m * a.row_stride;
+  const float nan = __builtin_nanf("");
+  // tokens at or past kv_len read as NaN: "finite" alone decides what counts
+  float xv[NV > 0 ? 4 * NV : 1];
+  if constexpr (NV > 0) {
 #pragma unroll
-    for (int r = 0; r < kTriRows; ++r) {
-      const int Lrow = __shfl(Lr, r);
+    for (int i = 0; i < NV; ++i) {
+      const int t = 4 * (threadIdx.x + kTsThreads * i);
+      float4 q = make_float4(nan, nan, nan, nan);
+      if (t < Lr) q = *reinterpret_cast<const float4*>(row + t);  // t + 3 < row_stride
+      xv[4 * i] = q.x;
+      xv[4 * i + 1] = t + 1 < Lr ? q.y : nan;
+      xv[4 * i + 2] = t + 2 < Lr ? q.z : nan;
+      xv[4 * i + 3] = t + 3 < Lr ? q.w : nan;
+    }
+  }
+  // every token of the thread (a wave-uniform trip count)
+  auto each = [&](auto&& body) __attribute__((always_inline)) {
+    if constexpr (NV > 0) {
 #pragma unroll
-      for (int i = 0; i < kTriPieces; ++i) {
-        const int t = t0 + 64 * i + lane;
-        v[r][i] = (r < nrows && t < Lrow) ? base[(int64_t)r * a.row_stride + t] : -__builtin_inff();
+      for (int j = 0; j < 4 * NV; ++j) body(xv[j]);
+    } else {
+      for (int t0 = 64 * wid; t0 < Lr; t0 += kTsThreads) {
+        const int t = t0 + lane;
+        body(t < Lr ? row[t] : nan);
       }
     }
   };
-  auto store_tile = [&](const float (&v)[kTriRows][kTriPieces]) {
-#pragma unroll
-    for (int r = 0; r < kTriRows; ++r)
-#pragma unroll
-      for (int i = 0; i < kTriPieces; ++i) tile[r][64 * i + lane] = v[r][i];
-  };
-  // one pass: the chain over the row in token order; `second` selects the
-  // squared deviations from mu
-  auto pass = [&](bool second, double mu, int& n) -> double {
-    double acc = 0.0;
-    n = 0;
-    float v[kTriRows][kTriPieces];
-    load_tile(0, v);
-    for (int t0 = 0; t0 < Lmax; t0 += kTriTile) {
-      store_tile(v);
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      // the next tile's loads go out before this tile's chains run
-      if (t0 + kTriTile < Lmax) load_tile(t0 + kTriTile, v);
-      if (lane < nrows) {
-        const int tend = min(kTriTile, Lr - t0);
-        for (int j = 0; j < tend; ++j) {
-          const float x = tile[lane][j];
-          if (__builtin_isfinite(x)) {
-            if (second) {
-              const double d = __dsub_rn((double)x, mu);
-              acc = __dadd_rn(acc, __dmul_rn(d, d));
-            } else {
-              acc = __dadd_rn(acc, (double)x);
-            }
-            ++n;
-          }
-        }
+  // the exact sum of term(x) over the row by long accumulation (every thread gets it)
+  auto long_sum = [&](auto&& term) __attribute__((always_inline)) -> double {
+    TsLong acc{0, 0, 0, 0};
+    each([&](float x) {
+      const double v = term(x);
+      const uint64_t bits = (uint64_t)__double_as_longlong(v);
+      uint64_t live = __builtin_amdgcn_ballot_w64(v != 0.0);
+      while (live) {
+        const int j = __builtin_ctzll(live);
+        live &= live - 1;
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)bits, j);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(bits >> 32), j);
+        long_add(acc, ((uint64_t)hi << 32) | lo, lane);
       }
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
+    });
+    if (lane < kLongWords) {
+      sh.words[wid][0][lane] = acc.p;
+      sh.words[wid][1][lane] = acc.cp;
+      sh.words[wid][2][lane] = acc.n;
+      sh.words[wid][3][lane] = acc.cn;
     }
-    return acc;
+    __syncthreads();
+    if (threadIdx.x == 0) sh.sum = long_round(sh);
+    __syncthreads();
+    return sh.sum;
   };
+
+  // count and extremes of the finite scores
   int n = 0;
-  const double s1 = pass(false, 0.0, n);
-  const double mu = n > 0 ? __ddiv_rn(s1, (double)n) : 0.0;
-  const double s2 = pass(true, mu, n);
-  if (lane < nrows) {
-    const double sigma = n > 0 ? __dsqrt_rn(__ddiv_rn(s2, (double)n)) : 0.0;
-    a.stats[2 * (int64_t)(m0 + lane)] = mu;
-    a.stats[2 * (int64_t)(m0 + lane) + 1] = sigma;
+  float vmax = -__builtin_inff(), vmin = __builtin_inff();
+  each([&](float x) {
+    const bool ok = __builtin_isfinite(x);
+    n += ok ? 1 : 0;
+    vmax = ok ? fmaxf(vmax, x) : vmax;
+    vmin = ok ? fminf(vmin, x) : vmin;
+  });
+  n = wave_sum(n);
+  vmax = wave_max(vmax);
+  vmin = -wave_max(-vmin);
+  if (lane == 0) {
+    sh.n[wid] = n;
+    sh.vmax[wid] = vmax;
+    sh.vmin[wid] = vmin;
+  }
+  __syncthreads();
+  n = 0;
+#pragma unroll
+  for (int w = 0; w < kTsWaves; ++w) {
+    n += sh.n[w];
+    vmax = fmaxf(vmax, sh.vmax[w]);
+    vmin = fminf(vmin, sh.vmin[w]);
+  }
+  const bool force_long = a.exact_slow != 0;
+  const int c = ceil_log2(n);
+  double mu = 0.0, sigma = 0.0;
+  if (n > 0) {
+    // S1: the exactly rounded sum of the finite scores
+    double s1 = 0.0;
+    const double amax = fmax(fabs((double)vmax), fabs((double)vmin));
+    if (amax != 0.0) {
+      const int k1 = exponent_bound(amax) + 2 + c, k2 = k1 - 51 + c;
+      if (force_long || k2 - 52 < -1022) {
+        s1 = long_sum([&](float x) { return __builtin_isfinite(x) ? (double)x : 0.0; });
+      } else {
+        const double g1 = ldexp(1.5, k1), g2 = ldexp(1.5, k2);
+        double A1 = 0.0, A2 = 0.0;
+        bool rest = false;
+        each([&](float x) {
+          const double v = __builtin_isfinite(x) ? (double)x : 0.0;
+          const double h1 = grid_part(v, g1), l1 = __dsub_rn(v, h1);
+          const double h2 = grid_part(l1, g2), l2 = __dsub_rn(l1, h2);
+          A1 = __dadd_rn(A1, h1);
+          A2 = __dadd_rn(A2, h2);
+          rest = rest || l2 != 0.0;
+        });
+        A1 = wave_sum(A1);
+        A2 = wave_sum(A2);
+        const bool wrest = __builtin_amdgcn_ballot_w64(rest) != 0;
+        if (lane == 0) {
+          sh.part1[wid][0] = A1;
+          sh.part1[wid][1] = A2;
+          sh.rest1[wid] = wrest;
+        }
+        __syncthreads();
+        A1 = A2 = 0.0;
+        bool brest = false;
+#pragma unroll
+        for (int w = 0; w < kTsWaves; ++w) {
+          A1 = __dadd_rn(A1, sh.part1[w][0]);
+          A2 = __dadd_rn(A2, sh.part1[w][1]);
+          brest = brest || sh.rest1[w] != 0;
+        }
+        if (brest) s1 = long_sum([&](float x) { return __builtin_isfinite(x) ? (double)x : 0.0; });
+        else s1 = __dadd_rn(A1, A2);
+      }
+    }
+    mu = __ddiv_rn(s1, (double)n);
+    // S2: the exactly rounded sum of RN(RN(x - mu)^2); its largest term is
+    // that of an extreme score (both roundings are monotone)
+    auto sq = [&](float x) __attribute__((always_inline)) {
+      const double d = __dsub_rn((double)x, mu);
+      return __builtin_isfinite(x) ? __dmul_rn(d, d) : 0.0;
+    };
+    double s2 = 0.0;
+    const double dmax = fmax(fabs(__dsub_rn((double)vmax, mu)), fabs(__dsub_rn((double)vmin, mu)));
+    const double ddmax = __dmul_rn(dmax, dmax);
+    if (ddmax != 0.0) {
+      const int k1 = exponent_bound(ddmax) + 2 + c, k2 = k1 - 51 + c, k3 = k2 - 51 + c;
+      if (force_long || k3 - 52 < -1022) {
+        s2 = long_sum(sq);
+      } else {
+        const double g1 = ldexp(1.5, k1), g2 = ldexp(1.5, k2), g3 = ldexp(1.5, k3);
+        double A1 = 0.0, A2 = 0.0, A3 = 0.0;
+        bool rest = false;
+        each([&](float x) {
+          const double v = sq(x);
+          const double h1 = grid_part(v, g1), l1 = __dsub_rn(v, h1);
+          const double h2 = grid_part(l1, g2), l2 = __dsub_rn(l1, h2);
+          const double h3 = grid_part(l2, g3), l3 = __dsub_rn(l2, h3);
+          A1 = __dadd_rn(A1, h1);
+          A2 = __dadd_rn(A2, h2);
+          A3 = __dadd_rn(A3, h3);
+          rest = rest || l3 != 0.0;
+        });
+        A1 = wave_sum(A1);
+        A2 = wave_sum(A2);
+        A3 = wave_sum(A3);
+        const bool wrest = __builtin_amdgcn_ballot_w64(rest) != 0;
+        if (lane == 0) {
+          sh.part2[wid][0] = A1;
+          sh.part2[wid][1] = A2;
+          sh.part2[wid][2] = A3;
+          sh.rest2[wid] = wrest;
+        }
+        __syncthreads();
+        A1 = A2 = A3 = 0.0;
+        bool brest = false;
+#pragma unroll
+        for (int w = 0; w < kTsWaves; ++w) {
+          A1 = __dadd_rn(A1, sh.part2[w][0]);
+          A2 = __dadd_rn(A2, sh.part2[w][1]);
+          A3 = __dadd_rn(A3, sh.part2[w][2]);
+          brest = brest || sh.rest2[w] != 0;
+        }
+        if (brest) s2 = long_sum(sq);
+        else s2 = round_three(A1, A2, A3, k3 - 52, 51 - c);
+      }
+    }
+    sigma = __dsqrt_rn(__ddiv_rn(s2, (double)n));
+  }
+  if (threadIdx.x == 0) {
+    a.stats[2 * (int64_t)m] = mu;
+    a.stats[2 * (int64_t)m + 1] = sigma;
   }
 }
 
@@ -321,157 +573,20 @@ int tri_out_rows(int layers, int batch, int groups, int mode) {
   return mode == 0 ? layers * batch * groups : (mode == 1 ? batch * groups : batch);
 }
 
-// Statistics, streamed: wave w (a block of its own) owns member rows
-// 64 w .. 64 w + 63, lane r the chain of row 64 w + r.  The rows come in as
-// 64-token tiles (64 rows x 256 bytes, 16 KB) through a five-stage LDS ring
-// by DMA (global_load_lds), the two passes back to back as one sequence of
-// tiles (the second pass's loads do not depend on mu).  DMA instruction i of
-// a tile moves rows 4i .. 4i+3: lane l takes 16 bytes (4 tokens) of row
-// 4i + l/16 into LDS position l%16 of that row, holding data chunk
-// (l%16) ^ (row%16); lane r then reads its own row four tokens at a time
-// (ds_read_b128 at chunk position (j/4) ^ (r%16)): the 16 lanes of each
-// 256-byte phase hit 16 different 4-bank groups.  A token past the row's
-// kv_len, or not finite, adds +0.0 to the chain, which leaves every partial
-// sum unchanged (a sum of binary64 values starting at +0.0 is never -0.0),
-// so the chain rounds exactly as the token-order definition above.
-// Requires 16-byte aligned rows (row_stride % 4 == 0, aligned pointer).
-constexpr int kTsStages = 5;
-constexpr int kTsTok = 64;                          // tokens per tile
-constexpr int kTsTileBytes = 64 * kTsTok * 4;       // 16 KB
-constexpr int kTsInsts = kTsTileBytes / 1024;       // 16 DMA instructions per tile
-static_assert(kTsInsts * (kTsStages - 2) <= 63, "the DMA counter holds the tiles in flight");
-
-// The 16 b128 reads of this lane's row in one tile (64 tokens), one wait.
-__device__ __forceinline__ void ts_read_row(float4 (&v)[16], const uint32_t (&addr)[16]) {
-  asm volatile(
-      "ds_read_b128 %0, %16\n\tds_read_b128 %1, %17\n\tds_read_b128 %2, %18\n\tds_read_b128 %3, %19\n\t"
-      "ds_read_b128 %4, %20\n\tds_read_b128 %5, %21\n\tds_read_b128 %6, %22\n\tds_read_b128 %7, %23\n\t"
-      "ds_read_b128 %8, %24\n\tds_read_b128 %9, %25\n\tds_read_b128 %10, %26\n\tds_read_b128 %11, %27\n\t"
-      "ds_read_b128 %12, %28\n\tds_read_b128 %13, %29\n\tds_read_b128 %14, %30\n\tds_read_b128 %15, %31\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]),
-        "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]), "=&v"(v[13]), "=&v"(v[14]), "=&v"(v[15])
-      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "v"(addr[4]), "v"(addr[5]), "v"(addr[6]),
-        "v"(addr[7]), "v"(addr[8]), "v"(addr[9]), "v"(addr[10]), "v"(addr[11]), "v"(addr[12]), "v"(addr[13]),
-        "v"(addr[14]), "v"(addr[15])
-      : "memory");
-}
-
-__global__ __launch_bounds__(64) void tri_stats_stream_kernel(TriArgs a) {
-  __shared__ __attribute__((aligned(1024))) float s_ring[kTsStages][64 * kTsTok];
-  const int lane = threadIdx.x;
-  const int members = a.layers * a.batch * a.groups;
-  const int m0 = blockIdx.x * 64;
-  const int nrows = min(64, members - m0);
-  int Lr = 0;
-  if (lane < nrows) {
-    const int m = m0 + lane;
-    const int b = (m / a.groups) % a.batch;
-    Lr = clamp_len(a.kv_lens[b], a.row_stride);
-    if (a.lens && (m % a.groups) == 0) a.lens[m / a.groups] = a.kv_lens[b];
-  }
-  const int Lmax = wave_max(Lr);
-  const int ntiles = (Lmax + kTsTok - 1) / kTsTok;
-  const int nseq = 2 * ntiles;  // both passes
-  // DMA slots of this lane: instruction i, row 4i + l/16 (rows past the
-  // wave's last read row 0), data chunk (l%16) ^ (row%16)
-  const int prow = lane >> 4, ppos = lane & 15;
-  const float* rbase = a.scores + (int64_t)m0 * a.row_stride;
-  const uint32_t ring0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)s_ring;
-  auto issue = [&](int k) __attribute__((always_inline)) {  // tile k of the sequence into stage k % S
-    const int T = k < ntiles ? k : k - ntiles;
-    const uint32_t dst = ring0 + (uint32_t)((k % kTsStages) * kTsTileBytes);
-#pragma unroll
-    for (int i = 0; i < kTsInsts; ++i) {
-      const int r = 4 * i + prow;
-      const int rr = r < nrows ? r : 0;
-      const int c = ppos ^ (r & 15);
-      // 16 bytes inside the row: tiles stop at the wave's longest kv_len <= row_stride,
-      // and row_stride is a whole number of 4-token chunks
-      const int t = min(kTsTok * T + 4 * c, a.row_stride - 4);
-      __builtin_amdgcn_global_load_lds(rbase + (int64_t)rr * a.row_stride + t,
-                                       (__attribute__((address_space(3))) void*)(uintptr_t)(dst + 1024u * i), 16, 0,
-                                       kLoadStream);
-    }
-  };
-  uint32_t raddr[16];
-#pragma unroll
-  for (int q = 0; q < 16; ++q) raddr[q] = ring0 + (uint32_t)(lane * 256 + 16 * (q ^ (lane & 15)));
-
-  for (int k = 0; k < min(nseq, kTsStages - 1); ++k) issue(k);
-  double acc = 0.0, mu = 0.0;
-  int n = 0;
-  for (int k = 0; k < nseq; ++k) {
-    const int ahead = min(nseq - 1 - k, kTsStages - 2);  // later tiles in flight
-    if (ahead >= 3) asm volatile("s_waitcnt vmcnt(48)" ::: "memory");
-    else if (ahead == 2) asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
-    else if (ahead == 1) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    float4 v[16];
-    uint32_t ra[16];
-#pragma unroll
-    for (int q = 0; q < 16; ++q) ra[q] = raddr[q] + (uint32_t)((k % kTsStages) * kTsTileBytes);
-    ts_read_row(v, ra);
-    // the stage just read is free: the tile S - 1 ahead goes there
-    if (k + kTsStages - 1 < nseq) issue(k + kTsStages - 1);
-    const bool second = k >= ntiles;  // (wave-uniform)
-    const int t0 = kTsTok * (second ? k - ntiles : k);
-    if (k == ntiles) {  // first pass done
-      mu = n > 0 ? __ddiv_rn(acc, (double)n) : 0.0;
-      acc = 0.0;
-    }
-    // this lane's 64 values; a token past kv_len reads as NaN (only in the
-    // tile that crosses it), so that "finite" alone decides what counts
-    float xv[64];
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      xv[4 * q] = v[q].x;
-      xv[4 * q + 1] = v[q].y;
-      xv[4 * q + 2] = v[q].z;
-      xv[4 * q + 3] = v[q].w;
-    }
-    if (__builtin_amdgcn_ballot_w64(t0 + kTsTok > Lr) != 0) {
-#pragma unroll
-      for (int j = 0; j < 64; ++j) xv[j] = t0 + j < Lr ? xv[j] : __builtin_nanf("");
-    }
-    // groups of 16 values, kept apart so that their masks do not all live at once
-    if (!second) {
-#pragma unroll
-      for (int j = 0; j < 64; ++j) {
-        const bool ok = __builtin_isfinite(xv[j]);
-        acc = __dadd_rn(acc, (double)(ok ? xv[j] : 0.0f));
-        n += ok;
-        if ((j & 15) == 15) __builtin_amdgcn_sched_barrier(0);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 64; ++j) {
-        const double d = __dsub_rn((double)xv[j], mu);
-        const double dd = __dmul_rn(d, d);
-        acc = __dadd_rn(acc, __builtin_isfinite(xv[j]) ? dd : 0.0);
-        if ((j & 15) == 15) __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  }
-  if (ntiles == 0) mu = 0.0;
-  if (lane < nrows) {
-    const double sigma = n > 0 ? __dsqrt_rn(__ddiv_rn(acc, (double)n)) : 0.0;
-    a.stats[2 * (int64_t)(m0 + lane)] = mu;
-    a.stats[2 * (int64_t)(m0 + lane) + 1] = sigma;
-  }
-}
-
-hipError_t launch_tri(const TriArgs& a, hipStream_t st) {
+hipError_t launch_tri(const TriArgs& args, hipStream_t st) {
+  TriArgs a = args;
+  // SD_TRI_EXACT_SLOW=1 (tests): every sum by long accumulation
+  const char* slow = getenv("SD_TRI_EXACT_SLOW");
+  a.exact_slow = (slow && slow[0] == '1') ? 1 : 0;
   const int members = a.layers * a.batch * a.groups;
   const int out_rows = tri_out_rows(a.layers, a.batch, a.groups, a.mode);
   if (members == 0 || a.row_stride == 0) return hipSuccess;
   const bool rows16 = (a.row_stride % 4) == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0;
-  if (rows16) {
-    tri_stats_stream_kernel<<<(members + 63) / 64, 64, 0, st>>>(a);
-  } else {
-    const int stat_blocks = (members + kTriWaves * kTriRows - 1) / (kTriWaves * kTriRows);
-    tri_stats_kernel<<<stat_blocks, kTriThreads, 0, st>>>(a);
-  }
+  const int units = (a.row_stride + 4 * kTsThreads - 1) / (4 * kTsThreads);  // 16-byte units per thread
+  if (rows16 && units <= 1) tri_stats_kernel<1><<<members, kTsThreads, 0, st>>>(a);
+  else if (rows16 && units == 2) tri_stats_kernel<2><<<members, kTsThreads, 0, st>>>(a);
+  else if (rows16 && units <= 4) tri_stats_kernel<4><<<members, kTsThreads, 0, st>>>(a);
+  else tri_stats_kernel<0><<<members, kTsThreads, 0, st>>>(a);
   const int nm = a.mode == 0 ? 1 : (a.mode == 1 ? a.layers : a.layers * a.groups);
   const bool vec = (a.row_stride % 4) == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(a.reduced) & 15) == 0;
