@@ -131,10 +131,11 @@ def test_tri_exact_sums_on_wide_range_rows(mode):
     check(s, kv, mode, 300, "wide range")
 
 
-@pytest.mark.parametrize("S", [1000, 2048, 4096, 4100, 4099])
+@pytest.mark.parametrize("S", [1000, 2048, 4096, 4100, 12000, 4099])
 def test_tri_every_row_layout(S):
-    # rows held in one, two or four 16-byte units per thread, and rows read
-    # again in every pass (longer, or a stride that is not a multiple of four)
+    # rows held in registers by one wave (up to 1024, 2048, 4096 tokens) or
+    # by four (up to 8192, 16384), and rows read again in every pass (a
+    # stride that is not a multiple of four)
     s = random_scores(46, 2, 3, 2, S)
     kv = np.array([S, S - 1, 1], np.int32)
     check(s, kv, "per_layer_perhead", 64, f"layout S={S}")

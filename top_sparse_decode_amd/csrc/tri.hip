@@ -35,33 +35,34 @@ constexpr int kTriSpan = 4096;  // tokens per block of the one-slice reduce
 
 // Statistics.  Both sums are exactly rounded, so their terms may be added in
 // any order: a member row is spread over one block (thread c holds tokens
-// 4 (c + 256 i) .. +3 when the row is held in registers), and the
-// partial sums meet in any order.  Each sum is taken exactly by splitting
-// every term over a few fixed grids (the error-free extraction of Rump, Ogita
-// and Oishi): with sigma = 1.5 * 2^k and |v| < 2^(k-1), h = (v + sigma) -
-// sigma is v rounded to a multiple of G = 2^(k-52), and v - h is exact, so
-// v = h + (v - h) with no error and the next grid takes v - h.  k comes from
-// a bound M on |v| (from the row's extremes) and the term count n:
+// 4 (c + 256 i) .. +3 when the row is held in registers), and the partial
+// sums meet in any order.  Each sum is taken exactly by splitting every term
+// over two fixed grids (the error-free extraction of Rump, Ogita and Oishi):
+// with sigma = 1.5 * 2^k and |v| < 2^(k-1), h = (v + sigma) - sigma is v
+// rounded to a multiple of G = 2^(k-52), and v - h is exact, so
+// v = h + (v - h) with no error and the second grid takes v - h.  k comes
+// from a bound M on |v| (from the row's extremes) and the term count n:
 // k = log2 M + 1 + ceil(log2 n), so that every partial sum of the h of one
 // grid is a multiple of G below 2^53 G, hence exact in any order, across
-// lanes and waves too.  Each grid is 2^(51 - ceil(log2 n)) finer than the one
-// before.  A term is taken whole once the last grid divides it (two grids for
-// the scores: binary32 values down to about 2^-54 of the largest at 4096
-// tokens; three for the squared deviations: down to about 2^-64 of the
-// largest).  A row where some term is not, or every row when asked, is summed
-// instead in a long accumulator of 64-bit words spanning all of binary64
-// (word w in lane w), exact for any input.  The exact total is then rounded
-// once: a single binary64 addition for two grids, an integer form for three.
-constexpr int kTsThreads = 256;
-constexpr int kTsWaves = kTsThreads / 64;
+// lanes and waves too.  The second grid is 2^(51 - ceil(log2 n)) finer.
+// What the second grid leaves of a term is at most half its step, so the
+// exact total lies within n/2 steps of the two grids' sum T; where every
+// value in that interval rounds to the same binary64 it is the result (for
+// binary32 scores nothing is left unless they span more than about 2^54 at
+// 4096 tokens; for the squared deviations the interval is far below their
+// sum's last place unless the row is built for it).  Otherwise, and for
+// every row when asked, the sum is taken in a long accumulator of 64-bit
+// words spanning all of binary64 (word w in lane w), exact for any input.
 constexpr int kLongWords = 35;  // bit 0 = 2^-1074; 2240 bits hold 2^31 terms of any binary64 magnitude
 
+// shared state of a row's block of W waves
+template <int W>
 struct TsShared {
-  int n[kTsWaves];
-  float vmax[kTsWaves], vmin[kTsWaves];
-  double part1[kTsWaves][2], part2[kTsWaves][3];
-  int rest1[kTsWaves], rest2[kTsWaves];
-  uint64_t words[kTsWaves][4][kLongWords];  // per wave: positive words, their carries, negative words, carries
+  int n[W];
+  float vmax[W], vmin[W];
+  double part1[W][2], part2[W][2];
+  int rest1[W], rest2[W];
+  uint64_t words[W][4][kLongWords];  // per wave: positive words, their carries, negative words, carries
   uint64_t tot[2][kLongWords];
   double sum;
 };
@@ -76,10 +77,9 @@ __device__ __forceinline__ int exponent_bound(double v) {
 // one grid of the extraction: v rounded to a multiple of the grid of sigma
 __device__ __forceinline__ double grid_part(double v, double sigma) { return __dsub_rn(__dadd_rn(v, sigma), sigma); }
 
-// The nearest binary64 to (mag + f) * 2^e, ties to even, where f = 0 when
-// !sticky and 0 < f < 1 otherwise (then mag >= 2^53).  The callers' values
-// lie in binary64's normal range.
-__device__ double round_mag(unsigned __int128 mag, bool sticky, int e) {
+// The nearest binary64 to mag * 2^e, ties to even.  The callers' values lie
+// in binary64's normal range.
+__device__ double round_mag(unsigned __int128 mag, int e) {
   if (mag == 0) return 0.0;
   const uint64_t hi = (uint64_t)(mag >> 64), lo = (uint64_t)mag;
   const int p = hi ? 127 - __clzll((long long)hi) : 63 - __clzll((long long)lo);  // top bit
@@ -88,29 +88,29 @@ __device__ double round_mag(unsigned __int128 mag, bool sticky, int e) {
   uint64_t mant = (uint64_t)(mag >> sh);
   const unsigned __int128 rem = mag & (((unsigned __int128)1 << sh) - 1);
   const unsigned __int128 half = (unsigned __int128)1 << (sh - 1);
-  if (rem > half || (rem == half && (sticky || (mant & 1)))) ++mant;  // 2^53 is still exact
+  if (rem > half || (rem == half && (mant & 1))) ++mant;  // 2^53 is still exact
   return ldexp((double)mant, e + sh);
 }
 
 __device__ double round_int(__int128 v, int e) {
-  if (v < 0) return -round_mag((unsigned __int128)(-v), false, e);
-  return round_mag((unsigned __int128)v, false, e);
+  if (v < 0) return -round_mag((unsigned __int128)(-v), e);
+  return round_mag((unsigned __int128)v, e);
 }
 
-// The nearest binary64 to A1 + A2 + A3, where A_j is a multiple of G_j with
-// |A_j| < 2^53 G_j, G3 = 2^g3, G2 = G3 2^s, G1 = G2 2^s (20 <= s <= 51).
-__device__ double round_three(double A1, double A2, double A3, int g3, int s) {
-  const int64_t a1 = (int64_t)ldexp(A1, -(g3 + 2 * s));  // integers of at most 53 bits: exact
-  const int64_t a2 = (int64_t)ldexp(A2, -(g3 + s));
-  const int64_t a3 = (int64_t)ldexp(A3, -g3);
-  const int64_t q = a3 >> s;          // floor(a3 / 2^s)
-  const int64_t r = a3 - (q << s);    // 0 <= r < 2^s
-  const __int128 N = ((__int128)a1 << s) + a2 + q;  // the total is (N + r / 2^s) G2
-  const __int128 lim = (__int128)1 << 54;
-  if (N >= -lim && N <= lim) return round_int((N << s) + r, g3);  // below 2^106 G3: whole
-  // |N| > 2^54: r / 2^s only decides ties
-  if (N > 0) return round_mag((unsigned __int128)N, r != 0, g3 + s);
-  return -round_mag((unsigned __int128)(-N) - (r != 0 ? 1 : 0), r != 0, g3 + s);
+// The exactly rounded sum from two grids: A1, A2 multiples of G1 = G2 2^s
+// and G2 = 2^g2 below 2^53 of their steps, plus a remainder of at most
+// n G2 / 2 when `rest`.  False when the remainder could change the rounding.
+__device__ bool round_two(double A1, double A2, int g2, int s, bool rest, int n, double& out) {
+  const int64_t a1 = (int64_t)ldexp(A1, -(g2 + s));  // integers of at most 53 bits: exact
+  const int64_t a2 = (int64_t)ldexp(A2, -g2);
+  const __int128 T = ((__int128)a1 << s) + a2;
+  if (!rest) {
+    out = round_int(T, g2);
+    return true;
+  }
+  const int64_t r = (n + 1) / 2;
+  out = round_int(T - r, g2);
+  return out == round_int(T + r, g2);
 }
 
 // Long accumulation: lane w holds word w of the positive terms' magnitudes
@@ -138,12 +138,13 @@ __device__ __forceinline__ void long_add(TsLong& acc, uint64_t bits, int lane) {
 
 // Thread 0: the waves' words summed with their carries, the difference of
 // the positive and negative totals rounded to the nearest binary64.
-__device__ double long_round(TsShared& sh) {
+template <int W>
+__device__ double long_round(TsShared<W>& sh) {
   for (int sgn = 0; sgn < 2; ++sgn) {
     unsigned __int128 carry = 0;
     for (int w = 0; w < kLongWords; ++w) {
       unsigned __int128 t = carry;
-      for (int v = 0; v < kTsWaves; ++v) {
+      for (int v = 0; v < W; ++v) {
         t += sh.words[v][2 * sgn][w];
         if (w > 0) t += sh.words[v][2 * sgn + 1][w - 1];
       }
@@ -185,31 +186,31 @@ __device__ double long_round(TsShared& sh) {
   return cmp > 0 ? mag : -mag;
 }
 
-// NV > 0: the row is held in registers, NV 16-byte units per thread (rows of
-// at most 1024 NV tokens, 16-byte aligned, row_stride % 4 == 0); NV == 0:
-// every pass reads the row again.  One block per member row.
-template <int NV>
-__global__ __launch_bounds__(kTsThreads) void tri_stats_kernel(TriArgs a) {
-  __shared__ TsShared sh;
-  const int m = blockIdx.x;
+template <bool B>
+struct TsFlag {
+  static constexpr bool value = B;
+};
+
+// The statistics of member row m, by a block of W waves (every thread takes
+// part).  NV > 0: the row is in xv, NV 16-byte units per thread; NV == 0:
+// every pass reads the row again.  With one wave the partial results meet
+// in registers alone.
+template <int NV, int W>
+__device__ __forceinline__ void tri_stats_row(const TriArgs& a, TsShared<W>& sh, int m, int kv_len,
+                                              float (&xv)[NV > 0 ? 4 * NV : 1]) {
+  constexpr int T = 64 * W;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int b = (m / a.groups) % a.batch;
-  const int Lr = clamp_len(a.kv_lens[b], a.row_stride);
-  if (threadIdx.x == 0 && a.lens && (m % a.groups) == 0) a.lens[m / a.groups] = a.kv_lens[b];
+  const int Lr = clamp_len(kv_len, a.row_stride);
+  if (threadIdx.x == 0 && a.lens && (m % a.groups) == 0) a.lens[m / a.groups] = kv_len;
   const float* row = a.scores + (int64_t)m * a.row_stride;
   const float nan = __builtin_nanf("");
-  // tokens at or past kv_len read as NaN: "finite" alone decides what counts
-  float xv[NV > 0 ? 4 * NV : 1];
   if constexpr (NV > 0) {
+    // tokens at or past kv_len read as NaN, so that "finite" alone decides
+    // what counts (units wholly past it were never loaded)
+    if (Lr < 4 * NV * T) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int t = 4 * (threadIdx.x + kTsThreads * i);
-      float4 q = make_float4(nan, nan, nan, nan);
-      if (t < Lr) q = *reinterpret_cast<const float4*>(row + t);  // t + 3 < row_stride
-      xv[4 * i] = q.x;
-      xv[4 * i + 1] = t + 1 < Lr ? q.y : nan;
-      xv[4 * i + 2] = t + 2 < Lr ? q.z : nan;
-      xv[4 * i + 3] = t + 3 < Lr ? q.w : nan;
+      for (int j = 0; j < 4 * NV; ++j)
+        if (4 * (threadIdx.x + T * (j / 4)) + j % 4 >= Lr) xv[j] = nan;
     }
   }
   // every token of the thread (a wave-uniform trip count)
@@ -218,7 +219,7 @@ __global__ __launch_bounds__(kTsThreads) void tri_stats_kernel(TriArgs a) {
 #pragma unroll
       for (int j = 0; j < 4 * NV; ++j) body(xv[j]);
     } else {
-      for (int t0 = 64 * wid; t0 < Lr; t0 += kTsThreads) {
+      for (int t0 = 64 * wid; t0 < Lr; t0 += T) {
         const int t = t0 + lane;
         body(t < Lr ? row[t] : nan);
       }
@@ -251,74 +252,107 @@ __global__ __launch_bounds__(kTsThreads) void tri_stats_kernel(TriArgs a) {
     return sh.sum;
   };
 
-  // count and extremes of the finite scores
+  // count and extremes of the finite scores (maxima skip NaN; an infinite
+  // score sends them to a second look that skips it)
   int n = 0;
   float vmax = -__builtin_inff(), vmin = __builtin_inff();
   each([&](float x) {
-    const bool ok = __builtin_isfinite(x);
-    n += ok ? 1 : 0;
-    vmax = ok ? fmaxf(vmax, x) : vmax;
-    vmin = ok ? fminf(vmin, x) : vmin;
+    n += __builtin_popcountll(__builtin_amdgcn_ballot_w64(__builtin_isfinite(x)));  // per wave
+    vmax = fmaxf(vmax, x);
+    vmin = fminf(vmin, x);
   });
-  n = wave_sum(n);
   vmax = wave_max(vmax);
   vmin = -wave_max(-vmin);
-  if (lane == 0) {
-    sh.n[wid] = n;
-    sh.vmax[wid] = vmax;
-    sh.vmin[wid] = vmin;
-  }
-  __syncthreads();
-  n = 0;
+  if constexpr (W > 1) {
+    if (lane == 0) {
+      sh.n[wid] = n;
+      sh.vmax[wid] = vmax;
+      sh.vmin[wid] = vmin;
+    }
+    __syncthreads();
+    n = 0;
 #pragma unroll
-  for (int w = 0; w < kTsWaves; ++w) {
-    n += sh.n[w];
-    vmax = fmaxf(vmax, sh.vmax[w]);
-    vmin = fminf(vmin, sh.vmin[w]);
+    for (int w = 0; w < W; ++w) {
+      n += sh.n[w];
+      vmax = fmaxf(vmax, sh.vmax[w]);
+      vmin = fminf(vmin, sh.vmin[w]);
+    }
   }
+  if (n > 0 && (vmax == __builtin_inff() || vmin == -__builtin_inff())) {
+    if constexpr (W > 1) __syncthreads();  // every thread has read the slots
+    vmax = -__builtin_inff();
+    vmin = __builtin_inff();
+    each([&](float x) {
+      const bool ok = __builtin_isfinite(x);
+      vmax = ok ? fmaxf(vmax, x) : vmax;
+      vmin = ok ? fminf(vmin, x) : vmin;
+    });
+    vmax = wave_max(vmax);
+    vmin = -wave_max(-vmin);
+    if constexpr (W > 1) {
+      if (lane == 0) {
+        sh.vmax[wid] = vmax;
+        sh.vmin[wid] = vmin;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        vmax = fmaxf(vmax, sh.vmax[w]);
+        vmin = fminf(vmin, sh.vmin[w]);
+      }
+    }
+  }
+  // every token of every thread present and finite: no selects below
+  const bool all_live = NV > 0 && n == 4 * NV * T;
   const bool force_long = a.exact_slow != 0;
   const int c = ceil_log2(n);
   double mu = 0.0, sigma = 0.0;
   if (n > 0) {
     // S1: the exactly rounded sum of the finite scores
+    auto val = [&](float x) __attribute__((always_inline)) { return __builtin_isfinite(x) ? (double)x : 0.0; };
     double s1 = 0.0;
     const double amax = fmax(fabs((double)vmax), fabs((double)vmin));
     if (amax != 0.0) {
       const int k1 = exponent_bound(amax) + 2 + c, k2 = k1 - 51 + c;
-      if (force_long || k2 - 52 < -1022) {
-        s1 = long_sum([&](float x) { return __builtin_isfinite(x) ? (double)x : 0.0; });
-      } else {
+      bool done = false;
+      if (!force_long && k2 - 52 >= -1022) {
         const double g1 = ldexp(1.5, k1), g2 = ldexp(1.5, k2);
         double A1 = 0.0, A2 = 0.0;
         bool rest = false;
-        each([&](float x) {
-          const double v = __builtin_isfinite(x) ? (double)x : 0.0;
-          const double h1 = grid_part(v, g1), l1 = __dsub_rn(v, h1);
-          const double h2 = grid_part(l1, g2), l2 = __dsub_rn(l1, h2);
-          A1 = __dadd_rn(A1, h1);
-          A2 = __dadd_rn(A2, h2);
-          rest = rest || l2 != 0.0;
-        });
+        auto pass = [&](auto live) __attribute__((always_inline)) {
+          each([&](float x) {
+            const double v = decltype(live)::value ? (double)x : val(x);
+            const double h1 = grid_part(v, g1), l1 = __dsub_rn(v, h1);
+            const double h2 = grid_part(l1, g2);
+            A1 = __dadd_rn(A1, h1);
+            A2 = __dadd_rn(A2, h2);
+            rest = rest || l1 != h2;
+          });
+        };
+        if (all_live) pass(TsFlag<true>{});
+        else pass(TsFlag<false>{});
         A1 = wave_sum(A1);
         A2 = wave_sum(A2);
-        const bool wrest = __builtin_amdgcn_ballot_w64(rest) != 0;
-        if (lane == 0) {
-          sh.part1[wid][0] = A1;
-          sh.part1[wid][1] = A2;
-          sh.rest1[wid] = wrest;
-        }
-        __syncthreads();
-        A1 = A2 = 0.0;
-        bool brest = false;
+        bool brest = __builtin_amdgcn_ballot_w64(rest) != 0;
+        if constexpr (W > 1) {
+          if (lane == 0) {
+            sh.part1[wid][0] = A1;
+            sh.part1[wid][1] = A2;
+            sh.rest1[wid] = brest;
+          }
+          __syncthreads();
+          A1 = A2 = 0.0;
+          brest = false;
 #pragma unroll
-        for (int w = 0; w < kTsWaves; ++w) {
-          A1 = __dadd_rn(A1, sh.part1[w][0]);
-          A2 = __dadd_rn(A2, sh.part1[w][1]);
-          brest = brest || sh.rest1[w] != 0;
+          for (int w = 0; w < W; ++w) {
+            A1 = __dadd_rn(A1, sh.part1[w][0]);
+            A2 = __dadd_rn(A2, sh.part1[w][1]);
+            brest = brest || sh.rest1[w] != 0;
+          }
         }
-        if (brest) s1 = long_sum([&](float x) { return __builtin_isfinite(x) ? (double)x : 0.0; });
-        else s1 = __dadd_rn(A1, A2);
+        done = round_two(A1, A2, k2 - 52, 51 - c, brest, n, s1);
       }
+      if (!done) s1 = long_sum(val);
     }
     mu = __ddiv_rn(s1, (double)n);
     // S2: the exactly rounded sum of RN(RN(x - mu)^2); its largest term is
@@ -331,52 +365,97 @@ __global__ __launch_bounds__(kTsThreads) void tri_stats_kernel(TriArgs a) {
     const double dmax = fmax(fabs(__dsub_rn((double)vmax, mu)), fabs(__dsub_rn((double)vmin, mu)));
     const double ddmax = __dmul_rn(dmax, dmax);
     if (ddmax != 0.0) {
-      const int k1 = exponent_bound(ddmax) + 2 + c, k2 = k1 - 51 + c, k3 = k2 - 51 + c;
-      if (force_long || k3 - 52 < -1022) {
-        s2 = long_sum(sq);
-      } else {
-        const double g1 = ldexp(1.5, k1), g2 = ldexp(1.5, k2), g3 = ldexp(1.5, k3);
-        double A1 = 0.0, A2 = 0.0, A3 = 0.0;
+      const int k1 = exponent_bound(ddmax) + 2 + c, k2 = k1 - 51 + c;
+      bool done = false;
+      if (!force_long && k2 - 52 >= -1022) {
+        const double g1 = ldexp(1.5, k1), g2 = ldexp(1.5, k2);
+        double A1 = 0.0, A2 = 0.0;
         bool rest = false;
-        each([&](float x) {
-          const double v = sq(x);
-          const double h1 = grid_part(v, g1), l1 = __dsub_rn(v, h1);
-          const double h2 = grid_part(l1, g2), l2 = __dsub_rn(l1, h2);
-          const double h3 = grid_part(l2, g3), l3 = __dsub_rn(l2, h3);
-          A1 = __dadd_rn(A1, h1);
-          A2 = __dadd_rn(A2, h2);
-          A3 = __dadd_rn(A3, h3);
-          rest = rest || l3 != 0.0;
-        });
+        auto pass = [&](auto live) __attribute__((always_inline)) {
+          each([&](float x) {
+            double v;
+            if constexpr (decltype(live)::value) {
+              const double d = __dsub_rn((double)x, mu);
+              v = __dmul_rn(d, d);
+            } else {
+              v = sq(x);
+            }
+            const double h1 = grid_part(v, g1), l1 = __dsub_rn(v, h1);
+            const double h2 = grid_part(l1, g2);
+            A1 = __dadd_rn(A1, h1);
+            A2 = __dadd_rn(A2, h2);
+            rest = rest || l1 != h2;
+          });
+        };
+        if (all_live) pass(TsFlag<true>{});
+        else pass(TsFlag<false>{});
         A1 = wave_sum(A1);
         A2 = wave_sum(A2);
-        A3 = wave_sum(A3);
-        const bool wrest = __builtin_amdgcn_ballot_w64(rest) != 0;
-        if (lane == 0) {
-          sh.part2[wid][0] = A1;
-          sh.part2[wid][1] = A2;
-          sh.part2[wid][2] = A3;
-          sh.rest2[wid] = wrest;
-        }
-        __syncthreads();
-        A1 = A2 = A3 = 0.0;
-        bool brest = false;
+        bool brest = __builtin_amdgcn_ballot_w64(rest) != 0;
+        if constexpr (W > 1) {
+          if (lane == 0) {
+            sh.part2[wid][0] = A1;
+            sh.part2[wid][1] = A2;
+            sh.rest2[wid] = brest;
+          }
+          __syncthreads();
+          A1 = A2 = 0.0;
+          brest = false;
 #pragma unroll
-        for (int w = 0; w < kTsWaves; ++w) {
-          A1 = __dadd_rn(A1, sh.part2[w][0]);
-          A2 = __dadd_rn(A2, sh.part2[w][1]);
-          A3 = __dadd_rn(A3, sh.part2[w][2]);
-          brest = brest || sh.rest2[w] != 0;
+          for (int w = 0; w < W; ++w) {
+            A1 = __dadd_rn(A1, sh.part2[w][0]);
+            A2 = __dadd_rn(A2, sh.part2[w][1]);
+            brest = brest || sh.rest2[w] != 0;
+          }
         }
-        if (brest) s2 = long_sum(sq);
-        else s2 = round_three(A1, A2, A3, k3 - 52, 51 - c);
+        done = round_two(A1, A2, k2 - 52, 51 - c, brest, n, s2);
       }
+      if (!done) s2 = long_sum(sq);
     }
     sigma = __dsqrt_rn(__ddiv_rn(s2, (double)n));
   }
   if (threadIdx.x == 0) {
     a.stats[2 * (int64_t)m] = mu;
     a.stats[2 * (int64_t)m + 1] = sigma;
+  }
+}
+
+// Row m into registers: thread c of the T = 64 W takes tokens
+// 4 (c + T i) .. +3 when the unit starts below kv_len (others hold NaN).
+// Rows of at most 4 T NV tokens, 16-byte aligned, row_stride % 4 == 0.
+template <int NV, int W>
+__device__ __forceinline__ void tri_load_row(const TriArgs& a, int m, int kv_len, float (&xv)[4 * NV]) {
+  constexpr int T = 64 * W;
+  const int Lr = clamp_len(kv_len, a.row_stride);
+  const float* row = a.scores + (int64_t)m * a.row_stride;
+  const float nan = __builtin_nanf("");
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int t = 4 * (threadIdx.x + T * i);
+    float4 q = make_float4(nan, nan, nan, nan);
+    if (t < Lr) q = *reinterpret_cast<const float4*>(row + t);  // t + 3 < row_stride
+    xv[4 * i] = q.x;
+    xv[4 * i + 1] = q.y;
+    xv[4 * i + 2] = q.z;
+    xv[4 * i + 3] = q.w;
+  }
+}
+
+__device__ __forceinline__ int tri_kv_len(const TriArgs& a, int m) { return a.kv_lens[(m / a.groups) % a.batch]; }
+
+// One block of W waves per member row.  NV > 0: the row is held in
+// registers (NV 16-byte units per thread); NV == 0: read again in every pass.
+template <int NV, int W>
+__global__ __launch_bounds__(64 * W) void tri_stats_kernel(TriArgs a) {
+  __shared__ TsShared<W> sh;
+  const int len = tri_kv_len(a, blockIdx.x);
+  if constexpr (NV > 0) {
+    float cur[4 * NV];
+    tri_load_row<NV, W>(a, blockIdx.x, len, cur);
+    tri_stats_row<NV, W>(a, sh, blockIdx.x, len, cur);
+  } else {
+    float none[1] = {0.0f};
+    tri_stats_row<0, W>(a, sh, blockIdx.x, len, none);
   }
 }
 
@@ -582,11 +661,15 @@ hipError_t launch_tri(const TriArgs& args, hipStream_t st) {
   const int out_rows = tri_out_rows(a.layers, a.batch, a.groups, a.mode);
   if (members == 0 || a.row_stride == 0) return hipSuccess;
   const bool rows16 = (a.row_stride % 4) == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0;
-  const int units = (a.row_stride + 4 * kTsThreads - 1) / (4 * kTsThreads);  // 16-byte units per thread
-  if (rows16 && units <= 1) tri_stats_kernel<1><<<members, kTsThreads, 0, st>>>(a);
-  else if (rows16 && units == 2) tri_stats_kernel<2><<<members, kTsThreads, 0, st>>>(a);
-  else if (rows16 && units <= 4) tri_stats_kernel<4><<<members, kTsThreads, 0, st>>>(a);
-  else tri_stats_kernel<0><<<members, kTsThreads, 0, st>>>(a);
+  // rows held in registers: one wave per row up to 4096 tokens (up to 64 per
+  // lane), four waves up to 16384; longer rows, or rows that are not whole
+  // 16-byte units, are read again in every pass
+  if (rows16 && a.row_stride <= 1024) tri_stats_kernel<4, 1><<<members, 64, 0, st>>>(a);
+  else if (rows16 && a.row_stride <= 2048) tri_stats_kernel<8, 1><<<members, 64, 0, st>>>(a);
+  else if (rows16 && a.row_stride <= 4096) tri_stats_kernel<16, 1><<<members, 64, 0, st>>>(a);
+  else if (rows16 && a.row_stride <= 8192) tri_stats_kernel<8, 4><<<members, 256, 0, st>>>(a);
+  else if (rows16 && a.row_stride <= 16384) tri_stats_kernel<16, 4><<<members, 256, 0, st>>>(a);
+  else tri_stats_kernel<0, 4><<<members, 256, 0, st>>>(a);
   const int nm = a.mode == 0 ? 1 : (a.mode == 1 ? a.layers : a.layers * a.groups);
   const bool vec = (a.row_stride % 4) == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(a.reduced) & 15) == 0;
