@@ -106,6 +106,7 @@ struct TriArgs {
   int32_t* lens;           // [layers*batch]: kv_lens repeated per layer (mode 0), or null
   float* reduced;          // [out_rows][row_stride]
   int32_t exact_slow;      // 1: every sum by long accumulation (set by launch_tri)
+  int32_t z_rows;          // 1: the statistics kernel writes each member's z row (set by launch_tri)
 };
 int tri_out_rows(int layers, int batch, int groups, int mode);
 hipError_t launch_tri(const TriArgs& a, hipStream_t st);

@@ -186,6 +186,12 @@ __device__ double long_round(TsShared<W>& sh) {
   return cmp > 0 ? mag : -mag;
 }
 
+__device__ __forceinline__ float tri_z(float s, double mu, double sigma) {
+  if (!__builtin_isfinite(s)) return -__builtin_inff();
+  if (sigma == 0.0) return 0.0f;
+  return __double2float_rn(__ddiv_rn(__dsub_rn((double)s, mu), sigma));
+}
+
 template <bool B>
 struct TsFlag {
   static constexpr bool value = B;
@@ -418,6 +424,21 @@ __device__ __forceinline__ void tri_stats_row(const TriArgs& a, TsShared<W>& sh,
     a.stats[2 * (int64_t)m] = mu;
     a.stats[2 * (int64_t)m + 1] = sigma;
   }
+  if constexpr (NV > 0) {
+    // per layer and head the reduced row is the member's own z: written from
+    // the registers (reduced rows 16-byte aligned, row_stride % 4 == 0)
+    if (a.z_rows) {
+      float* out = a.reduced + (int64_t)m * a.row_stride;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int t = 4 * (threadIdx.x + T * i);
+        if (t < a.row_stride)
+          *reinterpret_cast<float4*>(out + t) =
+              make_float4(tri_z(xv[4 * i], mu, sigma), tri_z(xv[4 * i + 1], mu, sigma),
+                          tri_z(xv[4 * i + 2], mu, sigma), tri_z(xv[4 * i + 3], mu, sigma));
+      }
+    }
+  }
 }
 
 // Row m into registers: thread c of the T = 64 W takes tokens
@@ -459,11 +480,6 @@ __global__ __launch_bounds__(64 * W) void tri_stats_kernel(TriArgs a) {
   }
 }
 
-__device__ __forceinline__ float tri_z(float s, double mu, double sigma) {
-  if (!__builtin_isfinite(s)) return -__builtin_inff();
-  if (sigma == 0.0) return 0.0f;
-  return __double2float_rn(__ddiv_rn(__dsub_rn((double)s, mu), sigma));
-}
 
 // Lane = token.  SLICES = 4 (rows with many members): one block per
 // (64-token tile, output row), wave j takes the j-th quarter of the row's
@@ -661,6 +677,9 @@ hipError_t launch_tri(const TriArgs& args, hipStream_t st) {
   const int out_rows = tri_out_rows(a.layers, a.batch, a.groups, a.mode);
   if (members == 0 || a.row_stride == 0) return hipSuccess;
   const bool rows16 = (a.row_stride % 4) == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0;
+  // per layer and head, rows held in registers give their z rows at once
+  a.z_rows = (a.mode == 0 && rows16 && a.row_stride <= 16384 && (reinterpret_cast<uintptr_t>(a.reduced) & 15) == 0)
+                 ? 1 : 0;
   // rows held in registers: one wave per row up to 4096 tokens (up to 64 per
   // lane), four waves up to 16384; longer rows, or rows that are not whole
   // 16-byte units, are read again in every pass
@@ -670,6 +689,7 @@ hipError_t launch_tri(const TriArgs& args, hipStream_t st) {
   else if (rows16 && a.row_stride <= 8192) tri_stats_kernel<8, 4><<<members, 256, 0, st>>>(a);
   else if (rows16 && a.row_stride <= 16384) tri_stats_kernel<16, 4><<<members, 256, 0, st>>>(a);
   else tri_stats_kernel<0, 4><<<members, 256, 0, st>>>(a);
+  if (a.z_rows) return hipGetLastError();
   const int nm = a.mode == 0 ? 1 : (a.mode == 1 ? a.layers : a.layers * a.groups);
   const bool vec = (a.row_stride % 4) == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(a.reduced) & 15) == 0;
