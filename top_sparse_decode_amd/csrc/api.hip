@@ -319,7 +319,7 @@ sd_status plan_tri(int32_t layers, int32_t batch, int32_t groups, int32_t row_st
   p->out_batch = mode == SD_SELECT_PER_LAYER_PERHEAD ? layers * batch : batch;
   p->out_groups = mode == SD_SELECT_UNION ? 1 : groups;
   size_t off = 0;
-  p->off_stats = off; off += align_up((size_t)layers * batch * groups * 16);
+  p->off_stats = off; off += align_up((size_t)layers * batch * groups * 32);
   p->off_lens = off; off += align_up((size_t)layers * batch * 4);
   p->off_reduced = off; off += own_reduced ? 0 : align_up((size_t)p->out_rows * row_stride * 4);
   p->off_select = off; off += align_up(sd::select_workspace_bytes(p->out_rows, row_stride));

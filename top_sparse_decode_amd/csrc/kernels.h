@@ -102,7 +102,7 @@ struct TriArgs {
   int32_t layers, batch, groups, row_stride;
   const int32_t* kv_lens;  // [batch]
   int32_t mode;            // 0 per layer per head, 1 per head, 2 union
-  double* stats;           // [layers*batch*groups][2]: mu, sigma
+  double* stats;           // [layers*batch*groups][4]: mu, sigma, RN(1 / sigma), (unused)
   int32_t* lens;           // [layers*batch]: kv_lens repeated per layer (mode 0), or null
   float* reduced;          // [out_rows][row_stride]
   int32_t exact_slow;      // 1: every sum by long accumulation (set by launch_tri)

@@ -186,10 +186,25 @@ __device__ double long_round(TsShared<W>& sh) {
   return cmp > 0 ? mag : -mag;
 }
 
-__device__ __forceinline__ float tri_z(float s, double mu, double sigma) {
+// z of a score from its member's mu, sigma and rinv = RN(1 / sigma): the
+// binary64 quotient (s - mu) / sigma, correctly rounded, then rounded to
+// binary32.  q = (s - mu) * rinv is within 2.5 binary64 ulps of that quotient
+// (two roundings of relative size 2^-53 each, plus the quotient's own half
+// ulp), so q rounds to the same binary32 unless it lies within 3 ulps of a
+// binary32 rounding midpoint (its 29 bits below binary32's last place within
+// 3 of 2^28) or below binary32's normal range; those few take the division.
+// Binade edges are binary32 values, far from any midpoint, so they need no
+// care.
+__device__ __forceinline__ float tri_z(float s, double mu, double sigma, double rinv) {
   if (!__builtin_isfinite(s)) return -__builtin_inff();
   if (sigma == 0.0) return 0.0f;
-  return __double2float_rn(__ddiv_rn(__dsub_rn((double)s, mu), sigma));
+  const double d = __dsub_rn((double)s, mu);
+  const double q = __dmul_rn(d, rinv);
+  const uint64_t b = (uint64_t)__double_as_longlong(q);
+  const uint32_t low = (uint32_t)b & 0x1FFFFFFFu;
+  const uint32_t ex = (uint32_t)(b >> 52) & 0x7FFu;
+  if (low - ((1u << 28) - 3u) > 6u && ex >= 1023u - 126u) return __double2float_rn(q);
+  return __double2float_rn(__ddiv_rn(d, sigma));
 }
 
 template <bool B>
@@ -420,9 +435,11 @@ __device__ __forceinline__ void tri_stats_row(const TriArgs& a, TsShared<W>& sh,
     }
     sigma = __dsqrt_rn(__ddiv_rn(s2, (double)n));
   }
+  const double rinv = sigma > 0.0 ? __ddiv_rn(1.0, sigma) : 0.0;
   if (threadIdx.x == 0) {
-    a.stats[2 * (int64_t)m] = mu;
-    a.stats[2 * (int64_t)m + 1] = sigma;
+    a.stats[4 * (int64_t)m] = mu;
+    a.stats[4 * (int64_t)m + 1] = sigma;
+    a.stats[4 * (int64_t)m + 2] = rinv;
   }
   if constexpr (NV > 0) {
     // per layer and head the reduced row is the member's own z: written from
@@ -434,8 +451,8 @@ __device__ __forceinline__ void tri_stats_row(const TriArgs& a, TsShared<W>& sh,
         const int t = 4 * (threadIdx.x + T * i);
         if (t < a.row_stride)
           *reinterpret_cast<float4*>(out + t) =
-              make_float4(tri_z(xv[4 * i], mu, sigma), tri_z(xv[4 * i + 1], mu, sigma),
-                          tri_z(xv[4 * i + 2], mu, sigma), tri_z(xv[4 * i + 3], mu, sigma));
+              make_float4(tri_z(xv[4 * i], mu, sigma, rinv), tri_z(xv[4 * i + 1], mu, sigma, rinv),
+                          tri_z(xv[4 * i + 2], mu, sigma, rinv), tri_z(xv[4 * i + 3], mu, sigma, rinv));
       }
     }
   }
@@ -535,13 +552,13 @@ __global__ __launch_bounds__(kTriThreads) void tri_reduce_kernel(TriArgs a) {
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const float z = tri_z(x[u], a.stats[2 * m[u]], a.stats[2 * m[u] + 1]);
+        const float z = tri_z(x[u], a.stats[4 * m[u]], a.stats[4 * m[u] + 1], a.stats[4 * m[u] + 2]);
         if (z > r) r = z;
       }
     }
     for (; j < j1; ++j) {
       const int64_t m = ((int64_t)(l0 + j / ng) * a.batch + b) * a.groups + g0 + j % ng;
-      const float z = tri_z(a.scores[m * a.row_stride + t], a.stats[2 * m], a.stats[2 * m + 1]);
+      const float z = tri_z(a.scores[m * a.row_stride + t], a.stats[4 * m], a.stats[4 * m + 1], a.stats[4 * m + 2]);
       if (z > r) r = z;
     }
     return r;
@@ -569,13 +586,14 @@ __global__ __launch_bounds__(kTriThreads) void tri_reduce_kernel(TriArgs a) {
 
 // The same reduction with four consecutive tokens per lane and 16-byte loads
 // (rows whose stride is a multiple of four floats): a wave reads a member's
-// 256 tokens with one instruction.  SLICES = 4: one block per (256-token
-// tile, output row), wave j takes the j-th quarter of the members, partial
-// maxima combined in wave order; SLICES = 1: a block covers kTriSpan tokens.
-// Per token the arithmetic and the order are those of tri_reduce_kernel.
+// 256 tokens with one instruction.  SLICES > 1: one block of SLICES waves per
+// (256-token tile, output row), wave j takes the j-th of SLICES ordered
+// parts of the members, partial maxima combined in wave order; SLICES = 1: a
+// block of kTriThreads covers kTriSpan tokens.  Per token the arithmetic and
+// the order are those of tri_reduce_kernel.
 template <int SLICES>
-__global__ __launch_bounds__(kTriThreads) void tri_reduce4_kernel(TriArgs a) {
-  __shared__ float4 s_part[kTriThreads / 64][64];
+__global__ __launch_bounds__(SLICES > 1 ? 64 * SLICES : kTriThreads) void tri_reduce4_kernel(TriArgs a) {
+  __shared__ float4 s_part[SLICES][64];
   const int o = blockIdx.y;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   int b, g0, ng, nl, l0;
@@ -618,11 +636,11 @@ __global__ __launch_bounds__(kTriThreads) void tri_reduce4_kernel(TriArgs a) {
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const double mu = a.stats[2 * m[u]], sg = a.stats[2 * m[u] + 1];
+        const double mu = a.stats[4 * m[u]], sg = a.stats[4 * m[u] + 1], ri = a.stats[4 * m[u] + 2];
         const float xs[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float z = t0 + e < L ? tri_z(xs[e], mu, sg) : -__builtin_inff();
+          const float z = t0 + e < L ? tri_z(xs[e], mu, sg, ri) : -__builtin_inff();
           if (z > r[e]) r[e] = z;
         }
       }
@@ -630,11 +648,11 @@ __global__ __launch_bounds__(kTriThreads) void tri_reduce4_kernel(TriArgs a) {
     for (; j < j1; ++j) {
       const int64_t m = member(j);
       const float4 x = *reinterpret_cast<const float4*>(a.scores + m * a.row_stride + t0);
-      const double mu = a.stats[2 * m], sg = a.stats[2 * m + 1];
+      const double mu = a.stats[4 * m], sg = a.stats[4 * m + 1], ri = a.stats[4 * m + 2];
       const float xs[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float z = t0 + e < L ? tri_z(xs[e], mu, sg) : -__builtin_inff();
+        const float z = t0 + e < L ? tri_z(xs[e], mu, sg, ri) : -__builtin_inff();
         if (z > r[e]) r[e] = z;
       }
     }
@@ -693,8 +711,10 @@ hipError_t launch_tri(const TriArgs& args, hipStream_t st) {
   const int nm = a.mode == 0 ? 1 : (a.mode == 1 ? a.layers : a.layers * a.groups);
   const bool vec = (a.row_stride % 4) == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(a.reduced) & 15) == 0;
-  if (vec && nm >= 16)
-    tri_reduce4_kernel<4><<<dim3((a.row_stride + 255) / 256, out_rows), kTriThreads, 0, st>>>(a);
+  if (vec && nm >= 128)
+    tri_reduce4_kernel<16><<<dim3((a.row_stride + 255) / 256, out_rows), 1024, 0, st>>>(a);
+  else if (vec && nm >= 16)
+    tri_reduce4_kernel<4><<<dim3((a.row_stride + 255) / 256, out_rows), 256, 0, st>>>(a);
   else if (vec)
     tri_reduce4_kernel<1><<<dim3((a.row_stride + kTriSpan - 1) / kTriSpan, out_rows), kTriThreads, 0, st>>>(a);
   else if (nm >= 16)
