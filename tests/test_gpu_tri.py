@@ -150,3 +150,18 @@ def test_tri_long_accumulation_forced(S, monkeypatch):
     kv = np.array([S, S - 3], np.int32)
     check(s, kv, "per_layer_perhead", 64, f"forced long S={S}")
     check(s, kv, "union", 64, f"forced long S={S}")
+
+
+@pytest.mark.parametrize("ragged", [False, True])
+def test_tri_full_size_all_modes(ragged):
+    # the benchmarked shape: 36 layers x 32 requests x 8 KV heads x 4096
+    # tokens (151 MB), per-row location U(-50, 50), spread exp(U(-2, 2)),
+    # keep 2048; every reduced row, index and count compared
+    rs = np.random.default_rng(2048)
+    layers, B, G, S, k = 36, 32, 8, 4096, 2048
+    loc = rs.uniform(-50, 50, size=(layers, B, G, 1))
+    spread = np.exp(rs.uniform(-2, 2, size=(layers, B, G, 1)))
+    s = (rs.standard_normal((layers, B, G, S), dtype=np.float32) * spread + loc).astype(np.float32)
+    kv = rs.integers(2049, S + 1, size=B).astype(np.int32) if ragged else np.full(B, S, np.int32)
+    for mode in MODES:
+        check(s, kv, mode, k, f"full size ragged={ragged}")
