@@ -490,7 +490,19 @@ sd_status sd_triattention_select(const float* scores, int32_t layers, int32_t ba
   t.stats = reinterpret_cast<double*>(ws + p.off_stats);
   t.lens = mode == SD_SELECT_PER_LAYER_PERHEAD ? reinterpret_cast<int32_t*>(ws + p.off_lens) : nullptr;
   t.reduced = reduced_out ? reduced_out : reinterpret_cast<float*>(ws + p.off_reduced);
+  t.want_reduced = reduced_out ? 1 : 0;
+  // per layer and head, rows of one wave's registers are selected by the
+  // normalization kernel itself
+  // (SD_TRI_FUSE_SELECT=0, tests: the separate selection pass)
+  const char* fuse_env = getenv("SD_TRI_FUSE_SELECT");
+  const bool fused_select = sd::tri_fuses_select(t) && !(fuse_env && fuse_env[0] == '0');
+  if (fused_select) {
+    t.sel_k = k;
+    t.sel_indices = indices;
+    t.sel_counts = counts;
+  }
   if ((st = hip_status(sd::launch_tri(t, stream), "triattention normalize/reduce")) != SD_OK) return st;
+  if (fused_select) return SD_OK;
   sd::SelectArgs a{};
   a.scores = t.reduced;
   a.batch = p.out_batch;

@@ -107,7 +107,14 @@ struct TriArgs {
   float* reduced;          // [out_rows][row_stride]
   int32_t exact_slow;      // 1: every sum by long accumulation (set by launch_tri)
   int32_t z_rows;          // 1: the statistics kernel writes each member's z row (set by launch_tri)
+  int32_t want_reduced;    // 1: the caller reads the reduced rows
+  // per layer and head, with tri_fuses_select(): the statistics kernel also
+  // selects each member row's k largest z (indices [members][k], counts)
+  int32_t sel_k;
+  int32_t* sel_indices;
+  int32_t* sel_counts;
 };
+bool tri_fuses_select(const TriArgs& a);
 int tri_out_rows(int layers, int batch, int groups, int mode);
 hipError_t launch_tri(const TriArgs& a, hipStream_t st);
 

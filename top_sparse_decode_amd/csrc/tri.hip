@@ -24,9 +24,12 @@
 // into four ordered quarters).  Selection then runs on the reduced rows.
 #include "common.h"
 #include "kernels.h"
+#include "wave_select.h"
 
 #include <math.h>
 #include <stdlib.h>
+
+#include <type_traits>
 
 namespace sd {
 
@@ -207,6 +210,20 @@ __device__ __forceinline__ float tri_z(float s, double mu, double sigma, double 
   return __double2float_rn(__ddiv_rn(d, sigma));
 }
 
+// The same z without the division: `exact` is set where the product is not
+// safe (near a binary32 midpoint or tiny); the caller then uses tri_z.
+__device__ __forceinline__ float tri_z_product(float s, double mu, double sigma, double rinv, bool& exact) {
+  exact = false;
+  if (!__builtin_isfinite(s)) return -__builtin_inff();
+  if (sigma == 0.0) return 0.0f;
+  const double q = __dmul_rn(__dsub_rn((double)s, mu), rinv);
+  const uint64_t b = (uint64_t)__double_as_longlong(q);
+  const uint32_t low = (uint32_t)b & 0x1FFFFFFFu;
+  const uint32_t ex = (uint32_t)(b >> 52) & 0x7FFu;
+  exact = !(low - ((1u << 28) - 3u) > 6u && ex >= 1023u - 126u);
+  return __double2float_rn(q);
+}
+
 template <bool B>
 struct TsFlag {
   static constexpr bool value = B;
@@ -216,9 +233,10 @@ struct TsFlag {
 // part).  NV > 0: the row is in xv, NV 16-byte units per thread; NV == 0:
 // every pass reads the row again.  With one wave the partial results meet
 // in registers alone.
-template <int NV, int W>
+template <int NV, int W, bool ZROWS, bool SEL>
 __device__ __forceinline__ void tri_stats_row(const TriArgs& a, TsShared<W>& sh, int m, int kv_len,
-                                              float (&xv)[NV > 0 ? 4 * NV : 1]) {
+                                              float (&xv)[NV > 0 ? 4 * NV : 1],
+                                              WaveSelectSmem<(SEL && NV > 0 ? NV : 1)>& ssel) {
   constexpr int T = 64 * W;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int Lr = clamp_len(kv_len, a.row_stride);
@@ -441,18 +459,85 @@ __device__ __forceinline__ void tri_stats_row(const TriArgs& a, TsShared<W>& sh,
     a.stats[4 * (int64_t)m + 1] = sigma;
     a.stats[4 * (int64_t)m + 2] = rinv;
   }
-  if constexpr (NV > 0) {
+  if constexpr (NV > 0 && ZROWS) {
     // per layer and head the reduced row is the member's own z: written from
     // the registers (reduced rows 16-byte aligned, row_stride % 4 == 0)
-    if (a.z_rows) {
+    {
       float* out = a.reduced + (int64_t)m * a.row_stride;
+      // the product form first; a lane with any unsafe product writes its
+      // row again with the division (rare)
+      bool slow = false;
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         const int t = 4 * (threadIdx.x + T * i);
-        if (t < a.row_stride)
-          *reinterpret_cast<float4*>(out + t) =
-              make_float4(tri_z(xv[4 * i], mu, sigma, rinv), tri_z(xv[4 * i + 1], mu, sigma, rinv),
-                          tri_z(xv[4 * i + 2], mu, sigma, rinv), tri_z(xv[4 * i + 3], mu, sigma, rinv));
+        bool e0, e1, e2, e3;
+        const float4 z = make_float4(tri_z_product(xv[4 * i], mu, sigma, rinv, e0),
+                                     tri_z_product(xv[4 * i + 1], mu, sigma, rinv, e1),
+                                     tri_z_product(xv[4 * i + 2], mu, sigma, rinv, e2),
+                                     tri_z_product(xv[4 * i + 3], mu, sigma, rinv, e3));
+        slow = slow || e0 || e1 || e2 || e3;
+        if (t < a.row_stride) *reinterpret_cast<float4*>(out + t) = z;
+      }
+      if (__builtin_amdgcn_ballot_w64(slow) != 0 && slow) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+          const int t = 4 * (threadIdx.x + T * i);
+          if (t < a.row_stride)
+            *reinterpret_cast<float4*>(out + t) =
+                make_float4(tri_z(xv[4 * i], mu, sigma, rinv), tri_z(xv[4 * i + 1], mu, sigma, rinv),
+                            tri_z(xv[4 * i + 2], mu, sigma, rinv), tri_z(xv[4 * i + 3], mu, sigma, rinv));
+        }
+      }
+    }
+  }
+  if constexpr (NV > 0 && W == 1 && SEL) {
+    // per layer and head, the member's selection from the z it has just
+    // formed (the lanes hold positions as the one-wave selection expects)
+    {
+      const int k = a.sel_k;
+      int32_t* out = a.sel_indices + (int64_t)m * k;
+      if (Lr <= k) {
+        for (int i = lane; i < k; i += 64) out[i] = i < Lr ? i : -1;
+        if (a.sel_counts && lane == 0) a.sel_counts[m] = Lr;
+      } else {
+        uint32_t key[NV][4];
+        uint32_t kmin1 = 0xFFFFFFFFu, kmax = 0u;
+        bool slow = false;  // some element's z needs the division (rare)
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            bool ex;
+            const float z = tri_z_product(xv[4 * i + e], mu, sigma, rinv, ex);
+            slow = slow || ex;
+            key[i][e] = max(wave_key(z), 1u);
+          }
+        if (__builtin_amdgcn_ballot_w64(slow) != 0 && slow) {
+          // such a lane forms all its z again with the division, reading its
+          // scores again (each below kv_len; the others are not used)
+#pragma unroll
+          for (int i = 0; i < NV; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int t = 4 * (lane + 64 * i) + e;
+              if (t < Lr) key[i][e] = max(wave_key(tri_z(row[t], mu, sigma, rinv)), 1u);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int t = 4 * (lane + 64 * i) + e;
+            uint32_t kk = t < Lr ? key[i][e] : 0u;
+            asm volatile("" : "+v"(kk));  // the scores are not kept beside their keys
+            key[i][e] = kk;
+            kmin1 = min(kmin1, kk - 1u);
+            kmax = max(kmax, kk);
+          }
+        const uint32_t kmin = uniform_u32(wave_min_u32(kmin1)) + 1u;
+        kmax = uniform_u32(wave_max_u32(kmax));
+        wave_select<NV>(key, kmin, kmax, k, out, nullptr, ssel);
+        if (a.sel_counts && lane == 0) a.sel_counts[m] = k;
       }
     }
   }
@@ -483,18 +568,27 @@ __device__ __forceinline__ int tri_kv_len(const TriArgs& a, int m) { return a.kv
 
 // One block of W waves per member row.  NV > 0: the row is held in
 // registers (NV 16-byte units per thread); NV == 0: read again in every pass.
-template <int NV, int W>
+// ZROWS: also the member's z row (per layer and head); SEL: also its
+// selection (per layer and head, one wave per row).  Separate instances, so
+// that the plain statistics keep their registers.
+template <int NV, int W, bool ZROWS = false, bool SEL = false>
 __global__ __launch_bounds__(64 * W) void tri_stats_kernel(TriArgs a) {
   __shared__ TsShared<W> sh;
+  __shared__ WaveSelectSmem<(SEL && NV > 0 ? NV : 1)> ssel;
   const int len = tri_kv_len(a, blockIdx.x);
   if constexpr (NV > 0) {
     float cur[4 * NV];
     tri_load_row<NV, W>(a, blockIdx.x, len, cur);
-    tri_stats_row<NV, W>(a, sh, blockIdx.x, len, cur);
+    tri_stats_row<NV, W, ZROWS, SEL>(a, sh, blockIdx.x, len, cur, ssel);
   } else {
     float none[1] = {0.0f};
-    tri_stats_row<0, W>(a, sh, blockIdx.x, len, none);
+    tri_stats_row<0, W, false, false>(a, sh, blockIdx.x, len, none, ssel);
   }
+}
+
+bool tri_fuses_select(const TriArgs& a) {
+  return a.mode == 0 && (a.row_stride % 4) == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0 &&
+         a.row_stride <= 4096;
 }
 
 
@@ -696,18 +790,40 @@ hipError_t launch_tri(const TriArgs& args, hipStream_t st) {
   if (members == 0 || a.row_stride == 0) return hipSuccess;
   const bool rows16 = (a.row_stride % 4) == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0;
   // per layer and head, rows held in registers give their z rows at once
-  a.z_rows = (a.mode == 0 && rows16 && a.row_stride <= 16384 && (reinterpret_cast<uintptr_t>(a.reduced) & 15) == 0)
+  // (not at all when the kernel also selects and the caller does not read them)
+  const bool fused_sel = a.sel_indices != nullptr;
+  a.z_rows = (a.mode == 0 && rows16 && a.row_stride <= 16384 && (reinterpret_cast<uintptr_t>(a.reduced) & 15) == 0 &&
+              (!fused_sel || a.want_reduced))
                  ? 1 : 0;
   // rows held in registers: one wave per row up to 4096 tokens (up to 64 per
   // lane), four waves up to 16384; longer rows, or rows that are not whole
-  // 16-byte units, are read again in every pass
-  if (rows16 && a.row_stride <= 1024) tri_stats_kernel<4, 1><<<members, 64, 0, st>>>(a);
-  else if (rows16 && a.row_stride <= 2048) tri_stats_kernel<8, 1><<<members, 64, 0, st>>>(a);
-  else if (rows16 && a.row_stride <= 4096) tri_stats_kernel<16, 1><<<members, 64, 0, st>>>(a);
-  else if (rows16 && a.row_stride <= 8192) tri_stats_kernel<8, 4><<<members, 256, 0, st>>>(a);
-  else if (rows16 && a.row_stride <= 16384) tri_stats_kernel<16, 4><<<members, 256, 0, st>>>(a);
-  else tri_stats_kernel<0, 4><<<members, 256, 0, st>>>(a);
-  if (a.z_rows) return hipGetLastError();
+  // 16-byte units, are read again in every pass.  Per layer and head, the
+  // z rows (when read) and the selection (when asked) come from the same
+  // kernel.
+  const bool zr = a.z_rows != 0;
+  if (rows16 && a.row_stride <= 4096) {
+    const int nv = a.row_stride <= 1024 ? 4 : (a.row_stride <= 2048 ? 8 : 16);
+    auto go = [&](auto nvc) {
+      constexpr int NV = decltype(nvc)::value;
+      if (fused_sel && zr) tri_stats_kernel<NV, 1, true, true><<<members, 64, 0, st>>>(a);
+      else if (fused_sel) tri_stats_kernel<NV, 1, false, true><<<members, 64, 0, st>>>(a);
+      else if (zr) tri_stats_kernel<NV, 1, true, false><<<members, 64, 0, st>>>(a);
+      else tri_stats_kernel<NV, 1><<<members, 64, 0, st>>>(a);
+    };
+    if (nv == 4) go(std::integral_constant<int, 4>{});
+    else if (nv == 8) go(std::integral_constant<int, 8>{});
+    else go(std::integral_constant<int, 16>{});
+  } else if (rows16 && a.row_stride <= 8192) {
+    if (zr) tri_stats_kernel<8, 4, true><<<members, 256, 0, st>>>(a);
+    else tri_stats_kernel<8, 4><<<members, 256, 0, st>>>(a);
+  } else if (rows16 && a.row_stride <= 16384) {
+    if (zr) tri_stats_kernel<16, 4, true><<<members, 256, 0, st>>>(a);
+    else tri_stats_kernel<16, 4><<<members, 256, 0, st>>>(a);
+  } else {
+    tri_stats_kernel<0, 4><<<members, 256, 0, st>>>(a);
+  }
+  // per layer and head with the z rows written (or not wanted): no reduce pass
+  if (zr || fused_sel) return hipGetLastError();
   const int nm = a.mode == 0 ? 1 : (a.mode == 1 ? a.layers : a.layers * a.groups);
   const bool vec = (a.row_stride % 4) == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(a.reduced) & 15) == 0;
