@@ -165,3 +165,27 @@ def test_tri_full_size_all_modes(ragged):
     kv = rs.integers(2049, S + 1, size=B).astype(np.int32) if ragged else np.full(B, S, np.int32)
     for mode in MODES:
         check(s, kv, mode, k, f"full size ragged={ragged}")
+
+
+@pytest.mark.parametrize("S", [1000, 2048, 4096, 3001])
+def test_tri_selection_without_reduced_rows(S):
+    # no reduced rows asked for: per layer and head the statistics kernel
+    # selects without writing z rows; indices and counts still exact
+    s = random_scores(49, 3, 2, 4, S)
+    s[0, 0, 0, :] = np.float32(1.5)                                   # one value
+    s[1, 1, 1, ::5] = -np.inf
+    kv = np.array([S, S // 2 + 1], np.int32)
+    layers, B, G, _ = s.shape
+    for mode, k in (("per_layer_perhead", 64), ("per_layer_perhead", S // 2), ("union", 128)):
+        out_rows = {"per_layer_perhead": layers * B * G, "per_head": B * G, "union": B}[mode]
+        idx = torch.empty((out_rows, k), dtype=torch.int32, device="cuda")
+        cnt = torch.empty((out_rows,), dtype=torch.int32, device="cuda")
+        ws = torch.empty(api.triattention_select_workspace_size(layers, B, G, S, mode, k), dtype=torch.uint8,
+                         device="cuda")
+        say(f"[tri] no reduced rows mode={mode} S={S} k={k}")
+        api.triattention_select(torch.from_numpy(s).cuda(), torch.from_numpy(kv).cuda(), mode, k, idx, cnt, None,
+                                ws)
+        torch.cuda.synchronize()
+        ref = oracle.tri_select(s, kv, mode, k)
+        assert np.array_equal(idx.cpu().numpy(), ref["indices"]), mode
+        assert np.array_equal(cnt.cpu().numpy(), ref["counts"]), mode
