@@ -75,7 +75,7 @@ extern "C" {
 typedef enum sd_status {
   SD_OK = 0,
   SD_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size or alignment          */
-  SD_ERR_UNSUPPORTED = 2,      /* valid request this build has no kernel for   */
+  SD_ERR_UNSUPPORTED = 2,      /* valid request the library has no kernel for */
   SD_ERR_WORKSPACE_TOO_SMALL = 3,
   SD_ERR_HIP = 4               /* a HIP launch or runtime call failed          */
 } sd_status;
