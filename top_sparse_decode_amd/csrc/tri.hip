@@ -64,7 +64,7 @@ struct TsShared {
   int n[W];
   float vmax[W], vmin[W];
   double part1[W][2], part2[W][2];
-  int rest1[W], rest2[W];
+  int rest1[W], rest1b[W], rest2[W];
   uint64_t words[W][4][kLongWords];  // per wave: positive words, their carries, negative words, carries
   uint64_t tot[2][kLongWords];
   double sum;
@@ -104,14 +104,34 @@ __device__ double round_int(__int128 v, int e) {
 // and G2 = 2^g2 below 2^53 of their steps, plus a remainder of at most
 // n G2 / 2 when `rest`.  False when the remainder could change the rounding.
 __device__ bool round_two(double A1, double A2, int g2, int s, bool rest, int n, double& out) {
+  // A1 + A2 rounded once is the exactly rounded total when nothing is left
+  const double sum = __dadd_rn(A1, A2);
+  if (!rest) {
+    out = sum;
+    return true;
+  }
+  // with a remainder R, |R| <= r G2: sum + e (e from TwoSum, exact) is
+  // A1 + A2, and sum stands when |e| + r G2 stays below half its gap to
+  // either neighbour (a power of two, with its closer lower neighbour, and
+  // anything near that bound take the integer form below)
+  const int64_t r = (n + 1) / 2;
+  {
+    const double bb = __dsub_rn(sum, A1);
+    const double e = __dadd_rn(__dsub_rn(A1, __dsub_rn(sum, bb)), __dsub_rn(A2, bb));
+    const uint64_t sb = (uint64_t)__double_as_longlong(sum);
+    const int ex = (int)((sb >> 52) & 0x7FF);
+    if (sum != 0.0 && (sb & ((1ull << 52) - 1)) != 0 && ex > 53) {
+      const double half_ulp = ldexp(1.0, ex - 1023 - 53);
+      const double lhs = __dadd_rn(fabs(e), ldexp((double)r, g2));  // within a relative 2^-53 of the exact
+      if (lhs <= half_ulp * (1.0 - 0x1p-40)) {
+        out = sum;
+        return true;
+      }
+    }
+  }
   const int64_t a1 = (int64_t)ldexp(A1, -(g2 + s));  // integers of at most 53 bits: exact
   const int64_t a2 = (int64_t)ldexp(A2, -g2);
   const __int128 T = ((__int128)a1 << s) + a2;
-  if (!rest) {
-    out = round_int(T, g2);
-    return true;
-  }
-  const int64_t r = (n + 1) / 2;
   out = round_int(T - r, g2);
   return out == round_int(T + r, g2);
 }
@@ -356,37 +376,65 @@ __device__ __forceinline__ void tri_stats_row(const TriArgs& a, TsShared<W>& sh,
       bool done = false;
       if (!force_long && k2 - 52 >= -1022) {
         const double g1 = ldexp(1.5, k1), g2 = ldexp(1.5, k2);
+        // the first grid alone: binary32 scores within about 2^15 of the
+        // largest are taken whole by it; the second grid only where some
+        // term is not (a second pass over the registers)
         double A1 = 0.0, A2 = 0.0;
-        bool rest = false;
-        auto pass = [&](auto live) __attribute__((always_inline)) {
+        bool rem = false, rest = false;
+        auto pass1 = [&](auto live) __attribute__((always_inline)) {
+          each([&](float x) {
+            const double v = decltype(live)::value ? (double)x : val(x);
+            const double h1 = grid_part(v, g1);
+            A1 = __dadd_rn(A1, h1);
+            rem = rem || v != h1;
+          });
+        };
+        auto pass2 = [&](auto live) __attribute__((always_inline)) {
           each([&](float x) {
             const double v = decltype(live)::value ? (double)x : val(x);
             const double h1 = grid_part(v, g1), l1 = __dsub_rn(v, h1);
             const double h2 = grid_part(l1, g2);
-            A1 = __dadd_rn(A1, h1);
             A2 = __dadd_rn(A2, h2);
             rest = rest || l1 != h2;
           });
         };
-        if (all_live) pass(TsFlag<true>{});
-        else pass(TsFlag<false>{});
+        if (all_live) pass1(TsFlag<true>{});
+        else pass1(TsFlag<false>{});
         A1 = wave_sum(A1);
-        A2 = wave_sum(A2);
-        bool brest = __builtin_amdgcn_ballot_w64(rest) != 0;
+        bool brem = __builtin_amdgcn_ballot_w64(rem) != 0;
         if constexpr (W > 1) {
           if (lane == 0) {
             sh.part1[wid][0] = A1;
-            sh.part1[wid][1] = A2;
-            sh.rest1[wid] = brest;
+            sh.rest1[wid] = brem;
           }
           __syncthreads();
-          A1 = A2 = 0.0;
-          brest = false;
+          A1 = 0.0;
+          brem = false;
 #pragma unroll
           for (int w = 0; w < W; ++w) {
             A1 = __dadd_rn(A1, sh.part1[w][0]);
-            A2 = __dadd_rn(A2, sh.part1[w][1]);
-            brest = brest || sh.rest1[w] != 0;
+            brem = brem || sh.rest1[w] != 0;
+          }
+        }
+        bool brest = false;
+        if (brem) {
+          if (all_live) pass2(TsFlag<true>{});
+          else pass2(TsFlag<false>{});
+          A2 = wave_sum(A2);
+          brest = __builtin_amdgcn_ballot_w64(rest) != 0;
+          if constexpr (W > 1) {
+            if (lane == 0) {
+              sh.part1[wid][1] = A2;
+              sh.rest1b[wid] = brest;
+            }
+            __syncthreads();
+            A2 = 0.0;
+            brest = false;
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+              A2 = __dadd_rn(A2, sh.part1[w][1]);
+              brest = brest || sh.rest1b[w] != 0;
+            }
           }
         }
         done = round_two(A1, A2, k2 - 52, 51 - c, brest, n, s1);
