@@ -456,46 +456,100 @@ __device__ __forceinline__ void tri_stats_row(const TriArgs& a, TsShared<W>& sh,
       bool done = false;
       if (!force_long && k2 - 52 >= -1022) {
         const double g1 = ldexp(1.5, k1), g2 = ldexp(1.5, k2);
-        double A1 = 0.0, A2 = 0.0;
-        bool rest = false;
-        auto pass = [&](auto live) __attribute__((always_inline)) {
-          each([&](float x) {
-            double v;
-            if constexpr (decltype(live)::value) {
-              const double d = __dsub_rn((double)x, mu);
-              v = __dmul_rn(d, d);
-            } else {
-              v = sq(x);
-            }
-            const double h1 = grid_part(v, g1), l1 = __dsub_rn(v, h1);
-            const double h2 = grid_part(l1, g2);
-            A1 = __dadd_rn(A1, h1);
-            A2 = __dadd_rn(A2, h2);
-            rest = rest || l1 != h2;
-          });
-        };
-        if (all_live) pass(TsFlag<true>{});
-        else pass(TsFlag<false>{});
-        A1 = wave_sum(A1);
-        A2 = wave_sum(A2);
-        bool brest = __builtin_amdgcn_ballot_w64(rest) != 0;
-        if constexpr (W > 1) {
-          if (lane == 0) {
-            sh.part2[wid][0] = A1;
-            sh.part2[wid][1] = A2;
-            sh.rest2[wid] = brest;
+        auto term = [&](auto live, float x) __attribute__((always_inline)) {
+          if constexpr (decltype(live)::value) {
+            const double d = __dsub_rn((double)x, mu);
+            return __dmul_rn(d, d);
+          } else {
+            return sq(x);
           }
-          __syncthreads();
-          A1 = A2 = 0.0;
-          brest = false;
+        };
+        // The first grid exactly (A1) and what it leaves summed in plain
+        // binary64 (R1): every leftover is at most G1 / 2, so R1 is within
+        // E = gamma_{n-1} n G1 / 2 <= n^2 G1 2^-54 (1 + 2^-18) of their exact
+        // sum, in any order.  With s = RN(A1 + R1) and e its exact TwoSum
+        // error, the total lies within |e| + E of s: s stands when that is
+        // below half of s's last place (s not a power of two).  Otherwise the
+        // second grid is taken exactly.
+        {
+          double A1 = 0.0, R1 = 0.0;
+          auto pass1 = [&](auto live) __attribute__((always_inline)) {
+            each([&](float x) {
+              const double v = term(live, x);
+              const double h1 = grid_part(v, g1);
+              A1 = __dadd_rn(A1, h1);
+              R1 = __dadd_rn(R1, __dsub_rn(v, h1));
+            });
+          };
+          if (all_live) pass1(TsFlag<true>{});
+          else pass1(TsFlag<false>{});
+          A1 = wave_sum(A1);
+          R1 = wave_sum(R1);
+          if constexpr (W > 1) {
+            if (lane == 0) {
+              sh.part2[wid][0] = A1;
+              sh.part2[wid][1] = R1;
+            }
+            __syncthreads();
+            A1 = R1 = 0.0;
 #pragma unroll
-          for (int w = 0; w < W; ++w) {
-            A1 = __dadd_rn(A1, sh.part2[w][0]);
-            A2 = __dadd_rn(A2, sh.part2[w][1]);
-            brest = brest || sh.rest2[w] != 0;
+            for (int w = 0; w < W; ++w) {
+              A1 = __dadd_rn(A1, sh.part2[w][0]);
+              R1 = __dadd_rn(R1, sh.part2[w][1]);
+            }
+            __syncthreads();  // the slots are read again below
+          }
+          const double sum = __dadd_rn(A1, R1);
+          const double bb = __dsub_rn(sum, A1);
+          const double e = __dadd_rn(__dsub_rn(A1, __dsub_rn(sum, bb)), __dsub_rn(R1, bb));
+          const uint64_t sb = (uint64_t)__double_as_longlong(sum);
+          const int ex = (int)((sb >> 52) & 0x7FF);
+          if (sum != 0.0 && (sb & ((1ull << 52) - 1)) != 0 && ex > 53 && n <= (1 << 26)) {
+            const double E = ldexp((double)n * (double)n, k1 - 52 - 54) * (1.0 + 0x1p-18);
+            const double lhs = __dadd_rn(fabs(e), E);
+            if (lhs <= ldexp(1.0, ex - 1023 - 53) * (1.0 - 0x1p-40)) {
+              s2 = sum;
+              done = true;
+            }
           }
         }
-        done = round_two(A1, A2, k2 - 52, 51 - c, brest, n, s2);
+        double A1 = 0.0, A2 = 0.0;
+        bool brest = false;
+        if (!done) {
+          bool rest = false;
+          auto pass = [&](auto live) __attribute__((always_inline)) {
+            each([&](float x) {
+              const double v = term(live, x);
+              const double h1 = grid_part(v, g1), l1 = __dsub_rn(v, h1);
+              const double h2 = grid_part(l1, g2);
+              A1 = __dadd_rn(A1, h1);
+              A2 = __dadd_rn(A2, h2);
+              rest = rest || l1 != h2;
+            });
+          };
+          if (all_live) pass(TsFlag<true>{});
+          else pass(TsFlag<false>{});
+          A1 = wave_sum(A1);
+          A2 = wave_sum(A2);
+          brest = __builtin_amdgcn_ballot_w64(rest) != 0;
+          if constexpr (W > 1) {
+            if (lane == 0) {
+              sh.part2[wid][0] = A1;
+              sh.part2[wid][1] = A2;
+              sh.rest2[wid] = brest;
+            }
+            __syncthreads();
+            A1 = A2 = 0.0;
+            brest = false;
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+              A1 = __dadd_rn(A1, sh.part2[w][0]);
+              A2 = __dadd_rn(A2, sh.part2[w][1]);
+              brest = brest || sh.rest2[w] != 0;
+            }
+          }
+          done = round_two(A1, A2, k2 - 52, 51 - c, brest, n, s2);
+        }
       }
       if (!done) s2 = long_sum(sq);
     }
