@@ -611,7 +611,11 @@ __global__ __launch_bounds__(512) void attn_mla_combine_kernel(AttnArgs a, int n
   const int tid = threadIdx.x;
   const int lane = tid & 63, n = tid >> 7;  // tile within the quarter: 0..3
   const int jh = (tid >> 6) & 1;            // which eight of the lane's 16 values
-  const int quarter = blockIdx.x % 4, w = (blockIdx.x / 4) % nw, b = blockIdx.x / (4 * nw);
+  // the same XCD placement as attn_mla_kernel: a request's items run where
+  // its splits ran (blocks go to the 8 XCDs round robin by index)
+  int item = blockIdx.x;
+  if ((gridDim.x & 7) == 0) item = (item & 7) * (gridDim.x >> 3) + (item >> 3);
+  const int quarter = item % 4, w = (item / 4) % nw, b = item / (4 * nw);
   const int col = lane & 31, hf = lane >> 5;
   const int S = a.splits;
   const int tile = 4 * quarter + n;  // N tile of the partial layout (0..15)

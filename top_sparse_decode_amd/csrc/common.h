@@ -164,6 +164,18 @@ __device__ __forceinline__ int2 ld_coherent2(const int32_t* p) {
   return int2{(int)(uint32_t)v, (int)(uint32_t)(v >> 32)};
 }
 
+// v + (v of lane ^ 16), then + (that of lane ^ 32): the sum over a lane's
+// four 16-lane rows, in every lane, by gfx950's lane-swap instructions (VALU
+// only, no LDS permute).  Each add takes its own value first, so the result
+// equals `v += shfl_xor(v, 16); v += shfl_xor(v, 32)` bit for bit (a
+// floating-point add is commutative).
+__device__ __forceinline__ float rows4_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
 // Wait until this thread's stores and atomics have completed.
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" : : : "memory"); }
 

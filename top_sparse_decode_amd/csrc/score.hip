@@ -604,8 +604,7 @@ __global__ __launch_bounds__(NW * 64) void score_dsa_kernel(ScoreArgs a, int ite
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) sum = __builtin_fmaf(wv[mt][r], relu_bits(acc[mt][r]), sum);
-      sum += __shfl_xor(sum, 16);
-      sum += __shfl_xor(sum, 32);
+      sum = rows4_sum(sum);
       const int t = t0 + 16 * n + col;
       const bool ok = t < L && half_page(t0 + 16 * n) >= 0;
       if (ok) {
@@ -894,16 +893,14 @@ __global__ __launch_bounds__(NW * 64) void score_dsa_fp8_kernel(ScoreArgs a, int
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int r = 0; r < 4; ++r) sum = __builtin_fmaf(wv[mt][r], relu_bits(acc[mt][r]), sum);
-        sum += __shfl_xor(sum, 16);
-        sum += __shfl_xor(sum, 32);
+        sum = rows4_sum(sum);
         sum = __fmul_rn(sig[n], sum);
       } else {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int r = 0; r < 4; ++r) sum = __builtin_fmaf(wv[mt][r], relu_bits(__fmul_rn(sig[n], acc[mt][r])), sum);
-        sum += __shfl_xor(sum, 16);
-        sum += __shfl_xor(sum, 32);
+        sum = rows4_sum(sum);
       }
       const int t = t0 + 16 * n + col;
       const bool ok = t < L && half_page(t0 + 16 * n) >= 0;
