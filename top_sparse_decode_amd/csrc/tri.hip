@@ -19,9 +19,11 @@
 //   value only when strictly larger.
 //
 // Kernels: tri_stats_kernel (one block per member row, the sums split over
-// exact grids so that the tokens are summed in parallel) and
+// exact grids so that the tokens are summed in parallel; per layer and head
+// it also writes the member's z row and/or selects from it) and
 // tri_reduce_kernel / tri_reduce4_kernel (a token per lane, the members split
-// into four ordered quarters).  Selection then runs on the reduced rows.
+// into ordered slices whose maxima meet in order).  Selection then runs on
+// the reduced rows.
 #include "common.h"
 #include "kernels.h"
 #include "wave_select.h"
@@ -37,25 +39,31 @@ constexpr int kTriThreads = 256;
 constexpr int kTriSpan = 4096;  // tokens per block of the one-slice reduce
 
 // Statistics.  Both sums are exactly rounded, so their terms may be added in
-// any order: a member row is spread over one block (thread c holds tokens
-// 4 (c + 256 i) .. +3 when the row is held in registers), and the partial
-// sums meet in any order.  Each sum is taken exactly by splitting every term
-// over two fixed grids (the error-free extraction of Rump, Ogita and Oishi):
-// with sigma = 1.5 * 2^k and |v| < 2^(k-1), h = (v + sigma) - sigma is v
-// rounded to a multiple of G = 2^(k-52), and v - h is exact, so
-// v = h + (v - h) with no error and the second grid takes v - h.  k comes
-// from a bound M on |v| (from the row's extremes) and the term count n:
-// k = log2 M + 1 + ceil(log2 n), so that every partial sum of the h of one
-// grid is a multiple of G below 2^53 G, hence exact in any order, across
-// lanes and waves too.  The second grid is 2^(51 - ceil(log2 n)) finer.
-// What the second grid leaves of a term is at most half its step, so the
-// exact total lies within n/2 steps of the two grids' sum T; where every
-// value in that interval rounds to the same binary64 it is the result (for
-// binary32 scores nothing is left unless they span more than about 2^54 at
-// 4096 tokens; for the squared deviations the interval is far below their
-// sum's last place unless the row is built for it).  Otherwise, and for
-// every row when asked, the sum is taken in a long accumulator of 64-bit
-// words spanning all of binary64 (word w in lane w), exact for any input.
+// any order: a member row is spread over one block (thread c of its T
+// threads holds tokens 4 (c + T i) .. +3 when the row is held in registers),
+// and the partial sums meet in any order.  The error-free extraction of Rump,
+// Ogita and Oishi splits a term over a fixed grid: with sigma = 1.5 * 2^k and
+// |v| < 2^(k-1), h = (v + sigma) - sigma is v rounded to a multiple of
+// G = 2^(k-52), and v - h is exact.  k comes from a bound M on |v| (from the
+// row's extremes) and the term count n: k = log2 M + 1 + ceil(log2 n), so
+// every partial sum of the h of one grid is a multiple of G below 2^53 G,
+// hence exact in any order, across lanes and waves too.
+//  * S1 (the scores): one grid first; binary32 scores within about 2^15 of
+//    the largest are taken whole, and only where some term is not does a
+//    second pass add a second grid 2^(51 - ceil(log2 n)) finer, whose
+//    leftovers are at most half its step each.
+//  * S2 (the squared deviations): one grid exactly (A1) plus its leftovers,
+//    each at most G1 / 2, in plain binary64 (R1), which is within
+//    E = n^2 G1 2^-54 (1 + 2^-18) of their exact sum in any order.
+//  * The final rounding (round_two): s = RN(A1 + A2) (or A1 + R1) stands
+//    when s is not a power of two and its exact TwoSum error plus the
+//    leftover bound stays below half of s's last place; else S2 takes the
+//    second grid exactly too, and both decide by the 128-bit integer form
+//    (the grids' sum T in units of the finer grid: RN(T - n/2) = RN(T + n/2)).
+//  * A row where that fails too (scores spanning more than about 2^54, or a
+//    sum within about 2^-21 of a rounding midpoint), and every row when
+//    asked, is summed in a long accumulator of 64-bit words spanning all of
+//    binary64 (word w in lane w), exact for any input.
 constexpr int kLongWords = 35;  // bit 0 = 2^-1074; 2240 bits hold 2^31 terms of any binary64 magnitude
 
 // shared state of a row's block of W waves
