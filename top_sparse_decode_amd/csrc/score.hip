@@ -227,12 +227,8 @@ __global__ __launch_bounds__(256) void score_exact_staged_kernel(ScoreArgs a) {
   typedef typename QElem<KT>::type QT;
   // the group's G query rows: UPR units of K meet UPR * EPU query elements each
   constexpr int kQUnits = G * UPR * EPU * (int)sizeof(QT) / 16;
-  // Small groups read the query (the same in every lane) with scalar loads
-  // and widen it on the scalar unit, so each product takes it as a scalar
-  // operand; larger groups stage it in LDS (broadcast reads).
-  constexpr bool kScalarQ = G <= 8;
   __shared__ uint4 s_rows[4][64 * UPR];
-  __shared__ uint4 s_q[kScalarQ ? 1 : kQUnits];
+  __shared__ uint4 s_q[kQUnits];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int b = blockIdx.y / a.num_kv_heads, g = blockIdx.y % a.num_kv_heads;
   const int cap = min(a.max_kv_len, a.max_pages * a.page_size);
@@ -251,11 +247,11 @@ __global__ __launch_bounds__(256) void score_exact_staged_kernel(ScoreArgs a) {
   }
   // the query rows (contiguous: heads g*G .. g*G+G-1 of request b), loaded
   // with the K rows below and written to LDS after them
-  constexpr int kQPerThread = kScalarQ ? 1 : (kQUnits + 255) / 256;
-  const uint4* qsrc = reinterpret_cast<const uint4*>(reinterpret_cast<const QT*>(a.q) +
-                                                     ((int64_t)b * a.q_heads + g * G) * a.head_dim);
+  constexpr int kQPerThread = (kQUnits + 255) / 256;
   uint4 qreg[kQPerThread];
-  if constexpr (!kScalarQ) {
+  {
+    const uint4* qsrc = reinterpret_cast<const uint4*>(reinterpret_cast<const QT*>(a.q) +
+                                                       ((int64_t)b * a.q_heads + g * G) * a.head_dim);
 #pragma unroll
     for (int k = 0; k < kQPerThread; ++k) qreg[k] = qsrc[min((int)threadIdx.x + 256 * k, kQUnits - 1)];
   }
@@ -281,10 +277,8 @@ __global__ __launch_bounds__(256) void score_exact_staged_kernel(ScoreArgs a) {
     s_rows[wid][r * UPR + (p ^ swz(r))] = v[c];
   }
   // (threads past the last unit all write the last one, the same value)
-  if constexpr (!kScalarQ) {
 #pragma unroll
-    for (int k = 0; k < kQPerThread; ++k) s_q[min((int)threadIdx.x + 256 * k, kQUnits - 1)] = qreg[k];
-  }
+  for (int k = 0; k < kQPerThread; ++k) s_q[min((int)threadIdx.x + 256 * k, kQUnits - 1)] = qreg[k];
   __syncthreads();
   float s = -__builtin_inff();
   if (ok) {
@@ -294,34 +288,9 @@ __global__ __launch_bounds__(256) void score_exact_staged_kernel(ScoreArgs a) {
     // query units: QT elements u*EPU .. of head j (one 16-byte unit for bf16 or
     // f32 K, two for fp8 K), the same address in every lane
     constexpr int kQPerK = EPU * (int)sizeof(QT) / 16;
-    if constexpr (kScalarQ) {
-      // the group's query rows through the constant address space: uniform
-      // addresses, read-only for the kernel's duration, so scalar loads
-      typedef const __attribute__((address_space(4))) uint4* cq_ptr;
-      const cq_ptr qc = (cq_ptr)(uintptr_t)qsrc;
-      s = exact_token_score<KT, G, UPR>(
-          a, b, g, [&](int u, float (&kv)[EPU]) { cvt_k_unit<KT>(mine[u ^ sw], ksc, kv); },
-          [&](int j, int u, float (&qv)[EPU]) {
-            const int q0 = (j * UPR + u) * kQPerK;
-            if constexpr (kQPerK == 1) {
-              unpack_unit(qc[q0], qv);
-            } else {
-              const uint4 w0 = qc[q0], w1 = qc[q0 + 1];
-              float lo[8], hi[8];
-              unpack_unit(w0, lo);
-              unpack_unit(w1, hi);
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                qv[e] = lo[e];
-                qv[8 + e] = hi[e];
-              }
-            }
-          });
-    } else {
-      s = exact_token_score<KT, G, UPR>(
-          a, b, g, [&](int u, float (&kv)[EPU]) { cvt_k_unit<KT>(mine[u ^ sw], ksc, kv); },
-          [&](int j, int u, float (&qv)[EPU]) { load_q_unit<KT>(&s_q[(j * UPR + u) * kQPerK], qv); });
-    }
+    s = exact_token_score<KT, G, UPR>(
+        a, b, g, [&](int u, float (&kv)[EPU]) { cvt_k_unit<KT>(mine[u ^ sw], ksc, kv); },
+        [&](int j, int u, float (&qv)[EPU]) { load_q_unit<KT>(&s_q[(j * UPR + u) * kQPerK], qv); });
   }
   if (in_row) row[t] = s;
   if (a.row_stats) note_minmax(a.row_stats + (int64_t)blockIdx.y * kStatStride, s, ok && __builtin_isfinite(s));
