@@ -136,6 +136,28 @@ __device__ __forceinline__ void note_minmax(int32_t* stat, float s, bool finite)
 // in head order.  kunit(u, v) yields K unit u and qunit(j, u, v) the query
 // elements of head j that meet it, as binary32 values; UNITS > 0 fixes the
 // number of units at compile time (else head_dim / units per element).
+// The group reduction of the G dot products, in head order.
+template <int G>
+__device__ __forceinline__ float group_score(const ScoreArgs& a, int b, int g, const float (&acc)[G]) {
+  float s = 0.0f;
+  if (a.mode == 0) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) s = __fadd_rn(s, __fmul_rn(acc[j], a.head_scale));
+  } else if (a.mode == 1) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) s = __fadd_rn(s, acc[j]);
+    s = __fmul_rn(s, a.inv_g);
+  } else {
+    const float* w = a.head_weights + (int64_t)b * a.q_heads + g * G;
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const float r = acc[j] > 0.0f ? acc[j] : 0.0f;
+      s = __fadd_rn(s, __fmul_rn(w[j], r));
+    }
+  }
+  return s;
+}
+
 template <typename KT, int G, int UNITS, typename KUnit, typename QUnit>
 __device__ __forceinline__ float exact_token_score(const ScoreArgs& a, int b, int g, KUnit&& kunit, QUnit&& qunit) {
   constexpr int EPU = Elems<KT>::kPerUnit;
@@ -160,23 +182,7 @@ __device__ __forceinline__ float exact_token_score(const ScoreArgs& a, int b, in
     const int units = a.head_dim / EPU;
     for (int u = 0; u < units; ++u) step(u);
   }
-  float s = 0.0f;
-  if (a.mode == 0) {
-#pragma unroll
-    for (int j = 0; j < G; ++j) s = __fadd_rn(s, __fmul_rn(acc[j], a.head_scale));
-  } else if (a.mode == 1) {
-#pragma unroll
-    for (int j = 0; j < G; ++j) s = __fadd_rn(s, acc[j]);
-    s = __fmul_rn(s, a.inv_g);
-  } else {
-    const float* w = a.head_weights + (int64_t)b * a.q_heads + g * G;
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const float r = acc[j] > 0.0f ? acc[j] : 0.0f;
-      s = __fadd_rn(s, __fmul_rn(w[j], r));
-    }
-  }
-  return s;
+  return group_score<G>(a, b, g, acc);
 }
 
 // Each lane reads its own K row from memory (any layout).
@@ -292,6 +298,147 @@ __global__ __launch_bounds__(256) void score_exact_staged_kernel(ScoreArgs a) {
         a, b, g, [&](int u, float (&kv)[EPU]) { cvt_k_unit<KT>(mine[u ^ sw], ksc, kv); },
         [&](int j, int u, float (&qv)[EPU]) { load_q_unit<KT>(&s_q[(j * UPR + u) * kQPerK], qv); });
   }
+  if (in_row) row[t] = s;
+  if (a.row_stats) note_minmax(a.row_stats + (int64_t)blockIdx.y * kStatStride, s, ok && __builtin_isfinite(s));
+}
+
+// Four heads' dot products over one 8-element unit: acc_j + q_j,e k_e for
+// e = 0..7 in order, each a fused multiply-add (one rounding, as fmaf), the
+// four chains interleaved so that no product waits on the one before it.
+// q_j,e comes from lane L_j of this lane's 16-lane row by a DPP row
+// broadcast, so every lane of the row uses the same query unit.  One asm
+// block: two wait states first, for a query register written by the vector
+// unit just before (the block writes none of its broadcast sources).
+template <int L0, int L1, int L2, int L3>
+__device__ __forceinline__ void fmac8x4_row_bcast(float (&acc)[4], const float (&q0)[8], const float (&q1)[8],
+                                                  const float (&q2)[8], const float (&q3)[8], const float (&k)[8]) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %4, %36 row_newbcast:%44 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %12, %36 row_newbcast:%45 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %20, %36 row_newbcast:%46 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %28, %36 row_newbcast:%47 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %5, %37 row_newbcast:%44 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %13, %37 row_newbcast:%45 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %21, %37 row_newbcast:%46 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %29, %37 row_newbcast:%47 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %6, %38 row_newbcast:%44 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %14, %38 row_newbcast:%45 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %22, %38 row_newbcast:%46 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %30, %38 row_newbcast:%47 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %7, %39 row_newbcast:%44 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %15, %39 row_newbcast:%45 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %23, %39 row_newbcast:%46 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %31, %39 row_newbcast:%47 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %8, %40 row_newbcast:%44 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %16, %40 row_newbcast:%45 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %24, %40 row_newbcast:%46 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %32, %40 row_newbcast:%47 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %9, %41 row_newbcast:%44 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %17, %41 row_newbcast:%45 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %25, %41 row_newbcast:%46 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %33, %41 row_newbcast:%47 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %10, %42 row_newbcast:%44 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %18, %42 row_newbcast:%45 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %26, %42 row_newbcast:%46 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %34, %42 row_newbcast:%47 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %11, %43 row_newbcast:%44 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %19, %43 row_newbcast:%45 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %27, %43 row_newbcast:%46 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %35, %43 row_newbcast:%47 row_mask:0xf bank_mask:0xf\n\t"
+      : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])
+      : "v"(q0[0]), "v"(q0[1]), "v"(q0[2]), "v"(q0[3]), "v"(q0[4]), "v"(q0[5]), "v"(q0[6]), "v"(q0[7]), "v"(q1[0]), "v"(q1[1]), "v"(q1[2]), "v"(q1[3]), "v"(q1[4]), "v"(q1[5]), "v"(q1[6]), "v"(q1[7]), "v"(q2[0]), "v"(q2[1]), "v"(q2[2]), "v"(q2[3]), "v"(q2[4]), "v"(q2[5]), "v"(q2[6]), "v"(q2[7]), "v"(q3[0]), "v"(q3[1]), "v"(q3[2]), "v"(q3[3]), "v"(q3[4]), "v"(q3[5]), "v"(q3[6]), "v"(q3[7]),
+        "v"(k[0]), "v"(k[1]), "v"(k[2]), "v"(k[3]), "v"(k[4]), "v"(k[5]), "v"(k[6]), "v"(k[7]), "i"(L0), "i"(L1), "i"(L2), "i"(L3));
+}
+
+// The exact scores of bf16 K rows (128 or 256 bytes, staged through LDS as in
+// score_exact_staged_kernel) with the query in registers: the group's G x
+// UPR query units, widened to binary32 once, sit one unit per lane of every
+// 16-lane row (unit F = 16 n + i in lane i, registers qv[n]), and each
+// product takes its query element from the row by a DPP broadcast.  The
+// per-token work is then the K widening and one fused multiply-add per
+// product: no per-lane query reads or widening, no LDS traffic for the query.
+// The order is exact_token_score's (each head's dot left to right, then the
+// group reduction).  Every lane runs the products (a broadcast must not read
+// an inactive lane); tokens that are not usable are dropped afterwards.
+template <int G, int UPR>
+__global__ __launch_bounds__(256) void score_exact_bcast_kernel(ScoreArgs a) {
+  constexpr int NG = G * UPR / 16;  // query registers groups of eight values
+  static_assert((G * UPR) % 16 == 0 && NG >= 1 && NG <= 8, "query units must fill whole 16-lane rows");
+  __shared__ uint4 s_rows[4][64 * UPR];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int b = blockIdx.y / a.num_kv_heads, g = blockIdx.y % a.num_kv_heads;
+  const int cap = min(a.max_kv_len, a.max_pages * a.page_size);
+  const int L = clamp_len(a.kv_lens[b], cap);
+  const int t = (blockIdx.x * 4 + wid) * kWave + lane;
+  float* row = a.scores + (int64_t)blockIdx.y * a.max_kv_len;
+  const bool in_row = t < a.max_kv_len;
+  bool ok = in_row && t < L;
+  int64_t off = 0;
+  if (ok) {
+    const int page = a.block_table[(int64_t)b * a.max_pages + t / a.page_size];
+    ok = page >= 0 && page < a.num_pages;
+    off = (int64_t)page * a.page_stride + (int64_t)g * a.head_stride + (int64_t)(t % a.page_size) * a.token_stride;
+  }
+  // query unit F of the group (head F / UPR, unit F % UPR) for F = 16 n + lane % 16
+  uint4 qraw[NG];
+  {
+    const uint4* qsrc = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q) +
+                                                       ((int64_t)b * a.q_heads + g * G) * a.head_dim);
+#pragma unroll
+    for (int n = 0; n < NG; ++n) qraw[n] = qsrc[16 * n + (lane & 15)];
+  }
+  const int64_t rb = ok ? off * 2 : -1;
+  const uint32_t rb_lo = (uint32_t)(uint64_t)rb, rb_hi = (uint32_t)((uint64_t)rb >> 32);
+  const char* kb = reinterpret_cast<const char*>(a.k);
+  constexpr int kRowsPerRead = 64 / UPR;
+  auto swz = [](int r) { return (r / (16 / UPR)) & (UPR - 1); };
+  uint4 v[UPR];
+#pragma unroll
+  for (int c = 0; c < UPR; ++c) {
+    const int r = c * kRowsPerRead + lane / UPR, p = lane % UPR;
+    const uint32_t lo = (uint32_t)__shfl((int)rb_lo, r), hi = (uint32_t)__shfl((int)rb_hi, r);
+    const int64_t src = (int64_t)(((uint64_t)hi << 32) | lo);
+    v[c] = *reinterpret_cast<const uint4*>(kb + (src >= 0 ? src + 16 * p : 0));
+  }
+#pragma unroll
+  for (int c = 0; c < UPR; ++c) {
+    const int r = c * kRowsPerRead + lane / UPR, p = lane % UPR;
+    s_rows[wid][r * UPR + (p ^ swz(r))] = v[c];
+  }
+  float qv[NG][8];
+#pragma unroll
+  for (int n = 0; n < NG; ++n) unpack_unit(qraw[n], qv[n]);
+  // a wave reads only the rows it staged: a wave-level barrier suffices
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const uint4* mine = &s_rows[wid][lane * UPR];
+  const int sw = swz(lane);
+  float acc[G];
+  // heads in fours
+  static_assert(G % 4 == 0, "the products run four heads at a time");
+  constexpr int GQ = G / 4;
+  float acc4[GQ][4];
+#pragma unroll
+  for (int c = 0; c < GQ; ++c)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc4[c][j] = 0.0f;
+  static_for<0, UPR>([&](auto uc) {
+    constexpr int u = decltype(uc)::value;
+    float kv[8];
+    unpack_unit(mine[u ^ sw], kv);
+    static_for<0, GQ>([&](auto cc) {
+      constexpr int c = decltype(cc)::value;
+      constexpr int j0 = 4 * c, j1 = j0 + 1, j2 = j0 + 2, j3 = j0 + 3;
+      constexpr int F0 = j0 * UPR + u, F1 = j1 * UPR + u, F2 = j2 * UPR + u, F3 = j3 * UPR + u;
+      fmac8x4_row_bcast<F0 % 16, F1 % 16, F2 % 16, F3 % 16>(acc4[c], qv[F0 / 16], qv[F1 / 16], qv[F2 / 16],
+                                                           qv[F3 / 16], kv);
+    });
+  });
+#pragma unroll
+  for (int j = 0; j < G; ++j) acc[j] = acc4[j / 4][j % 4];
+  const float s = ok ? group_score<G>(a, b, g, acc) : -__builtin_inff();
   if (in_row) row[t] = s;
   if (a.row_stats) note_minmax(a.row_stats + (int64_t)blockIdx.y * kStatStride, s, ok && __builtin_isfinite(s));
 }
@@ -963,6 +1110,30 @@ static hipError_t launch_exact_t(const ScoreArgs& a, hipStream_t st) {
   const int64_t es = (int64_t)sizeof(KT), rbytes = (int64_t)a.head_dim * es;
   const bool aligned = (reinterpret_cast<uintptr_t>(a.k) & 15) == 0 && (a.token_stride * es) % 16 == 0 &&
                        (a.page_stride * es) % 16 == 0 && (a.head_stride * es) % 16 == 0;
+  if constexpr (std::is_same<KT, uint16_t>::value) {
+    static const bool bcast = [] {
+      const char* e = getenv("SD_EXACT_BCAST");
+      return !(e && e[0] == '0');
+    }();
+    if (bcast && aligned && a.num_pages > 0 && (rbytes == 256 || rbytes == 128)) {
+      hipError_t e = hipErrorInvalidValue;
+      if (rbytes == 256) {
+        switch (G) {
+          case 4: score_exact_bcast_kernel<4, 16><<<grid, 256, 0, st>>>(a); e = hipSuccess; break;
+          case 8: score_exact_bcast_kernel<8, 16><<<grid, 256, 0, st>>>(a); e = hipSuccess; break;
+          default: break;
+        }
+      } else {
+        switch (G) {
+          case 4: score_exact_bcast_kernel<4, 8><<<grid, 256, 0, st>>>(a); e = hipSuccess; break;
+          case 8: score_exact_bcast_kernel<8, 8><<<grid, 256, 0, st>>>(a); e = hipSuccess; break;
+          case 16: score_exact_bcast_kernel<16, 8><<<grid, 256, 0, st>>>(a); e = hipSuccess; break;
+          default: break;
+        }
+      }
+      if (e == hipSuccess) return hipGetLastError();
+    }
+  }
   if (aligned && a.num_pages > 0 && rbytes == 256) return launch_exact_g<KT, 16>(a, grid, st);
   if (aligned && a.num_pages > 0 && rbytes == 128) return launch_exact_g<KT, 8>(a, grid, st);
   switch (G) {
