@@ -83,6 +83,43 @@ def test_exact_scores_bitwise(name):
     assert torch.all(bound == -1.0)
 
 
+# bf16 K with groups of 4, 8 and 16 heads and 64- or 128-dim rows: the
+# exact scorer that holds the query in registers (one variant per group and
+# row size), ragged lengths, page sizes below and above the 64-token tile
+GROUP_SHAPES = {
+    "g8_d128": dict(batch=3, q_heads=32, kv_heads=4, head_dim=128, kv_len=[3000, 64, 2049], topk=512),
+    "g4_d64_p16": dict(batch=2, q_heads=8, kv_heads=2, head_dim=64, kv_len=[1500, 777], topk=256, page_size=16),
+    "g8_d64": dict(batch=2, q_heads=16, kv_heads=2, head_dim=64, kv_len=[4096, 1], topk=128),
+    "g16_d64_p128": dict(batch=2, q_heads=32, kv_heads=2, head_dim=64, kv_len=[2500, 1300], topk=300,
+                         page_size=128),
+}
+
+
+@pytest.mark.parametrize("name", list(GROUP_SHAPES))
+def test_exact_scores_bitwise_head_groups(name):
+    w = synth.make_workload(3, **GROUP_SHAPES[name])
+    say(f"[scores] {name}")
+    # scores alone (a group of 16 heads has no attention path, so no fused step)
+    bt = api.to_device_array(w.block_table, "cuda")
+    kl = api.to_device_array(w.kv_lens, "cuda")
+    sk = api.to_device_array(w.score_k, "cuda")
+    sq = api.to_device_array(w.score_q, "cuda")
+    groups = w.score_k.shape[1]
+    scores = torch.empty((w.batch, groups, w.max_kv_len), dtype=torch.float32, device="cuda")
+    bound = torch.full((w.batch, groups), -1.0, device="cuda")
+    api.sparse_score_paged(api.pages(bt, kl, w.max_kv_len), api.pool(sk), sq, w.score_q.shape[1], None,
+                           api.MODES[w.mode], w.head_scale, api.EXACT, scores, bound)
+    torch.cuda.synchronize()
+    ref = oracle.score(w.block_table, w.kv_lens, w.score_k, w.score_q, w.head_weights, w.mode,
+                       w.head_scale, w.max_kv_len)
+    assert np.array_equal(scores.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+def test_fused_gqa_group_of_eight():
+    w = synth.make_workload(3, **GROUP_SHAPES["g8_d128"])
+    check_fused(w, api.EXACT, what="g8_d128")
+
+
 @pytest.mark.parametrize("kw", [dict(batch=2, kv_len=[9000, 4100]),
                                 dict(batch=2, kv_lens=[6000, 3000], bias_frac=0.01),
                                 dict(batch=2, kv_len=[3000, 1500], idx_heads=16, page_size=16),
