@@ -367,7 +367,7 @@ __device__ __forceinline__ void mla_static_for(F&& f) {
   }
 }
 
-template <int NW>
+template <int NW, bool QSTAGE>
 __global__ __launch_bounds__(NW * 64, 1) void attn_mla_kernel(AttnArgs a) {
   constexpr int KSTEPS = kMlaD / 16;  // 36
   __shared__ __attribute__((aligned(16))) uint4 s_kv[kMlaSplitRows * kMlaStride];
@@ -401,7 +401,42 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_mla_kernel(AttnArgs a) {
   // 16 s + 8 (l/32) .. +8)
   bf16x8 qf[KSTEPS];
   int64_t off_lo, off_hi;
-  {
+  if constexpr (QSTAGE) {
+    // The wave's 32 query rows are contiguous (36 KB): whole-row loads (lane
+    // l of load i: 16-byte unit 64 i + l), written to the LDS the latent rows
+    // take later, 73 units per row (one pad unit: the fragment reads of 16
+    // lanes, rows 73 units apart, then hit distinct banks), read back as
+    // fragments (head col, units 2 s + hf).  A fragment load straight from
+    // memory touches a different 32-byte piece of a different row in every
+    // lane pair; these loads cover 1 KB each.
+    constexpr int kQRowUnits = kMlaUnits + 1;  // 73
+    static_assert(NW * 32 * kQRowUnits <= kMlaSplitRows * kMlaStride, "the query staging fits the row buffer");
+    const int i0 = r0 + lane, i1 = r0 + 64 + lane;
+    const int t0 = i0 < r1 ? sel[i0] : -1;
+    const int t1 = i1 < r1 ? sel[i1] : -1;
+    const uint4* qw = reinterpret_cast<const uint4*>(qrow0 + (int64_t)head0 * kMlaD * 2);
+    uint4 qraw[KSTEPS];
+#pragma unroll
+    for (int i = 0; i < KSTEPS; ++i) qraw[i] = qw[64 * i + lane];
+    const int64_t e0 = sel_row(a, bt, L, t0, 0, a.k_page_stride, a.k_head_stride, a.k_token_stride, a.k_num_pages);
+    const int64_t e1 = sel_row(a, bt, L, t1, 0, a.k_page_stride, a.k_head_stride, a.k_token_stride, a.k_num_pages);
+    off_lo = e0 < 0 ? -1 : e0 * 2;
+    off_hi = e1 < 0 ? -1 : e1 * 2;
+    uint4* qs = s_kv + wid * 32 * kQRowUnits;
+#pragma unroll
+    for (int i = 0; i < KSTEPS; ++i) {
+      const int u = 64 * i + lane;
+      qs[(u / kMlaUnits) * kQRowUnits + u % kMlaUnits] = qraw[i];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) qf[s] = __builtin_bit_cast(bf16x8, qs[col * kQRowUnits + 2 * s + hf]);
+    // every wave holds its fragments before any DMA overwrites the staging
+    // (no DMA is in flight yet, so this barrier drains nothing)
+    __syncthreads();
+  } else {
     const int i0 = r0 + lane, i1 = r0 + 64 + lane;
     const int t0 = i0 < r1 ? sel[i0] : -1;
     const int t1 = i1 < r1 ? sel[i1] : -1;
@@ -767,10 +802,17 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
     if (a.chunk != kMlaSplitRows || a.splits > kMlaMaxSplits) return hipErrorInvalidValue;
     dim3 grid(a.splits * a.batch);
     const int nw = a.q_heads / 32;
-    switch (nw) {
-      case 1: attn_mla_kernel<1><<<grid, 64, 0, st>>>(a); break;
-      case 2: attn_mla_kernel<2><<<grid, 128, 0, st>>>(a); break;
-      case 4: attn_mla_kernel<4><<<grid, 256, 0, st>>>(a); break;
+    static const int qstage = [] {
+      const char* e = getenv("SD_MLA_QSTAGE");
+      return e && e[0] == '0' ? 0 : 1;
+    }();
+    switch (nw * 2 + qstage) {
+      case 2: attn_mla_kernel<1, false><<<grid, 64, 0, st>>>(a); break;
+      case 4: attn_mla_kernel<2, false><<<grid, 128, 0, st>>>(a); break;
+      case 8: attn_mla_kernel<4, false><<<grid, 256, 0, st>>>(a); break;
+      case 3: attn_mla_kernel<1, true><<<grid, 64, 0, st>>>(a); break;
+      case 5: attn_mla_kernel<2, true><<<grid, 128, 0, st>>>(a); break;
+      case 9: attn_mla_kernel<4, true><<<grid, 256, 0, st>>>(a); break;
       default: return hipErrorInvalidValue;
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
