@@ -605,8 +605,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_mla_kernel(AttnArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // partials in register order, bf16: part_o[((b*splits+split)*NW + w)][n][lane][16]
-    // (n < 8: dv 0..255, n >= 8: dv 256..511)
+    // partials in register order, bf16: part_o[((b*splits+split)*NW + w)][n][h][lane][8]:
+    // lane l's 16 values of tile n as two halves h of 8 (n < 8: dv 0..255, n >= 8: dv
+    // 256..511), so that each store instruction writes 1 KB in one piece
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
       u32x4 w0, w1;
@@ -615,9 +616,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_mla_kernel(AttnArgs a) {
         w0[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector((float2v){acc[n][2 * e], acc[n][2 * e + 1]}, bf16x2));
         w1[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector((float2v){acc[n][8 + 2 * e], acc[n][8 + 2 * e + 1]}, bf16x2));
       }
-      uint4* dst = reinterpret_cast<uint4*>(po + ((int64_t)(8 * half + n) * 64 + lane) * 16);
+      uint4* dst = reinterpret_cast<uint4*>(po + ((int64_t)(8 * half + n) * 128 + lane) * 8);
       dst[0] = make_uint4(w0[0], w0[1], w0[2], w0[3]);
-      dst[1] = make_uint4(w1[0], w1[1], w1[2], w1[3]);
+      dst[64] = make_uint4(w1[0], w1[1], w1[2], w1[3]);
     }
   }
   // m / l per head: part_ml[(b*splits+split)*q_heads + h][2]
@@ -654,13 +655,14 @@ __global__ __launch_bounds__(512) void attn_mla_combine_kernel(AttnArgs a, int n
   const int col = lane & 31, hf = lane >> 5;
   const int S = a.splits;
   const int tile = 4 * quarter + n;  // N tile of the partial layout (0..15)
-  const uint16_t* pbase = reinterpret_cast<const uint16_t*>(a.part_o) + (((int64_t)w * 16 + tile) * 64 + lane) * 16;
+  const uint16_t* pbase =
+      reinterpret_cast<const uint16_t*>(a.part_o) + ((((int64_t)w * 16 + tile) * 2 + jh) * 64 + lane) * 8;
   const int64_t sstride = (int64_t)nw * 16 * 64 * 16;  // one split's partial, in elements
   // ---- this thread's partials of the first 16 splits, requested first
   uint4 q[16];
 #pragma unroll
   for (int u = 0; u < 16; ++u)
-    if (u < S) q[u] = reinterpret_cast<const uint4*>(pbase + ((int64_t)b * S + u) * sstride)[jh];
+    if (u < S) q[u] = *reinterpret_cast<const uint4*>(pbase + ((int64_t)b * S + u) * sstride);
   // ---- m and l of (split, head), all loads at once
   for (int i = tid; i < S * 32; i += 512) {
     const int sp = i >> 5, h = i & 31;
@@ -691,7 +693,7 @@ __global__ __launch_bounds__(512) void attn_mla_combine_kernel(AttnArgs a, int n
     if (s0 > 0) {
 #pragma unroll
       for (int u = 0; u < 16; ++u)
-        if (s0 + u < S) q[u] = reinterpret_cast<const uint4*>(pbase + ((int64_t)b * S + s0 + u) * sstride)[jh];
+        if (s0 + u < S) q[u] = *reinterpret_cast<const uint4*>(pbase + ((int64_t)b * S + s0 + u) * sstride);
     }
 #pragma unroll
     for (int u = 0; u < 16; ++u)
