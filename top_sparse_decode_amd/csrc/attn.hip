@@ -643,7 +643,7 @@ constexpr int kMlaMaxSplits = 64;
 __global__ __launch_bounds__(512) void attn_mla_combine_kernel(AttnArgs a, int nw) {
   __shared__ float s_m[kMlaMaxSplits][32], s_l[kMlaMaxSplits][32];
   __shared__ float s_w[kMlaMaxSplits][32];   // weight of split s for head 32w + h
-  __shared__ float s_out[32][128 + 4];       // [head][dv in the quarter], padded
+  __shared__ __attribute__((aligned(16))) float s_out[32][128 + 4];  // [head][dv in the quarter], padded
   const int tid = threadIdx.x;
   const int lane = tid & 63, n = tid >> 7;  // tile within the quarter: 0..3
   const int jh = (tid >> 6) & 1;            // which eight of the lane's 16 values
@@ -714,13 +714,32 @@ __global__ __launch_bounds__(512) void attn_mla_combine_kernel(AttnArgs a, int n
     s_out[8 * (rr / 4) + 4 * hf + (rr % 4)][32 * n + col] = o[r];
   }
   __syncthreads();
-  for (int i = tid; i < 32 * 128; i += 512) {
-    const int h = i / 128, d = i % 128;
-    const int64_t oi = ((int64_t)b * a.q_heads + 32 * w + h) * kMlaDv + 128 * quarter + d;
-    if (a.out_dtype == 0)
-      reinterpret_cast<float*>(a.out)[oi] = s_out[h][d];
-    else
-      reinterpret_cast<uint16_t*>(a.out)[oi] = f32_to_bf16(s_out[h][d]);
+  if ((reinterpret_cast<uintptr_t>(a.out) & 15) == 0) {
+    // eight consecutive values per thread: one 16-byte store (bf16) or two (fp32)
+    const int h = tid >> 4, d0 = 8 * (tid & 15);
+    const int64_t oi = ((int64_t)b * a.q_heads + 32 * w + h) * kMlaDv + 128 * quarter + d0;
+    const float4 v0 = *reinterpret_cast<const float4*>(&s_out[h][d0]);
+    const float4 v1 = *reinterpret_cast<const float4*>(&s_out[h][d0 + 4]);
+    if (a.out_dtype == 0) {
+      float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + oi);
+      dst[0] = v0;
+      dst[1] = v1;
+    } else {
+      const uint32_t p0 = f32_to_bf16(v0.x) | ((uint32_t)f32_to_bf16(v0.y) << 16);
+      const uint32_t p1 = f32_to_bf16(v0.z) | ((uint32_t)f32_to_bf16(v0.w) << 16);
+      const uint32_t p2 = f32_to_bf16(v1.x) | ((uint32_t)f32_to_bf16(v1.y) << 16);
+      const uint32_t p3 = f32_to_bf16(v1.z) | ((uint32_t)f32_to_bf16(v1.w) << 16);
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.out) + oi) = make_uint4(p0, p1, p2, p3);
+    }
+  } else {
+    for (int i = tid; i < 32 * 128; i += 512) {
+      const int h = i / 128, d = i % 128;
+      const int64_t oi = ((int64_t)b * a.q_heads + 32 * w + h) * kMlaDv + 128 * quarter + d;
+      if (a.out_dtype == 0)
+        reinterpret_cast<float*>(a.out)[oi] = s_out[h][d];
+      else
+        reinterpret_cast<uint16_t*>(a.out)[oi] = f32_to_bf16(s_out[h][d]);
+    }
   }
 }
 
