@@ -658,13 +658,23 @@ __global__ __launch_bounds__(512) void attn_mla_combine_kernel(AttnArgs a, int n
   const uint16_t* pbase =
       reinterpret_cast<const uint16_t*>(a.part_o) + ((((int64_t)w * 16 + tile) * 2 + jh) * 64 + lane) * 8;
   const int64_t sstride = (int64_t)nw * 16 * 64 * 16;  // one split's partial, in elements
-  // ---- this thread's partials of the first 16 splits, requested first
+  // ---- m and l of (split, head) for the first 16 splits (one pair per
+  // thread), then this thread's partials of those splits: the pairs land
+  // first, so the split weights are formed while the partials are in flight
+  float2 ml0 = make_float2(0.0f, 0.0f);
+  if (tid < S * 32) {
+    const int sp = tid >> 5, h = tid & 31;
+    ml0 = *reinterpret_cast<const float2*>(a.part_ml + (((int64_t)b * S + sp) * a.q_heads + 32 * w + h) * 2);
+  }
   uint4 q[16];
 #pragma unroll
-  for (int u = 0; u < 16; ++u)
-    if (u < S) q[u] = *reinterpret_cast<const uint4*>(pbase + ((int64_t)b * S + u) * sstride);
-  // ---- m and l of (split, head), all loads at once
-  for (int i = tid; i < S * 32; i += 512) {
+  for (int u = 0; u < 16; ++u)  // (branch-free: fewer splits re-read the last)
+    q[u] = *reinterpret_cast<const uint4*>(pbase + ((int64_t)b * S + min(u, S - 1)) * sstride);
+  if (tid < S * 32) {
+    s_m[tid >> 5][tid & 31] = ml0.x;
+    s_l[tid >> 5][tid & 31] = ml0.y;
+  }
+  for (int i = tid + 512; i < S * 32; i += 512) {  // more than 16 splits
     const int sp = i >> 5, h = i & 31;
     const float* ml = a.part_ml + (((int64_t)b * S + sp) * a.q_heads + 32 * w + h) * 2;
     s_m[sp][h] = ml[0];
