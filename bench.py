@@ -154,7 +154,7 @@ def bench_triattention(args, api, torch, dev):
 
 
 def bench_blocks(args, api, torch, dev, synth, np):
-    """Sparse MLA attention over block-granular selections: the config-4
+    """Sparse MLA attention over block-granular selections: the 64K-context DSA-MLA
     latent cache (16 requests, 64K tokens), 128 distinct random 16-token
     blocks per request (2048 tokens), against the same tokens given as a
     token list."""
@@ -196,7 +196,7 @@ def bench_blocks(args, api, torch, dev, synth, np):
         "metric": "block-granular sparse MLA attention calls/s",
         "value": round(1000.0 / ms_b, 2), "unit": "calls/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_b, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (config-4 latent pool, seeded random blocks)",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (64K-context DSA-MLA latent pool, seeded random blocks)",
         "config": {"workload": "sparse MLA 128 heads x 576/512 over 128 blocks of 16 tokens per request, "
                                "16 requests at 64K", "batch": B, "k_blocks": kb, "block_size": bs},
         "token_list_ms": round(ms_t, 5),
@@ -264,7 +264,7 @@ def bench_gqa(args, api, torch, dev, synth):
 def bench_mixed(args, api, torch, dev, synth):
     """The fused step on the mixed-length DSA sparse-MLA workload: 64
     requests with kv_len uniform in [4096, 131072] over one fragmented page
-    pool (about 4M cached tokens), the config-4 indexer and latent cache,
+    pool (about 4M cached tokens), the 64K-context DSA-MLA indexer and latent cache,
     top-k 2048.  One replica (7 GB of pools: nothing stays in the last-level
     cache between steps).  The roofline entry is the fast indexer scorer."""
     say("[bench] generating dsa_mixed workload (B64, L ~ U[4096, 131072]) ...")

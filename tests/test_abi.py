@@ -224,7 +224,7 @@ def test_fused_workspace_and_validation():
 
 
 def test_noalloc_rejects_calls_beyond_its_scratch():
-    # host-side checks only: nothing reaches a device.  Config-5 sizes (64
+    # host-side checks only: nothing reaches a device.  Mixed-length DSA-MLA sizes (64
     # requests up to 131072 tokens) need more scratch than the library holds.
     lib = _lib()
     cap = lib.sd_sparse_decode_noalloc_max_bytes()

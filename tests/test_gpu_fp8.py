@@ -160,12 +160,12 @@ def test_fp8_band_overflow_falls_back_exactly():
 
 def test_fp8_full_dsa_all_requests():
     w = synth.make_workload(4, index_dtype="fp8")
-    say("[fp8 config 4, all requests]")
+    say("[fp8 DSA-MLA 16 x 64K, all requests]")
     step = api.prepare(w, precision=api.FAST)
     step.run()
     torch.cuda.synchronize()
     ref = oracle_run(w)
     assert np.array_equal(step.indices.cpu().numpy(), ref["indices"])
     assert np.array_equal(step.counts.cpu().numpy(), ref["counts"])
-    worst = assert_outputs_close(out_to_numpy(step.out), ref["out"], w.out_dtype, "fp8 config 4")
-    say(f"fp8 config 4: worst row rel-L2 {worst:.3e}")
+    worst = assert_outputs_close(out_to_numpy(step.out), ref["out"], w.out_dtype, "fp8 DSA-MLA 16 x 64K")
+    say(f"fp8 DSA-MLA 16 x 64K: worst row rel-L2 {worst:.3e}")

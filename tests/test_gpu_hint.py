@@ -120,5 +120,5 @@ def test_full_dsa_with_hint_all_requests():
     torch.cuda.synchronize()
     ref = oracle_run(w)
     assert np.array_equal(step.indices.cpu().numpy(), ref["indices"])
-    assert_outputs_close(out_to_numpy(step.out), ref["out"], w.out_dtype, "config 4 hinted")
+    assert_outputs_close(out_to_numpy(step.out), ref["out"], w.out_dtype, "DSA-MLA 16 x 64K hinted")
     assert torch.equal(step.hint, step.indices)

@@ -60,6 +60,6 @@ def test_mq_with_hint_writeback():
 
 def test_mq_full_dsa_all_requests():
     w = synth.make_workload(4, next_n=2)
-    worst, step = check(w, api.FAST, what="config 4 next_n 2 (all requests)")
-    say(f"config 4 next_n 2: worst row rel-L2 {worst:.3e}")
+    worst, step = check(w, api.FAST, what="DSA-MLA 16 x 64K next_n 2 (all requests)")
+    say(f"DSA-MLA 16 x 64K next_n 2: worst row rel-L2 {worst:.3e}")
     assert torch.isfinite(step.out.float()).all()

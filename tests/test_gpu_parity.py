@@ -332,15 +332,15 @@ def dsa_mixed_full():
 
 
 def test_full_dsa_all_requests(dsa_full):
-    worst, step = check_fused(dsa_full, api.FAST, what="config 4 (all 16 requests)")
-    say(f"config 4: worst row rel-L2 {worst:.3e}")
+    worst, step = check_fused(dsa_full, api.FAST, what="DSA-MLA 16 x 64K (all 16 requests)")
+    say(f"DSA-MLA 16 x 64K: worst row rel-L2 {worst:.3e}")
     assert torch.isfinite(step.out.float()).all()
 
 
 def test_full_dsa_mixed_all_requests(dsa_mixed_full):
     w = dsa_mixed_full
-    worst, step = check_fused(w, api.FAST, what="config 5 (all 64 requests)")
-    say(f"config 5: worst row rel-L2 {worst:.3e}, lengths {int(w.kv_lens.min())}..{int(w.kv_lens.max())}")
+    worst, step = check_fused(w, api.FAST, what="mixed-length DSA-MLA (all 64 requests)")
+    say(f"mixed-length DSA-MLA: worst row rel-L2 {worst:.3e}, lengths {int(w.kv_lens.min())}..{int(w.kv_lens.max())}")
     assert torch.isfinite(step.out.float()).all()
 
 

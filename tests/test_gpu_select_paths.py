@@ -85,7 +85,7 @@ def test_standalone_selection_shapes(name):
 @pytest.mark.parametrize("name", list(SHAPES))
 @pytest.mark.parametrize("index_dtype", ["bf16", "fp8"])
 def test_fused_step_selection_shapes(name, index_dtype):
-    # config-4 shapes with fast scores: the band re-score inside the one launch
+    # DSA-MLA shapes (64K rows, top-k 2048) with fast scores: the band re-score inside the one launch
     w = synth.make_workload(4, batch=4, kv_len=[65536, 40000, 9000, 2047], topk=2048, index_dtype=index_dtype)
     ref = oracle_run(w)
     for hint in (False, True):

@@ -37,7 +37,7 @@ def both(w, precision):
 def test_noalloc_matches_workspace_entry_point(precision):
     cap = api.sparse_decode_noalloc_max_bytes()
     cases = [
-        # config-4 shapes (8 requests of 64K), then a smaller call
+        # DSA-MLA shapes (8 requests of 64K), then a smaller call
         synth.make_workload(4, batch=8, kv_len=[65536, 40000, 65536, 9000, 30000, 65536, 2047, 50000]),
         synth.make_workload(4, batch=3, kv_len=[5000, 100, 4100], topk=512, idx_heads=32, heads=64),
     ]
